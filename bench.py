@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of the selective scan on one MI355X.
+
+A step is one ss_scan_fwd call (every step of the scan: B/C re-layout, Delta,
+Abar, state recurrence, readout, skip, gate, final state) over one batch of the
+2.8B-shaped layer workload: batch 8, D = 5120, N = 16, L = 2048, bf16 I/O with
+an fp32 state.  Inputs are generated on the device before timing and stay
+resident in HBM.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--decode] [--copy-calib BYTES]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "selective-scan Gtok·ch/s + achieved HBM GB/s (% roofline), 2.8B-shape L=2048"
+
+# MI355X published peaks and the derived VALU issue rate
+HBM_PEAK_GBS = 8000.0
+CUS, SIMDS_PER_CU, LANES_PER_SIMD_CLK, CLOCK_GHZ = 256, 4, 16, 2.4
+VALU_PEAK_TOPS = CUS * SIMDS_PER_CU * LANES_PER_SIMD_CLK * CLOCK_GHZ / 1000.0   # 39.32 T lane-slots/s
+TRANS_SLOTS = 2   # transcendentals issue at half rate on gfx950 and do not co-issue with FMAs
+
+KERNEL_SOURCES = ["selective_state_space_62_amd/csrc/scan_fwd.hip",
+                  "selective_state_space_62_amd/csrc/device_common.h"]
+COUNTERS_FILE = ROOT / "profiles" / "scan_2.8b_bf16_counters.json"
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update((ROOT / f).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes_per_tokch(cfg) -> float:
+    """HBM bytes per (token, channel) that the method must move: x, dt, z read once,
+    y written once; B and C read once per (batch, token); A, Dskip, dt_bias once;
+    the final state once."""
+    eb = 4 if cfg.io == "f32" else 2
+    per = 4 * eb
+    shared = (2 * cfg.batch * cfg.dstate * cfg.seqlen * eb + cfg.dim * (cfg.dstate + 2) * 4
+              + cfg.batch * cfg.dim * cfg.dstate * 4)
+    return per + shared / cfg.tokch
+
+
+def algorithmic_slots_per_tokch(N: int) -> float:
+    """VALU issue slots per (token, channel): per state component a multiply for
+    Delta*A, the exponential, a multiply for Delta*x*B, the state FMA and the
+    readout FMA (4 ops + 1 transcendental); per (token, channel) 8 more ops and 4
+    transcendentals (softplus: exp, log; silu: exp, reciprocal).  A
+    transcendental costs TRANS_SLOTS slots."""
+    return 4 * N + 8 + TRANS_SLOTS * (N + 4)
+
+
+def cpu_baseline(cfg, budget_s: float):
+    """The oracle (as it stands) on host cores over whole batch rows of the workload,
+    row by row until ~budget_s of oracle time; inputs drawn on the host, untimed."""
+    import numpy as np
+    import oracle
+    from workloads import inputs
+    o = oracle.default()
+    A, dskip, bias = inputs.params(cfg)
+    tokch = 0
+    spent = 0.0
+    rows = 0
+    chans_per_call = 1024
+    for b in range(cfg.batch):
+        for d0 in range(0, cfg.dim, chans_per_call):
+            ch = [(b, d) for d in range(d0, min(cfg.dim, d0 + chans_per_call))]
+            sub = inputs.scan_inputs(cfg, channels=ch)
+            f = {k: inputs.raw_to_f64(v, cfg.io) for k, v in sub.items()}
+            idx = np.array([d for _, d in ch])
+            t0 = time.perf_counter()
+            o.scan(f["x"][None], f["dt"][None], f["B"][b:b + 1], f["C"][b:b + 1], A[idx], z=f["z"][None],
+                   Dskip=dskip[idx], dt_bias=bias[idx])
+            spent += time.perf_counter() - t0
+            tokch += len(ch) * cfg.seqlen
+            if spent >= budget_s:
+                break
+        rows += 1
+        if spent >= budget_s:
+            break
+    return {"value": tokch / spent / 1e9, "unit": "Gtok·ch/s", "cores": o.max_threads(), "kind": "oracle",
+            "sample": "%d channels x L=%d of the %s workload (%.1f s of oracle time, float64)"
+                      % (tokch // cfg.seqlen, cfg.seqlen, cfg.name, spent)}
+
+
+def measured_traffic(cfg):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None if
+    the kernel sources changed since the counters were taken."""
+    try:
+        d = json.loads(COUNTERS_FILE.read_text())
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_hash") != kernel_hash() or d.get("workload") != cfg.name:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def run_decode(ss, torch, dev, steps, warmup):
+    """Decode step timing (secondary): 128-step trajectory of the decode workload,
+    warm (back to back, state may stay in the 256 MB MALL) and cold (a 1 GB buffer
+    written between steps)."""
+    from workloads import DECODE
+    from workloads import device as wdev
+    cfg = DECODE
+    A, dskip, bias = wdev.params(cfg, dev)
+    state = wdev.decode_state0(cfg, dev)
+    t = wdev.decode_inputs(cfg, 0, dev)
+    args = (t["x"], t["dt"], t["B"], t["C"], A)
+    kw = dict(z=t["z"], Dskip=dskip, dt_bias=bias)
+    for _ in range(warmup):
+        ss.state_update(state, *args, **kw)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        ss.state_update(state, *args, **kw)
+    e1.record()
+    torch.cuda.synchronize()
+    warm_ms = e0.elapsed_time(e1) / steps
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cold = 0.0
+    for _ in range(steps):
+        flush.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        ss.state_update(state, *args, **kw)
+        b.record()
+        torch.cuda.synchronize()
+        cold += a.elapsed_time(b)
+    cold_ms = cold / steps
+    nbd = cfg.batch * cfg.dim
+    bytes_step = nbd * (2 * cfg.dstate * 4 + 4 * 2) + 2 * cfg.batch * cfg.dstate * 2 + cfg.dim * (cfg.dstate + 2) * 4
+    return {"workload": cfg.name, "bd_per_step": nbd, "ms_per_step_cold": round(cold_ms, 5),
+            "ms_per_step_warm": round(warm_ms, 5), "hbm_gbs_cold": round(bytes_step / cold_ms / 1e6, 1),
+            "frac_hbm_cold": round(bytes_step / cold_ms / 1e6 / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes_per_step": bytes_step}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="2.8b-layer-bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--decode", action="store_true", help="also time the decode step")
+    ap.add_argument("--copy-calib", type=int, default=0, help="only run a plain copy of this many bytes")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the selective scan is built and measured on a single MI355X; "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import selective_state_space_62_amd as ss
+    from workloads import BY_NAME
+    from workloads import device as wdev
+
+    dev = torch.device("cuda:0")
+    if args.copy_calib:
+        src = torch.ones(args.copy_calib // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes": args.copy_calib}))
+        return
+
+    cfg = BY_NAME[args.workload]
+    assert cfg.mode == "scan"
+    io = ss.SS_BF16 if cfg.io == "bf16" else ss.SS_F32
+    t = wdev.scan_inputs(cfg, dev)
+    A, dskip, bias = wdev.params(cfg, dev)
+    plan = ss.ss_scan_fwd_plan(cfg.batch, cfg.dim, cfg.dstate, cfg.seqlen, io)
+    ws = torch.empty(ss.workspace_bytes(cfg.batch, cfg.dim, cfg.dstate, cfg.seqlen, t["x"].dtype), dtype=torch.uint8,
+                     device=dev)
+    y = torch.empty_like(t["x"])
+    hf = torch.empty((cfg.batch, cfg.dim, cfg.dstate), dtype=torch.float32, device=dev)
+
+    def step():
+        ss.scan_fwd(t["x"], t["dt"], t["B"], t["C"], A, z=t["z"], Dskip=dskip, dt_bias=bias, workspace=ws, y=y,
+                    h_final=hf)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ss.ss_timing_reset()
+    ss.ss_timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ss.ss_timing_enable(False)
+    kern_ms_total, calls = ss.ss_timing_read()
+    ss.ss_timing_reset()
+    assert calls == args.steps
+    ms_step = elapsed * 1e3 / args.steps
+    kern_ms = kern_ms_total / calls
+    tokch = cfg.tokch
+    value = tokch / (ms_step * 1e-3) / 1e9
+    bpt = algorithmic_bytes_per_tokch(cfg)
+    spt = algorithmic_slots_per_tokch(cfg.dstate)
+    achieved_slots = spt * tokch / (kern_ms * 1e-3) / 1e12
+    achieved_gbs = bpt * tokch / (kern_ms * 1e-3) / 1e9
+    traffic = measured_traffic(cfg)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "Gtok·ch/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.io == "bf16" else "f32",
+        "data": "synthetic (seeded Philox4x32-10 draws through an inverse-normal table, generated on the device)",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "channels": cfg.dim, "dstate": cfg.dstate,
+                   "seq_len": cfg.seqlen, "io": cfg.io, "state": "f32", "plan": {"state_groups": plan[0],
+                   "chunk_len": plan[1]}},
+        "hbm_gbs": round(bpt * tokch / (ms_step * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "alu", "achieved": round(achieved_slots, 3), "peak": round(VALU_PEAK_TOPS, 3),
+                     "unit": "T VALU-slot/s", "frac": round(achieved_slots / VALU_PEAK_TOPS, 4),
+                     "traffic": traffic, "kernel": "scan_kernel<16,4,bf16>", "kernel_ms": round(kern_ms, 5),
+                     "slots_per_tokch": spt},
+        "roofline_hbm": {"achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "bytes_per_tokch": round(bpt, 4)},
+    }
+    if args.decode:
+        out["decode"] = run_decode(ss, torch, dev, 20, 3)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,136 @@
+/*
+ * ssscan.h — C ABI of the MI355X (gfx950) selective state-space (S6) scan library.
+ *
+ * What the library computes.  For every batch row b and channel d, with an
+ * N-wide fp32 state h (N = dstate):
+ *
+ *     Delta_t = softplus(dt[b,d,t] + dt_bias[d])
+ *     Abar_tn = exp(Delta_t * A[d,n])
+ *     h_tn    = Abar_tn * h_(t-1)n + Delta_t * B[b,n,t] * x[b,d,t]
+ *     y[b,d,t] = (sum_n C[b,n,t] * h_tn + Dskip[d] * x[b,d,t]) * silu(z[b,d,t])
+ *
+ * Sources: the reader's notes on the Mamba paper (kurisu.si), section "What they
+ * did", item "Selective SSM (S6)" — Delta, B, C are computed from the input,
+ * Delta through a softplus of a parameter plus a projection, A is a fixed
+ * parameter entering as Abar = exp(Delta A), and the time-varying system is
+ * evaluated as a recurrent scan whose expanded state never leaves on-chip
+ * memory; same notes, "Architecture" — the state holds D x N numbers per
+ * sequence; the tellworld.net summary, section "Architecture" — training runs the
+ * recurrence over the whole sequence, generation needs one state update per
+ * token.  The input term uses the first-order discretisation Bbar = Delta * B
+ * (the pages give only Abar); the skip term Dskip and the silu gate (the gated
+ * branch of the Mamba block, "Architecture" in the notes) multiply the whole sum.
+ * silu(z) = z / (1 + exp(-z)).
+ *
+ * Layouts (row-major, last index fastest, all tensors contiguous):
+ *     x, dt, z, y     (batch, dim, seqlen)    io dtype         decode: (batch, dim)
+ *     B, C            (batch, dstate, seqlen) io dtype         decode: (batch, dstate)
+ *     A               (dim, dstate)           fp32
+ *     Dskip, dt_bias  (dim)                   fp32, NULL means all zeros
+ *     h0, h_final     (batch, dim, dstate)    fp32, NULL h0 means a zero state
+ *     state (decode)  (batch, dim, dstate)    fp32, updated in place
+ * io dtype is SS_F32 (IEEE binary32) or SS_BF16 (bfloat16; y is rounded to
+ * nearest-even).  The state and all internal arithmetic are fp32.
+ *
+ * Ownership and memory.  Every pointer is a device pointer owned by the caller
+ * (e.g. a PyTorch tensor's data_ptr()); tensor base addresses must be 16-byte
+ * aligned.  The library never allocates device memory: the scan's scratch space
+ * is the caller's `workspace`, of at least ss_scan_fwd_workspace_bytes() bytes,
+ * 256-byte aligned.  y must not overlap any input.  Inputs are read-only.
+ *
+ * Streams and synchronisation.  All work is enqueued on `stream` (a hipStream_t;
+ * NULL = the default stream) and the calls return without waiting.  Calls that
+ * share a workspace, y, state or h_final must be ordered on one stream.  The
+ * library keeps no state between calls apart from the opt-in timing record
+ * (ss_timing_*), and is safe to call from several host threads.
+ *
+ * Errors.  Every entry point returns an ss_status.  Arguments are validated on
+ * the host before anything is launched; on a non-OK return nothing was enqueued
+ * (except SS_ERR_HIP, reported when a launch itself fails, after which earlier
+ * launches of the same call may have been enqueued).  ss_last_error() returns a
+ * per-thread message describing the last non-OK status.  A fault inside a
+ * kernel surfaces at the caller's next synchronisation, as for any HIP kernel.
+ * No C++ exception crosses this interface and nothing aborts.
+ */
+#ifndef SSSCAN_H
+#define SSSCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SS_ABI_VERSION 1
+
+typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
+
+typedef enum {
+  SS_OK = 0,
+  SS_ERR_INVALID_ARG = 1,   /* NULL required pointer, negative/zero size, misalignment, overlap */
+  SS_ERR_UNSUPPORTED = 2,   /* dstate not in {1, 2, 4, 8, 16}, or an unknown dtype / plan */
+  SS_ERR_WORKSPACE = 3,     /* workspace missing, misaligned or smaller than required */
+  SS_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+} ss_status;
+
+/* Plan of one scan call: how the work is laid onto the GPU.
+ *   state_groups: waves per workgroup; each wave owns dstate/state_groups state
+ *                 components of 64 channels (1, 2 or 4; at most dstate).
+ *   chunk_len:    tokens per sequence chunk; chunk_len >= seqlen means one chunk.
+ *                 Chunks are scanned in parallel and joined by an exclusive scan
+ *                 of their (decay, end state) pairs, then rescanned from their
+ *                 true initial states.  A multiple of the plan's tile length. */
+typedef struct {
+  int32_t state_groups;
+  int32_t reserved;
+  int64_t chunk_len;
+} ss_scan_plan;
+
+/* The plan ss_scan_fwd chooses for this shape on the current device. */
+ss_status ss_scan_fwd_plan(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io,
+                           ss_scan_plan* plan_out);
+
+/* Bytes of workspace the scan needs for this shape under `plan` (NULL = the
+ * automatic plan).  Returns 0 when the arguments are invalid. */
+size_t ss_scan_fwd_workspace_bytes(int64_t batch, int64_t dim, int dstate, int64_t seqlen,
+                                   ss_dtype io, const ss_scan_plan* plan);
+
+/* Full-sequence selective scan.  Writes y (batch, dim, seqlen) and, when
+ * h_final is non-NULL, the state after the last token (batch, dim, dstate).
+ * z == NULL means no gate.  plan == NULL uses ss_scan_fwd_plan()'s choice. */
+ss_status ss_scan_fwd(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io,
+                      const void* x, const void* dt, const void* z,
+                      const void* B, const void* C, const float* A,
+                      const float* Dskip, const float* dt_bias, const float* h0,
+                      void* y, float* h_final,
+                      void* workspace, size_t workspace_bytes,
+                      const ss_scan_plan* plan, void* stream);
+
+/* One autoregressive decode step: for each (b, d), advance `state` by one token
+ * with the same update as the scan and write y (batch, dim).  z == NULL means no
+ * gate.  Needs no workspace. */
+ss_status ss_state_update(int64_t batch, int64_t dim, int dstate, ss_dtype io, float* state,
+                          const void* x, const void* dt, const void* z,
+                          const void* B, const void* C, const float* A,
+                          const float* Dskip, const float* dt_bias,
+                          void* y, void* stream);
+
+/* Opt-in timing of the main scan kernel (for benchmarks).  While enabled, each
+ * ss_scan_fwd call records HIP events around its scan kernel launches on its
+ * stream.  ss_timing_read synchronises on the recorded events and returns the
+ * summed kernel time in milliseconds and the number of calls recorded since the
+ * last ss_timing_reset. */
+ss_status ss_timing_enable(int enable);
+ss_status ss_timing_reset(void);
+ss_status ss_timing_read(double* total_ms, int64_t* calls);
+
+const char* ss_status_string(ss_status status);
+const char* ss_last_error(void);
+int ss_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSSCAN_H */

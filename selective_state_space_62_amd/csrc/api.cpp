@@ -1,0 +1,437 @@
+// C ABI of the selective-scan library: argument validation, planning, launches,
+// error reporting and the opt-in kernel timing record.  See include/ssscan.h.
+#include "ssscan.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ss_status fail(ss_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+ss_status hip_fail(hipError_t e, const char* what) {
+  return fail(SS_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool valid_dstate(int n) { return n == 1 || n == 2 || n == 4 || n == 8 || n == 16; }
+
+int elem_bytes(ss_dtype io) { return io == SS_BF16 ? 2 : 4; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Range {
+  const char* name;
+  uintptr_t lo, hi;   // [lo, hi)
+};
+
+Range rng(const char* name, const void* p, int64_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{name, lo, p ? lo + (uintptr_t)bytes : lo};
+}
+
+bool overlap(const Range& a, const Range& b) {
+  if (a.lo == a.hi || b.lo == b.hi) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+// Device properties are queried once per device.
+int device_cus() {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
+
+constexpr int64_t kMaxDim = int64_t(1) << 40;
+
+ss_status check_sizes(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io) {
+  if (io != SS_F32 && io != SS_BF16) return fail(SS_ERR_UNSUPPORTED, "io dtype %d is not SS_F32 or SS_BF16", (int)io);
+  if (!valid_dstate(dstate)) return fail(SS_ERR_UNSUPPORTED, "dstate %d is not one of 1, 2, 4, 8, 16", dstate);
+  if (batch < 1 || dim < 1 || seqlen < 0)
+    return fail(SS_ERR_INVALID_ARG, "sizes must be batch >= 1, dim >= 1, seqlen >= 0 (got %lld, %lld, %lld)",
+                (long long)batch, (long long)dim, (long long)seqlen);
+  if (batch > kMaxDim || dim > kMaxDim || seqlen > kMaxDim)
+    return fail(SS_ERR_INVALID_ARG, "a size exceeds 2^40");
+  const __int128 elems = (__int128)batch * dim * (seqlen > 0 ? seqlen : 1) * 16;
+  if (elems > ((__int128)1 << 62)) return fail(SS_ERR_INVALID_ARG, "tensor sizes overflow 64-bit byte offsets");
+  return SS_OK;
+}
+
+struct Plan {
+  int groups;
+  int64_t chunk_len;
+  int num_chunks;
+  int tile;
+};
+
+int io_code(ss_dtype io) { return io == SS_BF16 ? ssscan::kIoBf16 : ssscan::kIoF32; }
+
+// Automatic plan.  Wave groups: 4 when N allows (more waves in flight for the
+// same work, state components spread over SIMDs).  Chunking doubles the VALU
+// work of all but the first chunk, so it is used only when the unchunked launch
+// would leave most SIMDs idle; then chunks are sized for ~4 waves per SIMD.
+Plan auto_plan(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io) {
+  Plan p;
+  p.groups = dstate >= 4 ? 4 : dstate;
+  p.tile = ssscan::tile_len(p.groups, io_code(io));
+  const int64_t wgs = ((dim + 63) / 64) * batch;
+  const int64_t waves = wgs * p.groups;
+  const int64_t simds = (int64_t)device_cus() * 4;
+  int64_t chunks = 1;
+  if (waves * 2 < simds && seqlen >= 8192) {
+    chunks = (simds * 4 + waves - 1) / waves;
+    const int64_t max_chunks = seqlen / 2048;
+    if (chunks > max_chunks) chunks = max_chunks;
+    if (chunks < 1) chunks = 1;
+  }
+  int64_t cl = (seqlen + chunks - 1) / chunks;
+  cl = ((cl + p.tile - 1) / p.tile) * p.tile;
+  if (cl < p.tile) cl = p.tile;
+  p.chunk_len = cl;
+  p.num_chunks = seqlen > 0 ? (int)((seqlen + cl - 1) / cl) : 1;
+  return p;
+}
+
+ss_status make_plan(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io, const ss_scan_plan* in,
+                    Plan* out) {
+  if (!in) {
+    *out = auto_plan(batch, dim, dstate, seqlen, io);
+    return SS_OK;
+  }
+  Plan p;
+  p.groups = in->state_groups;
+  if (!(p.groups == 1 || p.groups == 2 || p.groups == 4) || p.groups > dstate)
+    return fail(SS_ERR_UNSUPPORTED, "plan.state_groups %d must be 1, 2 or 4 and at most dstate (%d)", p.groups,
+                dstate);
+  p.tile = ssscan::tile_len(p.groups, io_code(io));
+  int64_t cl = in->chunk_len;
+  if (cl <= 0) return fail(SS_ERR_INVALID_ARG, "plan.chunk_len must be positive (got %lld)", (long long)cl);
+  if (cl >= seqlen) {
+    cl = ((seqlen + p.tile - 1) / p.tile) * p.tile;
+    if (cl < p.tile) cl = p.tile;
+  }
+  if (cl % p.tile != 0)
+    return fail(SS_ERR_INVALID_ARG, "plan.chunk_len %lld is not a multiple of the tile length %d", (long long)cl,
+                p.tile);
+  const int64_t nc = seqlen > 0 ? (seqlen + cl - 1) / cl : 1;
+  if (nc > (1 << 20)) return fail(SS_ERR_INVALID_ARG, "plan gives %lld chunks (limit 2^20)", (long long)nc);
+  p.chunk_len = cl;
+  p.num_chunks = (int)nc;
+  *out = p;
+  return SS_OK;
+}
+
+struct WsLayout {
+  size_t bc, agg_h, agg_s, h_in, total;
+};
+
+size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
+
+WsLayout ws_layout(int64_t batch, int64_t dim, int dstate, int64_t seqlen, const Plan& p) {
+  WsLayout w{};
+  size_t off = 0;
+  w.bc = off;
+  off += round256((size_t)batch * seqlen * dstate * 2 * sizeof(float));
+  if (p.num_chunks > 1) {
+    const size_t st = (size_t)batch * dim * p.num_chunks * dstate * sizeof(float);
+    w.agg_h = off;
+    off += round256(st);
+    w.agg_s = off;
+    off += round256((size_t)batch * dim * p.num_chunks * sizeof(float));
+    w.h_in = off;
+    off += round256(st);
+  }
+  w.total = off;
+  return w;
+}
+
+// ---- timing record ----
+struct Timing {
+  std::mutex mu;
+  bool enabled = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pending;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pool;
+  double total_ms = 0.0;
+  int64_t calls = 0;
+};
+Timing g_timing;
+
+bool timing_on() {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  return g_timing.enabled;
+}
+
+ss_status timing_pair(hipEvent_t* a, hipEvent_t* b) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  if (!g_timing.pool.empty()) {
+    *a = g_timing.pool.back().first;
+    *b = g_timing.pool.back().second;
+    g_timing.pool.pop_back();
+    return SS_OK;
+  }
+  hipError_t e = hipEventCreate(a);
+  if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+  e = hipEventCreate(b);
+  if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+  return SS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ss_abi_version(void) { return SS_ABI_VERSION; }
+
+const char* ss_status_string(ss_status s) {
+  switch (s) {
+    case SS_OK: return "SS_OK";
+    case SS_ERR_INVALID_ARG: return "SS_ERR_INVALID_ARG";
+    case SS_ERR_UNSUPPORTED: return "SS_ERR_UNSUPPORTED";
+    case SS_ERR_WORKSPACE: return "SS_ERR_WORKSPACE";
+    case SS_ERR_HIP: return "SS_ERR_HIP";
+    default: return "SS_ERR_UNKNOWN";
+  }
+}
+
+const char* ss_last_error(void) { return g_last_error.c_str(); }
+
+ss_status ss_scan_fwd_plan(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io,
+                           ss_scan_plan* plan_out) {
+  ss_status st = check_sizes(batch, dim, dstate, seqlen, io);
+  if (st != SS_OK) return st;
+  if (!plan_out) return fail(SS_ERR_INVALID_ARG, "plan_out is NULL");
+  const Plan p = auto_plan(batch, dim, dstate, seqlen, io);
+  plan_out->state_groups = p.groups;
+  plan_out->reserved = 0;
+  plan_out->chunk_len = p.chunk_len;
+  return SS_OK;
+}
+
+size_t ss_scan_fwd_workspace_bytes(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io,
+                                   const ss_scan_plan* plan) {
+  if (check_sizes(batch, dim, dstate, seqlen, io) != SS_OK) return 0;
+  Plan p;
+  if (make_plan(batch, dim, dstate, seqlen, io, plan, &p) != SS_OK) return 0;
+  const WsLayout w = ws_layout(batch, dim, dstate, seqlen, p);
+  return w.total > 0 ? w.total : 256;
+}
+
+ss_status ss_scan_fwd(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io, const void* x,
+                      const void* dt, const void* z, const void* B, const void* C, const float* A,
+                      const float* Dskip, const float* dt_bias, const float* h0, void* y, float* h_final,
+                      void* workspace, size_t workspace_bytes, const ss_scan_plan* plan, void* stream) {
+  ss_status st = check_sizes(batch, dim, dstate, seqlen, io);
+  if (st != SS_OK) return st;
+  Plan p;
+  st = make_plan(batch, dim, dstate, seqlen, io, plan, &p);
+  if (st != SS_OK) return st;
+
+  const int64_t eb = elem_bytes(io);
+  const int64_t seq_bytes = batch * dim * seqlen * eb;
+  const int64_t bc_bytes = batch * dstate * seqlen * eb;
+  const int64_t st_bytes = batch * dim * dstate * 4;
+  if (seqlen > 0) {
+    if (!x) return fail(SS_ERR_INVALID_ARG, "x is NULL");
+    if (!dt) return fail(SS_ERR_INVALID_ARG, "dt is NULL");
+    if (!B) return fail(SS_ERR_INVALID_ARG, "B is NULL");
+    if (!C) return fail(SS_ERR_INVALID_ARG, "C is NULL");
+    if (!y) return fail(SS_ERR_INVALID_ARG, "y is NULL");
+  }
+  if (!A) return fail(SS_ERR_INVALID_ARG, "A is NULL");
+  const void* a16[] = {x, dt, z, B, C, A, h0, y, h_final};
+  const char* n16[] = {"x", "dt", "z", "B", "C", "A", "h0", "y", "h_final"};
+  for (int i = 0; i < 9; ++i)
+    if (a16[i] && !aligned(a16[i], 16)) return fail(SS_ERR_INVALID_ARG, "%s is not 16-byte aligned", n16[i]);
+  if (Dskip && !aligned(Dskip, 4)) return fail(SS_ERR_INVALID_ARG, "Dskip is not 4-byte aligned");
+  if (dt_bias && !aligned(dt_bias, 4)) return fail(SS_ERR_INVALID_ARG, "dt_bias is not 4-byte aligned");
+
+  const WsLayout wl = ws_layout(batch, dim, dstate, seqlen, p);
+  if (seqlen > 0) {
+    if (!workspace) return fail(SS_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", wl.total);
+    if (!aligned(workspace, 256)) return fail(SS_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    if (workspace_bytes < wl.total)
+      return fail(SS_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, wl.total);
+  }
+
+  // outputs must not overlap inputs, each other, or the workspace
+  const Range ins[] = {rng("x", x, seq_bytes), rng("dt", dt, seq_bytes), rng("z", z, seq_bytes),
+                       rng("B", B, bc_bytes), rng("C", C, bc_bytes), rng("A", A, dim * dstate * 4),
+                       rng("Dskip", Dskip, dim * 4), rng("dt_bias", dt_bias, dim * 4), rng("h0", h0, st_bytes)};
+  const Range outs[] = {rng("y", y, seq_bytes), rng("h_final", h_final, st_bytes),
+                        rng("workspace", workspace, seqlen > 0 ? (int64_t)wl.total : 0)};
+  for (const Range& o : outs) {
+    for (const Range& i : ins)
+      if (overlap(o, i)) return fail(SS_ERR_INVALID_ARG, "%s overlaps input %s", o.name, i.name);
+  }
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j])) return fail(SS_ERR_INVALID_ARG, "%s overlaps %s", outs[i].name, outs[j].name);
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (seqlen == 0) {
+    if (h_final) {
+      hipError_t e = ssscan::launch_copy_state(batch * dim * dstate, h0, h_final, s);
+      if (e != hipSuccess) return hip_fail(e, "copy_state launch");
+    }
+    return SS_OK;
+  }
+
+  ssscan::ScanDims dm{};
+  dm.batch = batch;
+  dm.dim = dim;
+  dm.seqlen = seqlen;
+  dm.chunk_len = p.chunk_len;
+  dm.num_chunks = p.num_chunks;
+  dm.dstate = dstate;
+  dm.groups = p.groups;
+  dm.io = io_code(io);
+  const int per_span = io == SS_BF16 ? 8 : 4;
+  dm.vec = (seqlen % per_span) == 0 ? 1 : 0;
+
+  const int64_t nwg = ((dim + 63) / 64) * batch * p.num_chunks;
+  if (nwg > 0x7fffffffLL) return fail(SS_ERR_INVALID_ARG, "launch needs %lld workgroups (limit 2^31-1)", (long long)nwg);
+
+  char* ws = static_cast<char*>(workspace);
+  ssscan::ScanPtrs sp{};
+  sp.x = x;
+  sp.dt = dt;
+  sp.z = z;
+  sp.bc = reinterpret_cast<const float*>(ws + wl.bc);
+  sp.A = A;
+  sp.Dskip = Dskip;
+  sp.dt_bias = dt_bias;
+  sp.h0 = h0;
+  sp.y = y;
+  sp.h_final = h_final;
+  float* bcw = reinterpret_cast<float*>(ws + wl.bc);
+
+  hipError_t e = ssscan::launch_prep_bc(dm, B, C, bcw, s);
+  if (e != hipSuccess) return hip_fail(e, "prep_bc launch");
+
+  const bool timed = timing_on();
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  if (timed) {
+    st = timing_pair(&ev0, &ev1);
+    if (st != SS_OK) return st;
+    e = hipEventRecord(ev0, s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+
+  if (p.num_chunks > 1) {
+    sp.agg_h = reinterpret_cast<float*>(ws + wl.agg_h);
+    sp.agg_s = reinterpret_cast<float*>(ws + wl.agg_s);
+    float* h_in = reinterpret_cast<float*>(ws + wl.h_in);
+    e = ssscan::launch_scan(dm, sp, /*aggregate=*/true, s);
+    if (e != hipSuccess) return hip_fail(e, "scan (aggregate) launch");
+    e = ssscan::launch_combine(dm, A, sp.agg_h, sp.agg_s, h0, h_in, s);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+    sp.h_in = h_in;
+  }
+  e = ssscan::launch_scan(dm, sp, /*aggregate=*/false, s);
+  if (e != hipSuccess) return hip_fail(e, "scan launch");
+
+  if (timed) {
+    e = hipEventRecord(ev1, s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    g_timing.pending.emplace_back(ev0, ev1);
+  }
+  return SS_OK;
+}
+
+ss_status ss_state_update(int64_t batch, int64_t dim, int dstate, ss_dtype io, float* state, const void* x,
+                          const void* dt, const void* z, const void* B, const void* C, const float* A,
+                          const float* Dskip, const float* dt_bias, void* y, void* stream) {
+  ss_status st = check_sizes(batch, dim, dstate, 1, io);
+  if (st != SS_OK) return st;
+  const char* names[] = {"state", "x", "dt", "B", "C", "A", "y"};
+  const void* req[] = {state, x, dt, B, C, A, y};
+  for (int i = 0; i < 7; ++i)
+    if (!req[i]) return fail(SS_ERR_INVALID_ARG, "%s is NULL", names[i]);
+  const void* a16[] = {state, x, dt, z, B, C, A, y};
+  const char* n16[] = {"state", "x", "dt", "z", "B", "C", "A", "y"};
+  for (int i = 0; i < 8; ++i)
+    if (a16[i] && !aligned(a16[i], 16)) return fail(SS_ERR_INVALID_ARG, "%s is not 16-byte aligned", n16[i]);
+  if (Dskip && !aligned(Dskip, 4)) return fail(SS_ERR_INVALID_ARG, "Dskip is not 4-byte aligned");
+  if (dt_bias && !aligned(dt_bias, 4)) return fail(SS_ERR_INVALID_ARG, "dt_bias is not 4-byte aligned");
+  const int64_t eb = elem_bytes(io);
+  const int64_t tok = batch * dim * eb;
+  const Range ins[] = {rng("x", x, tok), rng("dt", dt, tok), rng("z", z, tok),
+                       rng("B", B, batch * dstate * eb), rng("C", C, batch * dstate * eb),
+                       rng("A", A, dim * dstate * 4), rng("Dskip", Dskip, dim * 4),
+                       rng("dt_bias", dt_bias, dim * 4)};
+  const Range outs[] = {rng("state", state, batch * dim * dstate * 4), rng("y", y, tok)};
+  for (const Range& o : outs)
+    for (const Range& i : ins)
+      if (overlap(o, i)) return fail(SS_ERR_INVALID_ARG, "%s overlaps input %s", o.name, i.name);
+  if (overlap(outs[0], outs[1])) return fail(SS_ERR_INVALID_ARG, "state overlaps y");
+  hipError_t e = ssscan::launch_state_update(batch, dim, dstate, io_code(io), state, x, dt, z, B, C, A, Dskip,
+                                             dt_bias, y, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "state_update launch");
+  return SS_OK;
+}
+
+ss_status ss_timing_enable(int enable) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  g_timing.enabled = enable != 0;
+  return SS_OK;
+}
+
+ss_status ss_timing_reset(void) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  for (auto& pr : g_timing.pending) {
+    hipError_t e = hipEventSynchronize(pr.second);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    g_timing.pool.push_back(pr);
+  }
+  g_timing.pending.clear();
+  g_timing.total_ms = 0.0;
+  g_timing.calls = 0;
+  return SS_OK;
+}
+
+ss_status ss_timing_read(double* total_ms, int64_t* calls) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  for (auto& pr : g_timing.pending) {
+    hipError_t e = hipEventSynchronize(pr.second);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, pr.first, pr.second);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    g_timing.total_ms += ms;
+    g_timing.calls += 1;
+    g_timing.pool.push_back(pr);
+  }
+  g_timing.pending.clear();
+  if (total_ms) *total_ms = g_timing.total_ms;
+  if (calls) *calls = g_timing.calls;
+  return SS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,134 @@
+// Device-side helpers shared by the scan and decode kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace ssscan {
+namespace dev {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+// I/O element types.  Both load 16 bytes per lane per span.
+struct F32 {
+  using T = float;
+  static constexpr int kPerSpan = 4;
+};
+struct BF16 {
+  using T = uint16_t;
+  static constexpr int kPerSpan = 8;
+};
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t float_to_bf16_bits(float v) {
+  const __bf16 b = (__bf16)v;
+  return (uint32_t)__builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  const f2 v = {lo, hi};
+  const b2 r = __builtin_convertvector(v, b2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Element i of a 16-byte span held as four 32-bit words.
+template <typename IO>
+__device__ __forceinline__ float span_elem(const uint32_t (&w)[4], int i);
+template <>
+__device__ __forceinline__ float span_elem<F32>(const uint32_t (&w)[4], int i) { return __uint_as_float(w[i]); }
+template <>
+__device__ __forceinline__ float span_elem<BF16>(const uint32_t (&w)[4], int i) {
+  return (i & 1) ? __uint_as_float(w[i >> 1] & 0xffff0000u) : __uint_as_float(w[i >> 1] << 16);
+}
+
+// Load elements [idx, idx + kPerSpan) of `base`; elements at or beyond `valid`
+// (counted from idx) read as zero.  `vec` allows one 16-byte load when the whole
+// span is valid (the caller guarantees 16-byte alignment then).
+template <typename IO>
+__device__ __forceinline__ void load_span(const typename IO::T* __restrict__ base, int64_t idx, int valid,
+                                          bool vec, uint32_t (&w)[4]) {
+  if (vec && valid >= IO::kPerSpan) {
+    const uint4 v = *reinterpret_cast<const uint4*>(base + idx);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    return;
+  }
+  w[0] = w[1] = w[2] = w[3] = 0u;
+  if constexpr (IO::kPerSpan == 4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i < valid) w[i] = __float_as_uint(base[idx + i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i < valid) w[i >> 1] |= (uint32_t)base[idx + i] << ((i & 1) * 16);
+  }
+}
+
+// Store the first `valid` of kPerSpan values at base[idx...].
+template <typename IO>
+__device__ __forceinline__ void store_span(typename IO::T* __restrict__ base, int64_t idx, int valid, bool vec,
+                                           const float (&v)[IO::kPerSpan]) {
+  if constexpr (IO::kPerSpan == 4) {
+    if (vec && valid >= 4) {
+      *reinterpret_cast<float4*>(base + idx) = make_float4(v[0], v[1], v[2], v[3]);
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i < valid) base[idx + i] = v[i];
+  } else {
+    if (vec && valid >= 8) {
+      uint4 o;
+      o.x = pack_bf16x2(v[0], v[1]);
+      o.y = pack_bf16x2(v[2], v[3]);
+      o.z = pack_bf16x2(v[4], v[5]);
+      o.w = pack_bf16x2(v[6], v[7]);
+      *reinterpret_cast<uint4*>(base + idx) = o;
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i < valid) base[idx + i] = (uint16_t)float_to_bf16_bits(v[i]);
+  }
+}
+
+template <typename IO>
+__device__ __forceinline__ float load_one(const typename IO::T* __restrict__ base, int64_t idx) {
+  if constexpr (IO::kPerSpan == 4) return base[idx];
+  else return bf16_bits_to_float(base[idx]);
+}
+
+template <typename IO>
+__device__ __forceinline__ void store_one(typename IO::T* __restrict__ base, int64_t idx, float v) {
+  if constexpr (IO::kPerSpan == 4) base[idx] = v;
+  else base[idx] = (uint16_t)float_to_bf16_bits(v);
+}
+
+// Delta = softplus(dt + dt_bias), given bias2 = dt_bias * log2(e).
+// softplus(v) = max(v, 0) + log1p(e^-|v|).  With v2 = v log2(e) and e = 2^-|v2|,
+// u = 1 + e is rounded; c = (u - 1) - e is that rounding error exactly, so
+// log1p(e) = ln(u) - c/u ~= ln2 * log2(u) - c (u is in [1, 2]; the dropped
+// c (1 - 1/u) is below 2^-24 e).  Uses the hardware exp2 and log2.
+__device__ __forceinline__ float softplus_dt(float dt, float bias2) {
+  const float v2 = fmaf(dt, kLog2e, bias2);
+  const float e = __builtin_amdgcn_exp2f(-fabsf(v2));
+  const float u = 1.0f + e;
+  const float c = (u - 1.0f) - e;
+  const float l = __builtin_amdgcn_logf(u);
+  return fmaf(fmaxf(v2, 0.0f) + l, kLn2, -c);
+}
+
+// silu(z) = z / (1 + e^-z).  For z below about -88 the exponential overflows to
+// +inf and the result is -0, the correctly rounded limit.
+__device__ __forceinline__ float silu(float z) {
+  const float s = __builtin_amdgcn_exp2f(-z * kLog2e);
+  return z * __builtin_amdgcn_rcpf(1.0f + s);
+}
+
+}  // namespace dev
+}  // namespace ssscan

@@ -1,0 +1,55 @@
+// Internal interface between the C-ABI layer (api.cpp) and the HIP kernels.
+// Not installed; the public interface is include/ssscan.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace ssscan {
+
+enum IoType : int32_t { kIoF32 = 0, kIoBf16 = 1 };
+
+// Shape and plan of one scan launch.
+struct ScanDims {
+  int64_t batch;
+  int64_t dim;
+  int64_t seqlen;
+  int64_t chunk_len;    // tokens per chunk (a multiple of the tile length)
+  int32_t num_chunks;   // ceil(seqlen / chunk_len)
+  int32_t dstate;       // N
+  int32_t groups;       // waves per workgroup, each owning dstate/groups states
+  int32_t io;           // IoType
+  int32_t vec;          // 1: rows are 16-byte aligned, 16-byte vector loads allowed
+  int32_t pad_;
+};
+
+struct ScanPtrs {
+  const void* x;
+  const void* dt;
+  const void* z;        // nullable
+  const float* bc;      // workspace: (batch, seqlen, dstate, 2) fp32, B and C interleaved
+  const float* A;
+  const float* Dskip;   // nullable
+  const float* dt_bias; // nullable
+  const float* h0;      // nullable
+  const float* h_in;    // chunked: (batch, dim, num_chunks, dstate) initial state of each chunk
+  void* y;
+  float* h_final;       // nullable
+  float* agg_h;         // chunk end states from zero (batch, dim, num_chunks, dstate)
+  float* agg_s;         // chunk sums of Delta (batch, dim, num_chunks)
+};
+
+// Tokens per tile: each wave loads 16 bytes of every input row per tile.
+inline int tile_len(int groups, int io) { return groups * (io == kIoBf16 ? 8 : 4); }
+
+hipError_t launch_prep_bc(const ScanDims& dm, const void* B, const void* C, float* bc, hipStream_t s);
+hipError_t launch_scan(const ScanDims& dm, const ScanPtrs& p, bool aggregate, hipStream_t s);
+hipError_t launch_combine(const ScanDims& dm, const float* A, const float* agg_h, const float* agg_s,
+                          const float* h0, float* h_in, hipStream_t s);
+hipError_t launch_copy_state(int64_t count, const float* src, float* dst, hipStream_t s);
+hipError_t launch_state_update(int64_t batch, int64_t dim, int dstate, int io, float* state,
+                               const void* x, const void* dt, const void* z, const void* B, const void* C,
+                               const float* A, const float* Dskip, const float* dt_bias, void* y,
+                               hipStream_t s);
+
+}  // namespace ssscan

@@ -1,0 +1,108 @@
+"""Tensor-level calls over the C ABI: marshalling only.
+
+``scan_fwd`` and ``state_update`` check dtypes, shapes, devices and contiguity,
+allocate outputs and the workspace with torch on the inputs' device, and call
+the library on torch's current stream.  No arithmetic of the scan happens here.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import binding as _b
+
+_IO = {torch.float32: _b.SS_F32, torch.bfloat16: _b.SS_BF16}
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, name, dtype, shape, device):
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def workspace_bytes(batch, dim, dstate, seqlen, dtype=torch.bfloat16, plan=None) -> int:
+    return _b.ss_scan_fwd_workspace_bytes(batch, dim, dstate, seqlen, _IO[dtype], plan)
+
+
+def scan_fwd(x, dt, B, C, A, z=None, Dskip=None, dt_bias=None, h0=None, *, plan=None, workspace=None,
+             y=None, h_final=None, return_final_state=True):
+    """Selective scan over full sequences.
+
+    x, dt, z: (batch, D, L); B, C: (batch, N, L) — all float32 or all bfloat16;
+    A: (D, N) float32; Dskip, dt_bias: (D,) float32; h0: (batch, D, N) float32.
+    Returns (y, h_final); h_final is None when return_final_state is False.
+    """
+    if x.dtype not in _IO:
+        raise TypeError("x must be float32 or bfloat16")
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU")
+    batch, dim, L = x.shape
+    N = A.shape[1]
+    io = _IO[x.dtype]
+    _need(x, "x", x.dtype, (batch, dim, L), dev)
+    _need(dt, "dt", x.dtype, (batch, dim, L), dev)
+    _need(z, "z", x.dtype, (batch, dim, L), dev)
+    _need(B, "B", x.dtype, (batch, N, L), dev)
+    _need(C, "C", x.dtype, (batch, N, L), dev)
+    _need(A, "A", torch.float32, (dim, N), dev)
+    _need(Dskip, "Dskip", torch.float32, (dim,), dev)
+    _need(dt_bias, "dt_bias", torch.float32, (dim,), dev)
+    _need(h0, "h0", torch.float32, (batch, dim, N), dev)
+    if y is None:
+        y = torch.empty((batch, dim, L), dtype=x.dtype, device=dev)
+    _need(y, "y", x.dtype, (batch, dim, L), dev)
+    if return_final_state and h_final is None:
+        h_final = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
+    _need(h_final, "h_final", torch.float32, (batch, dim, N), dev)
+    nbytes = _b.ss_scan_fwd_workspace_bytes(batch, dim, N, L, io, plan)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    if workspace.numel() < nbytes:
+        raise ValueError("workspace has %d bytes, %d needed" % (workspace.numel(), nbytes))
+    _b.ss_scan_fwd(batch, dim, N, L, io, _ptr(x), _ptr(dt), _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(Dskip),
+                   _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_final), _ptr(workspace), workspace.numel(),
+                   plan, _stream(dev))
+    return y, h_final
+
+
+def state_update(state, x, dt, B, C, A, z=None, Dskip=None, dt_bias=None, *, y=None):
+    """One decode step; ``state`` (batch, D, N) float32 is updated in place.
+
+    x, dt, z: (batch, D); B, C: (batch, N) in float32 or bfloat16.  Returns y (batch, D).
+    """
+    if x.dtype not in _IO:
+        raise TypeError("x must be float32 or bfloat16")
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU")
+    batch, dim = x.shape
+    N = A.shape[1]
+    _need(state, "state", torch.float32, (batch, dim, N), dev)
+    _need(dt, "dt", x.dtype, (batch, dim), dev)
+    _need(z, "z", x.dtype, (batch, dim), dev)
+    _need(B, "B", x.dtype, (batch, N), dev)
+    _need(C, "C", x.dtype, (batch, N), dev)
+    _need(A, "A", torch.float32, (dim, N), dev)
+    _need(Dskip, "Dskip", torch.float32, (dim,), dev)
+    _need(dt_bias, "dt_bias", torch.float32, (dim,), dev)
+    if y is None:
+        y = torch.empty((batch, dim), dtype=x.dtype, device=dev)
+    _need(y, "y", x.dtype, (batch, dim), dev)
+    _b.ss_state_update(batch, dim, N, _IO[x.dtype], _ptr(state), _ptr(x), _ptr(dt), _ptr(z), _ptr(B), _ptr(C),
+                       _ptr(A), _ptr(Dskip), _ptr(dt_bias), _ptr(y), _stream(dev))
+    return y

@@ -1,0 +1,273 @@
+"""GPU path (through the C ABI) against the CPU oracle, element by element.
+
+Bars: rel-L2 <= 1e-5 with fp32 I/O, <= 2e-2 with bf16 I/O (fp32 state), for y
+and for the final state.  Inputs are seeded; the oracle always receives the
+exact values the GPU received (bf16 inputs widened exactly), drawn on the host.
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import log, random_problem, rel_l2, run_gpu_scan, run_oracle_scan, to_dev, to_f64
+from workloads import B28, DECODE, LONG, M130, TINY, inputs, tolerance
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def ss():
+    import selective_state_space_62_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def o():
+    return oracle.default()
+
+
+def _tol(io):
+    return 1e-5 if io == "f32" else 2e-2
+
+
+# ---------------------------------------------------------------- generator ---
+
+def test_device_generator_matches_host(dev):
+    from workloads import device as wdev, philox
+    import torch
+    ctr = np.array([[0, 0, 0, 0], [0xFFFFFFFF] * 4, [0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344]], np.uint64)
+    key = np.array([[0, 0], [0xFFFFFFFF] * 2, [0xA4093822, 0x299F31D0]], np.uint64)
+    got = wdev.philox_raw(ctr, key, dev)
+    for i in range(3):
+        w = philox.philox4x32_10(*[np.uint32(c) for c in ctr[i]], int(key[i, 0]), int(key[i, 1]))
+        assert tuple(int(v) for v in got[i]) == tuple(int(v) for v in w)
+    for cfg, stream, scale in ((B28, inputs.STREAM_X, 1.0), (B28, inputs.STREAM_DT, 0.5), (M130, inputs.STREAM_B, 1.0)):
+        for start, count in ((0, 1000), (3, 77), (123456789, 513)):
+            out = torch.empty(count, dtype=torch.float32 if cfg.io == "f32" else torch.bfloat16, device=dev)
+            wdev.fill(out, cfg, stream, start=start, scale=scale)
+            host = inputs.draw(cfg, stream, start, count, scale=scale)
+            if cfg.io == "f32":
+                assert np.array_equal(out.cpu().numpy(), host)
+            else:
+                assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), host)
+
+
+# ---------------------------------------------------------- small and ragged ---
+
+@pytest.mark.parametrize("plan", [None, (1, 64), (2, 64), (4, 64), (4, 16), (1, 4), (2, 8), (4, 32)])
+def test_tiny_workload_all_plans(ss, o, dev, plan):
+    cfg = TINY
+    log("tiny workload, plan %s" % (plan,))
+    raw = inputs.scan_inputs_full(cfg)
+    A, dskip, bias = inputs.params(cfg)
+    h0 = np.random.default_rng(11).standard_normal((1, cfg.dim, cfg.dstate)).astype(np.float32)
+    par = dict(A=A, Dskip=dskip, dt_bias=bias, h0=h0)
+    y, hf = run_gpu_scan(ss, raw, par, cfg.io, dev, plan=plan)
+    f64 = {k: inputs.raw_to_f64(v, cfg.io) for k, v in raw.items()}
+    yr, hr = run_oracle_scan(o, f64, par)
+    assert rel_l2(y, yr) <= 1e-5 and rel_l2(hf, hr) <= 1e-5, (rel_l2(y, yr), rel_l2(hf, hr))
+    assert np.max(np.abs(y - yr)) <= 1e-4 * max(1.0, np.max(np.abs(yr)))
+
+
+RAGGED = [
+    # batch, D, N, L, io, z, skip, bias, h0, plan
+    (1, 1, 1, 1, "f32", True, True, True, True, None),
+    (2, 100, 16, 37, "f32", True, True, True, True, None),
+    (3, 65, 8, 129, "bf16", True, False, True, False, None),
+    (1, 130, 4, 1000, "f32", False, True, False, True, (4, 96)),
+    (2, 64, 2, 77, "bf16", True, True, True, True, (2, 32)),
+    (1, 7, 16, 300, "f32", True, True, True, True, (4, 64)),
+    (2, 200, 16, 515, "bf16", True, True, True, True, (4, 128)),
+    (1, 64, 16, 8, "bf16", True, True, True, True, (1, 8)),
+    (1, 64, 1, 33, "f32", True, True, True, True, (1, 8)),
+    (4, 33, 16, 2, "f32", True, True, True, True, None),
+]
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=["-".join(map(str, c[:5])) + "-" + str(c[9]) for c in RAGGED])
+def test_ragged_shapes(ss, o, dev, case):
+    batch, D, N, L, io, wz, wsk, wb, wh, plan = case
+    log("ragged %s" % (case,))
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()))
+    raw, par, f64 = random_problem(rng, batch, D, N, L, io, wz, wsk, wb, wh)
+    y, hf = run_gpu_scan(ss, raw, par, io, dev, plan=plan)
+    yr, hr = run_oracle_scan(o, f64, par)
+    ey, eh = rel_l2(y, yr), rel_l2(hf, hr)
+    log("  rel-L2 y %.3e h %.3e" % (ey, eh))
+    assert ey <= _tol(io) and eh <= _tol(io)
+    if io == "bf16":
+        # bf16 output rounding dominates: also bound the per-element error by a few bf16 ulps
+        assert np.all(np.abs(y - yr) <= 2 ** -7 * np.abs(yr) + 1e-3 * np.max(np.abs(yr)))
+
+
+def test_empty_sequence_copies_state(ss, dev):
+    import torch
+    h0 = torch.randn(2, 70, 16, device=dev)
+    x = torch.zeros(2, 70, 0, device=dev)
+    A = -torch.ones(70, 16, device=dev)
+    Bm = torch.zeros(2, 16, 0, device=dev)
+    y, hf = ss.scan_fwd(x, x.clone(), Bm, Bm.clone(), A, h0=h0)
+    torch.cuda.synchronize()
+    assert y.shape == (2, 70, 0) and torch.equal(hf, h0)
+    _, hz = ss.scan_fwd(x, x.clone(), Bm, Bm.clone(), A)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(hz) == 0
+
+
+def test_extreme_values(ss, o, dev):
+    """dt far into both softplus tails, gates far into both silu tails."""
+    rng = np.random.default_rng(5)
+    batch, D, N, L = 1, 64, 16, 64
+    raw, par, f64 = random_problem(rng, batch, D, N, L, "f32")
+    dt = raw["dt"].copy()
+    dt[:, :16] = -40.0
+    dt[:, 16:32] = 40.0
+    dt[:, 32:48, ::2] = 25.0
+    z = raw["z"].copy()
+    z[:, 48:56] = -100.0
+    z[:, 56:] = 100.0
+    raw["dt"], raw["z"] = dt, z
+    f64["dt"], f64["z"] = dt.astype(np.float64), z.astype(np.float64)
+    y, hf = run_gpu_scan(ss, raw, par, "f32", dev)
+    yr, hr = run_oracle_scan(o, f64, par)
+    assert np.all(np.isfinite(y)) and np.all(np.isfinite(hf))
+    assert rel_l2(y, yr) <= 1e-5 and rel_l2(hf, hr) <= 1e-5, (rel_l2(y, yr), rel_l2(hf, hr))
+
+
+# ------------------------------------------------------------ the workloads ---
+
+def test_130m_layer_f32_full(ss, o, dev):
+    cfg = M130
+    log("130M-shaped layer, fp32, full oracle check")
+    raw = inputs.scan_inputs_full(cfg)
+    A, dskip, bias = inputs.params(cfg)
+    par = dict(A=A, Dskip=dskip, dt_bias=bias, h0=None)
+    y, hf = run_gpu_scan(ss, raw, par, cfg.io, dev)
+    f64 = {k: inputs.raw_to_f64(v, cfg.io) for k, v in raw.items()}
+    yr, hr = run_oracle_scan(o, f64, par)
+    ey, eh = rel_l2(y, yr), rel_l2(hf, hr)
+    log("  rel-L2 y %.3e h %.3e" % (ey, eh))
+    assert ey <= tolerance(cfg) and eh <= tolerance(cfg)
+
+
+def _sampled_oracle(o, cfg, chans, par):
+    """Oracle over sampled channels, drawn on the host; grouped by batch row."""
+    A, dskip, bias = par
+    ys, hs = {}, {}
+    rows = {}
+    for (b, d) in chans:
+        rows.setdefault(b, []).append(d)
+    for b, ds in rows.items():
+        sub = inputs.scan_inputs(cfg, channels=[(b, d) for d in ds])
+        f = {k: inputs.raw_to_f64(v, cfg.io) for k, v in sub.items()}
+        idx = np.array(ds)
+        yr, hr = o.scan(f["x"][None], f["dt"][None], f["B"][b:b + 1], f["C"][b:b + 1], A[idx], z=f["z"][None],
+                        Dskip=dskip[idx], dt_bias=bias[idx])
+        for i, d in enumerate(ds):
+            ys[(b, d)] = yr[0, i]
+            hs[(b, d)] = hr[0, i]
+    return ys, hs, rows
+
+
+def _device_scan(ss, cfg, dev):
+    import torch
+    from workloads import device as wdev
+    t = wdev.scan_inputs(cfg, dev)
+    A, dskip, bias = wdev.params(cfg, dev)
+    y, hf = ss.scan_fwd(t["x"], t["dt"], t["B"], t["C"], A, z=t["z"], Dskip=dskip, dt_bias=bias)
+    torch.cuda.synchronize()
+    return t, y, hf
+
+
+def _check_sampled(cfg, chans, t, y, hf, ys, hs):
+    import torch
+    idx_b = torch.tensor([b for b, _ in chans], device=y.device)
+    idx_d = torch.tensor([d for _, d in chans], device=y.device)
+    yg = to_f64(y[idx_b, idx_d])
+    hg = to_f64(hf[idx_b, idx_d])
+    # the inputs the GPU saw at these channels are the host draws the oracle used
+    xg = t["x"][idx_b, idx_d]
+    xh = inputs.scan_inputs(cfg, channels=chans[:4])["x"]
+    assert np.array_equal(xg[:4].view(torch.int16).cpu().numpy().view(np.uint16), xh)
+    yr = np.stack([ys[c] for c in chans])
+    hr = np.stack([hs[c] for c in chans])
+    return rel_l2(yg, yr), rel_l2(hg, hr)
+
+
+def test_28b_layer_bf16_sampled(ss, o, dev):
+    """The benchmarked workload, in the benchmark's launch configuration (automatic plan)."""
+    import torch
+    cfg = B28
+    log("2.8B-shaped layer, bf16, automatic plan %s" % (ss.ss_scan_fwd_plan(cfg.batch, cfg.dim, cfg.dstate,
+                                                                            cfg.seqlen, ss.SS_BF16),))
+    t, y, hf = _device_scan(ss, cfg, dev)
+    assert bool(torch.isfinite(y.float()).all()) and bool(torch.isfinite(hf).all())
+    chans = inputs.sample_channels(cfg, 256)
+    ys, hs, _ = _sampled_oracle(o, cfg, chans, inputs.params(cfg))
+    ey, eh = _check_sampled(cfg, chans, t, y, hf, ys, hs)
+    log("  256 sampled channels: rel-L2 y %.3e h %.3e" % (ey, eh))
+    assert ey <= tolerance(cfg) and eh <= tolerance(cfg)
+
+
+def test_long_context_bf16_sampled(ss, o, dev):
+    """L = 1,048,576 with 2048 channels: chunked plan; the oracle checks 64 channels in full."""
+    import torch
+    cfg = LONG
+    plan = ss.ss_scan_fwd_plan(cfg.batch, cfg.dim, cfg.dstate, cfg.seqlen, ss.SS_BF16)
+    log("long context, bf16, plan %s" % (plan,))
+    assert plan[1] < cfg.seqlen
+    t, y, hf = _device_scan(ss, cfg, dev)
+    chans = inputs.sample_channels(cfg, cfg.check_channels)
+    ys, hs, _ = _sampled_oracle(o, cfg, chans, inputs.params(cfg))
+    ey, eh = _check_sampled(cfg, chans, t, y, hf, ys, hs)
+    log("  64 channels x 1M tokens: rel-L2 y %.3e h %.3e" % (ey, eh))
+    assert ey <= tolerance(cfg) and eh <= tolerance(cfg)
+    del t, y, hf
+    torch.cuda.empty_cache()
+
+
+def test_decode_bf16_trajectory(ss, o, dev):
+    """128 decode steps from a seeded N(0,1) state; 512 sampled channels checked at every step."""
+    import torch
+    from workloads import device as wdev
+    cfg = DECODE
+    log("decode, bf16, %d steps" % cfg.steps)
+    A, dskip, bias = wdev.params(cfg, dev)
+    state = wdev.decode_state0(cfg, dev)
+    chans = inputs.sample_rows(cfg, 8, 64)
+    idx_b = torch.tensor([b for b, _ in chans], device=dev)
+    idx_d = torch.tensor([d for _, d in chans], device=dev)
+    ref_state = inputs.decode_state0(cfg, channels=chans).astype(np.float64)
+    assert np.array_equal(state[idx_b, idx_d].cpu().numpy(), ref_state.astype(np.float32))
+    An, dn, bn = inputs.params(cfg)
+    rows = {}
+    for i, (b, d) in enumerate(chans):
+        rows.setdefault(b, []).append((i, d))
+    ys_gpu, ys_ref = [], []
+    for step in range(cfg.steps):
+        t = wdev.decode_inputs(cfg, step, dev)
+        y = ss.state_update(state, t["x"], t["dt"], t["B"], t["C"], A, z=t["z"], Dskip=dskip, dt_bias=bias)
+        ys_gpu.append(to_f64(y[idx_b, idx_d]))
+        f = {k: inputs.raw_to_f64(v, cfg.io) for k, v in inputs.decode_inputs(cfg, step, channels=chans).items()}
+        yr = np.empty(len(chans))
+        for b, members in rows.items():
+            ii = np.array([i for i, _ in members])
+            dd = np.array([d for _, d in members])
+            yb, sb = o.state_update(ref_state[ii][None], f["x"][ii][None], f["dt"][ii][None], f["B"][b:b + 1],
+                                    f["C"][b:b + 1], An[dd], z=f["z"][ii][None], Dskip=dn[dd], dt_bias=bn[dd])
+            yr[ii] = yb[0]
+            ref_state[ii] = sb[0]
+        ys_ref.append(yr)
+    torch.cuda.synchronize()
+    ey = rel_l2(np.stack(ys_gpu), np.stack(ys_ref))
+    eh = rel_l2(to_f64(state[idx_b, idx_d]), ref_state)
+    log("  512 channels x %d steps: rel-L2 y %.3e, final state %.3e" % (cfg.steps, ey, eh))
+    assert ey <= tolerance(cfg) and eh <= tolerance(cfg)

@@ -79,6 +79,21 @@ def draw(cfg: ScanConfig, stream: int, start: int, count: int, step: int = 0,
     return table(cfg.io, scale)[idx]
 
 
+def draw_at(cfg: ScanConfig, stream: int, index: np.ndarray, step: int = 0, scale: float = 1.0,
+            io: str | None = None) -> np.ndarray:
+    """Draws at arbitrary element indices of one stream (vectorised)."""
+    from .philox import philox4x32_10
+    index = np.asarray(index, dtype=np.uint64)
+    blk = index >> np.uint64(3)
+    lo = (blk & np.uint64(0xFFFFFFFF)).astype(np.uint32)
+    hi = (blk >> np.uint64(32)).astype(np.uint32)
+    w = np.stack(philox4x32_10(lo, hi, np.uint32(stream), np.uint32(step), cfg.seed, KEY1), axis=-1)
+    k = (index & np.uint64(7)).astype(np.int64)
+    word = np.take_along_axis(w, (k >> 1)[..., None], axis=-1)[..., 0]
+    j = ((word >> ((k & 1) * 16).astype(np.uint32)) & 0xFFFF).astype(np.int64)
+    return table(io or cfg.io, scale)[j]
+
+
 def draw_state(cfg: ScanConfig, start: int, count: int) -> np.ndarray:
     """Initial decode state (always fp32), N(0, 1)."""
     idx = draw_u16(cfg.seed, KEY1, STREAM_H0, 0, start, count)
@@ -149,8 +164,8 @@ def decode_inputs(cfg: ScanConfig, step: int, channels=None):
         if channels is None:
             out[name] = draw(cfg, stream, 0, nch, step=step, scale=scale).reshape(cfg.batch, cfg.dim)
         else:
-            out[name] = np.array([draw(cfg, stream, b * cfg.dim + d, 1, step=step, scale=scale)[0]
-                                  for (b, d) in channels])
+            idx = np.array([b * cfg.dim + d for (b, d) in channels], dtype=np.uint64)
+            out[name] = draw_at(cfg, stream, idx, step=step, scale=scale)
     for name, stream in (("B", STREAM_B), ("C", STREAM_C)):
         out[name] = draw(cfg, stream, 0, cfg.batch * cfg.dstate, step=step).reshape(cfg.batch, cfg.dstate)
     return out
@@ -161,7 +176,8 @@ def decode_state0(cfg: ScanConfig, channels=None):
     N = cfg.dstate
     if channels is None:
         return draw_state(cfg, 0, cfg.batch * cfg.dim * N).reshape(cfg.batch, cfg.dim, N)
-    return np.stack([draw_state(cfg, (b * cfg.dim + d) * N, N) for (b, d) in channels])
+    idx = np.array([(b * cfg.dim + d) * N + n for (b, d) in channels for n in range(N)], dtype=np.uint64)
+    return draw_at(cfg, STREAM_H0, idx, io="f32").reshape(len(channels), N)
 
 
 def sample_channels(cfg: ScanConfig, count: int, seed_offset: int = 40):
@@ -170,3 +186,14 @@ def sample_channels(cfg: ScanConfig, count: int, seed_offset: int = 40):
     total = cfg.batch * cfg.dim
     flat = np.sort(rng.choice(total, size=min(count, total), replace=False))
     return [(int(f // cfg.dim), int(f % cfg.dim)) for f in flat]
+
+
+def sample_rows(cfg: ScanConfig, rows: int, per_row: int, seed_offset: int = 41):
+    """A seeded sample of ``per_row`` channels in each of ``rows`` batch rows, sorted."""
+    rng = np.random.Generator(np.random.PCG64(cfg.seed + seed_offset))
+    bs = np.sort(rng.choice(cfg.batch, size=min(rows, cfg.batch), replace=False))
+    out = []
+    for b in bs:
+        ds = np.sort(rng.choice(cfg.dim, size=min(per_row, cfg.dim), replace=False))
+        out.extend((int(b), int(d)) for d in ds)
+    return out
