@@ -111,7 +111,7 @@ def measured_traffic(cfg):
 def run_decode(ss, torch, dev, steps, warmup):
     """Decode step timing (secondary): 128-step trajectory of the decode workload,
     warm (back to back, state may stay in the 256 MB MALL) and cold (a 1 GB buffer
-    written between steps)."""
+    read between steps)."""
     from workloads import DECODE
     from workloads import device as wdev
     cfg = DECODE
@@ -130,10 +130,11 @@ def run_decode(ss, torch, dev, steps, warmup):
     e1.record()
     torch.cuda.synchronize()
     warm_ms = e0.elapsed_time(e1) / steps
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    # evict the 256 MB MALL with 1 GB of reads (clean lines, nothing to write back)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     cold = 0.0
     for _ in range(steps):
-        flush.fill_(1)
+        flush.sum()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         ss.state_update(state, *args, **kw)
@@ -236,11 +237,11 @@ def main():
         "data": "synthetic (seeded Philox4x32-10 draws through an inverse-normal table, generated on the device)",
         "config": {"workload": cfg.name, "batch": cfg.batch, "channels": cfg.dim, "dstate": cfg.dstate,
                    "seq_len": cfg.seqlen, "io": cfg.io, "state": "f32", "plan": {"state_groups": plan[0],
-                   "chunk_len": plan[1]}},
+                   "lanes_per_channel": plan[1], "chunk_len": plan[2]}},
         "hbm_gbs": round(bpt * tokch / (ms_step * 1e-3) / 1e9, 1),
         "roofline": {"bound": "alu", "achieved": round(achieved_slots, 3), "peak": round(VALU_PEAK_TOPS, 3),
                      "unit": "T VALU-slot/s", "frac": round(achieved_slots / VALU_PEAK_TOPS, 4),
-                     "traffic": traffic, "kernel": "scan_kernel<16,4,bf16>", "kernel_ms": round(kern_ms, 5),
+                     "traffic": traffic, "kernel": "scan_kernel<16,%d,%d,bf16>" % (plan[0], plan[1]), "kernel_ms": round(kern_ms, 5),
                      "slots_per_tokch": spt},
         "roofline_hbm": {"achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "bytes_per_tokch": round(bpt, 4)},

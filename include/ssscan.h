@@ -75,15 +75,20 @@ typedef enum {
 } ss_status;
 
 /* Plan of one scan call: how the work is laid onto the GPU.
- *   state_groups: waves per workgroup; each wave owns dstate/state_groups state
- *                 components of 64 channels (1, 2 or 4; at most dstate).
- *   chunk_len:    tokens per sequence chunk; chunk_len >= seqlen means one chunk.
- *                 Chunks are scanned in parallel and joined by an exclusive scan
- *                 of their (decay, end state) pairs, then rescanned from their
- *                 true initial states.  A multiple of the plan's tile length. */
+ *   state_groups:      waves per workgroup (1, 2 or 4); the state components are
+ *                      split over the waves.
+ *   lanes_per_channel: 1 or 2 (0 means 1).  With 2, two adjacent lanes share a
+ *                      channel and split that wave's components again, so a
+ *                      workgroup covers 32 channels instead of 64.
+ *                      state_groups * lanes_per_channel must divide into dstate.
+ *   chunk_len:         tokens per sequence chunk; chunk_len >= seqlen means one
+ *                      chunk.  Chunks are scanned in parallel and joined by an
+ *                      exclusive scan of their (decay, end state) pairs, then
+ *                      rescanned from their true initial states.  A multiple of
+ *                      the tile length, state_groups * (8 for bf16, 4 for fp32). */
 typedef struct {
   int32_t state_groups;
-  int32_t reserved;
+  int32_t lanes_per_channel;
   int64_t chunk_len;
 } ss_scan_plan;
 

@@ -24,7 +24,8 @@ _int = ctypes.c_int
 
 
 class ss_scan_plan(ctypes.Structure):
-    _fields_ = [("state_groups", ctypes.c_int32), ("reserved", ctypes.c_int32), ("chunk_len", ctypes.c_int64)]
+    _fields_ = [("state_groups", ctypes.c_int32), ("lanes_per_channel", ctypes.c_int32),
+                ("chunk_len", ctypes.c_int64)]
 
 
 class SsError(RuntimeError):
@@ -98,16 +99,21 @@ def _plan_ptr(plan):
         return None
     if isinstance(plan, ss_scan_plan):
         return ctypes.byref(plan)
-    groups, chunk_len = plan
-    return ctypes.byref(ss_scan_plan(int(groups), 0, int(chunk_len)))
+    if len(plan) == 2:
+        groups, chunk_len = plan
+        lanes = 1
+    else:
+        groups, lanes, chunk_len = plan
+    return ctypes.byref(ss_scan_plan(int(groups), int(lanes), int(chunk_len)))
 
 
 # --- the C entry points, same names, raw pointers (ints) -----------------------
 
 def ss_scan_fwd_plan(batch, dim, dstate, seqlen, io):
+    """The automatic plan: (state_groups, lanes_per_channel, chunk_len)."""
     p = ss_scan_plan()
     _check(lib.ss_scan_fwd_plan(batch, dim, dstate, seqlen, io, ctypes.byref(p)))
-    return int(p.state_groups), int(p.chunk_len)
+    return int(p.state_groups), int(p.lanes_per_channel), int(p.chunk_len)
 
 
 def ss_scan_fwd_workspace_bytes(batch, dim, dstate, seqlen, io, plan=None) -> int:

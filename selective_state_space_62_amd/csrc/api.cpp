@@ -85,6 +85,7 @@ ss_status check_sizes(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss
 
 struct Plan {
   int groups;
+  int lanes;
   int64_t chunk_len;
   int num_chunks;
   int tile;
@@ -92,15 +93,20 @@ struct Plan {
 
 int io_code(ss_dtype io) { return io == SS_BF16 ? ssscan::kIoBf16 : ssscan::kIoF32; }
 
-// Automatic plan.  Wave groups: 4 when N allows (more waves in flight for the
-// same work, state components spread over SIMDs).  Chunking doubles the VALU
-// work of all but the first chunk, so it is used only when the unchunked launch
-// would leave most SIMDs idle; then chunks are sized for ~4 waves per SIMD.
+// Automatic plan.  Four waves per workgroup split the state components, and for
+// N >= 8 two lanes per channel split them further, so a workgroup covers 32
+// channels: twice as many equal workgroups for the same work, which evens out
+// the per-CU load when the workgroup count is not a multiple of the CU count.
+// Chunking doubles the VALU work of all but the first chunk, so it is used only
+// when the unchunked launch would leave most SIMDs idle; then chunks are sized
+// for ~4 waves per SIMD.
 Plan auto_plan(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io) {
   Plan p;
   p.groups = dstate >= 4 ? 4 : dstate;
+  p.lanes = dstate >= 8 ? 2 : 1;
   p.tile = ssscan::tile_len(p.groups, io_code(io));
-  const int64_t wgs = ((dim + 63) / 64) * batch;
+  const int64_t cpb = 64 / p.lanes;
+  const int64_t wgs = ((dim + cpb - 1) / cpb) * batch;
   const int64_t waves = wgs * p.groups;
   const int64_t simds = (int64_t)device_cus() * 4;
   int64_t chunks = 1;
@@ -126,9 +132,14 @@ ss_status make_plan(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_d
   }
   Plan p;
   p.groups = in->state_groups;
+  p.lanes = in->lanes_per_channel == 0 ? 1 : in->lanes_per_channel;
   if (!(p.groups == 1 || p.groups == 2 || p.groups == 4) || p.groups > dstate)
     return fail(SS_ERR_UNSUPPORTED, "plan.state_groups %d must be 1, 2 or 4 and at most dstate (%d)", p.groups,
                 dstate);
+  if (!(p.lanes == 1 || p.lanes == 2) || p.groups * p.lanes > dstate)
+    return fail(SS_ERR_UNSUPPORTED,
+                "plan.lanes_per_channel %d must be 1 or 2, with state_groups * lanes_per_channel <= dstate (%d)",
+                in->lanes_per_channel, dstate);
   p.tile = ssscan::tile_len(p.groups, io_code(io));
   int64_t cl = in->chunk_len;
   if (cl <= 0) return fail(SS_ERR_INVALID_ARG, "plan.chunk_len must be positive (got %lld)", (long long)cl);
@@ -228,7 +239,7 @@ ss_status ss_scan_fwd_plan(int64_t batch, int64_t dim, int dstate, int64_t seqle
   if (!plan_out) return fail(SS_ERR_INVALID_ARG, "plan_out is NULL");
   const Plan p = auto_plan(batch, dim, dstate, seqlen, io);
   plan_out->state_groups = p.groups;
-  plan_out->reserved = 0;
+  plan_out->lanes_per_channel = p.lanes;
   plan_out->chunk_len = p.chunk_len;
   return SS_OK;
 }
@@ -310,11 +321,12 @@ ss_status ss_scan_fwd(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss
   dm.num_chunks = p.num_chunks;
   dm.dstate = dstate;
   dm.groups = p.groups;
+  dm.lanes = p.lanes;
   dm.io = io_code(io);
-  const int per_span = io == SS_BF16 ? 8 : 4;
-  dm.vec = (seqlen % per_span) == 0 ? 1 : 0;
+  dm.vec = (seqlen % ssscan::span_len(p.lanes, dm.io)) == 0 ? 1 : 0;
 
-  const int64_t nwg = ((dim + 63) / 64) * batch * p.num_chunks;
+  const int64_t cpb = 64 / p.lanes;
+  const int64_t nwg = ((dim + cpb - 1) / cpb) * batch * p.num_chunks;
   if (nwg > 0x7fffffffLL) return fail(SS_ERR_INVALID_ARG, "launch needs %lld workgroups (limit 2^31-1)", (long long)nwg);
 
   char* ws = static_cast<char*>(workspace);

@@ -36,64 +36,87 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// Element i of a 16-byte span held as four 32-bit words.
-template <typename IO>
-__device__ __forceinline__ float span_elem(const uint32_t (&w)[4], int i);
-template <>
-__device__ __forceinline__ float span_elem<F32>(const uint32_t (&w)[4], int i) { return __uint_as_float(w[i]); }
-template <>
-__device__ __forceinline__ float span_elem<BF16>(const uint32_t (&w)[4], int i) {
-  return (i & 1) ? __uint_as_float(w[i >> 1] & 0xffff0000u) : __uint_as_float(w[i >> 1] << 16);
+// A span is SPAN consecutive elements of one row, loaded or stored with one
+// vector access of SPAN * sizeof(element) bytes (16, 8 or 4) and held as 32-bit
+// words.
+template <typename IO, int SPAN>
+struct SpanT {
+  static constexpr int kBytes = SPAN * (int)sizeof(typename IO::T);
+  static constexpr int kWords = kBytes / 4;
+  static_assert(kBytes == 16 || kBytes == 8 || kBytes == 4, "span must be 4, 8 or 16 bytes");
+};
+
+// Element i of a span held as 32-bit words.
+template <typename IO, int W>
+__device__ __forceinline__ float span_elem(const uint32_t (&w)[W], int i) {
+  if constexpr (IO::kPerSpan == 4) {
+    return __uint_as_float(w[i]);
+  } else {
+    return (i & 1) ? __uint_as_float(w[i >> 1] & 0xffff0000u) : __uint_as_float(w[i >> 1] << 16);
+  }
 }
 
-// Load elements [idx, idx + kPerSpan) of `base`; elements at or beyond `valid`
-// (counted from idx) read as zero.  `vec` allows one 16-byte load when the whole
-// span is valid (the caller guarantees 16-byte alignment then).
-template <typename IO>
+// Load elements [idx, idx + SPAN) of `base`; elements at or beyond `valid`
+// (counted from idx) read as zero.  `vec` allows one vector load when the whole
+// span is valid (the caller guarantees the alignment then).
+template <typename IO, int SPAN>
 __device__ __forceinline__ void load_span(const typename IO::T* __restrict__ base, int64_t idx, int valid,
-                                          bool vec, uint32_t (&w)[4]) {
-  if (vec && valid >= IO::kPerSpan) {
-    const uint4 v = *reinterpret_cast<const uint4*>(base + idx);
-    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+                                          bool vec, uint32_t (&w)[SpanT<IO, SPAN>::kWords]) {
+  constexpr int B = SpanT<IO, SPAN>::kBytes;
+  if (vec && valid >= SPAN) {
+    if constexpr (B == 16) {
+      const uint4 v = *reinterpret_cast<const uint4*>(base + idx);
+      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else if constexpr (B == 8) {
+      const uint2 v = *reinterpret_cast<const uint2*>(base + idx);
+      w[0] = v.x; w[1] = v.y;
+    } else {
+      w[0] = *reinterpret_cast<const uint32_t*>(base + idx);
+    }
     return;
   }
-  w[0] = w[1] = w[2] = w[3] = 0u;
+#pragma unroll
+  for (int k = 0; k < SpanT<IO, SPAN>::kWords; ++k) w[k] = 0u;
   if constexpr (IO::kPerSpan == 4) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < SPAN; ++i)
       if (i < valid) w[i] = __float_as_uint(base[idx + i]);
   } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < SPAN; ++i)
       if (i < valid) w[i >> 1] |= (uint32_t)base[idx + i] << ((i & 1) * 16);
   }
 }
 
-// Store the first `valid` of kPerSpan values at base[idx...].
-template <typename IO>
+// Store the first `valid` of SPAN values at base[idx...].
+template <typename IO, int SPAN>
 __device__ __forceinline__ void store_span(typename IO::T* __restrict__ base, int64_t idx, int valid, bool vec,
-                                           const float (&v)[IO::kPerSpan]) {
-  if constexpr (IO::kPerSpan == 4) {
-    if (vec && valid >= 4) {
-      *reinterpret_cast<float4*>(base + idx) = make_float4(v[0], v[1], v[2], v[3]);
-      return;
-    }
+                                           const float (&v)[SPAN]) {
+  constexpr int B = SpanT<IO, SPAN>::kBytes;
+  if (vec && valid >= SPAN) {
+    uint32_t o[SpanT<IO, SPAN>::kWords];
+    if constexpr (IO::kPerSpan == 4) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (i < valid) base[idx + i] = v[i];
-  } else {
-    if (vec && valid >= 8) {
-      uint4 o;
-      o.x = pack_bf16x2(v[0], v[1]);
-      o.y = pack_bf16x2(v[2], v[3]);
-      o.z = pack_bf16x2(v[4], v[5]);
-      o.w = pack_bf16x2(v[6], v[7]);
-      *reinterpret_cast<uint4*>(base + idx) = o;
-      return;
-    }
+      for (int i = 0; i < SPAN; ++i) o[i] = __float_as_uint(v[i]);
+    } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (i < valid) base[idx + i] = (uint16_t)float_to_bf16_bits(v[i]);
+      for (int i = 0; i < SPAN; i += 2) o[i >> 1] = pack_bf16x2(v[i], v[i + 1]);
+    }
+    if constexpr (B == 16) {
+      *reinterpret_cast<uint4*>(base + idx) = make_uint4(o[0], o[1], o[2], o[3]);
+    } else if constexpr (B == 8) {
+      *reinterpret_cast<uint2*>(base + idx) = make_uint2(o[0], o[1]);
+    } else {
+      *reinterpret_cast<uint32_t*>(base + idx) = o[0];
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < SPAN; ++i) {
+    if (i < valid) {
+      if constexpr (IO::kPerSpan == 4) base[idx + i] = v[i];
+      else base[idx + i] = (uint16_t)float_to_bf16_bits(v[i]);
+    }
   }
 }
 

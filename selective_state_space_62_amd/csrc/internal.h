@@ -17,10 +17,10 @@ struct ScanDims {
   int64_t chunk_len;    // tokens per chunk (a multiple of the tile length)
   int32_t num_chunks;   // ceil(seqlen / chunk_len)
   int32_t dstate;       // N
-  int32_t groups;       // waves per workgroup, each owning dstate/groups states
+  int32_t groups;       // waves per workgroup
   int32_t io;           // IoType
-  int32_t vec;          // 1: rows are 16-byte aligned, 16-byte vector loads allowed
-  int32_t pad_;
+  int32_t vec;          // 1: every lane's span of a row is aligned for one vector access
+  int32_t lanes;        // lanes per channel (1 or 2); each lane owns dstate/(groups*lanes) states
 };
 
 struct ScanPtrs {
@@ -41,6 +41,8 @@ struct ScanPtrs {
 
 // Tokens per tile: each wave loads 16 bytes of every input row per tile.
 inline int tile_len(int groups, int io) { return groups * (io == kIoBf16 ? 8 : 4); }
+// Tokens of a row each lane loads per tile (its span).
+inline int span_len(int lanes, int io) { return (io == kIoBf16 ? 8 : 4) / lanes; }
 
 hipError_t launch_prep_bc(const ScanDims& dm, const void* B, const void* C, float* bc, hipStream_t s);
 hipError_t launch_scan(const ScanDims& dm, const ScanPtrs& p, bool aggregate, hipStream_t s);

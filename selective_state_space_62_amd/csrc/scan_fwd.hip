@@ -7,12 +7,15 @@
 // token) is never written to HBM; here it lives in VGPRs for the whole sequence.
 //
 // Mapping onto CDNA4:
-//  * One workgroup = 64 channels of one batch row (one channel per lane) and G
-//    waves.  Wave w owns state components [w N/G, (w+1) N/G) of all 64 channels,
-//    so the B_t, C_t values a wave needs are the same in every lane.
+//  * One workgroup = 64/K channels of one batch row and G waves; each channel
+//    has K adjacent lanes (K = 1 or 2) in every wave.  The N state components are
+//    split into G*K groups: lane k of a channel in wave w owns group w K + k.
+//    K = 2 halves the channels per workgroup, so there are twice as many equal
+//    workgroups (for the 2.8B-shaped layer 1280, exactly 5 per CU, where 640
+//    leave half the CUs with one more than the rest).
 //  * Tiles of T = G * 16B/elem tokens.  Each wave loads 16 bytes of x, dt, z per
-//    lane for its own T/G tokens, computes Delta and Delta*x once per
-//    (token, channel), and shares them with the other waves through LDS.  The
+//    channel for its own T/G tokens (16/K bytes per lane), computes Delta and
+//    Delta*x once per (token, channel), and shares them through LDS.  The
 //    tile's B and C (from a per-call fp32 re-layout, prep_bc_kernel) are staged in
 //    LDS with one 16-byte load per thread and read back as same-address
 //    (broadcast) LDS loads.  Everything the inner loop waits on is an in-order
@@ -20,10 +23,11 @@
 //    B/C and stalled every token (they return out of order, so each use waits
 //    for all outstanding scalar and LDS accesses).  All global loads of the next
 //    tile are issued one tile ahead.
-//  * Every wave runs its state components through all T tokens of the tile and
-//    writes one partial readout per (token, channel) to LDS; the owner of a token
-//    sums the G partials in a fixed order (deterministic results), adds the skip
-//    term, applies the gate and writes 16 bytes of y per lane.
+//  * Every lane runs its state components through all T tokens of the tile; the
+//    K lanes of a channel add their readouts with one DPP add, and each wave
+//    writes one partial readout per (token, channel) to LDS.  The owner of a
+//    token sums the G partials in a fixed order (deterministic results), adds the
+//    skip term, applies the gate and writes its span of y.
 //  * The per-(token, state) work is exp2, two multiplies and two FMAs; transcendentals
 //    are half-rate on gfx950 and do not co-issue with FMAs, so the kernel is bound
 //    by VALU issue, not by HBM.
@@ -87,34 +91,43 @@ struct BcPiece<1> {
   static constexpr int kFloats = 2;
 };
 
-template <int N, int G, typename IO, bool AGG>
+template <int N, int G, int K, typename IO, bool AGG>
 __global__ __launch_bounds__(64 * G) void scan_kernel(
     const ScanDims dm, const typename IO::T* __restrict__ x, const typename IO::T* __restrict__ dt,
     const typename IO::T* __restrict__ z, const float* __restrict__ bc, const float* __restrict__ A,
     const float* __restrict__ Dskip, const float* __restrict__ dt_bias, const float* __restrict__ h0,
     const float* __restrict__ h_in, typename IO::T* __restrict__ y, float* __restrict__ h_final,
     float* __restrict__ agg_h, float* __restrict__ agg_s) {
-  constexpr int NS = N / G;              // state components per wave
-  constexpr int TPW = IO::kPerSpan;      // tokens owned per wave per tile
+  constexpr int CPB = 64 / K;            // channels per workgroup (K adjacent lanes per channel)
+  constexpr int SG = G * K;              // state groups (one per lane of a channel per wave)
+  constexpr int NS = N / SG;             // state components per lane
+  constexpr int TPW = IO::kPerSpan;      // tokens owned per wave per tile (16 bytes of a row)
+  constexpr int SPAN = TPW / K;          // of which each lane of a channel owns SPAN
   constexpr int T = TPW * G;             // tile length
   constexpr int THREADS = 64 * G;
+  constexpr int SW = SpanT<IO, SPAN>::kWords;
   using Piece = typename BcPiece<N>::V;
   constexpr int PF = BcPiece<N>::kFloats;
   constexpr int BC_PIECES = T * 2 * N / PF;                      // pieces of B/C per tile
   constexpr int BC_PER_THREAD = (BC_PIECES + THREADS - 1) / THREADS;
   constexpr int TOK_PIECES = 2 * N / PF;                         // pieces per token
-  static_assert(NS >= 1 && N % G == 0, "G must divide N");
+  static_assert(NS >= 1 && N % SG == 0, "G * K must divide N");
+  static_assert(K == 1 || K == 2, "one or two lanes per channel");
+  constexpr bool SHARE_DD = (G * K) > 1;   // Delta is computed once and shared through LDS
 
-  __shared__ float2 s_dd[G > 1 ? T : 1][64];                 // (Delta, Delta*x) per token and channel
-  __shared__ float s_part[(G > 1 && !AGG) ? T : 1][G][64];   // partial readouts per token, wave, channel
-  __shared__ Piece s_bc[BC_PIECES];                          // the tile's B_n, C_n (token-major, n, B/C)
+  __shared__ float2 s_dd[SHARE_DD ? T : 1][CPB];              // (Delta, Delta*x) per token and channel
+  __shared__ float s_part[(SHARE_DD && !AGG) ? T : 1][G][CPB];   // partial readouts per token, wave, channel
+  __shared__ Piece s_bc[BC_PIECES];                           // the tile's B_n, C_n (token-major, n, B/C)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  const int c = lane / K;                 // channel within the block
+  const int hk = lane % K;                // lane of the channel
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int sg = w * K + hk;              // state group of this lane
 
   // logical block -> (chunk, batch row, channel block), channel block fastest
-  const int64_t cblocks = (dm.dim + 63) >> 6;
+  const int64_t cblocks = (dm.dim + CPB - 1) / CPB;
   const int64_t nwg = cblocks * dm.batch * dm.num_chunks;
   int64_t lb = xcd_logical_block(blockIdx.x, nwg);
   const int64_t cb = lb % cblocks;
@@ -122,7 +135,7 @@ __global__ __launch_bounds__(64 * G) void scan_kernel(
   const int64_t b = lb % dm.batch;
   const int64_t chunk = lb / dm.batch;
 
-  const int64_t d = cb * 64 + lane;
+  const int64_t d = cb * CPB + c;
   const bool act = d < dm.dim;
   const int64_t dc = act ? d : dm.dim - 1;   // clamped: inactive lanes compute on a valid row
   const int64_t L = dm.seqlen;
@@ -135,7 +148,7 @@ __global__ __launch_bounds__(64 * G) void scan_kernel(
 
   float A2[NS];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) A2[s] = A[dc * N + w * NS + s] * kLog2e;
+  for (int s = 0; s < NS; ++s) A2[s] = A[dc * N + sg * NS + s] * kLog2e;
   const float bias2 = dt_bias ? dt_bias[dc] * kLog2e : 0.0f;
   const float skip = Dskip ? Dskip[dc] : 0.0f;
 
@@ -143,8 +156,8 @@ __global__ __launch_bounds__(64 * G) void scan_kernel(
   {
     const float* hi = nullptr;
     if constexpr (!AGG) {
-      if (h_in) hi = h_in + (ch * dm.num_chunks + chunk) * N + w * NS;
-      else if (h0) hi = h0 + ch * N + w * NS;
+      if (h_in) hi = h_in + (ch * dm.num_chunks + chunk) * N + sg * NS;
+      else if (h0) hi = h0 + ch * N + sg * NS;
     }
 #pragma unroll
     for (int s = 0; s < NS; ++s) h[s] = hi ? hi[s] : 0.0f;
@@ -163,31 +176,37 @@ __global__ __launch_bounds__(64 * G) void scan_kernel(
       else cbc[k] = Piece{};
     }
   };
+  // first token of the span this lane owns in the tile starting at ts
+  auto own_first = [&](int64_t ts) { return ts + w * TPW + hk * SPAN; };
+  auto own_valid = [&](int64_t first) {
+    const int64_t v = t1 - first;
+    return (int)(v < 0 ? 0 : (v < SPAN ? v : SPAN));
+  };
 
-  // raw 16-byte spans of x, dt, z for this wave's tokens of the current tile (prefetched a tile ahead)
-  uint32_t cx[4], cdt[4], cz[4];
+  // raw spans of x, dt, z for this lane's tokens of the current tile (prefetched a tile ahead)
+  uint32_t cx[SW], cdt[SW], cz[SW];
   {
-    const int64_t tw = t0 + w * TPW;
-    const int valid = (int)((t1 - tw) < TPW ? (t1 - tw) : TPW);
-    load_span<IO>(x, row + tw, valid, vec, cx);
-    load_span<IO>(dt, row + tw, valid, vec, cdt);
-    if (has_z) load_span<IO>(z, row + tw, valid, vec, cz);
+    const int64_t tf = own_first(t0);
+    const int valid = own_valid(tf);
+    load_span<IO, SPAN>(x, row + tf, valid, vec, cx);
+    load_span<IO, SPAN>(dt, row + tf, valid, vec, cdt);
+    if (has_z) load_span<IO, SPAN>(z, row + tf, valid, vec, cz);
     load_bc_tile(t0);
   }
 
   for (int64_t ts = t0; ts < t1; ts += T) {
-    const int64_t tw = ts + w * TPW;                      // first token owned by this wave
-    const int64_t vown = t1 - tw;
-    const int valid = (int)(vown < 0 ? 0 : (vown < TPW ? vown : TPW));
+    const int64_t tf = own_first(ts);
+    const int valid = own_valid(tf);
+    const bool full = ts + T <= t1;
 
     // phase A: Delta and Delta*x for the owned tokens; stage the B/C tile
-    float xv[TPW], zv[TPW], dl[TPW], dx[TPW];
+    float xv[SPAN], zv[SPAN], dl[SPAN], dx[SPAN];
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
+    for (int i = 0; i < SPAN; ++i) {
       xv[i] = span_elem<IO>(cx, i);
       zv[i] = has_z ? span_elem<IO>(cz, i) : 0.0f;
       const float delta = softplus_dt(span_elem<IO>(cdt, i), bias2);
-      dl[i] = (i < valid) ? delta : 0.0f;                 // padding tokens leave the state alone
+      dl[i] = (full || i < valid) ? delta : 0.0f;         // padding tokens leave the state alone
       dx[i] = dl[i] * xv[i];
     }
 #pragma unroll
@@ -195,26 +214,25 @@ __global__ __launch_bounds__(64 * G) void scan_kernel(
       if (tid + k * THREADS < BC_PIECES) s_bc[tid + k * THREADS] = cbc[k];
     // prefetch the next tile
     if (ts + T < t1) {
-      const int64_t tn = tw + T;
-      const int64_t vn = t1 - tn;
-      const int validn = (int)(vn < 0 ? 0 : (vn < TPW ? vn : TPW));
-      load_span<IO>(x, row + tn, validn, vec, cx);
-      load_span<IO>(dt, row + tn, validn, vec, cdt);
-      if (has_z) load_span<IO>(z, row + tn, validn, vec, cz);
+      const int64_t tn = tf + T;
+      const int validn = own_valid(tn);
+      load_span<IO, SPAN>(x, row + tn, validn, vec, cx);
+      load_span<IO, SPAN>(dt, row + tn, validn, vec, cdt);
+      if (has_z) load_span<IO, SPAN>(z, row + tn, validn, vec, cz);
       load_bc_tile(ts + T);
     }
-    if constexpr (G > 1) {
+    if constexpr (SHARE_DD) {
 #pragma unroll
-      for (int i = 0; i < TPW; ++i) s_dd[w * TPW + i][lane] = make_float2(dl[i], dx[i]);
+      for (int i = 0; i < SPAN; ++i) s_dd[w * TPW + hk * SPAN + i][c] = make_float2(dl[i], dx[i]);
     }
     __syncthreads();
 
-    // phase B: this wave's state components through every token of the tile
-    float yp[G == 1 ? T : 1];
+    // phase B: this lane's state components through every token of the tile
+    float yp[SHARE_DD ? 1 : T];
     auto step = [&](int j) {
       float dj, dxj;
-      if constexpr (G > 1) {
-        const float2 v = s_dd[j][lane];
+      if constexpr (SHARE_DD) {
+        const float2 v = s_dd[j][c];
         dj = v.x;
         dxj = v.y;
       } else {
@@ -223,7 +241,7 @@ __global__ __launch_bounds__(64 * G) void scan_kernel(
       }
       float bcv[2 * NS];
       {
-        const float* src = reinterpret_cast<const float*>(s_bc) + j * (2 * N) + 2 * w * NS;
+        const float* src = reinterpret_cast<const float*>(s_bc) + j * (2 * N) + 2 * sg * NS;
         if constexpr (NS == 1) {
           const float2 v = *reinterpret_cast<const float2*>(src);
           bcv[0] = v.x;
@@ -248,13 +266,15 @@ __global__ __launch_bounds__(64 * G) void scan_kernel(
       }
       if constexpr (AGG) {
         dsum += dj;
-      } else if constexpr (G > 1) {
-        s_part[j][w][lane] = acc;
       } else {
-        yp[j] = acc;
+        // both lanes of a channel end with the channel's sum over this wave's components
+        if constexpr (K == 2) acc += __builtin_amdgcn_update_dpp(0.0f, acc, 0xB1, 0xf, 0xf, false);
+        if constexpr (G > 1) s_part[j][w][c] = acc;
+        else if constexpr (!SHARE_DD) yp[j] = acc;
+        else s_part[j][0][c] = acc;
       }
     };
-    if (ts + T <= t1) {
+    if (full) {
 #pragma unroll
       for (int j = 0; j < T; ++j) step(j);
     } else {
@@ -266,37 +286,36 @@ __global__ __launch_bounds__(64 * G) void scan_kernel(
 
     // phase C: the owner of each token sums the partial readouts, adds the skip
     // term, applies the gate and stores y
-    if constexpr (G > 1) __syncthreads();
+    if constexpr (SHARE_DD) __syncthreads();
     if constexpr (!AGG) {
-      float yv[TPW];
+      float yv[SPAN];
 #pragma unroll
-      for (int i = 0; i < TPW; ++i) {
+      for (int i = 0; i < SPAN; ++i) {
         float acc;
-        if constexpr (G > 1) {
-          acc = s_part[w * TPW + i][0][lane];
+        if constexpr (SHARE_DD) {
+          const int j = w * TPW + hk * SPAN + i;
+          acc = s_part[j][0][c];
 #pragma unroll
-          for (int g = 1; g < G; ++g) acc += s_part[w * TPW + i][g][lane];
+          for (int g = 1; g < G; ++g) acc += s_part[j][g][c];
         } else {
           acc = yp[i];
         }
         const float gate = has_z ? silu(zv[i]) : 1.0f;
         yv[i] = fmaf(skip, xv[i], acc) * gate;
       }
-      if (act && valid > 0) store_span<IO>(y, row + tw, valid, vec, yv);
+      if (act && valid > 0) store_span<IO, SPAN>(y, row + tf, valid, vec, yv);
     }
   }
 
-  if constexpr (AGG) {
-    if (act) {
-      float* o = agg_h + (ch * dm.num_chunks + chunk) * N + w * NS;
+  if (act) {
+    if constexpr (AGG) {
+      float* o = agg_h + (ch * dm.num_chunks + chunk) * N + sg * NS;
 #pragma unroll
       for (int s = 0; s < NS; ++s) o[s] = h[s];
-      if (w == 0) agg_s[ch * dm.num_chunks + chunk] = dsum;
-    }
-  } else {
-    if (h_final && act && chunk == dm.num_chunks - 1) {
+      if (sg == 0) agg_s[ch * dm.num_chunks + chunk] = dsum;
+    } else if (h_final && chunk == dm.num_chunks - 1) {
 #pragma unroll
-      for (int s = 0; s < NS; ++s) h_final[ch * N + w * NS + s] = h[s];
+      for (int s = 0; s < NS; ++s) h_final[ch * N + sg * NS + s] = h[s];
     }
   }
 }
@@ -328,23 +347,32 @@ __global__ __launch_bounds__(256) void copy_state_kernel(int64_t count, const fl
   if (i < count) dst[i] = src ? src[i] : 0.0f;
 }
 
-template <int N, int G, typename IO, bool AGG>
+template <int N, int G, int K, typename IO, bool AGG>
 hipError_t launch_scan_t(const ScanDims& dm, const ScanPtrs& p, hipStream_t s) {
   using E = typename IO::T;
-  const int64_t cblocks = (dm.dim + 63) / 64;
+  const int64_t cblocks = (dm.dim + 64 / K - 1) / (64 / K);
   const int64_t nwg = cblocks * dm.batch * dm.num_chunks;
-  hipLaunchKernelGGL((scan_kernel<N, G, IO, AGG>), dim3((unsigned)nwg), dim3(64 * G), 0, s, dm,
+  hipLaunchKernelGGL((scan_kernel<N, G, K, IO, AGG>), dim3((unsigned)nwg), dim3(64 * G), 0, s, dm,
                      (const E*)p.x, (const E*)p.dt, (const E*)p.z, p.bc, p.A, p.Dskip, p.dt_bias, p.h0, p.h_in,
                      (E*)p.y, p.h_final, p.agg_h, p.agg_s);
   return hipGetLastError();
 }
 
+template <int N, int G, typename IO, bool AGG>
+hipError_t launch_scan_k(const ScanDims& dm, const ScanPtrs& p, hipStream_t s) {
+  if (dm.lanes == 1) return launch_scan_t<N, G, 1, IO, AGG>(dm, p, s);
+  if constexpr (N >= 2 * G) {
+    if (dm.lanes == 2) return launch_scan_t<N, G, 2, IO, AGG>(dm, p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <int N, typename IO, bool AGG>
 hipError_t launch_scan_g(const ScanDims& dm, const ScanPtrs& p, hipStream_t s) {
   switch (dm.groups) {
-    case 1: return launch_scan_t<N, 1, IO, AGG>(dm, p, s);
-    case 2: if constexpr (N >= 2) return launch_scan_t<N, 2, IO, AGG>(dm, p, s); else break;
-    case 4: if constexpr (N >= 4) return launch_scan_t<N, 4, IO, AGG>(dm, p, s); else break;
+    case 1: return launch_scan_k<N, 1, IO, AGG>(dm, p, s);
+    case 2: if constexpr (N >= 2) return launch_scan_k<N, 2, IO, AGG>(dm, p, s); else break;
+    case 4: if constexpr (N >= 4) return launch_scan_k<N, 4, IO, AGG>(dm, p, s); else break;
     default: break;
   }
   return hipErrorInvalidValue;

@@ -88,6 +88,8 @@ def _scan_status(**kw):
     (dict(plan=(4, 24)), b.SS_ERR_INVALID_ARG),                  # not a multiple of the 16-token tile
     (dict(plan=(1, 0)), b.SS_ERR_INVALID_ARG),
     (dict(shape=(2, 64, 2, 256), plan=(4, 256)), b.SS_ERR_UNSUPPORTED),   # more groups than states
+    (dict(shape=(2, 64, 4, 256), plan=(4, 2, 256)), b.SS_ERR_UNSUPPORTED),  # 8 state groups > 4 states
+    (dict(plan=(4, 3, 256)), b.SS_ERR_UNSUPPORTED),                        # 3 lanes per channel
     (dict(shape=(1 << 41, 64, 16, 256)), b.SS_ERR_INVALID_ARG),
 ])
 def test_scan_validation(case, status):
@@ -119,12 +121,12 @@ def test_workspace_bytes():
 
 
 def test_plan_choice():
-    g, cl = b.ss_scan_fwd_plan(8, 5120, 16, 2048, b.SS_BF16)
-    assert g == 4 and cl >= 2048                      # enough channels: one chunk
-    g, cl = b.ss_scan_fwd_plan(1, 2048, 16, 1 << 20, b.SS_BF16)
-    assert g == 4 and cl < (1 << 20) and cl % 32 == 0  # few channels, long sequence: chunked
-    g, cl = b.ss_scan_fwd_plan(1, 16, 2, 64, b.SS_F32)
-    assert g == 2
+    g, k, cl = b.ss_scan_fwd_plan(8, 5120, 16, 2048, b.SS_BF16)
+    assert (g, k) == (4, 2) and cl >= 2048                 # enough channels: one chunk
+    g, k, cl = b.ss_scan_fwd_plan(1, 2048, 16, 1 << 20, b.SS_BF16)
+    assert g == 4 and cl < (1 << 20) and cl % 32 == 0      # few channels, long sequence: chunked
+    g, k, cl = b.ss_scan_fwd_plan(1, 16, 2, 64, b.SS_F32)
+    assert (g, k) == (2, 1)
 
 
 @pytest.mark.parametrize("case,status", [

@@ -62,7 +62,8 @@ def test_device_generator_matches_host(dev):
 
 # ---------------------------------------------------------- small and ragged ---
 
-@pytest.mark.parametrize("plan", [None, (1, 64), (2, 64), (4, 64), (4, 16), (1, 4), (2, 8), (4, 32)])
+@pytest.mark.parametrize("plan", [None, (1, 64), (2, 64), (4, 64), (4, 16), (1, 4), (2, 8), (4, 32),
+                                  (1, 2, 64), (2, 2, 64), (2, 2, 8), (1, 2, 4)])
 def test_tiny_workload_all_plans(ss, o, dev, plan):
     cfg = TINY
     log("tiny workload, plan %s" % (plan,))
@@ -89,10 +90,16 @@ RAGGED = [
     (1, 64, 16, 8, "bf16", True, True, True, True, (1, 8)),
     (1, 64, 1, 33, "f32", True, True, True, True, (1, 8)),
     (4, 33, 16, 2, "f32", True, True, True, True, None),
+    (2, 100, 16, 37, "f32", True, True, True, True, (4, 2, 1 << 20)),
+    (3, 65, 8, 129, "bf16", True, False, True, False, (4, 2, 1 << 20)),
+    (2, 200, 16, 515, "bf16", True, True, True, True, (4, 2, 128)),
+    (1, 31, 16, 301, "bf16", True, True, True, True, (2, 2, 48)),
+    (2, 64, 2, 77, "f32", True, True, True, True, (1, 2, 12)),
+    (1, 33, 4, 1000, "bf16", False, True, False, True, (2, 2, 64)),
 ]
 
 
-@pytest.mark.parametrize("case", RAGGED, ids=["-".join(map(str, c[:5])) + "-" + str(c[9]) for c in RAGGED])
+@pytest.mark.parametrize("case", RAGGED, ids=["-".join(map(str, c[:5])) + "-" + str(c[9]).replace(" ", "") for c in RAGGED])
 def test_ragged_shapes(ss, o, dev, case):
     batch, D, N, L, io, wz, wsk, wb, wh, plan = case
     log("ragged %s" % (case,))
@@ -223,7 +230,7 @@ def test_long_context_bf16_sampled(ss, o, dev):
     cfg = LONG
     plan = ss.ss_scan_fwd_plan(cfg.batch, cfg.dim, cfg.dstate, cfg.seqlen, ss.SS_BF16)
     log("long context, bf16, plan %s" % (plan,))
-    assert plan[1] < cfg.seqlen
+    assert plan[2] < cfg.seqlen
     t, y, hf = _device_scan(ss, cfg, dev)
     chans = inputs.sample_channels(cfg, cfg.check_channels)
     ys, hs, _ = _sampled_oracle(o, cfg, chans, inputs.params(cfg))
