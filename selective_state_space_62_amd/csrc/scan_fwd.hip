@@ -37,6 +37,8 @@
 //    pairs across chunks; the full pass then rescans every chunk from its true
 //    initial state.  The combine (P1, h1) o (P2, h2) = (P1 P2, P2 h1 + h2) follows
 //    from the linearity of the recurrence.
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -91,8 +93,11 @@ struct BcPiece<1> {
   static constexpr int kFloats = 2;
 };
 
+// At most 96 VGPRs (5 waves per SIMD): with 4 waves per workgroup and 28 KB of
+// LDS, five workgroups fit on a CU at once, which the two-lanes-per-channel plan
+// needs to keep every CU's share resident.
 template <int N, int G, int K, typename IO, bool AGG>
-__global__ __launch_bounds__(64 * G) void scan_kernel(
+__global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(5, 10))) void scan_kernel(
     const ScanDims dm, const typename IO::T* __restrict__ x, const typename IO::T* __restrict__ dt,
     const typename IO::T* __restrict__ z, const float* __restrict__ bc, const float* __restrict__ A,
     const float* __restrict__ Dskip, const float* __restrict__ dt_bias, const float* __restrict__ h0,
@@ -184,7 +189,7 @@ __global__ __launch_bounds__(64 * G) void scan_kernel(
   };
 
   // raw spans of x, dt, z for this lane's tokens of the current tile (prefetched a tile ahead)
-  uint32_t cx[SW], cdt[SW], cz[SW];
+  uint32_t cx[SW], cdt[SW], cz[SW] = {};
   {
     const int64_t tf = own_first(t0);
     const int valid = own_valid(tf);
@@ -194,19 +199,22 @@ __global__ __launch_bounds__(64 * G) void scan_kernel(
     load_bc_tile(t0);
   }
 
-  for (int64_t ts = t0; ts < t1; ts += T) {
+  // One tile.  FULL (a compile-time tag) means all T tokens lie inside the chunk:
+  // no per-token masks, no guards in the inner loop.
+  auto tile = [&](auto full_tag, int64_t ts) {
+    constexpr bool FULL = decltype(full_tag)::value;
     const int64_t tf = own_first(ts);
-    const int valid = own_valid(tf);
-    const bool full = ts + T <= t1;
+    const int valid = FULL ? SPAN : own_valid(tf);
 
     // phase A: Delta and Delta*x for the owned tokens; stage the B/C tile
     float xv[SPAN], zv[SPAN], dl[SPAN], dx[SPAN];
 #pragma unroll
     for (int i = 0; i < SPAN; ++i) {
       xv[i] = span_elem<IO>(cx, i);
-      zv[i] = has_z ? span_elem<IO>(cz, i) : 0.0f;
+      zv[i] = span_elem<IO>(cz, i);
       const float delta = softplus_dt(span_elem<IO>(cdt, i), bias2);
-      dl[i] = (full || i < valid) ? delta : 0.0f;         // padding tokens leave the state alone
+      if constexpr (FULL) dl[i] = delta;
+      else dl[i] = (i < valid) ? delta : 0.0f;            // padding tokens leave the state alone
       dx[i] = dl[i] * xv[i];
     }
 #pragma unroll
@@ -227,61 +235,64 @@ __global__ __launch_bounds__(64 * G) void scan_kernel(
     }
     __syncthreads();
 
-    // phase B: this lane's state components through every token of the tile
+    // phase B: this lane's state components through every token of the tile.
+    // The LDS operands of token j + 1 are read before token j is computed.
     float yp[SHARE_DD ? 1 : T];
-    auto step = [&](int j) {
-      float dj, dxj;
+    struct Ops {
+      float d, dx, bcv[2 * NS];
+    };
+    auto fetch = [&](int j, Ops& o) {
       if constexpr (SHARE_DD) {
         const float2 v = s_dd[j][c];
-        dj = v.x;
-        dxj = v.y;
+        o.d = v.x;
+        o.dx = v.y;
       } else {
-        dj = dl[j];
-        dxj = dx[j];
+        o.d = dl[j];
+        o.dx = dx[j];
       }
-      float bcv[2 * NS];
-      {
-        const float* src = reinterpret_cast<const float*>(s_bc) + j * (2 * N) + 2 * sg * NS;
-        if constexpr (NS == 1) {
-          const float2 v = *reinterpret_cast<const float2*>(src);
-          bcv[0] = v.x;
-          bcv[1] = v.y;
-        } else {
+      const float* src = reinterpret_cast<const float*>(s_bc) + j * (2 * N) + 2 * sg * NS;
+      if constexpr (NS == 1) {
+        const float2 v = *reinterpret_cast<const float2*>(src);
+        o.bcv[0] = v.x;
+        o.bcv[1] = v.y;
+      } else {
 #pragma unroll
-          for (int q = 0; q < 2 * NS; q += 4) {
-            const float4 v = *reinterpret_cast<const float4*>(src + q);
-            bcv[q] = v.x;
-            bcv[q + 1] = v.y;
-            bcv[q + 2] = v.z;
-            bcv[q + 3] = v.w;
-          }
+        for (int q = 0; q < 2 * NS; q += 4) {
+          const float4 v = *reinterpret_cast<const float4*>(src + q);
+          o.bcv[q] = v.x;
+          o.bcv[q + 1] = v.y;
+          o.bcv[q + 2] = v.z;
+          o.bcv[q + 3] = v.w;
         }
       }
+    };
+    auto compute = [&](int j, const Ops& o) {
       float acc = 0.0f;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const float E = __builtin_amdgcn_exp2f(dj * A2[s]);
-        h[s] = fmaf(E, h[s], dxj * bcv[2 * s]);
-        if constexpr (!AGG) acc = fmaf(bcv[2 * s + 1], h[s], acc);
+        const float E = __builtin_amdgcn_exp2f(o.d * A2[s]);
+        h[s] = fmaf(E, h[s], o.dx * o.bcv[2 * s]);
+        if constexpr (!AGG) acc = (s == 0) ? o.bcv[1] * h[0] : fmaf(o.bcv[2 * s + 1], h[s], acc);
       }
       if constexpr (AGG) {
-        dsum += dj;
+        dsum += o.d;
       } else {
         // both lanes of a channel end with the channel's sum over this wave's components
         if constexpr (K == 2) acc += __builtin_amdgcn_update_dpp(0.0f, acc, 0xB1, 0xf, 0xf, false);
-        if constexpr (G > 1) s_part[j][w][c] = acc;
-        else if constexpr (!SHARE_DD) yp[j] = acc;
-        else s_part[j][0][c] = acc;
+        if constexpr (SHARE_DD) s_part[j][w][c] = acc;
+        else yp[j] = acc;
       }
     };
-    if (full) {
+    const int nj = FULL ? T : (int)(t1 - ts);
+    Ops cur, nxt;
+    fetch(0, cur);
 #pragma unroll
-      for (int j = 0; j < T; ++j) step(j);
-    } else {
-      const int nj = (int)(t1 - ts);
-#pragma unroll
-      for (int j = 0; j < T; ++j)
-        if (j < nj) step(j);
+    for (int j = 0; j < T; ++j) {
+      if (FULL || j < nj) {
+        if (j + 1 < T && (FULL || j + 1 < nj)) fetch(j + 1, nxt);
+        compute(j, cur);
+        cur = nxt;
+      }
     }
 
     // phase C: the owner of each token sums the partial readouts, adds the skip
@@ -300,11 +311,19 @@ __global__ __launch_bounds__(64 * G) void scan_kernel(
         } else {
           acc = yp[i];
         }
-        const float gate = has_z ? silu(zv[i]) : 1.0f;
-        yv[i] = fmaf(skip, xv[i], acc) * gate;
+        yv[i] = fmaf(skip, xv[i], acc);
       }
-      if (act && valid > 0) store_span<IO, SPAN>(y, row + tf, valid, vec, yv);
+      if (has_z) {
+#pragma unroll
+        for (int i = 0; i < SPAN; ++i) yv[i] *= silu(zv[i]);
+      }
+      if (act && (FULL || valid > 0)) store_span<IO, SPAN>(y, row + tf, valid, vec, yv);
     }
+  };
+
+  for (int64_t ts = t0; ts < t1; ts += T) {
+    if (ts + T <= t1) tile(std::true_type{}, ts);
+    else tile(std::false_type{}, ts);
   }
 
   if (act) {
