@@ -12,15 +12,50 @@
 // 1 KB of contiguous state, so every load and store is fully coalesced.  The
 // readout of the N components is summed across the channel's lanes with DPP
 // quad permutes in a fixed order.  A (dim, N) is re-read per batch row from L2.
+// The state is streamed with non-temporal loads and stores (it is touched once
+// per step), and a bounded grid of workgroups strides over the items, which
+// kept more bytes in flight than one short-lived workgroup per 64 channels.
 #include "device_common.h"
 #include "internal.h"
+
+#ifndef DECODE_UNROLL
+#define DECODE_UNROLL 1
+#endif
+#ifndef DECODE_BLOCKS
+#define DECODE_BLOCKS 2048
+#endif
 
 namespace ssscan {
 namespace {
 
 using namespace dev;
 
-template <int N, typename IO>
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Load Q consecutive elements of a (batch, N) row of B or C as floats (one
+// vector load when Q * sizeof(element) is 8 or 16 bytes).
+template <typename IO, int Q>
+__device__ __forceinline__ void load_q(const typename IO::T* __restrict__ p, float (&v)[Q]) {
+  if constexpr (Q == 4 && IO::kPerSpan == 8) {
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    v[0] = __uint_as_float(w.x << 16);
+    v[1] = __uint_as_float(w.x & 0xffff0000u);
+    v[2] = __uint_as_float(w.y << 16);
+    v[3] = __uint_as_float(w.y & 0xffff0000u);
+  } else if constexpr (Q == 4 && IO::kPerSpan == 4) {
+    const float4 w = *reinterpret_cast<const float4*>(p);
+    v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+  } else {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) v[q] = load_one<IO>(p, q);
+  }
+}
+
+// Grid-stride over waves: each wave handles U x 64 consecutive (channel,
+// component group) items per iteration, all U state loads issued before any
+// arithmetic (more bytes in flight per wave); the loop bound is wave-uniform, so
+// every lane of a channel is active for the DPP sum.
+template <int N, typename IO, int U>
 __global__ __launch_bounds__(256) void state_update_kernel(
     int64_t nch, int64_t dim, float* __restrict__ state, const typename IO::T* __restrict__ x,
     const typename IO::T* __restrict__ dt, const typename IO::T* __restrict__ z,
@@ -28,59 +63,79 @@ __global__ __launch_bounds__(256) void state_update_kernel(
     const float* __restrict__ Dskip, const float* __restrict__ dt_bias, typename IO::T* __restrict__ y) {
   constexpr int Q = N < 4 ? N : 4;   // state components per lane
   constexpr int K = N / Q;           // lanes per channel (1, 2 or 4), adjacent within a quad
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t chr = gid / K;
-  const int j = (int)(gid - chr * K);
-  const bool act = chr < nch;
-  const int64_t ch = act ? chr : nch - 1;   // inactive lanes work on a valid channel, store nothing
-  const int64_t b = ch / dim;
-  const int64_t d = ch - b * dim;
-
-  float st[Q], a2[Q], bq[Q], cq[Q];
-  float* sp = state + ch * N + j * Q;
-  if constexpr (Q == 4) {
-    const float4 v = *reinterpret_cast<const float4*>(sp);
-    st[0] = v.x; st[1] = v.y; st[2] = v.z; st[3] = v.w;
-    const float4 av = *reinterpret_cast<const float4*>(A + d * N + j * Q);
-    a2[0] = av.x; a2[1] = av.y; a2[2] = av.z; a2[3] = av.w;
-  } else {
+  const int64_t items = nch * K;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave0 = ((int64_t)blockIdx.x * blockDim.x + (threadIdx.x & ~63)) * U;
+  const int64_t wstride = (int64_t)gridDim.x * blockDim.x * U;
+  for (int64_t wb = wave0; wb < items; wb += wstride) {
+    bool act[U];
+    int64_t ch[U], b[U], d[U];
+    int j[U];
+    float st[U][Q], a2[U][Q], bq[U][Q], cq[U][Q], xv[U], dtv[U], zv[U];
 #pragma unroll
-    for (int q = 0; q < Q; ++q) {
-      st[q] = sp[q];
-      a2[q] = A[d * N + j * Q + q];
+    for (int u = 0; u < U; ++u) {
+      const int64_t it = wb + u * 64 + lane;
+      act[u] = it < items;
+      const int64_t itc = act[u] ? it : items - 1;   // inactive lanes work on a valid item, store nothing
+      ch[u] = itc / K;
+      j[u] = (int)(itc - ch[u] * K);
+      b[u] = ch[u] / dim;
+      d[u] = ch[u] - b[u] * dim;
+      const float* sp = state + ch[u] * N + j[u] * Q;
+      if constexpr (Q == 4) {
+        const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp));
+        st[u][0] = v[0]; st[u][1] = v[1]; st[u][2] = v[2]; st[u][3] = v[3];
+      } else {
+#pragma unroll
+        for (int q = 0; q < Q; ++q) st[u][q] = sp[q];
+      }
     }
-  }
 #pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    a2[q] *= kLog2e;
-    bq[q] = load_one<IO>(B, b * N + j * Q + q);
-    cq[q] = load_one<IO>(C, b * N + j * Q + q);
-  }
-  const float xv = load_one<IO>(x, ch);
-  const float delta = softplus_dt(load_one<IO>(dt, ch), dt_bias ? dt_bias[d] * kLog2e : 0.0f);
-  const float dx = delta * xv;
-  float acc = 0.0f;
+    for (int u = 0; u < U; ++u) {
+      if constexpr (Q == 4) {
+        const float4 av = *reinterpret_cast<const float4*>(A + d[u] * N + j[u] * Q);
+        a2[u][0] = av.x; a2[u][1] = av.y; a2[u][2] = av.z; a2[u][3] = av.w;
+      } else {
 #pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    const float E = __builtin_amdgcn_exp2f(delta * a2[q]);
-    st[q] = fmaf(E, st[q], dx * bq[q]);
-    acc = fmaf(cq[q], st[q], acc);
-  }
-  // sum the channel's K partial readouts (lanes are adjacent inside one quad)
-  if constexpr (K >= 2) acc += __builtin_amdgcn_update_dpp(0.0f, acc, 0xB1, 0xf, 0xf, false);  // quad_perm [1,0,3,2]
-  if constexpr (K == 4) acc += __builtin_amdgcn_update_dpp(0.0f, acc, 0x4E, 0xf, 0xf, false);  // quad_perm [2,3,0,1]
-
-  if (act) {
-    if constexpr (Q == 4) {
-      *reinterpret_cast<float4*>(sp) = make_float4(st[0], st[1], st[2], st[3]);
-    } else {
-#pragma unroll
-      for (int q = 0; q < Q; ++q) sp[q] = st[q];
+        for (int q = 0; q < Q; ++q) a2[u][q] = A[d[u] * N + j[u] * Q + q];
+      }
+      load_q<IO, Q>(B + b[u] * N + j[u] * Q, bq[u]);
+      load_q<IO, Q>(C + b[u] * N + j[u] * Q, cq[u]);
+      xv[u] = load_one<IO>(x, ch[u]);
+      dtv[u] = load_one<IO>(dt, ch[u]);
+      zv[u] = z ? load_one<IO>(z, ch[u]) : 0.0f;
     }
-    if (j == 0) {
-      float out = fmaf(Dskip ? Dskip[d] : 0.0f, xv, acc);
-      if (z) out *= silu(load_one<IO>(z, ch));
-      store_one<IO>(y, ch, out);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float bias2 = dt_bias ? dt_bias[d[u]] * kLog2e : 0.0f;
+      const float skip = Dskip ? Dskip[d[u]] : 0.0f;
+      const float delta = softplus_dt(dtv[u], bias2);
+      const float dx = delta * xv[u];
+      float acc = 0.0f;
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const float E = __builtin_amdgcn_exp2f(delta * (a2[u][q] * kLog2e));
+        st[u][q] = fmaf(E, st[u][q], dx * bq[u][q]);
+        acc = fmaf(cq[u][q], st[u][q], acc);
+      }
+      // sum the channel's K partial readouts (lanes are adjacent inside one quad)
+      if constexpr (K >= 2) acc += __builtin_amdgcn_update_dpp(0.0f, acc, 0xB1, 0xf, 0xf, false);  // [1,0,3,2]
+      if constexpr (K == 4) acc += __builtin_amdgcn_update_dpp(0.0f, acc, 0x4E, 0xf, 0xf, false);  // [2,3,0,1]
+      if (act[u]) {
+        float* sp = state + ch[u] * N + j[u] * Q;
+        if constexpr (Q == 4) {
+          const f32x4 v = {st[u][0], st[u][1], st[u][2], st[u][3]};
+          __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(sp));
+        } else {
+#pragma unroll
+          for (int q = 0; q < Q; ++q) sp[q] = st[u][q];
+        }
+        if (j[u] == 0) {
+          float out = fmaf(skip, xv[u], acc);
+          if (z) out *= silu(zv[u]);
+          store_one<IO>(y, ch[u], out);
+        }
+      }
     }
   }
 }
@@ -91,10 +146,14 @@ hipError_t launch_t(int64_t nch, int64_t dim, float* state, const void* x, const
                     hipStream_t s) {
   using E = typename IO::T;
   constexpr int K = N < 4 ? 1 : N / 4;
-  const int64_t threads = nch * K;
-  hipLaunchKernelGGL((state_update_kernel<N, IO>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, nch,
-                     dim, state, (const E*)x, (const E*)dt, (const E*)z, (const E*)B, (const E*)C, A, Dskip,
-                     dt_bias, (E*)y);
+  constexpr int U = DECODE_UNROLL;
+  const int64_t threads = (nch * K + U - 1) / U;
+  int64_t blocks = (threads + 255) / 256;
+  // a bounded grid (DECODE_BLOCKS workgroups); the grid-stride loop covers the rest
+  const int64_t cap = DECODE_BLOCKS;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL((state_update_kernel<N, IO, U>), dim3((unsigned)blocks), dim3(256), 0, s, nch, dim, state,
+                     (const E*)x, (const E*)dt, (const E*)z, (const E*)B, (const E*)C, A, Dskip, dt_bias, (E*)y);
   return hipGetLastError();
 }
 
