@@ -172,12 +172,13 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(5, 10)))
   // B/C of this batch row, re-laid out (token, n, {B, C}); pieces never straddle tokens
   const Piece* __restrict__ bc_row = reinterpret_cast<const Piece*>(bc + b * L * (2 * N));
   Piece cbc[BC_PER_THREAD];
-  auto load_bc_tile = [&](int64_t ts) {
+  // `whole`: every token of the tile lies inside the chunk (no per-piece check)
+  auto load_bc_tile = [&](int64_t ts, bool whole) {
 #pragma unroll
     for (int k = 0; k < BC_PER_THREAD; ++k) {
       const int piece = tid + k * THREADS;
       const int64_t tok = ts + piece / TOK_PIECES;
-      if (piece < BC_PIECES && tok < t1) cbc[k] = bc_row[ts * TOK_PIECES + piece];
+      if (piece < BC_PIECES && (whole || tok < t1)) cbc[k] = bc_row[ts * TOK_PIECES + piece];
       else cbc[k] = Piece{};
     }
   };
@@ -196,7 +197,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(5, 10)))
     load_span<IO, SPAN>(x, row + tf, valid, vec, cx);
     load_span<IO, SPAN>(dt, row + tf, valid, vec, cdt);
     if (has_z) load_span<IO, SPAN>(z, row + tf, valid, vec, cz);
-    load_bc_tile(t0);
+    load_bc_tile(t0, t0 + T <= t1);
   }
 
   // One tile.  FULL (a compile-time tag) means all T tokens lie inside the chunk:
@@ -220,14 +221,21 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(5, 10)))
 #pragma unroll
     for (int k = 0; k < BC_PER_THREAD; ++k)
       if (tid + k * THREADS < BC_PIECES) s_bc[tid + k * THREADS] = cbc[k];
-    // prefetch the next tile
-    if (ts + T < t1) {
+    // prefetch the next tile: plain vector loads when it is whole and aligned
+    // (every tile but the last), masked loads otherwise
+    if (vec && ts + 2 * T <= t1) {
+      const int64_t tn = tf + T;
+      load_span<IO, SPAN>(x, row + tn, SPAN, true, cx);
+      load_span<IO, SPAN>(dt, row + tn, SPAN, true, cdt);
+      if (has_z) load_span<IO, SPAN>(z, row + tn, SPAN, true, cz);
+      load_bc_tile(ts + T, true);
+    } else if (ts + T < t1) {
       const int64_t tn = tf + T;
       const int validn = own_valid(tn);
       load_span<IO, SPAN>(x, row + tn, validn, vec, cx);
       load_span<IO, SPAN>(dt, row + tn, validn, vec, cdt);
       if (has_z) load_span<IO, SPAN>(z, row + tn, validn, vec, cz);
-      load_bc_tile(ts + T);
+      load_bc_tile(ts + T, ts + 2 * T <= t1);
     }
     if constexpr (SHARE_DD) {
 #pragma unroll
