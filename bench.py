@@ -8,7 +8,7 @@ an fp32 state.  Inputs are generated on the device before timing and stay
 resident in HBM.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                    [--decode] [--copy-calib BYTES]
+                    [--no-decode] [--no-zoh] [--copy-calib BYTES]
 """
 from __future__ import annotations
 
@@ -153,7 +153,8 @@ def main():
     ap.add_argument("--workload", default="2.8b-layer-bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
-    ap.add_argument("--decode", action="store_true", help="also time the decode step")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-step timing")
+    ap.add_argument("--no-zoh", action="store_true", help="skip the zero-order-hold scan timing")
     ap.add_argument("--copy-calib", type=int, default=0, help="only run a plain copy of this many bytes")
     args = ap.parse_args()
 
@@ -241,7 +242,24 @@ def main():
         "roofline_hbm": {"achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "bytes_per_tokch": round(bpt, 4)},
     }
-    if args.decode:
+    if not args.no_zoh:
+        # the same workload through the zero-order-hold entry point (secondary)
+        for _ in range(20):
+            ss.scan_fwd(t["x"], t["dt"], t["B"], t["C"], A, z=t["z"], Dskip=dskip, dt_bias=bias, workspace=ws, y=y,
+                        h_final=hf, zoh=True)
+        torch.cuda.synchronize()
+        ss.ss_timing_reset()
+        ss.ss_timing_enable(True)
+        for _ in range(20):
+            ss.scan_fwd(t["x"], t["dt"], t["B"], t["C"], A, z=t["z"], Dskip=dskip, dt_bias=bias, workspace=ws, y=y,
+                        h_final=hf, zoh=True)
+        torch.cuda.synchronize()
+        ss.ss_timing_enable(False)
+        zms, zn = ss.ss_timing_read()
+        ss.ss_timing_reset()
+        out["zoh"] = {"entry_point": "ss_scan_fwd_zoh", "kernel_ms": round(zms / zn, 5),
+                      "value": round(tokch / (zms / zn * 1e-3) / 1e9, 3), "unit": "Gtok·ch/s"}
+    if not args.no_decode:
         out["decode"] = run_decode(ss, torch, dev, 60, 60)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)

@@ -121,6 +121,25 @@ ss_status ss_state_update(int64_t batch, int64_t dim, int dstate, ss_dtype io, f
                           const float* Dskip, const float* dt_bias,
                           void* y, void* stream);
 
+/* The same two operations with the zero-order-hold discretisation of the input
+ * term: Bbar x = (exp(Delta A) - 1)/A * B * x (Delta * B * x where A = 0), the
+ * discretisation under which selection is exactly gating (Theorem 1 in the
+ * reader's notes on the Mamba paper, kurisu.si, "Main results (verified)").
+ * Arguments, layouts, ownership, streams and errors are those of ss_scan_fwd and
+ * ss_state_update. */
+ss_status ss_scan_fwd_zoh(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io,
+                          const void* x, const void* dt, const void* z,
+                          const void* B, const void* C, const float* A,
+                          const float* Dskip, const float* dt_bias, const float* h0,
+                          void* y, float* h_final,
+                          void* workspace, size_t workspace_bytes,
+                          const ss_scan_plan* plan, void* stream);
+ss_status ss_state_update_zoh(int64_t batch, int64_t dim, int dstate, ss_dtype io, float* state,
+                              const void* x, const void* dt, const void* z,
+                              const void* B, const void* C, const float* A,
+                              const float* Dskip, const float* dt_bias,
+                              void* y, void* stream);
+
 /* Opt-in timing of the main scan kernel (for benchmarks).  While enabled, each
  * ss_scan_fwd call records HIP events around its scan kernel launches on its
  * stream.  ss_timing_read synchronises on the recorded events and returns the

@@ -5,10 +5,10 @@
 """
 from . import binding  # noqa: F401  (raises ImportError if libssscan.so is missing)
 from .binding import (SS_BF16, SS_F32, SsError, ss_abi_version, ss_scan_fwd, ss_scan_fwd_plan,  # noqa: F401
-                      ss_scan_fwd_workspace_bytes, ss_state_update, ss_timing_enable, ss_timing_read,
-                      ss_timing_reset)
+                      ss_scan_fwd_workspace_bytes, ss_scan_fwd_zoh, ss_state_update, ss_state_update_zoh,
+                      ss_timing_enable, ss_timing_read, ss_timing_reset)
 from .torch_ops import scan_fwd, state_update, workspace_bytes  # noqa: F401
 
-__all__ = ["ss_scan_fwd", "ss_state_update", "ss_scan_fwd_plan", "ss_scan_fwd_workspace_bytes",
+__all__ = ["ss_scan_fwd", "ss_state_update", "ss_scan_fwd_zoh", "ss_state_update_zoh", "ss_scan_fwd_plan", "ss_scan_fwd_workspace_bytes",
            "ss_timing_enable", "ss_timing_read", "ss_timing_reset", "ss_abi_version", "scan_fwd",
            "state_update", "workspace_bytes", "SsError", "SS_F32", "SS_BF16"]

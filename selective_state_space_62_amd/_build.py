@@ -14,7 +14,8 @@ INCLUDE = ROOT / "include"
 BUILD = PKG / "_build"
 LIB = PKG / "libssscan.so"
 
-SOURCES = ["api.cpp", "scan_fwd.hip", "state_update.hip"]
+SOURCES = ["api.cpp", "scan_fwd.hip", "scan_bf16_euler.hip", "scan_bf16_zoh.hip", "scan_f32_euler.hip",
+           "scan_f32_zoh.hip", "state_update.hip"]
 ARCH = "gfx950"
 
 # Packed-FP32 VALU ops are disabled for all device code; see the design notes.

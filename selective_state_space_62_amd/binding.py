@@ -61,6 +61,10 @@ def _load():
                                 ctypes.POINTER(ss_scan_plan), _vp])
     lib.ss_state_update.restype = _int
     lib.ss_state_update.argtypes = [_i64, _i64, _int, _int] + [_vp] * 11
+    lib.ss_scan_fwd_zoh.restype = _int
+    lib.ss_scan_fwd_zoh.argtypes = lib.ss_scan_fwd.argtypes
+    lib.ss_state_update_zoh.restype = _int
+    lib.ss_state_update_zoh.argtypes = lib.ss_state_update.argtypes
     lib.ss_timing_enable.restype = _int
     lib.ss_timing_enable.argtypes = [_int]
     lib.ss_timing_reset.restype = _int
@@ -128,6 +132,16 @@ def ss_scan_fwd(batch, dim, dstate, seqlen, io, x, dt, z, B, C, A, Dskip, dt_bia
 
 def ss_state_update(batch, dim, dstate, io, state, x, dt, z, B, C, A, Dskip, dt_bias, y, stream=None):
     _check(lib.ss_state_update(batch, dim, dstate, io, state, x, dt, z, B, C, A, Dskip, dt_bias, y, stream))
+
+
+def ss_scan_fwd_zoh(batch, dim, dstate, seqlen, io, x, dt, z, B, C, A, Dskip, dt_bias, h0, y, h_final,
+                    workspace, workspace_bytes, plan=None, stream=None):
+    _check(lib.ss_scan_fwd_zoh(batch, dim, dstate, seqlen, io, x, dt, z, B, C, A, Dskip, dt_bias, h0, y, h_final,
+                               workspace, workspace_bytes, _plan_ptr(plan), stream))
+
+
+def ss_state_update_zoh(batch, dim, dstate, io, state, x, dt, z, B, C, A, Dskip, dt_bias, y, stream=None):
+    _check(lib.ss_state_update_zoh(batch, dim, dstate, io, state, x, dt, z, B, C, A, Dskip, dt_bias, y, stream))
 
 
 def ss_timing_enable(enable: bool):

@@ -257,10 +257,14 @@ size_t ss_scan_fwd_workspace_bytes(int64_t batch, int64_t dim, int dstate, int64
   return w.total > 0 ? w.total : 256;
 }
 
-ss_status ss_scan_fwd(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io, const void* x,
-                      const void* dt, const void* z, const void* B, const void* C, const float* A,
-                      const float* Dskip, const float* dt_bias, const float* h0, void* y, float* h_final,
-                      void* workspace, size_t workspace_bytes, const ss_scan_plan* plan, void* stream) {
+}  // extern "C"
+
+namespace {
+
+ss_status scan_fwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io, const void* x,
+                        const void* dt, const void* z, const void* B, const void* C, const float* A,
+                        const float* Dskip, const float* dt_bias, const float* h0, void* y, float* h_final,
+                        void* workspace, size_t workspace_bytes, const ss_scan_plan* plan, void* stream, bool zoh) {
   ss_status st = check_sizes(batch, dim, dstate, seqlen, io);
   if (st != SS_OK) return st;
   Plan p;
@@ -363,13 +367,13 @@ ss_status ss_scan_fwd(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss
     sp.agg_h = reinterpret_cast<float*>(ws + wl.agg_h);
     sp.agg_s = reinterpret_cast<float*>(ws + wl.agg_s);
     float* h_in = reinterpret_cast<float*>(ws + wl.h_in);
-    e = ssscan::launch_scan(dm, sp, /*aggregate=*/true, s);
+    e = ssscan::launch_scan(dm, sp, /*aggregate=*/true, zoh, s);
     if (e != hipSuccess) return hip_fail(e, "scan (aggregate) launch");
     e = ssscan::launch_combine(dm, A, sp.agg_h, sp.agg_s, h0, h_in, s);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
     sp.h_in = h_in;
   }
-  e = ssscan::launch_scan(dm, sp, /*aggregate=*/false, s);
+  e = ssscan::launch_scan(dm, sp, /*aggregate=*/false, zoh, s);
   if (e != hipSuccess) return hip_fail(e, "scan launch");
 
   if (timed) {
@@ -381,9 +385,9 @@ ss_status ss_scan_fwd(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss
   return SS_OK;
 }
 
-ss_status ss_state_update(int64_t batch, int64_t dim, int dstate, ss_dtype io, float* state, const void* x,
-                          const void* dt, const void* z, const void* B, const void* C, const float* A,
-                          const float* Dskip, const float* dt_bias, void* y, void* stream) {
+ss_status state_update_impl(int64_t batch, int64_t dim, int dstate, ss_dtype io, float* state, const void* x,
+                            const void* dt, const void* z, const void* B, const void* C, const float* A,
+                            const float* Dskip, const float* dt_bias, void* y, void* stream, bool zoh) {
   ss_status st = check_sizes(batch, dim, dstate, 1, io);
   if (st != SS_OK) return st;
   const char* names[] = {"state", "x", "dt", "B", "C", "A", "y"};
@@ -407,10 +411,42 @@ ss_status ss_state_update(int64_t batch, int64_t dim, int dstate, ss_dtype io, f
     for (const Range& i : ins)
       if (overlap(o, i)) return fail(SS_ERR_INVALID_ARG, "%s overlaps input %s", o.name, i.name);
   if (overlap(outs[0], outs[1])) return fail(SS_ERR_INVALID_ARG, "state overlaps y");
-  hipError_t e = ssscan::launch_state_update(batch, dim, dstate, io_code(io), state, x, dt, z, B, C, A, Dskip,
+  hipError_t e = ssscan::launch_state_update(batch, dim, dstate, io_code(io), zoh, state, x, dt, z, B, C, A, Dskip,
                                              dt_bias, y, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "state_update launch");
   return SS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ss_status ss_scan_fwd(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io, const void* x,
+                      const void* dt, const void* z, const void* B, const void* C, const float* A,
+                      const float* Dskip, const float* dt_bias, const float* h0, void* y, float* h_final,
+                      void* workspace, size_t workspace_bytes, const ss_scan_plan* plan, void* stream) {
+  return scan_fwd_impl(batch, dim, dstate, seqlen, io, x, dt, z, B, C, A, Dskip, dt_bias, h0, y, h_final,
+                       workspace, workspace_bytes, plan, stream, false);
+}
+
+ss_status ss_scan_fwd_zoh(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io, const void* x,
+                          const void* dt, const void* z, const void* B, const void* C, const float* A,
+                          const float* Dskip, const float* dt_bias, const float* h0, void* y, float* h_final,
+                          void* workspace, size_t workspace_bytes, const ss_scan_plan* plan, void* stream) {
+  return scan_fwd_impl(batch, dim, dstate, seqlen, io, x, dt, z, B, C, A, Dskip, dt_bias, h0, y, h_final,
+                       workspace, workspace_bytes, plan, stream, true);
+}
+
+ss_status ss_state_update(int64_t batch, int64_t dim, int dstate, ss_dtype io, float* state, const void* x,
+                          const void* dt, const void* z, const void* B, const void* C, const float* A,
+                          const float* Dskip, const float* dt_bias, void* y, void* stream) {
+  return state_update_impl(batch, dim, dstate, io, state, x, dt, z, B, C, A, Dskip, dt_bias, y, stream, false);
+}
+
+ss_status ss_state_update_zoh(int64_t batch, int64_t dim, int dstate, ss_dtype io, float* state, const void* x,
+                              const void* dt, const void* z, const void* B, const void* C, const float* A,
+                              const float* Dskip, const float* dt_bias, void* y, void* stream) {
+  return state_update_impl(batch, dim, dstate, io, state, x, dt, z, B, C, A, Dskip, dt_bias, y, stream, true);
 }
 
 ss_status ss_timing_enable(int enable) {

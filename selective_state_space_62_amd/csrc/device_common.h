@@ -146,6 +146,22 @@ __device__ __forceinline__ float softplus_dt(float dt, float bias2) {
   return fmaf(fmaxf(v2, 0.0f) + l, kLn2, -c);
 }
 
+// phi(u) = (e^u - 1)/u, phi(0) = 1, for the zero-order-hold input term
+// Bbar x = (e^(Delta A) - 1)/A B x = phi(Delta A) Delta B x (no division by A,
+// so A = 0 gives Delta B x).  Takes u2 = u log2(e) and E = 2^u2 = e^u, which the
+// caller already has.  |u| < 1/4: degree-5 Taylor polynomial (the next term is
+// below 5e-8 relative); otherwise (E - 1)/u, where E - 1 cancels no digits.
+__device__ __forceinline__ float zoh_phi(float u2, float E) {
+  const float u = u2 * kLn2;
+  float p = fmaf(u, 1.0f / 720.0f, 1.0f / 120.0f);
+  p = fmaf(p, u, 1.0f / 24.0f);
+  p = fmaf(p, u, 1.0f / 6.0f);
+  p = fmaf(p, u, 0.5f);
+  p = fmaf(p, u, 1.0f);
+  const float q = (E - 1.0f) * __builtin_amdgcn_rcpf(u);
+  return fabsf(u) < 0.25f ? p : q;
+}
+
 // silu(z) = z / (1 + e^-z).  For z below about -88 the exponential overflows to
 // +inf and the result is -0, the correctly rounded limit.
 __device__ __forceinline__ float silu(float z) {

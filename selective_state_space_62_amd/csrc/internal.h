@@ -45,11 +45,15 @@ inline int tile_len(int groups, int io) { return groups * (io == kIoBf16 ? 8 : 4
 inline int span_len(int lanes, int io) { return (io == kIoBf16 ? 8 : 4) / lanes; }
 
 hipError_t launch_prep_bc(const ScanDims& dm, const void* B, const void* C, float* bc, hipStream_t s);
-hipError_t launch_scan(const ScanDims& dm, const ScanPtrs& p, bool aggregate, hipStream_t s);
+hipError_t launch_scan(const ScanDims& dm, const ScanPtrs& p, bool aggregate, bool zoh, hipStream_t s);
+hipError_t launch_scan_bf16_euler(const ScanDims& dm, const ScanPtrs& p, bool aggregate, hipStream_t s);
+hipError_t launch_scan_bf16_zoh(const ScanDims& dm, const ScanPtrs& p, bool aggregate, hipStream_t s);
+hipError_t launch_scan_f32_euler(const ScanDims& dm, const ScanPtrs& p, bool aggregate, hipStream_t s);
+hipError_t launch_scan_f32_zoh(const ScanDims& dm, const ScanPtrs& p, bool aggregate, hipStream_t s);
 hipError_t launch_combine(const ScanDims& dm, const float* A, const float* agg_h, const float* agg_s,
                           const float* h0, float* h_in, hipStream_t s);
 hipError_t launch_copy_state(int64_t count, const float* src, float* dst, hipStream_t s);
-hipError_t launch_state_update(int64_t batch, int64_t dim, int dstate, int io, float* state,
+hipError_t launch_state_update(int64_t batch, int64_t dim, int dstate, int io, bool zoh, float* state,
                                const void* x, const void* dt, const void* z, const void* B, const void* C,
                                const float* A, const float* Dskip, const float* dt_bias, void* y,
                                hipStream_t s);

@@ -1,0 +1,10 @@
+// Instantiates the scan kernels for bf16 I/O with the first-order (Euler) discretisation of B.
+#include "scan_kernel.h"
+
+namespace ssscan {
+
+hipError_t launch_scan_bf16_euler(const ScanDims& dm, const ScanPtrs& p, bool aggregate, hipStream_t s) {
+  return scan_detail::launch_scan_impl<dev::BF16, false>(dm, p, aggregate, s);
+}
+
+}  // namespace ssscan

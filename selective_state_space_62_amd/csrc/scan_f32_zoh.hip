@@ -1,0 +1,10 @@
+// Instantiates the scan kernels for fp32 I/O with the zero-order-hold discretisation of B.
+#include "scan_kernel.h"
+
+namespace ssscan {
+
+hipError_t launch_scan_f32_zoh(const ScanDims& dm, const ScanPtrs& p, bool aggregate, hipStream_t s) {
+  return scan_detail::launch_scan_impl<dev::F32, true>(dm, p, aggregate, s);
+}
+
+}  // namespace ssscan

@@ -55,7 +55,7 @@ __device__ __forceinline__ void load_q(const typename IO::T* __restrict__ p, flo
 // component group) items per iteration, all U state loads issued before any
 // arithmetic (more bytes in flight per wave); the loop bound is wave-uniform, so
 // every lane of a channel is active for the DPP sum.
-template <int N, typename IO, int U>
+template <int N, typename IO, int U, bool ZOH>
 __global__ __launch_bounds__(256) void state_update_kernel(
     int64_t nch, int64_t dim, float* __restrict__ state, const typename IO::T* __restrict__ x,
     const typename IO::T* __restrict__ dt, const typename IO::T* __restrict__ z,
@@ -114,8 +114,11 @@ __global__ __launch_bounds__(256) void state_update_kernel(
       float acc = 0.0f;
 #pragma unroll
       for (int q = 0; q < Q; ++q) {
-        const float E = __builtin_amdgcn_exp2f(delta * (a2[u][q] * kLog2e));
-        st[u][q] = fmaf(E, st[u][q], dx * bq[u][q]);
+        const float u2 = delta * (a2[u][q] * kLog2e);
+        const float E = __builtin_amdgcn_exp2f(u2);
+        float in = dx * bq[u][q];                  // first order: Bbar x = Delta B x
+        if constexpr (ZOH) in *= zoh_phi(u2, E);   // zero-order hold: (e^u - 1)/u Delta B x
+        st[u][q] = fmaf(E, st[u][q], in);
         acc = fmaf(cq[u][q], st[u][q], acc);
       }
       // sum the channel's K partial readouts (lanes are adjacent inside one quad)
@@ -140,7 +143,7 @@ __global__ __launch_bounds__(256) void state_update_kernel(
   }
 }
 
-template <int N, typename IO>
+template <int N, typename IO, bool ZOH>
 hipError_t launch_t(int64_t nch, int64_t dim, float* state, const void* x, const void* dt, const void* z,
                     const void* B, const void* C, const float* A, const float* Dskip, const float* dt_bias, void* y,
                     hipStream_t s) {
@@ -152,33 +155,37 @@ hipError_t launch_t(int64_t nch, int64_t dim, float* state, const void* x, const
   // a bounded grid (DECODE_BLOCKS workgroups); the grid-stride loop covers the rest
   const int64_t cap = DECODE_BLOCKS;
   if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL((state_update_kernel<N, IO, U>), dim3((unsigned)blocks), dim3(256), 0, s, nch, dim, state,
+  hipLaunchKernelGGL((state_update_kernel<N, IO, U, ZOH>), dim3((unsigned)blocks), dim3(256), 0, s, nch, dim, state,
                      (const E*)x, (const E*)dt, (const E*)z, (const E*)B, (const E*)C, A, Dskip, dt_bias, (E*)y);
   return hipGetLastError();
 }
 
-template <typename IO>
+template <typename IO, bool ZOH>
 hipError_t launch_n(int64_t nch, int64_t dim, int dstate, float* state, const void* x, const void* dt, const void* z,
                     const void* B, const void* C, const float* A, const float* Dskip, const float* dt_bias, void* y,
                     hipStream_t s) {
   switch (dstate) {
-    case 1: return launch_t<1, IO>(nch, dim, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
-    case 2: return launch_t<2, IO>(nch, dim, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
-    case 4: return launch_t<4, IO>(nch, dim, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
-    case 8: return launch_t<8, IO>(nch, dim, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
-    case 16: return launch_t<16, IO>(nch, dim, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
+    case 1: return launch_t<1, IO, ZOH>(nch, dim, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
+    case 2: return launch_t<2, IO, ZOH>(nch, dim, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
+    case 4: return launch_t<4, IO, ZOH>(nch, dim, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
+    case 8: return launch_t<8, IO, ZOH>(nch, dim, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
+    case 16: return launch_t<16, IO, ZOH>(nch, dim, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_state_update(int64_t batch, int64_t dim, int dstate, int io, float* state, const void* x,
-                               const void* dt, const void* z, const void* B, const void* C, const float* A,
-                               const float* Dskip, const float* dt_bias, void* y, hipStream_t s) {
+hipError_t launch_state_update(int64_t batch, int64_t dim, int dstate, int io, bool zoh, float* state,
+                               const void* x, const void* dt, const void* z, const void* B, const void* C,
+                               const float* A, const float* Dskip, const float* dt_bias, void* y, hipStream_t s) {
   const int64_t nch = batch * dim;
-  if (io == kIoBf16) return launch_n<BF16>(nch, dim, dstate, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
-  return launch_n<F32>(nch, dim, dstate, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
+  if (io == kIoBf16) {
+    return zoh ? launch_n<BF16, true>(nch, dim, dstate, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s)
+               : launch_n<BF16, false>(nch, dim, dstate, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
+  }
+  return zoh ? launch_n<F32, true>(nch, dim, dstate, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s)
+             : launch_n<F32, false>(nch, dim, dstate, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
 }
 
 }  // namespace ssscan

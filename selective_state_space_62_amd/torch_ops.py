@@ -39,8 +39,8 @@ def workspace_bytes(batch, dim, dstate, seqlen, dtype=torch.bfloat16, plan=None)
 
 
 def scan_fwd(x, dt, B, C, A, z=None, Dskip=None, dt_bias=None, h0=None, *, plan=None, workspace=None,
-             y=None, h_final=None, return_final_state=True):
-    """Selective scan over full sequences.
+             y=None, h_final=None, return_final_state=True, zoh=False):
+    """Selective scan over full sequences (zoh=True: zero-order-hold input term).
 
     x, dt, z: (batch, D, L); B, C: (batch, N, L) — all float32 or all bfloat16;
     A: (D, N) float32; Dskip, dt_bias: (D,) float32; h0: (batch, D, N) float32.
@@ -74,14 +74,16 @@ def scan_fwd(x, dt, B, C, A, z=None, Dskip=None, dt_bias=None, h0=None, *, plan=
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
     if workspace.numel() < nbytes:
         raise ValueError("workspace has %d bytes, %d needed" % (workspace.numel(), nbytes))
-    _b.ss_scan_fwd(batch, dim, N, L, io, _ptr(x), _ptr(dt), _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(Dskip),
+    fn = _b.ss_scan_fwd_zoh if zoh else _b.ss_scan_fwd
+    fn(batch, dim, N, L, io, _ptr(x), _ptr(dt), _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(Dskip),
                    _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_final), _ptr(workspace), workspace.numel(),
                    plan, _stream(dev))
     return y, h_final
 
 
-def state_update(state, x, dt, B, C, A, z=None, Dskip=None, dt_bias=None, *, y=None):
-    """One decode step; ``state`` (batch, D, N) float32 is updated in place.
+def state_update(state, x, dt, B, C, A, z=None, Dskip=None, dt_bias=None, *, y=None, zoh=False):
+    """One decode step; ``state`` (batch, D, N) float32 is updated in place (zoh=True:
+    zero-order-hold input term).
 
     x, dt, z: (batch, D); B, C: (batch, N) in float32 or bfloat16.  Returns y (batch, D).
     """
@@ -103,6 +105,7 @@ def state_update(state, x, dt, B, C, A, z=None, Dskip=None, dt_bias=None, *, y=N
     if y is None:
         y = torch.empty((batch, dim), dtype=x.dtype, device=dev)
     _need(y, "y", x.dtype, (batch, dim), dev)
-    _b.ss_state_update(batch, dim, N, _IO[x.dtype], _ptr(state), _ptr(x), _ptr(dt), _ptr(z), _ptr(B), _ptr(C),
+    fn = _b.ss_state_update_zoh if zoh else _b.ss_state_update
+    fn(batch, dim, N, _IO[x.dtype], _ptr(state), _ptr(x), _ptr(dt), _ptr(z), _ptr(B), _ptr(C),
                        _ptr(A), _ptr(Dskip), _ptr(dt_bias), _ptr(y), _stream(dev))
     return y

@@ -1,0 +1,139 @@
+"""The zero-order-hold entry points (ss_scan_fwd_zoh, ss_state_update_zoh) on the GPU.
+
+Bbar x = (exp(Delta A) - 1)/A B x is the discretisation under which the reader's
+notes' Theorem 1 (selection is gating) holds exactly; the GPU must reproduce the
+gated RNN closed form and the oracle's ZOH mode.
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import log, random_problem, rel_l2, to_dev, to_f64
+from workloads import TINY, inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def ss():
+    import selective_state_space_62_amd as m
+    return m
+
+
+def _gpu(ss, raw, par, io, dev, plan=None):
+    import torch
+    t = {k: to_dev(v, io, dev) for k, v in raw.items()}
+    p = {k: (torch.from_numpy(v).to(dev) if v is not None else None) for k, v in par.items()}
+    y, hf = ss.scan_fwd(t["x"], t["dt"], t["B"], t["C"], p["A"], z=t.get("z"), Dskip=p["Dskip"],
+                        dt_bias=p["dt_bias"], h0=p["h0"], plan=plan, zoh=True)
+    torch.cuda.synchronize()
+    return to_f64(y), to_f64(hf)
+
+
+def test_theorem1_zoh_exact(ss, dev):
+    """N = 1, A = -1, B = C = 1, no skip or gate: the ZOH scan is the gated RNN
+    h_t = (1 - sigmoid(g_t)) h_(t-1) + sigmoid(g_t) x_t exactly."""
+    import torch
+    rng = np.random.default_rng(31)
+    batch, D, L = 2, 70, 300
+    g = (2.0 * rng.standard_normal((batch, D, L))).astype(np.float32)
+    x = rng.standard_normal((batch, D, L)).astype(np.float32)
+    h0 = rng.standard_normal((batch, D, 1)).astype(np.float32)
+    ones = np.ones((batch, 1, L), np.float32)
+    y, hf = ss.scan_fwd(torch.from_numpy(x).to(dev), torch.from_numpy(g).to(dev), torch.from_numpy(ones).to(dev),
+                        torch.from_numpy(ones).to(dev), -torch.ones(D, 1, device=dev),
+                        h0=torch.from_numpy(h0).to(dev), zoh=True)
+    torch.cuda.synchronize()
+    gd = g.astype(np.float64)
+    h = h0[..., 0].astype(np.float64)
+    ref = np.empty((batch, D, L))
+    for k in range(L):
+        sig = 1.0 / (1.0 + np.exp(-gd[..., k]))
+        h = (1.0 - sig) * h + sig * x[..., k]
+        ref[..., k] = h
+    ey, eh = rel_l2(to_f64(y), ref), rel_l2(to_f64(hf)[..., 0], h)
+    log("theorem 1 (zoh) on the GPU: rel-L2 y %.3e h %.3e" % (ey, eh))
+    assert ey <= 1e-5 and eh <= 1e-5
+
+
+CASES = [
+    # batch, D, N, L, io, plan
+    (1, 16, 4, 64, "f32", None),
+    (2, 100, 16, 37, "f32", (4, 2, 1 << 20)),
+    (2, 130, 16, 300, "f32", (4, 1, 64)),
+    (3, 65, 8, 129, "bf16", None),
+    (2, 200, 16, 515, "bf16", (4, 2, 128)),
+    (1, 64, 1, 33, "f32", (1, 8)),
+    (2, 96, 16, 1024, "f32", (2, 2, 256)),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=["-".join(map(str, c[:5])) + "-" + str(c[5]).replace(" ", "") for c in CASES])
+def test_zoh_scan_matches_oracle(ss, dev, case):
+    batch, D, N, L, io, plan = case
+    log("zoh scan %s" % (case,))
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()))
+    raw, par, f64 = random_problem(rng, batch, D, N, L, io)
+    # A spans tiny, moderate and large |Delta A|, and includes A = 0 and A > 0
+    A = par["A"].copy()
+    A[:, 0] = -1e-4
+    if N > 1:
+        A[:, 1] = 0.0
+    if N > 2:
+        A[:, 2] = 0.05
+    par["A"] = A
+    y, hf = _gpu(ss, raw, par, io, dev, plan)
+    yr, hr = oracle.default().scan(f64["x"], f64["dt"], f64["B"], f64["C"], A, z=f64["z"], Dskip=par["Dskip"],
+                                   dt_bias=par["dt_bias"], h0=par["h0"], zoh=True)
+    ey, eh = rel_l2(y, yr), rel_l2(hf, hr)
+    log("  rel-L2 y %.3e h %.3e" % (ey, eh))
+    tol = 1e-5 if io == "f32" else 2e-2
+    assert ey <= tol and eh <= tol
+
+
+def test_zoh_tiny_workload(ss, dev):
+    cfg = TINY
+    raw = inputs.scan_inputs_full(cfg)
+    A, dskip, bias = inputs.params(cfg)
+    h0 = np.random.default_rng(12).standard_normal((1, cfg.dim, cfg.dstate)).astype(np.float32)
+    par = dict(A=A, Dskip=dskip, dt_bias=bias, h0=h0)
+    y, hf = _gpu(ss, raw, par, cfg.io, dev)
+    f64 = {k: inputs.raw_to_f64(v, cfg.io) for k, v in raw.items()}
+    yr, hr = oracle.default().scan(f64["x"], f64["dt"], f64["B"], f64["C"], A, z=f64["z"], Dskip=dskip,
+                                   dt_bias=bias, h0=h0, zoh=True)
+    assert rel_l2(y, yr) <= 1e-5 and rel_l2(hf, hr) <= 1e-5
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_zoh_decode_equals_zoh_scan_and_oracle(ss, dev, io):
+    import torch
+    rng = np.random.default_rng(33)
+    T = 16
+    raw, par, f64 = random_problem(rng, 3, 96, 16, T, io)
+    t = {k: to_dev(v, io, dev) for k, v in raw.items()}
+    p = {k: torch.from_numpy(v).to(dev) for k, v in par.items()}
+    kw = dict(Dskip=p["Dskip"], dt_bias=p["dt_bias"])
+    y, hf = ss.scan_fwd(t["x"], t["dt"], t["B"], t["C"], p["A"], z=t["z"], h0=p["h0"], zoh=True, **kw)
+    st = p["h0"].clone()
+    ys = []
+    for k in range(T):
+        ys.append(ss.state_update(st, t["x"][..., k].contiguous(), t["dt"][..., k].contiguous(),
+                                  t["B"][..., k].contiguous(), t["C"][..., k].contiguous(), p["A"],
+                                  z=t["z"][..., k].contiguous(), zoh=True, **kw))
+    torch.cuda.synchronize()
+    yd = torch.stack(ys, -1)
+    assert rel_l2(to_f64(yd), to_f64(y)) <= (1e-6 if io == "f32" else 1e-2)
+    assert rel_l2(to_f64(st), to_f64(hf)) <= 1e-6
+    yr, hr = oracle.default().scan(f64["x"], f64["dt"], f64["B"], f64["C"], par["A"], z=f64["z"],
+                                   Dskip=par["Dskip"], dt_bias=par["dt_bias"], h0=par["h0"], zoh=True)
+    tol = 1e-5 if io == "f32" else 2e-2
+    assert rel_l2(to_f64(yd), yr) <= tol and rel_l2(to_f64(st), hr) <= tol

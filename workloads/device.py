@@ -14,8 +14,12 @@ from pathlib import Path
 
 import numpy as np
 
-from .configs import ScanConfig
-from . import inputs as _in
+try:
+    from .configs import ScanConfig
+    from . import inputs as _in
+except ImportError:  # loaded as a standalone file to build the generator library
+    ScanConfig = object
+    _in = None
 
 HERE = Path(__file__).resolve().parent
 SRC = HERE / "csrc" / "wlgen.hip"
