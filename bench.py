@@ -31,14 +31,22 @@ CUS, SIMDS_PER_CU, LANES_PER_SIMD_CLK, CLOCK_GHZ = 256, 4, 16, 2.4
 VALU_PEAK_TOPS = CUS * SIMDS_PER_CU * LANES_PER_SIMD_CLK * CLOCK_GHZ / 1000.0   # 39.32 T lane-slots/s
 TRANS_SLOTS = 2   # transcendentals issue at half rate on gfx950 and do not co-issue with FMAs
 
-KERNEL_SOURCES = ["selective_state_space_62_amd/csrc/scan_fwd.hip",
-                  "selective_state_space_62_amd/csrc/device_common.h"]
-COUNTERS_FILE = ROOT / "profiles" / "scan_2.8b_bf16_counters.json"
+_CSRC = "selective_state_space_62_amd/csrc/"
+# sources of each timed kernel: committed counters apply only while these are unchanged
+KERNEL_SOURCES = {
+    "scan": [_CSRC + f for f in ("scan_kernel.h", "scan_fwd.hip", "scan_bf16_euler.hip", "scan_f32_euler.hip",
+                                 "device_common.h", "internal.h")],
+    "decode": [_CSRC + f for f in ("state_update.hip", "device_common.h", "internal.h")],
+}
+COUNTERS_FILES = {
+    "scan": ROOT / "profiles" / "scan_2.8b_bf16_counters.json",
+    "decode": ROOT / "profiles" / "decode_256x5120_bf16_counters.json",
+}
 
 
-def kernel_hash() -> str:
+def kernel_hash(kind: str = "scan") -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kind]:
         h.update((ROOT / f).read_bytes())
     return h.hexdigest()[:16]
 
@@ -96,14 +104,14 @@ def cpu_baseline(cfg, budget_s: float):
                       % (tokch // cfg.seqlen, cfg.seqlen, cfg.name, spent)}
 
 
-def measured_traffic(cfg):
+def measured_traffic(cfg, kind: str = "scan"):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None if
     the kernel sources changed since the counters were taken."""
     try:
-        d = json.loads(COUNTERS_FILE.read_text())
+        d = json.loads(COUNTERS_FILES[kind].read_text())
     except (OSError, ValueError):
         return None
-    if d.get("kernel_hash") != kernel_hash() or d.get("workload") != cfg.name:
+    if d.get("kernel_hash") != kernel_hash(kind) or d.get("workload") != cfg.name:
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -138,10 +146,11 @@ def run_decode(ss, torch, dev, steps, warmup):
     cold_ms = timed(True)
     nbd = cfg.batch * cfg.dim
     bytes_step = nbd * (2 * cfg.dstate * 4 + 4 * 2) + 2 * cfg.batch * cfg.dstate * 2 + cfg.dim * (cfg.dstate + 2) * 4
-    return {"workload": cfg.name, "bd_per_step": nbd, "ms_per_step_cold": round(cold_ms, 5),
+    return {"workload": cfg.name, "kernel": "state_update_kernel<16,BF16,euler>", "bd_per_step": nbd,
+            "ms_per_step_cold": round(cold_ms, 5),
             "ms_per_step_warm": round(warm_ms, 5), "hbm_gbs_cold": round(bytes_step / cold_ms / 1e6, 1),
             "frac_hbm_cold": round(bytes_step / cold_ms / 1e6 / HBM_PEAK_GBS, 4),
-            "algorithmic_bytes_per_step": bytes_step,
+            "algorithmic_bytes_per_step": bytes_step, "traffic": measured_traffic(cfg, "decode"),
             "cold_method": "back-to-back steps rotating over 6 states (503 MB > 256 MB MALL)"}
 
 
@@ -237,7 +246,7 @@ def main():
         "hbm_gbs": round(bpt * tokch / (ms_step * 1e-3) / 1e9, 1),
         "roofline": {"bound": "alu", "achieved": round(achieved_slots, 3), "peak": round(VALU_PEAK_TOPS, 3),
                      "unit": "T VALU-slot/s", "frac": round(achieved_slots / VALU_PEAK_TOPS, 4),
-                     "traffic": traffic, "kernel": "scan_kernel<16,%d,%d,bf16>" % (plan[0], plan[1]), "kernel_ms": round(kern_ms, 5),
+                     "traffic": traffic, "kernel": "scan_kernel<%d,%d,%d,%s,euler>" % (cfg.dstate, plan[0], plan[1], cfg.io), "kernel_ms": round(kern_ms, 5),
                      "slots_per_tokch": spt},
         "roofline_hbm": {"achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "bytes_per_tokch": round(bpt, 4)},

@@ -114,7 +114,8 @@ ss_status ss_scan_fwd(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss
 
 /* One autoregressive decode step: for each (b, d), advance `state` by one token
  * with the same update as the scan and write y (batch, dim).  z == NULL means no
- * gate.  Needs no workspace. */
+ * gate.  Needs no workspace.  batch * dim above 2^34 channels (a state of 1 TB
+ * at dstate 16) returns SS_ERR_UNSUPPORTED. */
 ss_status ss_state_update(int64_t batch, int64_t dim, int dstate, ss_dtype io, float* state,
                           const void* x, const void* dt, const void* z,
                           const void* B, const void* C, const float* A,

@@ -390,6 +390,9 @@ ss_status state_update_impl(int64_t batch, int64_t dim, int dstate, ss_dtype io,
                             const float* Dskip, const float* dt_bias, void* y, void* stream, bool zoh) {
   ss_status st = check_sizes(batch, dim, dstate, 1, io);
   if (st != SS_OK) return st;
+  if ((__int128)batch * dim > ((__int128)1 << 34))
+    return fail(SS_ERR_UNSUPPORTED, "batch * dim exceeds 2^34 channels (%lld x %lld)", (long long)batch,
+                (long long)dim);
   const char* names[] = {"state", "x", "dt", "B", "C", "A", "y"};
   const void* req[] = {state, x, dt, B, C, A, y};
   for (int i = 0; i < 7; ++i)

@@ -6,23 +6,24 @@
 // Abar = exp(Delta A)), with the fp32 state read from and written back to HBM.
 //
 // The step moves about 136 bytes per (b, d) at N = 16 (64 B of state in, 64 B
-// out, 8 B of x, dt, z, y) against ~120 VALU slots, so it is bound by the state's
-// read-modify-write traffic.  Lanes map to (channel, group of 4 state
-// components): each lane moves one 16-byte piece of the state and a wave covers
-// 1 KB of contiguous state, so every load and store is fully coalesced.  The
-// readout of the N components is summed across the channel's lanes with DPP
-// quad permutes in a fixed order.  A (dim, N) is re-read per batch row from L2.
-// The state is streamed with non-temporal loads and stores (it is touched once
-// per step), and a bounded grid of workgroups strides over the items, which
-// kept more bytes in flight than one short-lived workgroup per 64 channels.
+// out, 8 B of x, dt, z, y) against ~100 VALU instructions per lane, so it is
+// bound by the state's read-modify-write traffic.  Lanes map to (channel, group
+// of 4 state components): each lane moves one 16-byte piece of the state and a
+// wave covers 1 KB of contiguous state, so every load and store is fully
+// coalesced.  The readout of the N components is summed across the channel's
+// lanes with DPP quad permutes in a fixed order.  A (dim, N) is re-read per
+// batch row from L2.  The state is streamed with non-temporal loads and stores
+// (it is touched once per step).  All of an item's loads are issued together,
+// and no lane divides: a grid of up to DECODE_BLOCKS workgroups strides over
+// (batch row, 64-item piece) pairs advanced by a host-computed quotient and
+// remainder.  At the 256 x 5120 x 16 decode shape the cap of 16384 workgroups
+// gives most waves a single item, which measured faster than fewer, longer-
+// lived waves (8192 blocks: +4%, 2048 blocks: +13%).
 #include "device_common.h"
 #include "internal.h"
 
-#ifndef DECODE_UNROLL
-#define DECODE_UNROLL 1
-#endif
 #ifndef DECODE_BLOCKS
-#define DECODE_BLOCKS 2048
+#define DECODE_BLOCKS 16384
 #endif
 
 namespace ssscan {
@@ -32,8 +33,8 @@ using namespace dev;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Load Q consecutive elements of a (batch, N) row of B or C as floats (one
-// vector load when Q * sizeof(element) is 8 or 16 bytes).
+// Load Q consecutive elements of a (batch, N) row of B or C as floats, with one
+// 8- or 16-byte vector load when Q == 4 (the row offsets are multiples of Q).
 template <typename IO, int Q>
 __device__ __forceinline__ void load_q(const typename IO::T* __restrict__ p, float (&v)[Q]) {
   if constexpr (Q == 4 && IO::kPerSpan == 8) {
@@ -51,125 +52,174 @@ __device__ __forceinline__ void load_q(const typename IO::T* __restrict__ p, flo
   }
 }
 
-// Grid-stride over waves: each wave handles U x 64 consecutive (channel,
-// component group) items per iteration, all U state loads issued before any
-// arithmetic (more bytes in flight per wave); the loop bound is wave-uniform, so
-// every lane of a channel is active for the DPP sum.
-template <int N, typename IO, int U, bool ZOH>
-__global__ __launch_bounds__(256) void state_update_kernel(
-    int64_t nch, int64_t dim, float* __restrict__ state, const typename IO::T* __restrict__ x,
-    const typename IO::T* __restrict__ dt, const typename IO::T* __restrict__ z,
-    const typename IO::T* __restrict__ B, const typename IO::T* __restrict__ C, const float* __restrict__ A,
-    const float* __restrict__ Dskip, const float* __restrict__ dt_bias, typename IO::T* __restrict__ y) {
+// One lane's operands for one item: Q state components with their A, B and C
+// values, and the channel's x, dt, z, dt_bias and Dskip.
+template <int Q>
+struct Item {
+  float st[Q], a2[Q], bq[Q], cq[Q];
+  float xv, dtv, zl, bl, sl;
+  int64_t ch;
+  int j;
+  bool act;
+};
+
+template <int N, typename IO>
+struct Operands {
+  int64_t dim, row_items;
+  float* __restrict__ state;
+  const typename IO::T* __restrict__ x;
+  const typename IO::T* __restrict__ dt;
+  const typename IO::T* __restrict__ z;
+  const typename IO::T* __restrict__ B;
+  const typename IO::T* __restrict__ C;
+  const float* __restrict__ A;
+  const float* __restrict__ Dskip;
+  const float* __restrict__ dt_bias;
+  typename IO::T* __restrict__ y;
+};
+
+// Issue every load of item (row b, piece) for this lane.  Optional operands are
+// read unconditionally from an always-valid stand-in (x for z, A for the
+// per-channel vectors) and selected later, so all loads are in flight at once
+// instead of one wait per branch.
+template <int N, typename IO, int Q, int K>
+__device__ __forceinline__ Item<Q> fetch(const Operands<N, IO>& o, int64_t b, uint32_t piece, int lane) {
+  Item<Q> r;
+  const int64_t it = (int64_t)piece * 64 + lane;
+  r.act = it < o.row_items;
+  const int64_t itc = r.act ? it : o.row_items - 1;   // padding lanes work on a valid item, store nothing
+  const int64_t d = itc / K;
+  r.j = (int)(itc - d * K);
+  r.ch = b * o.dim + d;
+  const float* sp = o.state + r.ch * N + r.j * Q;
+  if constexpr (Q == 4) {
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp));
+    r.st[0] = v[0]; r.st[1] = v[1]; r.st[2] = v[2]; r.st[3] = v[3];
+    const float4 av = *reinterpret_cast<const float4*>(o.A + d * N + r.j * Q);
+    r.a2[0] = av.x; r.a2[1] = av.y; r.a2[2] = av.z; r.a2[3] = av.w;
+  } else {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      r.st[q] = sp[q];
+      r.a2[q] = o.A[d * N + r.j * Q + q];
+    }
+  }
+  load_q<IO, Q>(o.B + b * N + r.j * Q, r.bq);
+  load_q<IO, Q>(o.C + b * N + r.j * Q, r.cq);
+  r.xv = load_one<IO>(o.x, r.ch);
+  r.dtv = load_one<IO>(o.dt, r.ch);
+  r.zl = load_one<IO>(o.z ? o.z : o.x, r.ch);
+  r.bl = (o.dt_bias ? o.dt_bias : o.A)[d];
+  r.sl = (o.Dskip ? o.Dskip : o.A)[d];
+  return r;
+}
+
+// Advance one item by one token and store the new state and the output.
+template <int N, typename IO, int Q, int K, bool ZOH>
+__device__ __forceinline__ void finish(const Operands<N, IO>& o, Item<Q>& r) {
+  float zv = o.z ? r.zl : 0.0f;
+  const float bias2 = o.dt_bias ? r.bl * kLog2e : 0.0f;
+  float skip = o.Dskip ? r.sl : 0.0f;
+  const float delta = softplus_dt(r.dtv, bias2);
+  const float dx = delta * r.xv;
+  float acc = 0.0f;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const float u2 = delta * (r.a2[q] * kLog2e);
+    const float E = __builtin_amdgcn_exp2f(u2);
+    float in = dx * r.bq[q];                   // first order: Bbar x = Delta B x
+    if constexpr (ZOH) in *= zoh_phi(u2, E);   // zero-order hold: (e^u - 1)/u Delta B x
+    r.st[q] = fmaf(E, r.st[q], in);
+    acc = fmaf(r.cq[q], r.st[q], acc);
+  }
+  // sum the channel's K partial readouts (lanes are adjacent inside one quad)
+  if constexpr (K >= 2) acc += __builtin_amdgcn_update_dpp(0.0f, acc, 0xB1, 0xf, 0xf, false);  // [1,0,3,2]
+  if constexpr (K == 4) acc += __builtin_amdgcn_update_dpp(0.0f, acc, 0x4E, 0xf, 0xf, false);  // [2,3,0,1]
+  // every lane forms the output; the empty asm pins z and Dskip here, so the
+  // compiler cannot sink their loads into the store branch behind a second wait
+  // for memory.  The channel's first lane stores the output.
+  __asm__ volatile("" : "+v"(zv), "+v"(skip));
+  float out = fmaf(skip, r.xv, acc);
+  if (o.z) out *= silu(zv);
+  if (r.act) {
+    float* sp = o.state + r.ch * N + r.j * Q;
+    if constexpr (Q == 4) {
+      const f32x4 v = {r.st[0], r.st[1], r.st[2], r.st[3]};
+      __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(sp));
+    } else {
+#pragma unroll
+      for (int q = 0; q < Q; ++q) sp[q] = r.st[q];
+    }
+    if (r.j == 0) store_one<IO>(o.y, r.ch, out);
+  }
+}
+
+// Work decomposition: lane items are (channel, group of Q state components),
+// K = N / Q items per channel, laid out row by row (one row per batch entry,
+// dim * K items, padded to whole waves of 64).  Each wave owns one 64-item
+// piece of one row per iteration and strides over pieces by the grid's wave
+// count; the (row, piece) pair is advanced with a quotient and remainder the
+// host precomputes, so no lane divides.  Row and piece are wave-uniform, so all
+// K lanes of a channel are active together for the DPP sum.
+template <int N, typename IO, bool ZOH>
+__global__ __launch_bounds__(256) void state_update_kernel(int64_t batch, uint32_t pieces_per_row,
+                                                           uint32_t stride_rows, uint32_t stride_pieces,
+                                                           Operands<N, IO> o) {
   constexpr int Q = N < 4 ? N : 4;   // state components per lane
   constexpr int K = N / Q;           // lanes per channel (1, 2 or 4), adjacent within a quad
-  const int64_t items = nch * K;
   const int lane = threadIdx.x & 63;
-  const int64_t wave0 = ((int64_t)blockIdx.x * blockDim.x + (threadIdx.x & ~63)) * U;
-  const int64_t wstride = (int64_t)gridDim.x * blockDim.x * U;
-  for (int64_t wb = wave0; wb < items; wb += wstride) {
-    bool act[U];
-    int64_t ch[U], b[U], d[U];
-    int j[U];
-    float st[U][Q], a2[U][Q], bq[U][Q], cq[U][Q], xv[U], dtv[U], zv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t it = wb + u * 64 + lane;
-      act[u] = it < items;
-      const int64_t itc = act[u] ? it : items - 1;   // inactive lanes work on a valid item, store nothing
-      ch[u] = itc / K;
-      j[u] = (int)(itc - ch[u] * K);
-      b[u] = ch[u] / dim;
-      d[u] = ch[u] - b[u] * dim;
-      const float* sp = state + ch[u] * N + j[u] * Q;
-      if constexpr (Q == 4) {
-        const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp));
-        st[u][0] = v[0]; st[u][1] = v[1]; st[u][2] = v[2]; st[u][3] = v[3];
-      } else {
-#pragma unroll
-        for (int q = 0; q < Q; ++q) st[u][q] = sp[q];
-      }
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
+  int64_t b = wave / pieces_per_row;
+  uint32_t piece = wave - (uint32_t)b * pieces_per_row;
+  // advance (b, piece) by the grid's wave count: stride_rows rows and stride_pieces pieces
+  auto advance = [&](int64_t& bb, uint32_t& pp) {
+    bb += stride_rows;
+    pp += stride_pieces;
+    if (pp >= pieces_per_row) {
+      pp -= pieces_per_row;
+      ++bb;
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if constexpr (Q == 4) {
-        const float4 av = *reinterpret_cast<const float4*>(A + d[u] * N + j[u] * Q);
-        a2[u][0] = av.x; a2[u][1] = av.y; a2[u][2] = av.z; a2[u][3] = av.w;
-      } else {
-#pragma unroll
-        for (int q = 0; q < Q; ++q) a2[u][q] = A[d[u] * N + j[u] * Q + q];
-      }
-      load_q<IO, Q>(B + b[u] * N + j[u] * Q, bq[u]);
-      load_q<IO, Q>(C + b[u] * N + j[u] * Q, cq[u]);
-      xv[u] = load_one<IO>(x, ch[u]);
-      dtv[u] = load_one<IO>(dt, ch[u]);
-      zv[u] = z ? load_one<IO>(z, ch[u]) : 0.0f;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float bias2 = dt_bias ? dt_bias[d[u]] * kLog2e : 0.0f;
-      const float skip = Dskip ? Dskip[d[u]] : 0.0f;
-      const float delta = softplus_dt(dtv[u], bias2);
-      const float dx = delta * xv[u];
-      float acc = 0.0f;
-#pragma unroll
-      for (int q = 0; q < Q; ++q) {
-        const float u2 = delta * (a2[u][q] * kLog2e);
-        const float E = __builtin_amdgcn_exp2f(u2);
-        float in = dx * bq[u][q];                  // first order: Bbar x = Delta B x
-        if constexpr (ZOH) in *= zoh_phi(u2, E);   // zero-order hold: (e^u - 1)/u Delta B x
-        st[u][q] = fmaf(E, st[u][q], in);
-        acc = fmaf(cq[u][q], st[u][q], acc);
-      }
-      // sum the channel's K partial readouts (lanes are adjacent inside one quad)
-      if constexpr (K >= 2) acc += __builtin_amdgcn_update_dpp(0.0f, acc, 0xB1, 0xf, 0xf, false);  // [1,0,3,2]
-      if constexpr (K == 4) acc += __builtin_amdgcn_update_dpp(0.0f, acc, 0x4E, 0xf, 0xf, false);  // [2,3,0,1]
-      if (act[u]) {
-        float* sp = state + ch[u] * N + j[u] * Q;
-        if constexpr (Q == 4) {
-          const f32x4 v = {st[u][0], st[u][1], st[u][2], st[u][3]};
-          __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(sp));
-        } else {
-#pragma unroll
-          for (int q = 0; q < Q; ++q) sp[q] = st[u][q];
-        }
-        if (j[u] == 0) {
-          float out = fmaf(skip, xv[u], acc);
-          if (z) out *= silu(zv[u]);
-          store_one<IO>(y, ch[u], out);
-        }
-      }
-    }
+  };
+  for (; b < batch; advance(b, piece)) {
+    Item<Q> it = fetch<N, IO, Q, K>(o, b, piece, lane);
+    finish<N, IO, Q, K, ZOH>(o, it);
   }
 }
 
 template <int N, typename IO, bool ZOH>
-hipError_t launch_t(int64_t nch, int64_t dim, float* state, const void* x, const void* dt, const void* z,
+hipError_t launch_t(int64_t batch, int64_t dim, float* state, const void* x, const void* dt, const void* z,
                     const void* B, const void* C, const float* A, const float* Dskip, const float* dt_bias, void* y,
                     hipStream_t s) {
   using E = typename IO::T;
   constexpr int K = N < 4 ? 1 : N / 4;
-  constexpr int U = DECODE_UNROLL;
-  const int64_t threads = (nch * K + U - 1) / U;
-  int64_t blocks = (threads + 255) / 256;
+  constexpr int64_t kWavesPerBlock = 4;
+  const int64_t pieces = (dim * K + 63) / 64;
+  const int64_t total_waves = batch * pieces;
+  // wave indices and pieces are 32-bit in the kernel
+  if (pieces >= (int64_t(1) << 31) || total_waves >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   // a bounded grid (DECODE_BLOCKS workgroups); the grid-stride loop covers the rest
-  const int64_t cap = DECODE_BLOCKS;
-  if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL((state_update_kernel<N, IO, U, ZOH>), dim3((unsigned)blocks), dim3(256), 0, s, nch, dim, state,
-                     (const E*)x, (const E*)dt, (const E*)z, (const E*)B, (const E*)C, A, Dskip, dt_bias, (E*)y);
+  int64_t blocks = (total_waves + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (blocks > DECODE_BLOCKS) blocks = DECODE_BLOCKS;
+  const int64_t grid_waves = blocks * kWavesPerBlock;
+  const uint32_t stride_rows = (uint32_t)(grid_waves / pieces);
+  const uint32_t stride_pieces = (uint32_t)(grid_waves % pieces);
+  const Operands<N, IO> o{dim, dim * K, state, (const E*)x, (const E*)dt, (const E*)z,
+                          (const E*)B, (const E*)C, A, Dskip, dt_bias, (E*)y};
+  hipLaunchKernelGGL((state_update_kernel<N, IO, ZOH>), dim3((unsigned)blocks),
+                     dim3(64 * kWavesPerBlock), 0, s, batch, (uint32_t)pieces, stride_rows, stride_pieces, o);
   return hipGetLastError();
 }
 
 template <typename IO, bool ZOH>
-hipError_t launch_n(int64_t nch, int64_t dim, int dstate, float* state, const void* x, const void* dt, const void* z,
+hipError_t launch_n(int64_t batch, int64_t dim, int dstate, float* state, const void* x, const void* dt, const void* z,
                     const void* B, const void* C, const float* A, const float* Dskip, const float* dt_bias, void* y,
                     hipStream_t s) {
   switch (dstate) {
-    case 1: return launch_t<1, IO, ZOH>(nch, dim, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
-    case 2: return launch_t<2, IO, ZOH>(nch, dim, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
-    case 4: return launch_t<4, IO, ZOH>(nch, dim, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
-    case 8: return launch_t<8, IO, ZOH>(nch, dim, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
-    case 16: return launch_t<16, IO, ZOH>(nch, dim, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
+    case 1: return launch_t<1, IO, ZOH>(batch, dim, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
+    case 2: return launch_t<2, IO, ZOH>(batch, dim, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
+    case 4: return launch_t<4, IO, ZOH>(batch, dim, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
+    case 8: return launch_t<8, IO, ZOH>(batch, dim, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
+    case 16: return launch_t<16, IO, ZOH>(batch, dim, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -179,13 +229,12 @@ hipError_t launch_n(int64_t nch, int64_t dim, int dstate, float* state, const vo
 hipError_t launch_state_update(int64_t batch, int64_t dim, int dstate, int io, bool zoh, float* state,
                                const void* x, const void* dt, const void* z, const void* B, const void* C,
                                const float* A, const float* Dskip, const float* dt_bias, void* y, hipStream_t s) {
-  const int64_t nch = batch * dim;
   if (io == kIoBf16) {
-    return zoh ? launch_n<BF16, true>(nch, dim, dstate, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s)
-               : launch_n<BF16, false>(nch, dim, dstate, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
+    return zoh ? launch_n<BF16, true>(batch, dim, dstate, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s)
+               : launch_n<BF16, false>(batch, dim, dstate, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
   }
-  return zoh ? launch_n<F32, true>(nch, dim, dstate, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s)
-             : launch_n<F32, false>(nch, dim, dstate, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
+  return zoh ? launch_n<F32, true>(batch, dim, dstate, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s)
+             : launch_n<F32, false>(batch, dim, dstate, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
 }
 
 }  // namespace ssscan

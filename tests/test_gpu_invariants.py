@@ -113,6 +113,30 @@ def test_decode_matches_oracle(ss, dev, dstate):
     assert rel_l2(to_f64(y), yr) <= 1e-6 and rel_l2(to_f64(st), sr) <= 1e-6
 
 
+@pytest.mark.parametrize("dstate,optional", [(16, True), (16, False), (4, False), (2, True)])
+def test_decode_grid_stride_ragged(ss, dev, dstate, optional):
+    """More waves than the bounded grid holds (the grid-stride loop wraps over
+    rows), rows that end inside a wave (dim * lanes-per-channel not a multiple of
+    64), and the optional z, Dskip and dt_bias present or absent."""
+    import torch
+    rng = np.random.default_rng(40 + dstate + 100 * optional)
+    batch, D = 2100, 77
+    raw, par, f64 = random_problem(rng, batch, D, dstate, 1, "f32", with_z=optional, with_skip=optional,
+                                   with_bias=optional)
+    t, p = _upload(raw, par, "f32", dev)
+    st = p["h0"].clone()
+    col = lambda k: t[k][..., 0].contiguous() if k in t else None  # noqa: E731
+    y = ss.state_update(st, col("x"), col("dt"), col("B"), col("C"), p["A"], z=col("z"), Dskip=p["Dskip"],
+                        dt_bias=p["dt_bias"])
+    torch.cuda.synchronize()
+    fcol = lambda k: f64[k][..., 0] if k in f64 else None  # noqa: E731
+    yr, sr = oracle.default().state_update(par["h0"], fcol("x"), fcol("dt"), fcol("B"), fcol("C"), par["A"],
+                                           z=fcol("z"), Dskip=par["Dskip"], dt_bias=par["dt_bias"])
+    assert rel_l2(to_f64(y), yr) <= 1e-6 and rel_l2(to_f64(st), sr) <= 1e-6
+    # every row, including the last one, was written
+    assert np.abs(to_f64(y)[-1] - yr[-1]).max() <= 1e-4 * max(1.0, np.abs(yr[-1]).max())
+
+
 def test_theorem1_euler_closed_form(ss, dev):
     """N = 1, A = -1, B = C = 1, no skip or gate: h_t = (1 - sigmoid(g_t)) h_(t-1) + softplus(g_t) x_t
     (reader's notes, Theorem 1, in the Euler discretisation the kernel uses)."""
