@@ -62,6 +62,9 @@ class Oracle:
         self.lib.ss_oracle_state_update.restype = ctypes.c_int
         self.lib.ss_oracle_state_update.argtypes = [_i64, _i64, _i64, _dp] + [_dp] * 8 + [ctypes.c_int, _dp, ctypes.c_int]
         self.lib.ss_oracle_max_threads.restype = ctypes.c_int
+        self.lib.ss_oracle_scan_bwd.restype = ctypes.c_int
+        self.lib.ss_oracle_scan_bwd.argtypes = ([_i64, _i64, _i64, _i64] + [_dp] * 9 + [ctypes.c_int] + [_dp] * 2
+                                                + [_dp] * 9 + [ctypes.c_int])
 
     def max_threads(self) -> int:
         return int(self.lib.ss_oracle_max_threads())
@@ -89,6 +92,38 @@ class Oracle:
         if rc != 0:
             raise ValueError("ss_oracle_scan rejected its arguments (%d)" % rc)
         return y, hf
+
+    def scan_bwd(self, x, dt, B, C, A, dy, z=None, Dskip=None, dt_bias=None, h0=None, dh_final=None,
+                 zoh=False, nthreads=0):
+        """Gradients of the full-sequence scan for upstream gradients dy (batch, D, L) and
+        dh_final (batch, D, N) (None = 0).
+
+        Returns a dict of float64 arrays: dx, ddt, dz (None without z) (batch, D, L);
+        dB, dC (batch, N, L); dA (D, N); dDskip, ddt_bias (D,); dh0 (batch, D, N).
+        The gradients with respect to Dskip, dt_bias and h0 are returned also when those
+        inputs are None (they are then taken as zeros).
+        """
+        x, dt, z, B, C, A, dy = map(_as_f64, (x, dt, z, B, C, A, dy))
+        Dskip, dt_bias, h0, dh_final = map(_as_f64, (Dskip, dt_bias, h0, dh_final))
+        batch, D, L = x.shape
+        N = A.shape[1]
+        assert dt.shape == x.shape and dy.shape == x.shape
+        assert B.shape == (batch, N, L) and C.shape == (batch, N, L) and A.shape == (D, N)
+        assert z is None or z.shape == x.shape
+        assert h0 is None or h0.shape == (batch, D, N)
+        assert dh_final is None or dh_final.shape == (batch, D, N)
+        out = dict(dx=np.empty((batch, D, L)), ddt=np.empty((batch, D, L)),
+                   dz=np.empty((batch, D, L)) if z is not None else None,
+                   dB=np.empty((batch, N, L)), dC=np.empty((batch, N, L)), dA=np.empty((D, N)),
+                   dDskip=np.empty(D), ddt_bias=np.empty(D), dh0=np.empty((batch, D, N)))
+        rc = self.lib.ss_oracle_scan_bwd(batch, D, N, L, _ptr(x), _ptr(dt), _ptr(z), _ptr(B), _ptr(C), _ptr(A),
+                                         _ptr(Dskip), _ptr(dt_bias), _ptr(h0), int(bool(zoh)), _ptr(dy),
+                                         _ptr(dh_final), _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dz"]),
+                                         _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dA"]), _ptr(out["dDskip"]),
+                                         _ptr(out["ddt_bias"]), _ptr(out["dh0"]), int(nthreads))
+        if rc != 0:
+            raise ValueError("ss_oracle_scan_bwd failed (%d)" % rc)
+        return out
 
     def state_update(self, state, x, dt, B, C, A, z=None, Dskip=None, dt_bias=None,
                      zoh=False, nthreads=0):

@@ -329,6 +329,112 @@ def pin_decode_formula(o):
         _close(y, yref, rtol=1e-12, atol=1e-14, what="decode output formula")
 
 
+# --- Backward pass.  Training differentiates the scan, recomputing the state in
+# the backward pass (reader's notes, "What they did", Selective SSM item).  The
+# oracle's gradients are pinned without re-deriving them: by central finite
+# differences of the oracle's own forward scan (which the pins above fix), and by
+# exact identities that follow from the scan being linear in some inputs.
+
+def _loss_and_inputs(rng, zoh, tiny_a=False, zero_a=False):
+    p = _rand_problem(rng, batch=2, D=3, N=4, L=9)
+    if tiny_a:
+        # Delta ~ 2-3 and |A| <= 2.5e-4: |Delta A| < 1e-3 (the series branch), with the
+        # ZOH term of dA (order Delta^2) comparable to the decay term
+        p["dt"] += 2.5
+        p["A"][:, 1] = -rng.uniform(1e-4, 2.5e-4, 3)
+    if zero_a:
+        p["A"][0, 2] = 0.0
+    dy = rng.standard_normal(p["x"].shape)
+    dhf = rng.standard_normal(p["h0"].shape)
+    return p, dy, dhf
+
+
+_GRAD_OF = {"x": "dx", "dt": "ddt", "z": "dz", "B": "dB", "C": "dC", "A": "dA", "Dskip": "dDskip",
+            "dt_bias": "ddt_bias", "h0": "dh0"}
+
+
+def _fd_check(o, p, dy, dhf, zoh, what):
+    def loss(q):
+        y, hf = o.scan(q["x"], q["dt"], q["B"], q["C"], q["A"], z=q["z"], Dskip=q["Dskip"], dt_bias=q["dt_bias"],
+                       h0=q["h0"], zoh=zoh)
+        return float(np.sum(dy * y) + np.sum(dhf * hf))
+
+    g = o.scan_bwd(p["x"], p["dt"], p["B"], p["C"], p["A"], dy, z=p["z"], Dskip=p["Dskip"],
+                   dt_bias=p["dt_bias"], h0=p["h0"], dh_final=dhf, zoh=zoh)
+    for name, gname in _GRAD_OF.items():
+        base = p[name]
+        fd = np.empty_like(base)
+        for idx in np.ndindex(base.shape):
+            eps = 1e-6 * max(1.0, abs(base[idx]))
+            q = dict(p)
+            q[name] = base.copy()
+            q[name][idx] = base[idx] + eps
+            lp = loss(q)
+            q[name][idx] = base[idx] - eps
+            lm = loss(q)
+            fd[idx] = (lp - lm) / (2.0 * eps)
+        _close(g[gname], fd, rtol=1e-6, atol=1e-7, what="%s: d/d%s vs finite differences" % (what, name))
+
+
+# B1: every gradient against central finite differences of the forward scan,
+# both discretisations, with gate, skip, bias, h0 and a final-state gradient.
+def pin_bwd_finite_differences(o):
+    rng = np.random.default_rng(120)
+    for zoh in (False, True):
+        p, dy, dhf = _loss_and_inputs(rng, zoh)
+        _fd_check(o, p, dy, dhf, zoh, "zoh" if zoh else "euler")
+
+
+# B2: the ZOH coefficient's derivative in A near A = 0 (series branch) and at A = 0.
+def pin_bwd_zoh_small_a(o):
+    rng = np.random.default_rng(121)
+    p, dy, dhf = _loss_and_inputs(rng, True, tiny_a=True, zero_a=True)
+    _fd_check(o, p, dy, dhf, True, "zoh small A")
+
+
+# B3: exact identities.  Without a gate, (y, h_final) is linear in (x, h0)
+# jointly for fixed dt, so <dy, y> + <dhf, h_final> = <dx, x> + <dh0, h0>.  With
+# h0 = 0, (y - Dskip x, h_final) is linear in B; y - Dskip x is linear in C; and
+# y depends on Dskip only through Dskip x.
+def pin_bwd_linear_identities(o):
+    rng = np.random.default_rng(122)
+    for zoh in (False, True):
+        p = _rand_problem(rng, batch=2, D=5, N=3, L=17)
+        dy = rng.standard_normal(p["x"].shape)
+        dhf = rng.standard_normal(p["h0"].shape)
+        kw = dict(Dskip=p["Dskip"], dt_bias=p["dt_bias"], zoh=zoh)
+        y, hf = o.scan(p["x"], p["dt"], p["B"], p["C"], p["A"], h0=p["h0"], **kw)
+        g = o.scan_bwd(p["x"], p["dt"], p["B"], p["C"], p["A"], dy, h0=p["h0"], dh_final=dhf, **kw)
+        lhs = np.sum(dy * y) + np.sum(dhf * hf)
+        _close(np.sum(g["dx"] * p["x"]) + np.sum(g["dh0"] * p["h0"]), lhs, rtol=1e-12, what="adjoint in (x, h0)")
+        skip_part = p["Dskip"][None, :, None] * p["x"]
+        _close(np.sum(g["dDskip"] * p["Dskip"]), np.sum(dy * skip_part), rtol=1e-12, what="adjoint in Dskip")
+        y0, hf0 = o.scan(p["x"], p["dt"], p["B"], p["C"], p["A"], **kw)
+        g0 = o.scan_bwd(p["x"], p["dt"], p["B"], p["C"], p["A"], dy, dh_final=dhf, **kw)
+        _close(np.sum(g0["dB"] * p["B"]), np.sum(dy * (y0 - skip_part)) + np.sum(dhf * hf0), rtol=1e-12,
+               what="adjoint in B")
+        _close(np.sum(g0["dC"] * p["C"]), np.sum(dy * (y0 - skip_part)), rtol=1e-12, what="adjoint in C")
+
+
+# B4: an empty sequence passes dh_final straight to dh0 and has no other gradient;
+# a single token with a huge dt forgets h0 (dh0 -> 0) while dx stays finite.
+def pin_bwd_edges(o):
+    rng = np.random.default_rng(123)
+    p = _rand_problem(rng, batch=2, D=3, N=4, L=0)
+    dhf = rng.standard_normal(p["h0"].shape)
+    g = o.scan_bwd(p["x"], p["dt"], p["B"], p["C"], p["A"], np.zeros(p["x"].shape), z=p["z"], h0=p["h0"],
+                   dh_final=dhf)
+    _close(g["dh0"], dhf, rtol=0, atol=0, what="empty sequence dh0")
+    assert not np.any(g["dA"]) and not np.any(g["dDskip"]) and not np.any(g["ddt_bias"]), "empty sequence"
+    p = _rand_problem(rng, batch=1, D=2, N=3, L=1)
+    p["dt"][:] = 40.0
+    p["A"] = -1.0 - np.abs(p["A"])        # Delta A <= -40: Abar < 5e-18
+    g = o.scan_bwd(p["x"], p["dt"], p["B"], p["C"], p["A"], np.ones(p["x"].shape), h0=p["h0"])
+    assert np.all(np.abs(g["dh0"]) < 1e-15) and np.all(np.isfinite(g["dx"])), "large Delta forgets h0"
+
+
+BWD_PINS = [pin_bwd_finite_differences, pin_bwd_zoh_small_a, pin_bwd_linear_identities, pin_bwd_edges]
+
 ALL_PINS = [pin_theorem1, pin_delta_limits, pin_lti_convolution, pin_unrolled,
             pin_state_decomposition, pin_split_resume, pin_decode_equals_scan,
-            pin_linearity_and_gate, pin_permutations, pin_decode_formula]
+            pin_linearity_and_gate, pin_permutations, pin_decode_formula] + BWD_PINS

@@ -48,6 +48,35 @@ MUTANTS = [
     ("decode-skip-dropped", "double out = acc + (Dskip ? Dskip[d] : 0.0) * x[ch];", "double out = acc;", None),
     ("decode-B-by-channel", "in = delta * B[b * dstate + n] * x[ch];", "in = delta * B[(d % batch) * dstate + n] * x[ch];", None),
     ("decode-gate-sign", "if (z) out *= z[ch] / (1.0 + exp(-z[ch]));", "if (z) out *= z[ch] / (1.0 + exp(z[ch]));", None),
+    # backward pass
+    ("bwd-adjoint-not-decayed", "          lam[n] *= abar;\n", "", None),
+    ("bwd-dC-previous-state", "pdC[n * L + t] += dr * hs[(t + 1) * N + n];", "pdC[n * L + t] += dr * hs[t * N + n];", None),
+    ("bwd-dAbar-new-state", "const double dabar = lam[n] * hs[t * N + n];",
+     "const double dabar = lam[n] * hs[(t + 1) * N + n];", None),
+    ("bwd-dDelta-no-input-term", "ddelta += dabar * abar * a + lam[n] * bt * xr[t] * dcd;", "ddelta += dabar * abar * a;", None),
+    ("bwd-dDelta-no-decay-term", "ddelta += dabar * abar * a + lam[n] * bt * xr[t] * dcd;",
+     "ddelta += lam[n] * bt * xr[t] * dcd;", None),
+    ("bwd-dA-missing-delta", "dA[d * N + n] += dabar * abar * delta + lam[n] * bt * xr[t] * dca;",
+     "dA[d * N + n] += dabar * abar + lam[n] * bt * xr[t] * dca;", None),
+    ("bwd-dA-no-zoh-term", "dA[d * N + n] += dabar * abar * delta + lam[n] * bt * xr[t] * dca;",
+     "dA[d * N + n] += dabar * abar * delta;", None),
+    ("bwd-dB-missing-x", "pdB[n * L + t] += lam[n] * c * xr[t];", "pdB[n * L + t] += lam[n] * c;", None),
+    ("bwd-dx-missing-skip", "double dxv = dr * skip;", "double dxv = 0.0;", None),
+    ("bwd-dx-missing-B", "dxv += lam[n] * c * bt;", "dxv += lam[n] * c;", None),
+    ("bwd-dz-sigmoid", "dz[ch * L + t] = dy[ch * L + t] * rr[t] * dsilu(zr[t]);",
+     "dz[ch * L + t] = dy[ch * L + t] * rr[t] * sigmoid(zr[t]);", None),
+    ("bwd-dr-ungated", "const double dr = dy[ch * L + t] * g;", "const double dr = dy[ch * L + t];", None),
+    ("bwd-softplus-derivative-no-bias", "const double dv = ddelta * sigmoid(dtr[t] + bias);",
+     "const double dv = ddelta * sigmoid(dtr[t]);", None),
+    ("bwd-dbias-dropped", "        ddt_bias[d] += dv;\n", "", None),
+    ("bwd-dDskip-ungated", "dDskip[d] += dr * xr[t];", "dDskip[d] += dy[ch * L + t] * xr[t];", None),
+    ("bwd-dB-one-row", "dB[b * N * L + i] += wk[i];", "dB[i] += wk[i];", None),
+    ("bwd-dh-final-ignored", "lam[n] = dh_final ? dh_final[ch * N + n] : 0.0;", "lam[n] = 0.0;", None),
+    ("bwd-readout-skip-missing", "rr[t] = acc + skip * xr[t];", "rr[t] = acc;", None),
+    ("bwd-psi-series", "0.5 + u * (1.0 / 3.0 + u * (1.0 / 8.0 + u * (1.0 / 30.0)))",
+     "0.5 + u * (1.0 / 6.0 + u * (1.0 / 8.0 + u * (1.0 / 30.0)))", None),
+    ("bwd-psi-closed-form", "psi = (u * eu - expm1(u)) / (u * u);", "psi = (u * eu + expm1(u)) / (u * u);", None),
+    ("bwd-zoh-dc-ddelta", "*dc_ddelta = eu;", "*dc_ddelta = 1.0;", None),
 ]
 
 
