@@ -141,9 +141,45 @@ ss_status ss_state_update_zoh(int64_t batch, int64_t dim, int dstate, ss_dtype i
                               const float* Dskip, const float* dt_bias,
                               void* y, void* stream);
 
-/* Opt-in timing of the main scan kernel (for benchmarks).  While enabled, each
+/* Backward pass of ss_scan_fwd (first-order input term): the gradients of a
+ * loss with respect to every input of the scan, given dy = dLoss/dy and
+ * dh_final = dLoss/dh_final.  Training differentiates the scan, and the state
+ * is recomputed in the backward pass instead of being stored (reader's notes on
+ * the Mamba paper, kurisu.si, "What they did", Selective SSM item): the call
+ * takes the forward's inputs, not its outputs.
+ *
+ * Inputs: x, dt, z, B, C, A, Dskip, dt_bias, h0 exactly as given to ss_scan_fwd
+ * (z, Dskip, dt_bias, h0 nullable); dy (batch, dim, seqlen) in the I/O dtype;
+ * dh_final (batch, dim, dstate) fp32, NULL = zero.
+ * Outputs, all written (never accumulated into):
+ *   dx, ddt (batch, dim, seqlen) and dB, dC (batch, dstate, seqlen) in the I/O
+ *     dtype, required when seqlen > 0;
+ *   dz (batch, dim, seqlen) in the I/O dtype, given exactly when z is;
+ *   dA (dim, dstate), dDskip (dim), ddt_bias (dim), dh0 (batch, dim, dstate)
+ *     fp32, each nullable (not computed when NULL).  They are the gradients
+ *     with respect to Dskip, dt_bias and h0 also when those inputs are NULL
+ *     (read as zero).
+ * Alignment, aliasing (no output may overlap an input, another output or the
+ * workspace) and stream rules are those of ss_scan_fwd.  The workspace (size
+ * from ss_scan_bwd_workspace_bytes, 256-byte aligned, caller-owned, contents
+ * need not be preserved between calls) holds the state checkpoints and the
+ * partial sums.  seqlen == 0 needs no workspace: dh0 = dh_final (or zero) and
+ * dA, dDskip, ddt_bias are zeroed.  Results are deterministic: every sum runs
+ * in a fixed order. */
+size_t ss_scan_bwd_workspace_bytes(int64_t batch, int64_t dim, int dstate, int64_t seqlen,
+                                   ss_dtype io);
+ss_status ss_scan_bwd(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io,
+                      const void* x, const void* dt, const void* z,
+                      const void* B, const void* C, const float* A,
+                      const float* Dskip, const float* dt_bias, const float* h0,
+                      const void* dy, const float* dh_final,
+                      void* dx, void* ddt, void* dz, void* dB, void* dC,
+                      float* dA, float* dDskip, float* ddt_bias, float* dh0,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Opt-in timing of the main scan kernels (for benchmarks).  While enabled, each
  * ss_scan_fwd call records HIP events around its scan kernel launches on its
- * stream.  ss_timing_read synchronises on the recorded events and returns the
+ * stream, and each ss_scan_bwd call around its backward kernels.  ss_timing_read synchronises on the recorded events and returns the
  * summed kernel time in milliseconds and the number of calls recorded since the
  * last ss_timing_reset. */
 ss_status ss_timing_enable(int enable);

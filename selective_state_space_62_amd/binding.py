@@ -65,6 +65,10 @@ def _load():
     lib.ss_scan_fwd_zoh.argtypes = lib.ss_scan_fwd.argtypes
     lib.ss_state_update_zoh.restype = _int
     lib.ss_state_update_zoh.argtypes = lib.ss_state_update.argtypes
+    lib.ss_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.ss_scan_bwd_workspace_bytes.argtypes = [_i64, _i64, _int, _i64, _int]
+    lib.ss_scan_bwd.restype = _int
+    lib.ss_scan_bwd.argtypes = [_i64, _i64, _int, _i64, _int] + [_vp] * 21 + [ctypes.c_size_t, _vp]
     lib.ss_timing_enable.restype = _int
     lib.ss_timing_enable.argtypes = [_int]
     lib.ss_timing_reset.restype = _int
@@ -142,6 +146,16 @@ def ss_scan_fwd_zoh(batch, dim, dstate, seqlen, io, x, dt, z, B, C, A, Dskip, dt
 
 def ss_state_update_zoh(batch, dim, dstate, io, state, x, dt, z, B, C, A, Dskip, dt_bias, y, stream=None):
     _check(lib.ss_state_update_zoh(batch, dim, dstate, io, state, x, dt, z, B, C, A, Dskip, dt_bias, y, stream))
+
+
+def ss_scan_bwd_workspace_bytes(batch, dim, dstate, seqlen, io) -> int:
+    return int(lib.ss_scan_bwd_workspace_bytes(batch, dim, dstate, seqlen, io))
+
+
+def ss_scan_bwd(batch, dim, dstate, seqlen, io, x, dt, z, B, C, A, Dskip, dt_bias, h0, dy, dh_final,
+                dx, ddt, dz, dB, dC, dA, dDskip, ddt_bias, dh0, workspace, workspace_bytes, stream=None):
+    _check(lib.ss_scan_bwd(batch, dim, dstate, seqlen, io, x, dt, z, B, C, A, Dskip, dt_bias, h0, dy, dh_final,
+                           dx, ddt, dz, dB, dC, dA, dDskip, ddt_bias, dh0, workspace, workspace_bytes, stream))
 
 
 def ss_timing_enable(enable: bool):

@@ -420,6 +420,173 @@ ss_status state_update_impl(int64_t batch, int64_t dim, int dstate, ss_dtype io,
   return SS_OK;
 }
 
+struct BwdLayout {
+  size_t bc, ckpt, part, dA_p, dD_p, dbias_p, total;
+  int64_t cblocks, chunks;
+};
+
+BwdLayout bwd_layout(int64_t batch, int64_t dim, int dstate, int64_t seqlen) {
+  BwdLayout w{};
+  const int64_t cpb = 64 / ssscan::bwd_lanes_per_channel(dstate);
+  const int64_t ck = ssscan::bwd_chunk_len(dstate);
+  w.cblocks = (dim + cpb - 1) / cpb;
+  w.chunks = (seqlen + ck - 1) / ck;
+  size_t off = 0;
+  w.bc = off;
+  off += round256((size_t)batch * seqlen * dstate * 2 * sizeof(float));
+  w.ckpt = off;
+  off += round256((size_t)batch * dim * w.chunks * dstate * sizeof(float));
+  w.part = off;
+  off += round256((size_t)batch * w.cblocks * seqlen * 2 * dstate * sizeof(float));
+  w.dA_p = off;
+  off += round256((size_t)batch * dim * dstate * sizeof(float));
+  w.dD_p = off;
+  off += round256((size_t)batch * dim * sizeof(float));
+  w.dbias_p = off;
+  off += round256((size_t)batch * dim * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+ss_status scan_bwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io, const void* x,
+                        const void* dt, const void* z, const void* B, const void* C, const float* A,
+                        const float* Dskip, const float* dt_bias, const float* h0, const void* dy,
+                        const float* dh_final, void* dx, void* ddt, void* dz, void* dB, void* dC, float* dA,
+                        float* dDskip, float* ddt_bias, float* dh0, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  ss_status st = check_sizes(batch, dim, dstate, seqlen, io);
+  if (st != SS_OK) return st;
+  if (!A) return fail(SS_ERR_INVALID_ARG, "A is NULL");
+  if (seqlen > 0) {
+    const char* names[] = {"x", "dt", "B", "C", "dy", "dx", "ddt", "dB", "dC"};
+    const void* req[] = {x, dt, B, C, dy, dx, ddt, dB, dC};
+    for (int i = 0; i < 9; ++i)
+      if (!req[i]) return fail(SS_ERR_INVALID_ARG, "%s is NULL", names[i]);
+  }
+  if ((z == nullptr) != (dz == nullptr))
+    return fail(SS_ERR_INVALID_ARG, "dz must be given exactly when z is (z %s, dz %s)", z ? "set" : "NULL",
+                dz ? "set" : "NULL");
+  const void* a16[] = {x, dt, z, B, C, A, h0, dy, dh_final, dx, ddt, dz, dB, dC, dA, dh0};
+  const char* n16[] = {"x", "dt", "z", "B", "C", "A", "h0", "dy", "dh_final", "dx", "ddt", "dz", "dB", "dC",
+                       "dA", "dh0"};
+  for (int i = 0; i < 16; ++i)
+    if (a16[i] && !aligned(a16[i], 16)) return fail(SS_ERR_INVALID_ARG, "%s is not 16-byte aligned", n16[i]);
+  const void* a4[] = {Dskip, dt_bias, dDskip, ddt_bias};
+  const char* n4[] = {"Dskip", "dt_bias", "dDskip", "ddt_bias"};
+  for (int i = 0; i < 4; ++i)
+    if (a4[i] && !aligned(a4[i], 4)) return fail(SS_ERR_INVALID_ARG, "%s is not 4-byte aligned", n4[i]);
+
+  const BwdLayout wl = bwd_layout(batch, dim, dstate, seqlen);
+  if (seqlen > 0) {
+    if (!workspace) return fail(SS_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", wl.total);
+    if (!aligned(workspace, 256)) return fail(SS_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    if (workspace_bytes < wl.total)
+      return fail(SS_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, wl.total);
+  }
+  const int64_t eb = elem_bytes(io);
+  const int64_t seq_bytes = batch * dim * seqlen * eb;
+  const int64_t bc_bytes = batch * dstate * seqlen * eb;
+  const int64_t st_bytes = batch * dim * dstate * 4;
+  const Range ins[] = {rng("x", x, seq_bytes), rng("dt", dt, seq_bytes), rng("z", z, seq_bytes),
+                       rng("B", B, bc_bytes), rng("C", C, bc_bytes), rng("A", A, dim * dstate * 4),
+                       rng("Dskip", Dskip, dim * 4), rng("dt_bias", dt_bias, dim * 4), rng("h0", h0, st_bytes),
+                       rng("dy", dy, seq_bytes), rng("dh_final", dh_final, st_bytes)};
+  const Range outs[] = {rng("dx", dx, seq_bytes), rng("ddt", ddt, seq_bytes), rng("dz", dz, seq_bytes),
+                        rng("dB", dB, bc_bytes), rng("dC", dC, bc_bytes), rng("dA", dA, dim * dstate * 4),
+                        rng("dDskip", dDskip, dim * 4), rng("ddt_bias", ddt_bias, dim * 4),
+                        rng("dh0", dh0, st_bytes), rng("workspace", workspace, seqlen > 0 ? (int64_t)wl.total : 0)};
+  constexpr int kOuts = sizeof(outs) / sizeof(outs[0]);
+  for (const Range& o : outs)
+    for (const Range& i : ins)
+      if (overlap(o, i)) return fail(SS_ERR_INVALID_ARG, "%s overlaps input %s", o.name, i.name);
+  for (int i = 0; i < kOuts; ++i)
+    for (int j = i + 1; j < kOuts; ++j)
+      if (overlap(outs[i], outs[j])) return fail(SS_ERR_INVALID_ARG, "%s overlaps %s", outs[i].name, outs[j].name);
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (seqlen == 0) {
+    // no tokens: the final state is h0, so dh0 = dh_final; every other gradient is zero
+    if (dh0) {
+      e = dh_final ? ssscan::launch_copy_state(batch * dim * dstate, dh_final, dh0, s)
+                   : ssscan::launch_fill_zero(dh0, batch * dim * dstate, s);
+      if (e != hipSuccess) return hip_fail(e, "dh0 launch");
+    }
+    float* zero[] = {dA, dDskip, ddt_bias};
+    const int64_t count[] = {dim * dstate, dim, dim};
+    for (int i = 0; i < 3; ++i) {
+      e = ssscan::launch_fill_zero(zero[i], count[i], s);
+      if (e != hipSuccess) return hip_fail(e, "zero-fill launch");
+    }
+    return SS_OK;
+  }
+  const int64_t nwg = wl.cblocks * batch;
+  if (nwg > 0x7fffffffLL) return fail(SS_ERR_INVALID_ARG, "launch needs %lld workgroups (limit 2^31-1)", (long long)nwg);
+
+  char* ws = static_cast<char*>(workspace);
+  ssscan::ScanDims pd{};
+  pd.batch = batch;
+  pd.dim = dim;
+  pd.seqlen = seqlen;
+  pd.dstate = dstate;
+  pd.io = io_code(io);
+  float* bcw = reinterpret_cast<float*>(ws + wl.bc);
+  e = ssscan::launch_prep_bc(pd, B, C, bcw, s);
+  if (e != hipSuccess) return hip_fail(e, "prep_bc launch");
+
+  ssscan::BwdDims dm{};
+  dm.batch = batch;
+  dm.dim = dim;
+  dm.seqlen = seqlen;
+  dm.cblocks = wl.cblocks;
+  dm.dstate = dstate;
+  dm.io = io_code(io);
+  dm.vec = (seqlen % 2) == 0 ? 1 : 0;
+  ssscan::BwdPtrs bp{};
+  bp.x = x;
+  bp.dt = dt;
+  bp.z = z;
+  bp.bc = bcw;
+  bp.A = A;
+  bp.Dskip = Dskip;
+  bp.dt_bias = dt_bias;
+  bp.h0 = h0;
+  bp.dy = dy;
+  bp.dh_final = dh_final;
+  bp.dx = dx;
+  bp.ddt = ddt;
+  bp.dz = dz;
+  bp.dB = dB;
+  bp.dC = dC;
+  bp.dA = dA;
+  bp.dDskip = dDskip;
+  bp.ddt_bias = ddt_bias;
+  bp.dh0 = dh0;
+  bp.ckpt = reinterpret_cast<float*>(ws + wl.ckpt);
+  bp.part = reinterpret_cast<float*>(ws + wl.part);
+  bp.dA_p = reinterpret_cast<float*>(ws + wl.dA_p);
+  bp.dD_p = reinterpret_cast<float*>(ws + wl.dD_p);
+  bp.dbias_p = reinterpret_cast<float*>(ws + wl.dbias_p);
+
+  const bool timed = timing_on();
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  if (timed) {
+    st = timing_pair(&ev0, &ev1);
+    if (st != SS_OK) return st;
+    e = hipEventRecord(ev0, s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  e = ssscan::launch_scan_bwd(dm, bp, s);
+  if (e != hipSuccess) return hip_fail(e, "scan_bwd launch");
+  if (timed) {
+    e = hipEventRecord(ev1, s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    g_timing.pending.emplace_back(ev0, ev1);
+  }
+  return SS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -450,6 +617,22 @@ ss_status ss_state_update_zoh(int64_t batch, int64_t dim, int dstate, ss_dtype i
                               const void* dt, const void* z, const void* B, const void* C, const float* A,
                               const float* Dskip, const float* dt_bias, void* y, void* stream) {
   return state_update_impl(batch, dim, dstate, io, state, x, dt, z, B, C, A, Dskip, dt_bias, y, stream, true);
+}
+
+size_t ss_scan_bwd_workspace_bytes(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io) {
+  if (check_sizes(batch, dim, dstate, seqlen, io) != SS_OK) return 0;
+  if (seqlen == 0) return 0;
+  return bwd_layout(batch, dim, dstate, seqlen).total;
+}
+
+ss_status ss_scan_bwd(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io, const void* x,
+                      const void* dt, const void* z, const void* B, const void* C, const float* A,
+                      const float* Dskip, const float* dt_bias, const float* h0, const void* dy,
+                      const float* dh_final, void* dx, void* ddt, void* dz, void* dB, void* dC, float* dA,
+                      float* dDskip, float* ddt_bias, float* dh0, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return scan_bwd_impl(batch, dim, dstate, seqlen, io, x, dt, z, B, C, A, Dskip, dt_bias, h0, dy, dh_final, dx,
+                       ddt, dz, dB, dC, dA, dDskip, ddt_bias, dh0, workspace, workspace_bytes, stream);
 }
 
 ss_status ss_timing_enable(int enable) {

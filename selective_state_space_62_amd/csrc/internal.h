@@ -39,6 +39,48 @@ struct ScanPtrs {
   float* agg_s;         // chunk sums of Delta (batch, dim, num_chunks)
 };
 
+// Shape of one backward launch.
+struct BwdDims {
+  int64_t batch;
+  int64_t dim;
+  int64_t seqlen;
+  int64_t cblocks;      // channel blocks per batch row (64 / lanes-per-channel channels each)
+  int32_t dstate;
+  int32_t io;
+  int32_t vec;          // 1: every lane's 2-token span of a row is aligned for one vector access
+};
+
+struct BwdPtrs {
+  const void* x;
+  const void* dt;
+  const void* z;          // nullable
+  const float* bc;        // workspace: (batch, seqlen, dstate, 2) fp32, B and C interleaved
+  const float* A;
+  const float* Dskip;     // nullable
+  const float* dt_bias;   // nullable
+  const float* h0;        // nullable
+  const void* dy;
+  const float* dh_final;  // nullable
+  void* dx;
+  void* ddt;
+  void* dz;               // non-null exactly when z is
+  void* dB;
+  void* dC;
+  float* dA;              // nullable
+  float* dDskip;          // nullable
+  float* ddt_bias;        // nullable
+  float* dh0;             // nullable
+  float* ckpt;            // workspace: (batch, dim, chunks, dstate) state at every chunk start
+  float* part;            // workspace: (batch, cblocks, seqlen, 2 dstate) dB/dC partial sums
+  float* dA_p;            // workspace: (batch, dim, dstate) per-row sums
+  float* dD_p;            // workspace: (batch, dim)
+  float* dbias_p;         // workspace: (batch, dim)
+};
+
+// Backward plan: lanes per channel and chunk length (tokens) for a state size.
+int bwd_lanes_per_channel(int dstate);
+int bwd_chunk_len(int dstate);
+
 // Tokens per tile: each wave loads 16 bytes of every input row per tile.
 inline int tile_len(int groups, int io) { return groups * (io == kIoBf16 ? 8 : 4); }
 // Tokens of a row each lane loads per tile (its span).
@@ -53,6 +95,8 @@ hipError_t launch_scan_f32_zoh(const ScanDims& dm, const ScanPtrs& p, bool aggre
 hipError_t launch_combine(const ScanDims& dm, const float* A, const float* agg_h, const float* agg_s,
                           const float* h0, float* h_in, hipStream_t s);
 hipError_t launch_copy_state(int64_t count, const float* src, float* dst, hipStream_t s);
+hipError_t launch_scan_bwd(const BwdDims& dm, const BwdPtrs& p, hipStream_t s);
+hipError_t launch_fill_zero(float* dst, int64_t n, hipStream_t s);
 hipError_t launch_state_update(int64_t batch, int64_t dim, int dstate, int io, bool zoh, float* state,
                                const void* x, const void* dt, const void* z, const void* B, const void* C,
                                const float* A, const float* Dskip, const float* dt_bias, void* y,

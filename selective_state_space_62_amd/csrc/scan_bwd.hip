@@ -1,0 +1,474 @@
+// Backward pass of the selective scan (ss_scan_bwd) for gfx950.
+//
+// Training runs the scan forward and then backward; the pages' fused kernel
+// keeps the expanded state on-chip and recomputes it in the backward pass
+// instead of storing it (reader's notes, kurisu.si, "What they did", Selective
+// SSM item).  The gradients are those of the forward definition
+//   Delta_t = softplus(dt_t + dt_bias),  Abar = exp(Delta_t A_n),
+//   h_t[n] = Abar h_(t-1)[n] + Delta_t B_t[n] x_t,
+//   y_t = r_t silu(z_t),  r_t = C_t . h_t + Dskip x_t,
+// taken in reverse token order with the adjoint state lam_t = dLoss/dh_t:
+//   dr_t = dy_t silu(z_t),  dz_t = dy_t r_t silu'(z_t),
+//   lam_t = Abar_(t+1) lam_(t+1) + dr_t C_t  (lam_L = dh_final),
+//   dC_t[n] += dr_t h_t[n],  dB_t[n] += lam_t[n] Delta_t x_t   (summed over channels),
+//   with dAbar = lam_t h_(t-1):  dDelta += dAbar Abar A,  dA += dAbar Abar Delta,
+//   dDelta += x_t sum_n lam_t[n] B_t[n],  dx_t = Delta_t sum_n lam_t[n] B_t[n] + dr_t Dskip,
+//   ddt_t = dDelta sigmoid(dt_t + dt_bias),  dh0 = Abar_0 lam_0.
+//
+// One workgroup owns 64/K channels of one batch row, laid out like the forward
+// kernel: G waves, K adjacent lanes per channel, each lane NS = N/(G K) state
+// components.  Work goes in chunks of CK = 2 G K tokens; each lane owns 2 tokens
+// of a chunk for the per-(token, channel) work (Delta, the gate, dx, ddt, dz).
+//  1. A forward sweep over the sequence stores the state at every chunk start
+//     (the checkpoints, in the workspace).
+//  2. Chunks are then visited last to first.  The chunk's states are recomputed
+//     from its checkpoint into registers, with the readout (dz needs r_t); the
+//     owner of each token forms dr and dz; then every lane runs the adjoint state
+//     back through the chunk.  The sums over state components (for dx and
+//     dDelta) reach the token's owner through LDS, as the forward's readout does.
+// dB and dC are sums over channels.  In a workgroup the two channels of a lane
+// pair are added with one DPP move (the even channel keeps dB, the odd one dC),
+// the pair sums are added in LDS in a fixed order, and one partial per
+// (workgroup, token) goes to the workspace; bwd_reduce_bc_kernel adds a batch
+// row's partials in a fixed order.  dA, dDskip and dt_bias's gradient are summed
+// per (row, channel) in registers and over rows by bwd_reduce_param_kernel.  All
+// sums have a fixed order: results are deterministic.
+#include "device_common.h"
+#include "internal.h"
+
+namespace ssscan {
+namespace {
+
+using namespace dev;
+
+constexpr int kSpan = 2;   // tokens of a chunk owned per lane
+
+// Workgroup index -> logical block so that the channel blocks of one batch row
+// share an XCD (workgroups are dealt to the 8 XCDs round-robin).
+__device__ __forceinline__ int64_t bwd_logical_block(int64_t wg, int64_t nwg) {
+  if ((nwg & 7) != 0) return wg;
+  return (wg & 7) * (nwg >> 3) + (wg >> 3);
+}
+
+// sigmoid(v) given v2 = v log2(e); 0 when e^-v overflows
+__device__ __forceinline__ float sigmoid2(float v2) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-v2));
+}
+
+template <int N, int G, int K, typename IO>
+__global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10))) void scan_bwd_kernel(
+    const BwdDims dm, const BwdPtrs p) {
+  using T = typename IO::T;
+  constexpr int CPB = 64 / K;                    // channels per workgroup
+  constexpr int SG = G * K;                      // state groups
+  constexpr int NS = N / SG;                     // state components per lane
+  constexpr int CK = kSpan * SG;                 // chunk length (tokens)
+  constexpr int HALF = CK >= 16 ? CK / 2 : CK;   // tokens per dB/dC reduction round
+  constexpr int NOUT = 2 * N;                    // dB and dC values per token
+  constexpr int THREADS = 64 * G;
+  constexpr int PAIRS = CPB / 2;                 // channel pairs per workgroup
+  constexpr int PLANE = PAIRS * NS + 1;          // floats per (token, group, dB|dC) plane, padded
+  constexpr int SW = SpanT<IO, kSpan>::kWords;
+  static_assert(NS >= 1 && N % SG == 0, "G * K must divide N");
+  static_assert(K == 1 || K == 2, "one or two lanes per channel");
+  static_assert(HALF * NOUT <= THREADS, "one reduction output per thread");
+  static_assert(CK * N <= THREADS, "one B/C piece per thread");
+  static_assert(CK % HALF == 0, "whole reduction rounds");
+
+  __shared__ float2 s_dd[CK][CPB];                 // (Delta, Delta x) per token and channel
+  __shared__ float s_bc[CK][2 * N];                // B_n, C_n of the chunk's tokens
+  __shared__ float2 s_pp[CK][G][CPB];              // per-wave partial sums (readout; dDelta, sum lam B)
+  __shared__ float s_dr[CK][CPB];                  // dr per token and channel
+  __shared__ float s_red[HALF * SG * 2 * PLANE];   // pair sums: [token][group][dB | dC][pair][component]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int c = lane / K;
+  const int hk = lane % K;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int sg = w * K + hk;
+
+  const int64_t nwg = dm.cblocks * dm.batch;
+  const int64_t lb = bwd_logical_block(blockIdx.x, nwg);
+  const int64_t cb = lb % dm.cblocks;
+  const int64_t b = lb / dm.cblocks;
+  const int64_t d = cb * CPB + c;
+  const bool act = d < dm.dim;
+  const int64_t dc = act ? d : dm.dim - 1;   // inactive lanes run a valid row with zero gradients
+  const int64_t L = dm.seqlen;
+  const int64_t ch = b * dm.dim + dc;
+  const int64_t row = ch * L;
+  const bool vec = dm.vec != 0;
+  const bool has_z = p.z != nullptr;
+  const int64_t nck = (L + CK - 1) / CK;
+
+  const T* __restrict__ x = static_cast<const T*>(p.x);
+  const T* __restrict__ dt = static_cast<const T*>(p.dt);
+  const T* __restrict__ z = static_cast<const T*>(p.z);
+  const T* __restrict__ dy = static_cast<const T*>(p.dy);
+
+  float A2[NS], An[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    An[s] = p.A[dc * N + sg * NS + s];
+    A2[s] = An[s] * kLog2e;
+  }
+  const float bias2 = p.dt_bias ? p.dt_bias[dc] * kLog2e : 0.0f;
+  const float skip = p.Dskip ? p.Dskip[dc] : 0.0f;
+  const float* __restrict__ bc_row = p.bc + b * L * (2 * N);
+  float* __restrict__ ck_row = p.ckpt + ch * nck * N + sg * NS;
+
+  const int j_own = sg * kSpan;   // first token of a chunk this lane owns
+  auto own_valid = [&](int64_t first, int64_t t1) {
+    const int64_t v = t1 - first;
+    return (int)(v < 0 ? 0 : (v < kSpan ? v : kSpan));
+  };
+  // Delta and Delta x of the owned tokens into LDS (zero Delta for padding
+  // tokens), and the chunk's B and C
+  auto stage = [&](int64_t t0, int64_t t1, const uint32_t (&cx)[SW], const uint32_t (&cdt)[SW], int valid,
+                   float (&xv)[kSpan], float (&dl)[kSpan], float (&v2)[kSpan]) {
+#pragma unroll
+    for (int i = 0; i < kSpan; ++i) {
+      xv[i] = span_elem<IO>(cx, i);
+      v2[i] = fmaf(span_elem<IO>(cdt, i), kLog2e, bias2);
+      dl[i] = (i < valid) ? softplus_dt(span_elem<IO>(cdt, i), bias2) : 0.0f;
+      s_dd[j_own + i][c] = make_float2(dl[i], dl[i] * xv[i]);
+    }
+    if (tid < CK * N) {
+      float2 v = make_float2(0.0f, 0.0f);
+      if (t0 + tid / N < t1) v = reinterpret_cast<const float2*>(bc_row + t0 * (2 * N))[tid];
+      reinterpret_cast<float2*>(&s_bc[0][0])[tid] = v;
+    }
+  };
+
+  // ---- 1. forward sweep: the state at every chunk start ----
+  {
+    float h[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) h[s] = p.h0 ? p.h0[ch * N + sg * NS + s] : 0.0f;
+    for (int64_t k = 0; k < nck; ++k) {
+      const int64_t t0 = k * CK;
+      const int64_t t1 = (t0 + CK < L) ? t0 + CK : L;
+      if (act) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) ck_row[k * N + s] = h[s];
+      }
+      uint32_t cx[SW], cdt[SW];
+      const int valid = own_valid(t0 + j_own, t1);
+      load_span<IO, kSpan>(x, row + t0 + j_own, valid, vec, cx);
+      load_span<IO, kSpan>(dt, row + t0 + j_own, valid, vec, cdt);
+      float xv[kSpan], dl[kSpan], v2[kSpan];
+      stage(t0, t1, cx, cdt, valid, xv, dl, v2);
+      __syncthreads();
+      const int nj = (int)(t1 - t0);
+#pragma unroll
+      for (int j = 0; j < CK; ++j) {
+        if (j < nj) {
+          const float2 o = s_dd[j][c];
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            const float E = __builtin_amdgcn_exp2f(o.x * A2[s]);
+            h[s] = fmaf(E, h[s], o.y * s_bc[j][2 * (sg * NS + s)]);
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- 2. chunks last to first ----
+  float lam[NS], dAacc[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    lam[s] = (act && p.dh_final) ? p.dh_final[ch * N + sg * NS + s] : 0.0f;
+    dAacc[s] = 0.0f;
+  }
+  float dD_acc = 0.0f, dbias_acc = 0.0f;
+  float* __restrict__ part_row = p.part + (b * dm.cblocks + cb) * L * NOUT;
+
+  for (int64_t k = nck - 1; k >= 0; --k) {
+    const int64_t t0 = k * CK;
+    const int64_t t1 = (t0 + CK < L) ? t0 + CK : L;
+    const int nj = (int)(t1 - t0);
+    const int64_t tf = t0 + j_own;
+    const int valid = own_valid(tf, t1);
+    uint32_t cx[SW], cdt[SW], cz[SW] = {}, cdy[SW];
+    load_span<IO, kSpan>(x, row + tf, valid, vec, cx);
+    load_span<IO, kSpan>(dt, row + tf, valid, vec, cdt);
+    if (has_z) load_span<IO, kSpan>(z, row + tf, valid, vec, cz);
+    load_span<IO, kSpan>(dy, row + tf, valid, vec, cdy);
+    float xv[kSpan], dl[kSpan], v2[kSpan];
+    stage(t0, t1, cx, cdt, valid, xv, dl, v2);
+    __syncthreads();
+
+    // recompute the chunk's states; hs[j] = the state before chunk token j
+    float hs[CK + 1][NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) hs[0][s] = act ? ck_row[k * N + s] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < CK; ++j) {
+      if (j < nj) {
+        const float2 o = s_dd[j][c];
+        float acc = 0.0f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const float E = __builtin_amdgcn_exp2f(o.x * A2[s]);
+          hs[j + 1][s] = fmaf(E, hs[j][s], o.y * s_bc[j][2 * (sg * NS + s)]);
+          acc = fmaf(s_bc[j][2 * (sg * NS + s) + 1], hs[j + 1][s], acc);
+        }
+        if constexpr (K == 2) acc += __builtin_amdgcn_update_dpp(0.0f, acc, 0xB1, 0xf, 0xf, false);
+        if (hk == 0) s_pp[j][w][c] = make_float2(acc, 0.0f);
+      }
+    }
+    __syncthreads();
+
+    // owners: r, dr = dy silu(z), dz = dy r silu'(z)
+    float drv[kSpan];
+    {
+      float dzv[kSpan];
+#pragma unroll
+      for (int i = 0; i < kSpan; ++i) {
+        const int j = j_own + i;
+        float r = 0.0f;
+        if (i < valid) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) r += s_pp[j][g][c].x;
+        }
+        r = fmaf(skip, xv[i], r);
+        const float dyv = act ? span_elem<IO>(cdy, i) : 0.0f;   // padding tokens load as zero
+        float gate = 1.0f;
+        dzv[i] = 0.0f;
+        if (has_z) {
+          const float zz = span_elem<IO>(cz, i);
+          const float sz = sigmoid2(zz * kLog2e);
+          gate = zz * sz;
+          dzv[i] = dyv * r * (sz * fmaf(zz, 1.0f - sz, 1.0f));
+        }
+        drv[i] = dyv * gate;
+        dD_acc = fmaf(drv[i], xv[i], dD_acc);
+        s_dr[j][c] = drv[i];
+      }
+      if (has_z && act && valid > 0) store_span<IO, kSpan>(static_cast<T*>(p.dz), row + tf, valid, vec, dzv);
+    }
+    __syncthreads();
+
+    // the adjoint state back through one token
+    auto back = [&](int j) {
+      const float dr = s_dr[j][c];
+      const float2 o = s_dd[j][c];
+      float ddp = 0.0f, sB = 0.0f;
+      float dBv[NS], dCv[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const float Bv = s_bc[j][2 * (sg * NS + s)];
+        const float Cv = s_bc[j][2 * (sg * NS + s) + 1];
+        lam[s] = fmaf(dr, Cv, lam[s]);
+        dCv[s] = dr * hs[j + 1][s];
+        const float E = __builtin_amdgcn_exp2f(o.x * A2[s]);
+        const float ga = lam[s] * hs[j][s] * E;
+        ddp = fmaf(ga, An[s], ddp);
+        dAacc[s] = fmaf(ga, o.x, dAacc[s]);
+        sB = fmaf(lam[s], Bv, sB);
+        dBv[s] = lam[s] * o.y;
+        lam[s] *= E;
+      }
+      if constexpr (K == 2) {
+        ddp += __builtin_amdgcn_update_dpp(0.0f, ddp, 0xB1, 0xf, 0xf, false);
+        sB += __builtin_amdgcn_update_dpp(0.0f, sB, 0xB1, 0xf, 0xf, false);
+      }
+      if (hk == 0) s_pp[j][w][c] = make_float2(ddp, sB);
+      // channel pair (c, c ^ 1), same hk: lanes 2 apart for K == 2, 1 apart for K == 1
+      const int odd = c & 1;
+      float* dst = s_red + ((j % HALF) * SG * 2 + sg * 2 + odd) * PLANE + (c >> 1) * NS;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const float give = odd ? dBv[s] : dCv[s];
+        const float keep = odd ? dCv[s] : dBv[s];
+        float got;
+        if constexpr (K == 2) got = __builtin_amdgcn_update_dpp(0.0f, give, 0x4E, 0xf, 0xf, false);   // [2,3,0,1]
+        else got = __builtin_amdgcn_update_dpp(0.0f, give, 0xB1, 0xf, 0xf, false);                  // [1,0,3,2]
+        dst[s] = keep + got;   // even channel: dB of the pair, odd channel: dC of the pair
+      }
+    };
+    // the channel sums of HALF tokens starting at chunk token j0, one per thread
+    auto reduce = [&](int j0) {
+      if (tid < HALF * NOUT) {
+        const int jj = tid / NOUT;
+        const int o = tid % NOUT;   // o < N: dB_n, else dC_n
+        const int which = o / N, n = o % N;
+        const float* src = s_red + (jj * SG * 2 + (n / NS) * 2 + which) * PLANE + (n % NS);
+        float acc = 0.0f;
+#pragma unroll 4
+        for (int q = 0; q < PAIRS; ++q) acc += src[q * NS];
+        const int64_t t = t0 + j0 + jj;
+        if (t < t1) part_row[t * NOUT + o] = acc;
+      }
+    };
+#pragma unroll
+    for (int r = CK / HALF - 1; r >= 0; --r) {
+#pragma unroll
+      for (int jj = HALF - 1; jj >= 0; --jj) {
+        const int j = r * HALF + jj;
+        if (j < nj) back(j);
+      }
+      __syncthreads();
+      reduce(r * HALF);
+      __syncthreads();
+    }
+
+    // owners: dx = Delta sum lam B + dr Dskip, ddt = (dDelta) sigmoid(v)
+    {
+      float dxv[kSpan], ddtv[kSpan];
+#pragma unroll
+      for (int i = 0; i < kSpan; ++i) {
+        const int j = j_own + i;
+        float ddp = 0.0f, sB = 0.0f;
+        if (i < valid) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const float2 v = s_pp[j][g][c];
+            ddp += v.x;
+            sB += v.y;
+          }
+        }
+        dxv[i] = fmaf(sB, dl[i], drv[i] * skip);
+        const float dv = fmaf(sB, xv[i], ddp) * sigmoid2(v2[i]);
+        ddtv[i] = dv;
+        if (i < valid) dbias_acc += dv;
+      }
+      if (act && valid > 0) {
+        store_span<IO, kSpan>(static_cast<T*>(p.dx), row + tf, valid, vec, dxv);
+        store_span<IO, kSpan>(static_cast<T*>(p.ddt), row + tf, valid, vec, ddtv);
+      }
+    }
+    __syncthreads();
+  }
+
+  // dh0 = Abar_0 lam_0 (lam already carries the factor); per-(row, channel) sums
+  if (act) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (p.dh0) p.dh0[ch * N + sg * NS + s] = lam[s];
+      p.dA_p[ch * N + sg * NS + s] = dAacc[s];
+    }
+  }
+  s_pp[sg][0][c] = make_float2(dD_acc, dbias_acc);   // CK >= SG rows
+  __syncthreads();
+  if (sg == 0 && act) {
+    float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+    for (int g = 0; g < SG; ++g) {
+      const float2 v = s_pp[g][0][c];
+      a0 += v.x;
+      a1 += v.y;
+    }
+    p.dD_p[ch] = a0;
+    p.dbias_p[ch] = a1;
+  }
+}
+
+// dB[b, n, t] and dC[b, n, t]: the channel blocks' partials, in block order.
+template <typename IO>
+__global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restrict__ part, int64_t batch,
+                                                            int64_t cblocks, int64_t L, int N,
+                                                            typename IO::T* __restrict__ dB,
+                                                            typename IO::T* __restrict__ dC) {
+  const int64_t nout = 2 * (int64_t)N;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= batch * L * nout) return;
+  const int64_t o = i % nout;
+  const int64_t t = (i / nout) % L;
+  const int64_t b = i / (nout * L);
+  const float* src = part + (b * cblocks * L + t) * nout + o;
+  float acc = 0.0f;
+  for (int64_t q = 0; q < cblocks; ++q) acc += src[q * L * nout];
+  const int64_t n = o % N;
+  store_one<IO>(o < N ? dB : dC, (b * N + n) * L + t, acc);
+}
+
+// dA, dDskip and dt_bias's gradient: sums over batch rows, in row order.
+__global__ __launch_bounds__(256) void bwd_reduce_param_kernel(const float* __restrict__ dA_p,
+                                                               const float* __restrict__ dD_p,
+                                                               const float* __restrict__ dbias_p, int64_t batch,
+                                                               int64_t dim, int N, float* __restrict__ dA,
+                                                               float* __restrict__ dD, float* __restrict__ dbias) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t na = dim * N;
+  if (i < na) {
+    if (dA) {
+      float acc = 0.0f;
+      for (int64_t b = 0; b < batch; ++b) acc += dA_p[b * na + i];
+      dA[i] = acc;
+    }
+  } else if (i < na + dim) {
+    const int64_t dd = i - na;
+    float a0 = 0.0f, a1 = 0.0f;
+    for (int64_t b = 0; b < batch; ++b) {
+      a0 += dD_p[b * dim + dd];
+      a1 += dbias_p[b * dim + dd];
+    }
+    if (dD) dD[dd] = a0;
+    if (dbias) dbias[dd] = a1;
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.0f;
+}
+
+template <int N, int G, int K, typename IO>
+hipError_t launch_bwd_t(const BwdDims& dm, const BwdPtrs& p, hipStream_t s) {
+  const int64_t nwg = dm.cblocks * dm.batch;
+  hipLaunchKernelGGL((scan_bwd_kernel<N, G, K, IO>), dim3((unsigned)nwg), dim3(64 * G), 0, s, dm, p);
+  return hipGetLastError();
+}
+
+template <typename IO>
+hipError_t launch_bwd_n(const BwdDims& dm, const BwdPtrs& p, hipStream_t s) {
+  switch (dm.dstate) {
+    case 1: return launch_bwd_t<1, 1, 1, IO>(dm, p, s);
+    case 2: return launch_bwd_t<2, 2, 1, IO>(dm, p, s);
+    case 4: return launch_bwd_t<4, 4, 1, IO>(dm, p, s);
+    case 8: return launch_bwd_t<8, 4, 2, IO>(dm, p, s);
+    case 16: return launch_bwd_t<16, 4, 2, IO>(dm, p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+int bwd_lanes_per_channel(int dstate) { return dstate >= 8 ? 2 : 1; }
+int bwd_chunk_len(int dstate) {
+  const int groups = dstate >= 4 ? 4 : dstate;
+  return kSpan * groups * bwd_lanes_per_channel(dstate);
+}
+
+hipError_t launch_scan_bwd(const BwdDims& dm, const BwdPtrs& p, hipStream_t s) {
+  hipError_t e = (dm.io == kIoBf16) ? launch_bwd_n<BF16>(dm, p, s) : launch_bwd_n<F32>(dm, p, s);
+  if (e != hipSuccess) return e;
+  const int64_t nbc = dm.batch * dm.seqlen * 2 * dm.dstate;
+  if (nbc > 0) {
+    const unsigned blocks = (unsigned)((nbc + 255) / 256);
+    if (dm.io == kIoBf16)
+      hipLaunchKernelGGL((bwd_reduce_bc_kernel<BF16>), dim3(blocks), dim3(256), 0, s, p.part, dm.batch, dm.cblocks,
+                         dm.seqlen, dm.dstate, static_cast<uint16_t*>(p.dB), static_cast<uint16_t*>(p.dC));
+    else
+      hipLaunchKernelGGL((bwd_reduce_bc_kernel<F32>), dim3(blocks), dim3(256), 0, s, p.part, dm.batch, dm.cblocks,
+                         dm.seqlen, dm.dstate, static_cast<float*>(p.dB), static_cast<float*>(p.dC));
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t npar = dm.dim * dm.dstate + dm.dim;
+  hipLaunchKernelGGL(bwd_reduce_param_kernel, dim3((unsigned)((npar + 255) / 256)), dim3(256), 0, s, p.dA_p, p.dD_p,
+                     p.dbias_p, dm.batch, dm.dim, dm.dstate, p.dA, p.dDskip, p.ddt_bias);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(float* dst, int64_t n, hipStream_t s) {
+  if (n <= 0 || !dst) return hipSuccess;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dst, n);
+  return hipGetLastError();
+}
+
+}  // namespace ssscan

@@ -109,3 +109,50 @@ def state_update(state, x, dt, B, C, A, z=None, Dskip=None, dt_bias=None, *, y=N
     fn(batch, dim, N, _IO[x.dtype], _ptr(state), _ptr(x), _ptr(dt), _ptr(z), _ptr(B), _ptr(C),
                        _ptr(A), _ptr(Dskip), _ptr(dt_bias), _ptr(y), _stream(dev))
     return y
+
+
+def bwd_workspace_bytes(batch, dim, dstate, seqlen, dtype=torch.bfloat16) -> int:
+    return _b.ss_scan_bwd_workspace_bytes(batch, dim, dstate, seqlen, _IO[dtype])
+
+
+def scan_bwd(x, dt, B, C, A, dy, z=None, Dskip=None, dt_bias=None, h0=None, dh_final=None, *, workspace=None,
+             need_dA=True, need_dDskip=True, need_ddt_bias=True, need_dh0=True):
+    """Gradients of ``scan_fwd`` (first-order input term) for upstream gradients dy
+    (batch, D, L) and dh_final (batch, D, N) float32 (None = 0).
+
+    Returns a dict: dx, ddt, dz (None without z) in the I/O dtype, shaped like x;
+    dB, dC shaped like B; dA (D, N), dDskip (D,), ddt_bias (D,), dh0 (batch, D, N)
+    in float32 (None where not requested).
+    """
+    if x.dtype not in _IO:
+        raise TypeError("x must be float32 or bfloat16")
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU")
+    batch, dim, L = x.shape
+    N = A.shape[1]
+    io = _IO[x.dtype]
+    for t, name, shape in ((x, "x", (batch, dim, L)), (dt, "dt", (batch, dim, L)), (z, "z", (batch, dim, L)),
+                           (dy, "dy", (batch, dim, L)), (B, "B", (batch, N, L)), (C, "C", (batch, N, L))):
+        _need(t, name, x.dtype, shape, dev)
+    _need(A, "A", torch.float32, (dim, N), dev)
+    _need(Dskip, "Dskip", torch.float32, (dim,), dev)
+    _need(dt_bias, "dt_bias", torch.float32, (dim,), dev)
+    _need(h0, "h0", torch.float32, (batch, dim, N), dev)
+    _need(dh_final, "dh_final", torch.float32, (batch, dim, N), dev)
+    out = dict(dx=torch.empty_like(x), ddt=torch.empty_like(x), dz=torch.empty_like(x) if z is not None else None,
+               dB=torch.empty_like(B), dC=torch.empty_like(C),
+               dA=torch.empty((dim, N), dtype=torch.float32, device=dev) if need_dA else None,
+               dDskip=torch.empty(dim, dtype=torch.float32, device=dev) if need_dDskip else None,
+               ddt_bias=torch.empty(dim, dtype=torch.float32, device=dev) if need_ddt_bias else None,
+               dh0=torch.empty((batch, dim, N), dtype=torch.float32, device=dev) if need_dh0 else None)
+    nbytes = _b.ss_scan_bwd_workspace_bytes(batch, dim, N, L, io)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    if workspace.numel() < nbytes:
+        raise ValueError("workspace has %d bytes, %d needed" % (workspace.numel(), nbytes))
+    _b.ss_scan_bwd(batch, dim, N, L, io, _ptr(x), _ptr(dt), _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(Dskip),
+                   _ptr(dt_bias), _ptr(h0), _ptr(dy), _ptr(dh_final), _ptr(out["dx"]), _ptr(out["ddt"]),
+                   _ptr(out["dz"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dA"]), _ptr(out["dDskip"]),
+                   _ptr(out["ddt_bias"]), _ptr(out["dh0"]), _ptr(workspace), workspace.numel(), _stream(dev))
+    return out

@@ -150,6 +150,66 @@ def test_state_update_validation(case, status):
     assert st == status, (st, b.last_error())
 
 
+_BWD_NAMES = ("x", "dt", "z", "B", "C", "A", "Dskip", "dt_bias", "h0", "dy", "dh_final", "dx", "ddt", "dz", "dB",
+              "dC", "dA", "dDskip", "ddt_bias", "dh0")
+
+
+def _bwd_status(**kw):
+    batch, dim, N, L = kw.pop("shape", (2, 64, 16, 256))
+    io = kw.pop("io", b.SS_F32)
+    eb = 2 if io == b.SS_BF16 else 4
+    seq, bcs, st, par = batch * dim * L * eb, batch * N * L * eb, batch * dim * N * 4, dim * 4
+    sizes = dict(x=seq, dt=seq, z=seq, B=bcs, C=bcs, A=dim * N * 4, Dskip=par, dt_bias=par, h0=st, dy=seq,
+                 dh_final=st, dx=seq, ddt=seq, dz=seq, dB=bcs, dC=bcs, dA=dim * N * 4, dDskip=par, ddt_bias=par, dh0=st)
+    ptrs, base = {}, ALIGNED
+    for name in _BWD_NAMES:
+        ptrs[name] = base
+        base += ((sizes[name] + 4095) // 4096) * 4096 + 4096
+    ptrs["workspace"] = base
+    ptrs["workspace_bytes"] = b.ss_scan_bwd_workspace_bytes(batch, dim, N, L, io) if N in (1, 2, 4, 8, 16) else 0
+    ptrs.update(kw)
+    stt = b.lib.ss_scan_bwd(batch, dim, N, L, io, *[ptrs[n] for n in _BWD_NAMES], ptrs["workspace"],
+                            ptrs["workspace_bytes"], None)
+    return stt, b.last_error()
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(shape=(2, 64, 5, 256)), b.SS_ERR_UNSUPPORTED),
+    (dict(io=9), b.SS_ERR_UNSUPPORTED),
+    (dict(shape=(0, 64, 16, 256)), b.SS_ERR_INVALID_ARG),
+    (dict(x=None), b.SS_ERR_INVALID_ARG),
+    (dict(dy=None), b.SS_ERR_INVALID_ARG),
+    (dict(dx=None), b.SS_ERR_INVALID_ARG),
+    (dict(ddt=None), b.SS_ERR_INVALID_ARG),
+    (dict(dB=None), b.SS_ERR_INVALID_ARG),
+    (dict(dC=None), b.SS_ERR_INVALID_ARG),
+    (dict(A=None), b.SS_ERR_INVALID_ARG),
+    (dict(dz=None), b.SS_ERR_INVALID_ARG),                 # z given, dz missing
+    (dict(z=None), b.SS_ERR_INVALID_ARG),                  # dz given, z missing
+    (dict(dB=ALIGNED + (1 << 36) + 4), b.SS_ERR_INVALID_ARG),
+    (dict(dDskip=ALIGNED + (1 << 36) + 2), b.SS_ERR_INVALID_ARG),
+    (dict(dx=ALIGNED), b.SS_ERR_INVALID_ARG),              # dx overlaps x
+    (dict(dh0=ALIGNED + (1 << 37) + 256, workspace=ALIGNED + (1 << 37)), b.SS_ERR_INVALID_ARG),  # dh0 in the workspace
+    (dict(workspace=None), b.SS_ERR_WORKSPACE),
+    (dict(workspace_bytes=4096), b.SS_ERR_WORKSPACE),
+    (dict(workspace=ALIGNED + (1 << 37) + 64), b.SS_ERR_WORKSPACE),
+])
+def test_bwd_validation(case, status):
+    st, msg = _bwd_status(**case)
+    assert st == status, (st, msg)
+    assert msg
+
+
+def test_bwd_workspace_bytes():
+    # (batch, L, N, 2) B/C re-layout + (batch, D, L/16, N) checkpoints + (batch, D/32, L, 2N) dB/dC partials
+    # + (batch, D, N) + 2 (batch, D) per-row sums, each rounded to 256 bytes
+    n = b.ss_scan_bwd_workspace_bytes(8, 5120, 16, 2048, b.SS_BF16)
+    expect = 8 * 2048 * 32 * 4 + 8 * 5120 * 128 * 16 * 4 + 8 * 160 * 2048 * 32 * 4 + 8 * 5120 * 16 * 4 + 2 * 8 * 5120 * 4
+    assert n == expect
+    assert b.ss_scan_bwd_workspace_bytes(2, 64, 16, 0, b.SS_F32) == 0
+    assert b.ss_scan_bwd_workspace_bytes(2, 64, 3, 16, b.SS_F32) == 0
+
+
 def test_timing_record_empty():
     b.ss_timing_enable(False)
     b.ss_timing_reset()

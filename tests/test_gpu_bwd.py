@@ -1,0 +1,199 @@
+"""The backward pass (ss_scan_bwd) on the GPU against the oracle's gradients.
+
+Training differentiates the scan and recomputes the state in the backward pass
+(reader's notes, kurisu.si, "What they did", Selective SSM item).  The oracle's
+backward is pinned by finite differences of the pinned forward and by exact
+adjoint identities (tests/pins.py); here the GPU matches it element by element.
+
+Tolerances (rel-L2 over each whole gradient tensor):
+* fp32 I/O: 1e-5 for the per-element gradients (dx, ddt, dz, dh0), as for the
+  forward; 5e-5 for the gradients that are sums over many terms in fp32 (dA, dDskip
+  and dt_bias's gradient sum over batch rows and tokens, dB and dC over channels:
+  up to ~2^14 terms, whose rounding grows like sqrt(terms) x 6e-8 ~ 1e-5).
+* bf16 I/O: 2e-2, as for the forward (dx, ddt, dz, dB, dC are rounded to bf16;
+  the fp32 gradients only carry the fp32 sums' rounding).
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import log, random_problem, rel_l2, to_dev, to_f64
+from workloads import inputs
+
+pytestmark = pytest.mark.gpu
+
+ELEMENT = ("dx", "ddt", "dz", "dh0")
+SUMS = ("dA", "dDskip", "ddt_bias", "dB", "dC")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def ss():
+    import selective_state_space_62_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def o():
+    return oracle.default()
+
+
+def _tol(io, name):
+    if io == "bf16":
+        return 2e-2
+    return 1e-5 if name in ELEMENT else 5e-5
+
+
+def _problem(rng, batch, D, N, L, io, optional=True):
+    raw, par, f64 = random_problem(rng, batch, D, N, L, io, with_z=optional, with_skip=optional,
+                                   with_bias=optional, with_h0=optional)
+    dy = rng.standard_normal((batch, D, L)).astype(np.float32)
+    raw["dy"] = dy if io == "f32" else inputs.f32_to_bf16_bits(dy)
+    f64["dy"] = inputs.raw_to_f64(raw["dy"], io)
+    par["dh_final"] = rng.standard_normal((batch, D, N)).astype(np.float32) if optional else None
+    return raw, par, f64
+
+
+def _run_gpu(ss, raw, par, io, dev, **need):
+    import torch
+    t = {k: to_dev(v, io, dev) for k, v in raw.items()}
+    p = {k: (torch.from_numpy(v).to(dev) if v is not None else None) for k, v in par.items()}
+    g = ss.scan_bwd(t["x"], t["dt"], t["B"], t["C"], p["A"], t["dy"], z=t.get("z"), Dskip=p["Dskip"],
+                    dt_bias=p["dt_bias"], h0=p["h0"], dh_final=p["dh_final"], **need)
+    torch.cuda.synchronize()
+    return g
+
+
+def _run_oracle(o, f64, par):
+    return o.scan_bwd(f64["x"], f64["dt"], f64["B"], f64["C"], par["A"], f64["dy"], z=f64.get("z"),
+                      Dskip=par["Dskip"], dt_bias=par["dt_bias"], h0=par["h0"], dh_final=par["dh_final"])
+
+
+def _compare(g, r, io, what):
+    errs = {}
+    for k in ELEMENT + SUMS:
+        if g.get(k) is None or r.get(k) is None:
+            continue
+        errs[k] = rel_l2(to_f64(g[k]), r[k])
+    log("%s: %s" % (what, ", ".join("%s %.2e" % kv for kv in errs.items())))
+    for k, e in errs.items():
+        assert e <= _tol(io, k), (what, k, e, errs)
+    return errs
+
+
+CASES = [
+    # (batch, D, N, L): ragged sequences (not a multiple of the chunk), D not a multiple of the block
+    (2, 77, 16, 37),
+    (1, 64, 16, 64),
+    (2, 33, 16, 50),
+    (3, 33, 8, 50),
+    (2, 20, 4, 31),
+    (2, 70, 2, 9),
+    (1, 130, 1, 13),
+    (2, 40, 16, 1),
+    (1, 32, 16, 2),
+    (2, 64, 16, 17),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=["x".join(map(str, c)) for c in CASES])
+@pytest.mark.parametrize("optional", [True, False], ids=["all-inputs", "no-optional"])
+def test_bwd_f32_matches_oracle(ss, o, dev, case, optional):
+    batch, D, N, L = case
+    log("bwd f32 %s optional=%s" % (case, optional))
+    rng = np.random.default_rng(zlib.crc32(repr((case, optional)).encode()))
+    raw, par, f64 = _problem(rng, batch, D, N, L, "f32", optional)
+    g = _run_gpu(ss, raw, par, "f32", dev)
+    r = _run_oracle(o, f64, par)
+    _compare(g, r, "f32", "bwd %s" % (case,))
+
+
+@pytest.mark.parametrize("case", [(2, 77, 16, 37), (1, 96, 16, 130), (2, 40, 8, 33), (1, 50, 4, 21)],
+                         ids=lambda c: "x".join(map(str, c)))
+def test_bwd_bf16_matches_oracle(ss, o, dev, case):
+    batch, D, N, L = case
+    log("bwd bf16 %s" % (case,))
+    rng = np.random.default_rng(zlib.crc32(repr(("bf16", case)).encode()))
+    raw, par, f64 = _problem(rng, batch, D, N, L, "bf16", True)
+    g = _run_gpu(ss, raw, par, "bf16", dev)
+    r = _run_oracle(o, f64, par)
+    _compare(g, r, "bf16", "bwd bf16 %s" % (case,))
+
+
+def test_bwd_empty_sequence(ss, dev):
+    import torch
+    rng = np.random.default_rng(31)
+    batch, D, N = 2, 40, 16
+    x = torch.empty((batch, D, 0), dtype=torch.float32, device=dev)
+    B = torch.empty((batch, N, 0), dtype=torch.float32, device=dev)
+    A = -torch.ones((D, N), device=dev)
+    dhf = torch.from_numpy(rng.standard_normal((batch, D, N)).astype(np.float32)).to(dev)
+    g = ss.scan_bwd(x, x, B, B, A, x, Dskip=torch.ones(D, device=dev), dh_final=dhf)
+    torch.cuda.synchronize()
+    assert torch.equal(g["dh0"], dhf)
+    assert not g["dA"].any() and not g["dDskip"].any() and not g["ddt_bias"].any()
+
+
+def test_bwd_optional_outputs_and_determinism(ss, o, dev):
+    """Gradients not asked for are skipped without changing the others; two runs
+    give identical bits (every sum has a fixed order)."""
+    import torch
+    rng = np.random.default_rng(32)
+    raw, par, f64 = _problem(rng, 2, 96, 16, 45, "f32", True)
+    full = _run_gpu(ss, raw, par, "f32", dev)
+    again = _run_gpu(ss, raw, par, "f32", dev)
+    for k, v in full.items():
+        assert torch.equal(v, again[k]), k
+    part = _run_gpu(ss, raw, par, "f32", dev, need_dA=False, need_dDskip=False, need_ddt_bias=False, need_dh0=False)
+    for k in ("dx", "ddt", "dz", "dB", "dC"):
+        assert torch.equal(part[k], full[k]), k
+    assert part["dA"] is None and part["dh0"] is None
+
+
+def test_bwd_130m_layer_full(ss, o, dev):
+    """The 130M-shaped layer (batch 8, D 1536, N 16, L 2048, fp32) in full."""
+    import torch
+    from workloads import M130
+    from workloads import device as wdev
+    cfg = M130
+    log("bwd %s" % cfg.name)
+    t = wdev.scan_inputs(cfg, dev)
+    A, dskip, bias = wdev.params(cfg, dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(62102)
+    dy = torch.randn(t["x"].shape, generator=gen, device=dev, dtype=torch.float32)
+    dhf = torch.randn((cfg.batch, cfg.dim, cfg.dstate), generator=gen, device=dev, dtype=torch.float32)
+    g = ss.scan_bwd(t["x"], t["dt"], t["B"], t["C"], A, dy, z=t["z"], Dskip=dskip, dt_bias=bias, dh_final=dhf)
+    torch.cuda.synchronize()
+    f = {k: to_f64(v) for k, v in t.items()}
+    r = o.scan_bwd(f["x"], f["dt"], f["B"], f["C"], to_f64(A), to_f64(dy), z=f["z"], Dskip=to_f64(dskip),
+                   dt_bias=to_f64(bias), dh_final=to_f64(dhf))
+    _compare(g, r, "f32", "bwd %s" % cfg.name)
+
+
+def test_bwd_2p8b_layer_full(ss, o, dev):
+    """The 2.8B-shaped layer (batch 8, D 5120, N 16, L 2048, bf16 I/O) in full."""
+    import torch
+    from workloads import B28
+    from workloads import device as wdev
+    cfg = B28
+    log("bwd %s" % cfg.name)
+    t = wdev.scan_inputs(cfg, dev)
+    A, dskip, bias = wdev.params(cfg, dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(62103)
+    dy = torch.randn(t["x"].shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    g = ss.scan_bwd(t["x"], t["dt"], t["B"], t["C"], A, dy, z=t["z"], Dskip=dskip, dt_bias=bias)
+    torch.cuda.synchronize()
+    f = {k: to_f64(v) for k, v in t.items()}
+    r = o.scan_bwd(f["x"], f["dt"], f["B"], f["C"], to_f64(A), to_f64(dy), z=f["z"], Dskip=to_f64(dskip),
+                   dt_bias=to_f64(bias))
+    _compare(g, r, "bf16", "bwd %s" % cfg.name)
