@@ -154,6 +154,36 @@ def run_decode(ss, torch, dev, steps, warmup):
             "cold_method": "back-to-back steps rotating over 6 states (503 MB > 256 MB MALL)"}
 
 
+def run_bwd(ss, torch, dev, cfg, t, A, dskip, bias, fwd_kernel_ms, calls=20):
+    """Backward pass of the same workload (secondary): ss_scan_bwd with a seeded
+    random dy, all gradients requested; kernels timed by the library's events."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(62200)
+    dy = torch.randn(t["x"].shape, generator=gen, device=dev, dtype=torch.float32).to(t["x"].dtype)
+    ws = torch.empty(max(ss.bwd_workspace_bytes(cfg.batch, cfg.dim, cfg.dstate, cfg.seqlen, t["x"].dtype), 256),
+                     dtype=torch.uint8, device=dev)
+
+    def call():
+        return ss.scan_bwd(t["x"], t["dt"], t["B"], t["C"], A, dy, z=t["z"], Dskip=dskip, dt_bias=bias, workspace=ws)
+
+    for _ in range(calls):
+        call()
+    torch.cuda.synchronize()
+    ss.ss_timing_reset()
+    ss.ss_timing_enable(True)
+    for _ in range(calls):
+        call()
+    torch.cuda.synchronize()
+    ss.ss_timing_enable(False)
+    ms, n = ss.ss_timing_read()
+    ss.ss_timing_reset()
+    kms = ms / n
+    return {"entry_point": "ss_scan_bwd", "kernel_ms": round(kms, 5),
+            "value": round(cfg.tokch / (kms * 1e-3) / 1e9, 3), "unit": "Gtok·ch/s",
+            "ratio_to_forward": round(kms / fwd_kernel_ms, 3),
+            "workspace_bytes": ws.numel()}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -164,6 +194,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step timing")
     ap.add_argument("--no-zoh", action="store_true", help="skip the zero-order-hold scan timing")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward-pass timing")
     ap.add_argument("--copy-calib", type=int, default=0, help="only run a plain copy of this many bytes")
     args = ap.parse_args()
 
@@ -268,6 +299,8 @@ def main():
         ss.ss_timing_reset()
         out["zoh"] = {"entry_point": "ss_scan_fwd_zoh", "kernel_ms": round(zms / zn, 5),
                       "value": round(tokch / (zms / zn * 1e-3) / 1e9, 3), "unit": "Gtok·ch/s"}
+    if not args.no_bwd:
+        out["bwd"] = run_bwd(ss, torch, dev, cfg, t, A, dskip, bias, kern_ms)
     if not args.no_decode:
         out["decode"] = run_decode(ss, torch, dev, 60, 60)
     if not args.no_cpu_baseline:

@@ -26,13 +26,17 @@
 //     owner of each token forms dr and dz; then every lane runs the adjoint state
 //     back through the chunk.  The sums over state components (for dx and
 //     dDelta) reach the token's owner through LDS, as the forward's readout does.
-// dB and dC are sums over channels.  In a workgroup the two channels of a lane
-// pair are added with one DPP move (the even channel keeps dB, the odd one dC),
-// the pair sums are added in LDS in a fixed order, and one partial per
-// (workgroup, token) goes to the workspace; bwd_reduce_bc_kernel adds a batch
-// row's partials in a fixed order.  dA, dDskip and dt_bias's gradient are summed
-// per (row, channel) in registers and over rows by bwd_reduce_param_kernel.  All
-// sums have a fixed order: results are deterministic.
+// dB and dC are sums over channels.  In a workgroup the channels of each
+// 16-lane row are summed with DPP (a channel pair first, the even channel keeping
+// dB and the odd one dC, then rotations within the row), the rows' sums are added
+// in LDS in a fixed order, and one partial per (workgroup, token) goes to the
+// workspace; bwd_reduce_bc_kernel adds a batch row's partials in a fixed order.
+// dA, dDskip and dt_bias's gradient are summed per (row, channel) in registers
+// and over rows by bwd_reduce_param_kernel.  All sums have a fixed order:
+// results are deterministic.  The next chunk's global operands are fetched while
+// the current one computes, and whole chunks run without per-token guards.
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -55,31 +59,30 @@ __device__ __forceinline__ float sigmoid2(float v2) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-v2));
 }
 
+// At most 96 VGPRs and 32 KB of LDS: five workgroups (one wave per SIMD each)
+// fit on a CU, so the 2.8B-shaped layer's 1280 workgroups are all resident at
+// once on 256 CUs.
 template <int N, int G, int K, typename IO>
-__global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10))) void scan_bwd_kernel(
+__global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(5, 10))) void scan_bwd_kernel(
     const BwdDims dm, const BwdPtrs p) {
   using T = typename IO::T;
-  constexpr int CPB = 64 / K;                    // channels per workgroup
-  constexpr int SG = G * K;                      // state groups
-  constexpr int NS = N / SG;                     // state components per lane
-  constexpr int CK = kSpan * SG;                 // chunk length (tokens)
-  constexpr int HALF = CK >= 16 ? CK / 2 : CK;   // tokens per dB/dC reduction round
-  constexpr int NOUT = 2 * N;                    // dB and dC values per token
+  constexpr int CPB = 64 / K;          // channels per workgroup
+  constexpr int SG = G * K;            // state groups
+  constexpr int NS = N / SG;           // state components per lane
+  constexpr int CK = kSpan * SG;       // chunk length (tokens)
+  constexpr int NOUT = 2 * N;          // dB and dC values per token
   constexpr int THREADS = 64 * G;
-  constexpr int PAIRS = CPB / 2;                 // channel pairs per workgroup
-  constexpr int PLANE = PAIRS * NS + 1;          // floats per (token, group, dB|dC) plane, padded
+  constexpr int RED = 4 * 2 * K * NS;  // floats per (token, wave) of 8- or 16-channel sums
   constexpr int SW = SpanT<IO, kSpan>::kWords;
   static_assert(NS >= 1 && N % SG == 0, "G * K must divide N");
   static_assert(K == 1 || K == 2, "one or two lanes per channel");
-  static_assert(HALF * NOUT <= THREADS, "one reduction output per thread");
   static_assert(CK * N <= THREADS, "one B/C piece per thread");
-  static_assert(CK % HALF == 0, "whole reduction rounds");
 
-  __shared__ float2 s_dd[CK][CPB];                 // (Delta, Delta x) per token and channel
-  __shared__ float s_bc[CK][2 * N];                // B_n, C_n of the chunk's tokens
-  __shared__ float2 s_pp[CK][G][CPB];              // per-wave partial sums (readout; dDelta, sum lam B)
-  __shared__ float s_dr[CK][CPB];                  // dr per token and channel
-  __shared__ float s_red[HALF * SG * 2 * PLANE];   // pair sums: [token][group][dB | dC][pair][component]
+  __shared__ float2 s_dd[CK][CPB];     // (Delta, Delta x) per token and channel
+  __shared__ float s_bc[CK][2 * N];    // B_n, C_n of the chunk's tokens
+  __shared__ float2 s_pp[CK][G][CPB];  // per-wave partial sums (readout; dDelta and sum lam B)
+  __shared__ float s_dr[CK][CPB];      // dr per token and channel
+  __shared__ float s_red[CK][G][RED];  // per-row channel sums of dB (even) and dC (odd)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -107,38 +110,50 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10)))
   const T* __restrict__ z = static_cast<const T*>(p.z);
   const T* __restrict__ dy = static_cast<const T*>(p.dy);
 
-  float A2[NS], An[NS];
+  float A2[NS];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    An[s] = p.A[dc * N + sg * NS + s];
-    A2[s] = An[s] * kLog2e;
-  }
+  for (int s = 0; s < NS; ++s) A2[s] = p.A[dc * N + sg * NS + s] * kLog2e;
   const float bias2 = p.dt_bias ? p.dt_bias[dc] * kLog2e : 0.0f;
   const float skip = p.Dskip ? p.Dskip[dc] : 0.0f;
   const float* __restrict__ bc_row = p.bc + b * L * (2 * N);
   float* __restrict__ ck_row = p.ckpt + ch * nck * N + sg * NS;
 
   const int j_own = sg * kSpan;   // first token of a chunk this lane owns
-  auto own_valid = [&](int64_t first, int64_t t1) {
-    const int64_t v = t1 - first;
+  auto chunk_end = [&](int64_t k) { return (k * CK + CK < L) ? k * CK + CK : L; };
+  auto own_valid = [&](int64_t k) {
+    const int64_t v = chunk_end(k) - (k * CK + j_own);
     return (int)(v < 0 ? 0 : (v < kSpan ? v : kSpan));
+  };
+
+  // A chunk's global operands, fetched one chunk ahead of their use.
+  struct Fetch {
+    uint32_t x[SW], dt[SW], z[SW], dy[SW];
+    float2 bc;
+  };
+  auto fetch = [&](int64_t k, bool grads, Fetch& f) {
+    const int64_t t0 = k * CK;
+    const int valid = own_valid(k);
+    load_span<IO, kSpan>(x, row + t0 + j_own, valid, vec, f.x);
+    load_span<IO, kSpan>(dt, row + t0 + j_own, valid, vec, f.dt);
+    if (grads) {
+      if (has_z) load_span<IO, kSpan>(z, row + t0 + j_own, valid, vec, f.z);
+      load_span<IO, kSpan>(dy, row + t0 + j_own, valid, vec, f.dy);
+    }
+    f.bc = make_float2(0.0f, 0.0f);
+    if (tid < CK * N && t0 + tid / N < chunk_end(k))
+      f.bc = reinterpret_cast<const float2*>(bc_row + t0 * (2 * N))[tid];
   };
   // Delta and Delta x of the owned tokens into LDS (zero Delta for padding
   // tokens), and the chunk's B and C
-  auto stage = [&](int64_t t0, int64_t t1, const uint32_t (&cx)[SW], const uint32_t (&cdt)[SW], int valid,
-                   float (&xv)[kSpan], float (&dl)[kSpan], float (&v2)[kSpan]) {
+  auto stage = [&](int valid, const Fetch& f, float (&xv)[kSpan], float (&dl)[kSpan], float (&v2)[kSpan]) {
 #pragma unroll
     for (int i = 0; i < kSpan; ++i) {
-      xv[i] = span_elem<IO>(cx, i);
-      v2[i] = fmaf(span_elem<IO>(cdt, i), kLog2e, bias2);
-      dl[i] = (i < valid) ? softplus_dt(span_elem<IO>(cdt, i), bias2) : 0.0f;
+      xv[i] = span_elem<IO>(f.x, i);
+      v2[i] = fmaf(span_elem<IO>(f.dt, i), kLog2e, bias2);
+      dl[i] = (i < valid) ? softplus_dt(span_elem<IO>(f.dt, i), bias2) : 0.0f;
       s_dd[j_own + i][c] = make_float2(dl[i], dl[i] * xv[i]);
     }
-    if (tid < CK * N) {
-      float2 v = make_float2(0.0f, 0.0f);
-      if (t0 + tid / N < t1) v = reinterpret_cast<const float2*>(bc_row + t0 * (2 * N))[tid];
-      reinterpret_cast<float2*>(&s_bc[0][0])[tid] = v;
-    }
+    if (tid < CK * N) reinterpret_cast<float2*>(&s_bc[0][0])[tid] = f.bc;
   };
 
   // ---- 1. forward sweep: the state at every chunk start ----
@@ -146,24 +161,23 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10)))
     float h[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) h[s] = p.h0 ? p.h0[ch * N + sg * NS + s] : 0.0f;
-    for (int64_t k = 0; k < nck; ++k) {
-      const int64_t t0 = k * CK;
-      const int64_t t1 = (t0 + CK < L) ? t0 + CK : L;
+    Fetch f;
+    fetch(0, false, f);
+    // FULL (a compile-time tag): all CK tokens of the chunk lie inside the sequence
+    auto sweep = [&](auto full_tag, int64_t k) {
+      constexpr bool FULL = decltype(full_tag)::value;
       if (act) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) ck_row[k * N + s] = h[s];
       }
-      uint32_t cx[SW], cdt[SW];
-      const int valid = own_valid(t0 + j_own, t1);
-      load_span<IO, kSpan>(x, row + t0 + j_own, valid, vec, cx);
-      load_span<IO, kSpan>(dt, row + t0 + j_own, valid, vec, cdt);
       float xv[kSpan], dl[kSpan], v2[kSpan];
-      stage(t0, t1, cx, cdt, valid, xv, dl, v2);
+      stage(FULL ? kSpan : own_valid(k), f, xv, dl, v2);
+      if (k + 1 < nck) fetch(k + 1, false, f);
       __syncthreads();
-      const int nj = (int)(t1 - t0);
+      const int nj = FULL ? CK : (int)(chunk_end(k) - k * CK);
 #pragma unroll
       for (int j = 0; j < CK; ++j) {
-        if (j < nj) {
+        if (FULL || j < nj) {
           const float2 o = s_dd[j][c];
 #pragma unroll
           for (int s = 0; s < NS; ++s) {
@@ -173,7 +187,10 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10)))
         }
       }
       __syncthreads();
-    }
+    };
+    const int64_t nfull = L / CK;
+    for (int64_t k = 0; k < nfull; ++k) sweep(std::true_type{}, k);
+    if (nfull < nck) sweep(std::false_type{}, nfull);
   }
 
   // ---- 2. chunks last to first ----
@@ -186,28 +203,40 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10)))
   float dD_acc = 0.0f, dbias_acc = 0.0f;
   float* __restrict__ part_row = p.part + (b * dm.cblocks + cb) * L * NOUT;
 
-  for (int64_t k = nck - 1; k >= 0; --k) {
+  Fetch f;
+  fetch(nck - 1, true, f);
+  float ckn[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) ckn[s] = act ? ck_row[(nck - 1) * N + s] : 0.0f;
+
+  auto chunk = [&](auto full_tag, int64_t k) {
+    constexpr bool FULL = decltype(full_tag)::value;
     const int64_t t0 = k * CK;
-    const int64_t t1 = (t0 + CK < L) ? t0 + CK : L;
-    const int nj = (int)(t1 - t0);
+    const int64_t t1 = chunk_end(k);
+    const int nj = FULL ? CK : (int)(t1 - t0);
     const int64_t tf = t0 + j_own;
-    const int valid = own_valid(tf, t1);
-    uint32_t cx[SW], cdt[SW], cz[SW] = {}, cdy[SW];
-    load_span<IO, kSpan>(x, row + tf, valid, vec, cx);
-    load_span<IO, kSpan>(dt, row + tf, valid, vec, cdt);
-    if (has_z) load_span<IO, kSpan>(z, row + tf, valid, vec, cz);
-    load_span<IO, kSpan>(dy, row + tf, valid, vec, cdy);
-    float xv[kSpan], dl[kSpan], v2[kSpan];
-    stage(t0, t1, cx, cdt, valid, xv, dl, v2);
+    const int valid = FULL ? kSpan : own_valid(k);
+    float xv[kSpan], dl[kSpan], v2[kSpan], zv[kSpan], dyv[kSpan];
+    stage(valid, f, xv, dl, v2);
+#pragma unroll
+    for (int i = 0; i < kSpan; ++i) {
+      zv[i] = span_elem<IO>(f.z, i);
+      dyv[i] = act ? span_elem<IO>(f.dy, i) : 0.0f;   // padding tokens load as zero
+    }
+    float hs[CK + 1][NS];   // hs[j] = the state before chunk token j
+#pragma unroll
+    for (int s = 0; s < NS; ++s) hs[0][s] = ckn[s];
+    if (k > 0) {
+      fetch(k - 1, true, f);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) ckn[s] = act ? ck_row[(k - 1) * N + s] : 0.0f;
+    }
     __syncthreads();
 
-    // recompute the chunk's states; hs[j] = the state before chunk token j
-    float hs[CK + 1][NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) hs[0][s] = act ? ck_row[k * N + s] : 0.0f;
+    // recompute the chunk's states, with the readout
 #pragma unroll
     for (int j = 0; j < CK; ++j) {
-      if (j < nj) {
+      if (FULL || j < nj) {
         const float2 o = s_dd[j][c];
         float acc = 0.0f;
 #pragma unroll
@@ -217,7 +246,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10)))
           acc = fmaf(s_bc[j][2 * (sg * NS + s) + 1], hs[j + 1][s], acc);
         }
         if constexpr (K == 2) acc += __builtin_amdgcn_update_dpp(0.0f, acc, 0xB1, 0xf, 0xf, false);
-        if (hk == 0) s_pp[j][w][c] = make_float2(acc, 0.0f);
+        s_pp[j][w][c].x = acc;   // both lanes of a channel hold the sum and store it
       }
     }
     __syncthreads();
@@ -230,92 +259,91 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10)))
       for (int i = 0; i < kSpan; ++i) {
         const int j = j_own + i;
         float r = 0.0f;
-        if (i < valid) {
+        if (FULL || i < valid) {
 #pragma unroll
           for (int g = 0; g < G; ++g) r += s_pp[j][g][c].x;
         }
         r = fmaf(skip, xv[i], r);
-        const float dyv = act ? span_elem<IO>(cdy, i) : 0.0f;   // padding tokens load as zero
         float gate = 1.0f;
         dzv[i] = 0.0f;
         if (has_z) {
-          const float zz = span_elem<IO>(cz, i);
-          const float sz = sigmoid2(zz * kLog2e);
-          gate = zz * sz;
-          dzv[i] = dyv * r * (sz * fmaf(zz, 1.0f - sz, 1.0f));
+          const float sz = sigmoid2(zv[i] * kLog2e);
+          gate = zv[i] * sz;
+          dzv[i] = dyv[i] * r * (sz * fmaf(zv[i], 1.0f - sz, 1.0f));
         }
-        drv[i] = dyv * gate;
+        drv[i] = dyv[i] * gate;
         dD_acc = fmaf(drv[i], xv[i], dD_acc);
         s_dr[j][c] = drv[i];
       }
-      if (has_z && act && valid > 0) store_span<IO, kSpan>(static_cast<T*>(p.dz), row + tf, valid, vec, dzv);
+      if (has_z && act && (FULL || valid > 0)) store_span<IO, kSpan>(static_cast<T*>(p.dz), row + tf, valid, vec, dzv);
     }
     __syncthreads();
 
-    // the adjoint state back through one token
-    auto back = [&](int j) {
-      const float dr = s_dr[j][c];
-      const float2 o = s_dd[j][c];
-      float ddp = 0.0f, sB = 0.0f;
-      float dBv[NS], dCv[NS];
+    // the adjoint state back through the chunk
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const float Bv = s_bc[j][2 * (sg * NS + s)];
-        const float Cv = s_bc[j][2 * (sg * NS + s) + 1];
-        lam[s] = fmaf(dr, Cv, lam[s]);
-        dCv[s] = dr * hs[j + 1][s];
-        const float E = __builtin_amdgcn_exp2f(o.x * A2[s]);
-        const float ga = lam[s] * hs[j][s] * E;
-        ddp = fmaf(ga, An[s], ddp);
-        dAacc[s] = fmaf(ga, o.x, dAacc[s]);
-        sB = fmaf(lam[s], Bv, sB);
-        dBv[s] = lam[s] * o.y;
-        lam[s] *= E;
-      }
-      if constexpr (K == 2) {
-        ddp += __builtin_amdgcn_update_dpp(0.0f, ddp, 0xB1, 0xf, 0xf, false);
-        sB += __builtin_amdgcn_update_dpp(0.0f, sB, 0xB1, 0xf, 0xf, false);
-      }
-      if (hk == 0) s_pp[j][w][c] = make_float2(ddp, sB);
-      // channel pair (c, c ^ 1), same hk: lanes 2 apart for K == 2, 1 apart for K == 1
-      const int odd = c & 1;
-      float* dst = s_red + ((j % HALF) * SG * 2 + sg * 2 + odd) * PLANE + (c >> 1) * NS;
+    for (int j = CK - 1; j >= 0; --j) {
+      if (FULL || j < nj) {
+        const float dr = s_dr[j][c];
+        const float2 o = s_dd[j][c];
+        float ddp = 0.0f, sB = 0.0f;   // ddp in units of A log2(e)
+        float dBv[NS], dCv[NS];
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const float give = odd ? dBv[s] : dCv[s];
-        const float keep = odd ? dCv[s] : dBv[s];
-        float got;
-        if constexpr (K == 2) got = __builtin_amdgcn_update_dpp(0.0f, give, 0x4E, 0xf, 0xf, false);   // [2,3,0,1]
-        else got = __builtin_amdgcn_update_dpp(0.0f, give, 0xB1, 0xf, 0xf, false);                  // [1,0,3,2]
-        dst[s] = keep + got;   // even channel: dB of the pair, odd channel: dC of the pair
-      }
-    };
-    // the channel sums of HALF tokens starting at chunk token j0, one per thread
-    auto reduce = [&](int j0) {
-      if (tid < HALF * NOUT) {
-        const int jj = tid / NOUT;
-        const int o = tid % NOUT;   // o < N: dB_n, else dC_n
-        const int which = o / N, n = o % N;
-        const float* src = s_red + (jj * SG * 2 + (n / NS) * 2 + which) * PLANE + (n % NS);
-        float acc = 0.0f;
-#pragma unroll 4
-        for (int q = 0; q < PAIRS; ++q) acc += src[q * NS];
-        const int64_t t = t0 + j0 + jj;
-        if (t < t1) part_row[t * NOUT + o] = acc;
-      }
-    };
+        for (int s = 0; s < NS; ++s) {
+          const float Bv = s_bc[j][2 * (sg * NS + s)];
+          const float Cv = s_bc[j][2 * (sg * NS + s) + 1];
+          lam[s] = fmaf(dr, Cv, lam[s]);
+          dCv[s] = dr * hs[j + 1][s];
+          const float E = __builtin_amdgcn_exp2f(o.x * A2[s]);
+          const float ga = lam[s] * hs[j][s] * E;
+          ddp = fmaf(ga, A2[s], ddp);
+          dAacc[s] = fmaf(ga, o.x, dAacc[s]);
+          sB = fmaf(lam[s], Bv, sB);
+          dBv[s] = lam[s] * o.y;
+          lam[s] *= E;
+        }
+        if constexpr (K == 2) {
+          ddp += __builtin_amdgcn_update_dpp(0.0f, ddp, 0xB1, 0xf, 0xf, false);
+          sB += __builtin_amdgcn_update_dpp(0.0f, sB, 0xB1, 0xf, 0xf, false);
+        }
+        s_pp[j][w][c] = make_float2(ddp * kLn2, sB);   // both lanes of a channel hold the sums
+        // dB and dC summed over the channels of each 16-lane row: the channel
+        // pair (c, c ^ 1) first, the even channel keeping dB and the odd one dC
+        // (lanes 2 apart for K == 2, 1 apart for K == 1), then rotations within
+        // the row; lanes (lane & 15) < 2K end with the row's sums
+        const bool odd = (c & 1) != 0;
+        float v[NS];
 #pragma unroll
-    for (int r = CK / HALF - 1; r >= 0; --r) {
+        for (int s = 0; s < NS; ++s) {
+          const float give = odd ? dBv[s] : dCv[s];
+          const float keep = odd ? dCv[s] : dBv[s];
+          if constexpr (K == 2) v[s] = keep + __builtin_amdgcn_update_dpp(0.0f, give, 0x4E, 0xf, 0xf, false);
+          else v[s] = keep + __builtin_amdgcn_update_dpp(0.0f, give, 0xB1, 0xf, 0xf, false);
+          if constexpr (K == 1) v[s] += __builtin_amdgcn_update_dpp(0.0f, v[s], 0x4E, 0xf, 0xf, false);   // lanes 2 apart
+          v[s] += __builtin_amdgcn_update_dpp(0.0f, v[s], 0x124, 0xf, 0xf, false);   // row_ror:4
+          v[s] += __builtin_amdgcn_update_dpp(0.0f, v[s], 0x128, 0xf, 0xf, false);   // row_ror:8
+          __asm__ volatile("" : "+v"(v[s]));   // finish the sums here, not inside the store branch
+        }
+        const int l = lane & 15;
+        if (l < 2 * K) {
 #pragma unroll
-      for (int jj = HALF - 1; jj >= 0; --jj) {
-        const int j = r * HALF + jj;
-        if (j < nj) back(j);
+          for (int s = 0; s < NS; ++s) s_red[j][w][((lane >> 4) * 2 * K + l) * NS + s] = v[s];
+        }
       }
-      __syncthreads();
-      reduce(r * HALF);
-      __syncthreads();
     }
+    __syncthreads();
 
+    // the chunk's dB/dC partials: per (token, output) the 4 row sums of the wave
+    // that holds the component, in row order
+    for (int idx = tid; idx < CK * NOUT; idx += THREADS) {
+      const int j = idx / NOUT;
+      const int o = idx % NOUT;   // o < N: dB_n, else dC_n
+      const int which = o / N, n = o % N;
+      const int gsg = n / NS;
+      const int l = which * K + gsg % K;
+      const float* src = &s_red[j][gsg / K][l * NS + n % NS];
+      const float acc = ((src[0] + src[2 * K * NS]) + src[4 * K * NS]) + src[6 * K * NS];
+      if (FULL || t0 + j < t1) part_row[(t0 + j) * NOUT + o] = acc;
+    }
     // owners: dx = Delta sum lam B + dr Dskip, ddt = (dDelta) sigmoid(v)
     {
       float dxv[kSpan], ddtv[kSpan];
@@ -323,25 +351,30 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10)))
       for (int i = 0; i < kSpan; ++i) {
         const int j = j_own + i;
         float ddp = 0.0f, sB = 0.0f;
-        if (i < valid) {
+        if (FULL || i < valid) {
 #pragma unroll
           for (int g = 0; g < G; ++g) {
-            const float2 v = s_pp[j][g][c];
-            ddp += v.x;
-            sB += v.y;
+            const float2 pv = s_pp[j][g][c];
+            ddp += pv.x;
+            sB += pv.y;
           }
         }
         dxv[i] = fmaf(sB, dl[i], drv[i] * skip);
         const float dv = fmaf(sB, xv[i], ddp) * sigmoid2(v2[i]);
         ddtv[i] = dv;
-        if (i < valid) dbias_acc += dv;
+        if (FULL || i < valid) dbias_acc += dv;
       }
-      if (act && valid > 0) {
+      if (act && (FULL || valid > 0)) {
         store_span<IO, kSpan>(static_cast<T*>(p.dx), row + tf, valid, vec, dxv);
         store_span<IO, kSpan>(static_cast<T*>(p.ddt), row + tf, valid, vec, ddtv);
       }
     }
     __syncthreads();
+  };
+  {
+    int64_t k = nck - 1;
+    if (L % CK != 0) chunk(std::false_type{}, k--);   // the ragged last chunk comes first
+    for (; k >= 0; --k) chunk(std::true_type{}, k);
   }
 
   // dh0 = Abar_0 lam_0 (lam already carries the factor); per-(row, channel) sums
