@@ -141,6 +141,43 @@ ss_status ss_state_update_zoh(int64_t batch, int64_t dim, int dstate, ss_dtype i
                               const float* Dskip, const float* dt_bias,
                               void* y, void* stream);
 
+/* Context (sequence) parallelism.  A sequence cut into shards, one per GPU,
+ * needs a single exchange: the recurrence is linear in the state, so a shard
+ * run from a zero state ends in h_end, and from a state h it ends in
+ * exp(A dsum) h + h_end, where dsum is the shard's sum of Delta (per component,
+ * exp(A[d,n] dsum[b,d])).  The pages evaluate the recurrence with a parallel
+ * algorithm in recurrent mode (Mamba abstract, on the "Mamba models" page, and
+ * the tellworld.net summary, "Architecture"); this is its two-level form.
+ *  1. Each shard: ss_scan_shard_state -> (dsum, h_end).
+ *  2. Exchange the (dsum, h_end) pairs (an all-gather), then ss_scan_shard_combine
+ *     -> the state entering each shard.
+ *  3. Each shard: ss_scan_fwd with h0 = its entering state.
+ *
+ * ss_scan_shard_state: inputs as for ss_scan_fwd (z, C, Dskip are not needed);
+ * outputs dsum (batch, dim) fp32 (4-byte aligned) and h_end (batch, dim, dstate)
+ * fp32 (16-byte aligned).  The workspace is that of ss_scan_fwd with the
+ * automatic plan (ss_scan_fwd_workspace_bytes(..., NULL)).  seqlen == 0 gives
+ * zeros.  The _zoh form uses the zero-order-hold input term. */
+ss_status ss_scan_shard_state(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io,
+                              const void* x, const void* dt, const void* B, const float* A,
+                              const float* dt_bias, float* dsum, float* h_end,
+                              void* workspace, size_t workspace_bytes, void* stream);
+ss_status ss_scan_shard_state_zoh(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io,
+                                  const void* x, const void* dt, const void* B, const float* A,
+                                  const float* dt_bias, float* dsum, float* h_end,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ss_scan_shard_combine: the exclusive scan over nshards shards in order.
+ * dsum (nshards, batch, dim) and h_end (nshards, batch, dim, dstate) are the
+ * shards' results stacked shard-major (as an all-gather leaves them); h0
+ * (batch, dim, dstate) is the sequence's initial state (NULL = zero).  Writes
+ * h_in (nshards, batch, dim, dstate), the state entering each shard, and
+ * h_final (batch, dim, dstate), the state after the last shard; either may be
+ * NULL.  All fp32, 4-byte aligned; outputs may not overlap inputs. */
+ss_status ss_scan_shard_combine(int64_t batch, int64_t dim, int dstate, int64_t nshards,
+                                const float* A, const float* dsum, const float* h_end,
+                                const float* h0, float* h_in, float* h_final, void* stream);
+
 /* Backward pass of ss_scan_fwd (first-order input term): the gradients of a
  * loss with respect to every input of the scan, given dy = dLoss/dy and
  * dh_final = dLoss/dh_final.  Training differentiates the scan, and the state

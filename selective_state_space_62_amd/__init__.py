@@ -5,11 +5,14 @@
 """
 from . import binding  # noqa: F401  (raises ImportError if libssscan.so is missing)
 from .binding import (SS_BF16, SS_F32, SsError, ss_abi_version, ss_scan_bwd, ss_scan_bwd_workspace_bytes,  # noqa: F401
-                      ss_scan_fwd, ss_scan_fwd_plan, ss_scan_fwd_workspace_bytes, ss_scan_fwd_zoh, ss_state_update,
+                      ss_scan_fwd, ss_scan_fwd_plan, ss_scan_fwd_workspace_bytes, ss_scan_fwd_zoh,
+                      ss_scan_shard_combine, ss_scan_shard_state, ss_scan_shard_state_zoh, ss_state_update,
                       ss_state_update_zoh, ss_timing_enable, ss_timing_read, ss_timing_reset)
-from .torch_ops import bwd_workspace_bytes, scan_bwd, scan_fwd, state_update, workspace_bytes  # noqa: F401
+from .torch_ops import (bwd_workspace_bytes, scan_bwd, scan_fwd, shard_combine, shard_state,  # noqa: F401
+                        state_update, workspace_bytes)
 
 __all__ = ["ss_scan_fwd", "ss_state_update", "ss_scan_fwd_zoh", "ss_state_update_zoh", "ss_scan_bwd",
            "ss_scan_fwd_plan", "ss_scan_fwd_workspace_bytes", "ss_scan_bwd_workspace_bytes", "ss_timing_enable",
            "ss_timing_read", "ss_timing_reset", "ss_abi_version", "scan_fwd", "scan_bwd", "state_update",
-           "workspace_bytes", "bwd_workspace_bytes", "SsError", "SS_F32", "SS_BF16"]
+           "workspace_bytes", "bwd_workspace_bytes", "ss_scan_shard_state", "ss_scan_shard_state_zoh",
+           "ss_scan_shard_combine", "shard_state", "shard_combine", "SsError", "SS_F32", "SS_BF16"]

@@ -69,6 +69,12 @@ def _load():
     lib.ss_scan_bwd_workspace_bytes.argtypes = [_i64, _i64, _int, _i64, _int]
     lib.ss_scan_bwd.restype = _int
     lib.ss_scan_bwd.argtypes = [_i64, _i64, _int, _i64, _int] + [_vp] * 21 + [ctypes.c_size_t, _vp]
+    lib.ss_scan_shard_state.restype = _int
+    lib.ss_scan_shard_state.argtypes = [_i64, _i64, _int, _i64, _int] + [_vp] * 7 + [_vp, ctypes.c_size_t, _vp]
+    lib.ss_scan_shard_state_zoh.restype = _int
+    lib.ss_scan_shard_state_zoh.argtypes = lib.ss_scan_shard_state.argtypes
+    lib.ss_scan_shard_combine.restype = _int
+    lib.ss_scan_shard_combine.argtypes = [_i64, _i64, _int, _i64] + [_vp] * 6 + [_vp]
     lib.ss_timing_enable.restype = _int
     lib.ss_timing_enable.argtypes = [_int]
     lib.ss_timing_reset.restype = _int
@@ -156,6 +162,22 @@ def ss_scan_bwd(batch, dim, dstate, seqlen, io, x, dt, z, B, C, A, Dskip, dt_bia
                 dx, ddt, dz, dB, dC, dA, dDskip, ddt_bias, dh0, workspace, workspace_bytes, stream=None):
     _check(lib.ss_scan_bwd(batch, dim, dstate, seqlen, io, x, dt, z, B, C, A, Dskip, dt_bias, h0, dy, dh_final,
                            dx, ddt, dz, dB, dC, dA, dDskip, ddt_bias, dh0, workspace, workspace_bytes, stream))
+
+
+def ss_scan_shard_state(batch, dim, dstate, seqlen, io, x, dt, B, A, dt_bias, dsum, h_end, workspace,
+                        workspace_bytes, stream=None):
+    _check(lib.ss_scan_shard_state(batch, dim, dstate, seqlen, io, x, dt, B, A, dt_bias, dsum, h_end, workspace,
+                                   workspace_bytes, stream))
+
+
+def ss_scan_shard_state_zoh(batch, dim, dstate, seqlen, io, x, dt, B, A, dt_bias, dsum, h_end, workspace,
+                            workspace_bytes, stream=None):
+    _check(lib.ss_scan_shard_state_zoh(batch, dim, dstate, seqlen, io, x, dt, B, A, dt_bias, dsum, h_end, workspace,
+                                       workspace_bytes, stream))
+
+
+def ss_scan_shard_combine(batch, dim, dstate, nshards, A, dsum, h_end, h0, h_in, h_final, stream=None):
+    _check(lib.ss_scan_shard_combine(batch, dim, dstate, nshards, A, dsum, h_end, h0, h_in, h_final, stream))
 
 
 def ss_timing_enable(enable: bool):

@@ -420,6 +420,82 @@ ss_status state_update_impl(int64_t batch, int64_t dim, int dstate, ss_dtype io,
   return SS_OK;
 }
 
+ss_status shard_state_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io, const void* x,
+                           const void* dt, const void* B, const float* A, const float* dt_bias, float* dsum,
+                           float* h_end, void* workspace, size_t workspace_bytes, void* stream, bool zoh) {
+  ss_status st = check_sizes(batch, dim, dstate, seqlen, io);
+  if (st != SS_OK) return st;
+  if (!A || !dsum || !h_end) return fail(SS_ERR_INVALID_ARG, "%s is NULL", !A ? "A" : (!dsum ? "dsum" : "h_end"));
+  if (seqlen > 0 && (!x || !dt || !B)) return fail(SS_ERR_INVALID_ARG, "%s is NULL", !x ? "x" : (!dt ? "dt" : "B"));
+  const void* a16[] = {x, dt, B, A, h_end};
+  const char* n16[] = {"x", "dt", "B", "A", "h_end"};
+  for (int i = 0; i < 5; ++i)
+    if (a16[i] && !aligned(a16[i], 16)) return fail(SS_ERR_INVALID_ARG, "%s is not 16-byte aligned", n16[i]);
+  if (dt_bias && !aligned(dt_bias, 4)) return fail(SS_ERR_INVALID_ARG, "dt_bias is not 4-byte aligned");
+  if (!aligned(dsum, 4)) return fail(SS_ERR_INVALID_ARG, "dsum is not 4-byte aligned");
+  const Plan p = auto_plan(batch, dim, dstate, seqlen, io);
+  const WsLayout wl = ws_layout(batch, dim, dstate, seqlen, p);
+  if (seqlen > 0) {
+    if (!workspace) return fail(SS_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", wl.total);
+    if (!aligned(workspace, 256)) return fail(SS_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    if (workspace_bytes < wl.total)
+      return fail(SS_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, wl.total);
+  }
+  const int64_t eb = elem_bytes(io);
+  const int64_t seq_bytes = batch * dim * seqlen * eb;
+  const Range ins[] = {rng("x", x, seq_bytes), rng("dt", dt, seq_bytes), rng("B", B, batch * dstate * seqlen * eb),
+                       rng("A", A, dim * dstate * 4), rng("dt_bias", dt_bias, dim * 4)};
+  const Range outs[] = {rng("dsum", dsum, batch * dim * 4), rng("h_end", h_end, batch * dim * dstate * 4),
+                        rng("workspace", workspace, seqlen > 0 ? (int64_t)wl.total : 0)};
+  for (const Range& o : outs)
+    for (const Range& i : ins)
+      if (overlap(o, i)) return fail(SS_ERR_INVALID_ARG, "%s overlaps input %s", o.name, i.name);
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j])) return fail(SS_ERR_INVALID_ARG, "%s overlaps %s", outs[i].name, outs[j].name);
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (seqlen == 0) {
+    e = ssscan::launch_fill_zero(h_end, batch * dim * dstate, s);
+    if (e == hipSuccess) e = ssscan::launch_fill_zero(dsum, batch * dim, s);
+    return e == hipSuccess ? SS_OK : hip_fail(e, "zero-fill launch");
+  }
+  ssscan::ScanDims dm{};
+  dm.batch = batch;
+  dm.dim = dim;
+  dm.seqlen = seqlen;
+  dm.chunk_len = p.chunk_len;
+  dm.num_chunks = p.num_chunks;
+  dm.dstate = dstate;
+  dm.groups = p.groups;
+  dm.lanes = p.lanes;
+  dm.io = io_code(io);
+  dm.vec = (seqlen % ssscan::span_len(p.lanes, dm.io)) == 0 ? 1 : 0;
+  char* ws = static_cast<char*>(workspace);
+  float* bcw = reinterpret_cast<float*>(ws + wl.bc);
+  e = ssscan::launch_prep_bc(dm, B, B, bcw, s);   // C is not read by the aggregate pass
+  if (e != hipSuccess) return hip_fail(e, "prep_bc launch");
+  ssscan::ScanPtrs sp{};
+  sp.x = x;
+  sp.dt = dt;
+  sp.bc = bcw;
+  sp.A = A;
+  sp.dt_bias = dt_bias;
+  if (p.num_chunks == 1) {
+    sp.agg_h = h_end;   // (batch, dim, 1, N) and (batch, dim, 1)
+    sp.agg_s = dsum;
+    e = ssscan::launch_scan(dm, sp, /*aggregate=*/true, zoh, s);
+    return e == hipSuccess ? SS_OK : hip_fail(e, "scan (aggregate) launch");
+  }
+  sp.agg_h = reinterpret_cast<float*>(ws + wl.agg_h);
+  sp.agg_s = reinterpret_cast<float*>(ws + wl.agg_s);
+  e = ssscan::launch_scan(dm, sp, /*aggregate=*/true, zoh, s);
+  if (e != hipSuccess) return hip_fail(e, "scan (aggregate) launch");
+  e = ssscan::launch_shard_reduce(dm, A, sp.agg_h, sp.agg_s, h_end, dsum, s);
+  return e == hipSuccess ? SS_OK : hip_fail(e, "shard reduce launch");
+}
+
 struct BwdLayout {
   size_t bc, ckpt, part, dA_p, dD_p, dbias_p, total;
   int64_t cblocks, chunks;
@@ -617,6 +693,48 @@ ss_status ss_state_update_zoh(int64_t batch, int64_t dim, int dstate, ss_dtype i
                               const void* dt, const void* z, const void* B, const void* C, const float* A,
                               const float* Dskip, const float* dt_bias, void* y, void* stream) {
   return state_update_impl(batch, dim, dstate, io, state, x, dt, z, B, C, A, Dskip, dt_bias, y, stream, true);
+}
+
+ss_status ss_scan_shard_state(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io, const void* x,
+                              const void* dt, const void* B, const float* A, const float* dt_bias, float* dsum,
+                              float* h_end, void* workspace, size_t workspace_bytes, void* stream) {
+  return shard_state_impl(batch, dim, dstate, seqlen, io, x, dt, B, A, dt_bias, dsum, h_end, workspace,
+                          workspace_bytes, stream, false);
+}
+
+ss_status ss_scan_shard_state_zoh(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io,
+                                  const void* x, const void* dt, const void* B, const float* A, const float* dt_bias,
+                                  float* dsum, float* h_end, void* workspace, size_t workspace_bytes, void* stream) {
+  return shard_state_impl(batch, dim, dstate, seqlen, io, x, dt, B, A, dt_bias, dsum, h_end, workspace,
+                          workspace_bytes, stream, true);
+}
+
+ss_status ss_scan_shard_combine(int64_t batch, int64_t dim, int dstate, int64_t nshards, const float* A,
+                                const float* dsum, const float* h_end, const float* h0, float* h_in, float* h_final,
+                                void* stream) {
+  if (!valid_dstate(dstate)) return fail(SS_ERR_UNSUPPORTED, "dstate %d is not one of 1, 2, 4, 8, 16", dstate);
+  if (batch < 1 || dim < 1 || nshards < 1)
+    return fail(SS_ERR_INVALID_ARG, "sizes must be batch, dim, nshards >= 1 (got %lld, %lld, %lld)",
+                (long long)batch, (long long)dim, (long long)nshards);
+  if (batch > kMaxDim || dim > kMaxDim || nshards > kMaxDim) return fail(SS_ERR_INVALID_ARG, "a size exceeds 2^40");
+  if ((__int128)nshards * batch * dim * dstate * 4 > ((__int128)1 << 62))
+    return fail(SS_ERR_INVALID_ARG, "tensor sizes overflow 64-bit byte offsets");
+  if (!A || !dsum || !h_end) return fail(SS_ERR_INVALID_ARG, "%s is NULL", !A ? "A" : (!dsum ? "dsum" : "h_end"));
+  const void* a4[] = {A, dsum, h_end, h0, h_in, h_final};
+  const char* n4[] = {"A", "dsum", "h_end", "h0", "h_in", "h_final"};
+  for (int i = 0; i < 6; ++i)
+    if (a4[i] && !aligned(a4[i], 4)) return fail(SS_ERR_INVALID_ARG, "%s is not 4-byte aligned", n4[i]);
+  const int64_t st_bytes = batch * dim * dstate * 4;
+  const Range ins[] = {rng("A", A, dim * dstate * 4), rng("dsum", dsum, nshards * batch * dim * 4),
+                       rng("h_end", h_end, nshards * st_bytes), rng("h0", h0, st_bytes)};
+  const Range outs[] = {rng("h_in", h_in, nshards * st_bytes), rng("h_final", h_final, st_bytes)};
+  for (const Range& o : outs)
+    for (const Range& i : ins)
+      if (overlap(o, i)) return fail(SS_ERR_INVALID_ARG, "%s overlaps input %s", o.name, i.name);
+  if (overlap(outs[0], outs[1])) return fail(SS_ERR_INVALID_ARG, "h_in overlaps h_final");
+  hipError_t e = ssscan::launch_shard_combine(batch, dim, dstate, nshards, A, dsum, h_end, h0, h_in, h_final,
+                                              reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SS_OK : hip_fail(e, "shard combine launch");
 }
 
 size_t ss_scan_bwd_workspace_bytes(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io) {

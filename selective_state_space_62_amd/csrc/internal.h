@@ -95,6 +95,11 @@ hipError_t launch_scan_f32_zoh(const ScanDims& dm, const ScanPtrs& p, bool aggre
 hipError_t launch_combine(const ScanDims& dm, const float* A, const float* agg_h, const float* agg_s,
                           const float* h0, float* h_in, hipStream_t s);
 hipError_t launch_copy_state(int64_t count, const float* src, float* dst, hipStream_t s);
+hipError_t launch_shard_reduce(const ScanDims& dm, const float* A, const float* agg_h, const float* agg_s,
+                               float* h_end, float* dsum, hipStream_t s);
+hipError_t launch_shard_combine(int64_t batch, int64_t dim, int dstate, int64_t nshards, const float* A,
+                                const float* dsum, const float* h_end, const float* h0, float* h_in, float* h_final,
+                                hipStream_t s);
 hipError_t launch_scan_bwd(const BwdDims& dm, const BwdPtrs& p, hipStream_t s);
 hipError_t launch_fill_zero(float* dst, int64_t n, hipStream_t s);
 hipError_t launch_state_update(int64_t batch, int64_t dim, int dstate, int io, bool zoh, float* state,

@@ -97,6 +97,54 @@ __global__ __launch_bounds__(256) void combine_kernel(int64_t nstate, int64_t di
   }
 }
 
+// A shard's aggregate from its chunks' aggregates, one lane per (b, d, n):
+// h = state after the last chunk from a zero start, and (n == 0) the sum of Delta.
+__global__ __launch_bounds__(256) void shard_reduce_kernel(int64_t nstate, int64_t dim, int dstate, int num_chunks,
+                                                           const float* __restrict__ A,
+                                                           const float* __restrict__ agg_h,
+                                                           const float* __restrict__ agg_s, float* __restrict__ h_end,
+                                                           float* __restrict__ dsum) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nstate) return;
+  const int64_t ch = i / dstate;
+  const int n = (int)(i - ch * dstate);
+  const int64_t d = ch % dim;
+  const float a2 = A[d * dstate + n] * dev::kLog2e;
+  float h = 0.0f, s = 0.0f;
+  for (int c = 0; c < num_chunks; ++c) {
+    const float sc = agg_s[ch * num_chunks + c];
+    h = fmaf(__builtin_amdgcn_exp2f(a2 * sc), h, agg_h[(ch * num_chunks + c) * dstate + n]);
+    s += sc;
+  }
+  h_end[i] = h;
+  if (n == 0) dsum[ch] = s;
+}
+
+// The state entering each of a sequence's shards, one lane per (b, d, n):
+// h_in[0] = h0, h_in[s + 1] = exp(A dsum[s]) h_in[s] + h_end[s]; h_final = the
+// state after the last shard.  Shard-major layouts: dsum (nshards, batch, dim),
+// h_end and h_in (nshards, batch, dim, N).
+__global__ __launch_bounds__(256) void shard_combine_kernel(int64_t nstate, int64_t dim, int dstate,
+                                                            int64_t nshards, const float* __restrict__ A,
+                                                            const float* __restrict__ dsum,
+                                                            const float* __restrict__ h_end,
+                                                            const float* __restrict__ h0, float* __restrict__ h_in,
+                                                            float* __restrict__ h_final) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nstate) return;
+  const int64_t ch = i / dstate;
+  const int n = (int)(i - ch * dstate);
+  const int64_t d = ch % dim;
+  const int64_t nch = nstate / dstate;
+  const float a2 = A[d * dstate + n] * dev::kLog2e;
+  float h = h0 ? h0[i] : 0.0f;
+  for (int64_t s = 0; s < nshards; ++s) {
+    if (h_in) h_in[s * nstate + i] = h;
+    h = fmaf(__builtin_amdgcn_exp2f(a2 * dsum[s * nch + ch]), h, h_end[s * nstate + i]);
+  }
+  if (h_final) h_final[i] = h;
+}
+
 __global__ __launch_bounds__(256) void copy_state_kernel(int64_t count, const float* __restrict__ src,
                                                          float* __restrict__ dst) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -136,6 +184,23 @@ hipError_t launch_combine(const ScanDims& dm, const float* A, const float* agg_h
   const int64_t nstate = dm.batch * dm.dim * dm.dstate;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((nstate + 255) / 256)), dim3(256), 0, s, nstate, dm.dim,
                      dm.dstate, dm.num_chunks, A, agg_h, agg_s, h0, h_in);
+  return hipGetLastError();
+}
+
+hipError_t launch_shard_reduce(const ScanDims& dm, const float* A, const float* agg_h, const float* agg_s,
+                               float* h_end, float* dsum, hipStream_t s) {
+  const int64_t nstate = dm.batch * dm.dim * dm.dstate;
+  hipLaunchKernelGGL(shard_reduce_kernel, dim3((unsigned)((nstate + 255) / 256)), dim3(256), 0, s, nstate, dm.dim,
+                     dm.dstate, dm.num_chunks, A, agg_h, agg_s, h_end, dsum);
+  return hipGetLastError();
+}
+
+hipError_t launch_shard_combine(int64_t batch, int64_t dim, int dstate, int64_t nshards, const float* A,
+                                const float* dsum, const float* h_end, const float* h0, float* h_in, float* h_final,
+                                hipStream_t s) {
+  const int64_t nstate = batch * dim * dstate;
+  hipLaunchKernelGGL(shard_combine_kernel, dim3((unsigned)((nstate + 255) / 256)), dim3(256), 0, s, nstate, dim,
+                     dstate, nshards, A, dsum, h_end, h0, h_in, h_final);
   return hipGetLastError();
 }
 

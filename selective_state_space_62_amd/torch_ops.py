@@ -156,3 +156,45 @@ def scan_bwd(x, dt, B, C, A, dy, z=None, Dskip=None, dt_bias=None, h0=None, dh_f
                    _ptr(out["dz"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dA"]), _ptr(out["dDskip"]),
                    _ptr(out["ddt_bias"]), _ptr(out["dh0"]), _ptr(workspace), workspace.numel(), _stream(dev))
     return out
+
+
+def shard_state(x, dt, B, A, dt_bias=None, *, zoh=False, workspace=None):
+    """One shard of a sequence from a zero state: returns (dsum (batch, D), h_end
+    (batch, D, N)) in float32, the shard's sum of Delta and final state."""
+    if x.dtype not in _IO:
+        raise TypeError("x must be float32 or bfloat16")
+    dev = x.device
+    batch, dim, L = x.shape
+    N = A.shape[1]
+    io = _IO[x.dtype]
+    _need(dt, "dt", x.dtype, (batch, dim, L), dev)
+    _need(B, "B", x.dtype, (batch, N, L), dev)
+    _need(A, "A", torch.float32, (dim, N), dev)
+    _need(dt_bias, "dt_bias", torch.float32, (dim,), dev)
+    dsum = torch.empty((batch, dim), dtype=torch.float32, device=dev)
+    h_end = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
+    nbytes = _b.ss_scan_fwd_workspace_bytes(batch, dim, N, L, io, None)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    if workspace.numel() < nbytes:
+        raise ValueError("workspace has %d bytes, %d needed" % (workspace.numel(), nbytes))
+    fn = _b.ss_scan_shard_state_zoh if zoh else _b.ss_scan_shard_state
+    fn(batch, dim, N, L, io, _ptr(x), _ptr(dt), _ptr(B), _ptr(A), _ptr(dt_bias), _ptr(dsum), _ptr(h_end),
+       _ptr(workspace), workspace.numel(), _stream(dev))
+    return dsum, h_end
+
+
+def shard_combine(A, dsum, h_end, h0=None):
+    """Exclusive scan over shards: dsum (S, batch, D), h_end (S, batch, D, N) ->
+    (h_in (S, batch, D, N), h_final (batch, D, N)), float32."""
+    dev = A.device
+    S, batch, dim, N = h_end.shape
+    _need(A, "A", torch.float32, (dim, N), dev)
+    _need(dsum, "dsum", torch.float32, (S, batch, dim), dev)
+    _need(h_end, "h_end", torch.float32, (S, batch, dim, N), dev)
+    _need(h0, "h0", torch.float32, (batch, dim, N), dev)
+    h_in = torch.empty_like(h_end)
+    h_final = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
+    _b.ss_scan_shard_combine(batch, dim, N, S, _ptr(A), _ptr(dsum), _ptr(h_end), _ptr(h0), _ptr(h_in),
+                             _ptr(h_final), _stream(dev))
+    return h_in, h_final

@@ -210,6 +210,45 @@ def test_bwd_workspace_bytes():
     assert b.ss_scan_bwd_workspace_bytes(2, 64, 3, 16, b.SS_F32) == 0
 
 
+@pytest.mark.parametrize("case,status", [
+    (dict(dstate=3), b.SS_ERR_UNSUPPORTED),
+    (dict(x=None), b.SS_ERR_INVALID_ARG),
+    (dict(h_end=None), b.SS_ERR_INVALID_ARG),
+    (dict(dsum=None), b.SS_ERR_INVALID_ARG),
+    (dict(h_end=ALIGNED + (1 << 33) + 8), b.SS_ERR_INVALID_ARG),
+    (dict(dsum=ALIGNED + (1 << 30)), b.SS_ERR_INVALID_ARG),        # dsum overlaps dt
+    (dict(workspace=None), b.SS_ERR_WORKSPACE),
+    (dict(workspace_bytes=64), b.SS_ERR_WORKSPACE),
+])
+def test_shard_state_validation(case, status):
+    a = dict(batch=2, dim=64, dstate=16, seqlen=512, io=b.SS_BF16, x=ALIGNED, dt=ALIGNED + (1 << 30),
+             B=ALIGNED + (1 << 31), A=ALIGNED + (1 << 32), dt_bias=None, dsum=ALIGNED + (1 << 33) + (1 << 20),
+             h_end=ALIGNED + (1 << 33), workspace=ALIGNED + (1 << 34), workspace_bytes=1 << 30)
+    a.update(case)
+    st = b.lib.ss_scan_shard_state(a["batch"], a["dim"], a["dstate"], a["seqlen"], a["io"], a["x"], a["dt"], a["B"],
+                                   a["A"], a["dt_bias"], a["dsum"], a["h_end"], a["workspace"], a["workspace_bytes"],
+                                   None)
+    assert st == status, (st, b.last_error())
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(nshards=0), b.SS_ERR_INVALID_ARG),
+    (dict(dstate=6), b.SS_ERR_UNSUPPORTED),
+    (dict(A=None), b.SS_ERR_INVALID_ARG),
+    (dict(h_end=None), b.SS_ERR_INVALID_ARG),
+    (dict(h_in=ALIGNED + 2), b.SS_ERR_INVALID_ARG),
+    (dict(h_in=ALIGNED + (1 << 31)), b.SS_ERR_INVALID_ARG),        # h_in overlaps h_end
+    (dict(h_final=ALIGNED), b.SS_ERR_INVALID_ARG),                 # h_final overlaps A
+])
+def test_shard_combine_validation(case, status):
+    a = dict(batch=2, dim=64, dstate=16, nshards=8, A=ALIGNED, dsum=ALIGNED + (1 << 30), h_end=ALIGNED + (1 << 31),
+             h0=None, h_in=ALIGNED + (1 << 32), h_final=ALIGNED + (1 << 33))
+    a.update(case)
+    st = b.lib.ss_scan_shard_combine(a["batch"], a["dim"], a["dstate"], a["nshards"], a["A"], a["dsum"], a["h_end"],
+                                     a["h0"], a["h_in"], a["h_final"], None)
+    assert st == status, (st, b.last_error())
+
+
 def test_timing_record_empty():
     b.ss_timing_enable(False)
     b.ss_timing_reset()
