@@ -34,13 +34,14 @@ TRANS_SLOTS = 2   # transcendentals issue at half rate on gfx950 and do not co-i
 _CSRC = "selective_state_space_62_amd/csrc/"
 # sources of each timed kernel: committed counters apply only while these are unchanged
 KERNEL_SOURCES = {
-    "scan": [_CSRC + f for f in ("scan_kernel.h", "scan_fwd.hip", "scan_bf16_euler.hip", "scan_f32_euler.hip",
-                                 "device_common.h", "internal.h")],
-    "decode": [_CSRC + f for f in ("state_update.hip", "device_common.h", "internal.h")],
+    "scan": [_CSRC + f for f in ("scan_kernel.h", "scan_bf16_euler.hip", "scan_f32_euler.hip", "device_common.h")],
+    "decode": [_CSRC + f for f in ("state_update.hip", "device_common.h")],
+    "bwd": [_CSRC + f for f in ("scan_bwd.hip", "device_common.h")],
 }
 COUNTERS_FILES = {
     "scan": ROOT / "profiles" / "scan_2.8b_bf16_counters.json",
     "decode": ROOT / "profiles" / "decode_256x5120_bf16_counters.json",
+    "bwd": ROOT / "profiles" / "bwd_2.8b_bf16_counters.json",
 }
 
 
@@ -69,6 +70,20 @@ def algorithmic_slots_per_tokch(N: int) -> float:
     transcendentals (softplus: exp, log; silu: exp, reciprocal).  A
     transcendental costs TRANS_SLOTS slots."""
     return 4 * N + 8 + TRANS_SLOTS * (N + 4)
+
+
+def algorithmic_slots_bwd_per_tokch(N: int) -> float:
+    """VALU issue slots per (token, channel) of the backward pass by recomputation:
+    per state component the checkpoint sweep (3 ops + exp), the chunk recompute with
+    the readout (4 ops + exp) and the adjoint step (10 ops + exp: adjoint update,
+    dC and dB terms, the decay's derivative for dDelta and dA, lam B for dx, the
+    adjoint decay, and Abar recomputed); per (token, channel) two softplus
+    evaluations (5 ops + 2 transcendentals each), sigmoid(dt + dt_bias) (2 + 2),
+    silu(z) and its derivative (7 + 2) and the six output formulas (8 ops).  A
+    transcendental costs TRANS_SLOTS slots."""
+    per_n = 17 + 3 * TRANS_SLOTS
+    per_tok = 10 + 2 + 7 + 8 + TRANS_SLOTS * (4 + 2 + 2)
+    return per_n * N + per_tok
 
 
 def cpu_baseline(cfg, budget_s: float):
@@ -178,10 +193,55 @@ def run_bwd(ss, torch, dev, cfg, t, A, dskip, bias, fwd_kernel_ms, calls=20):
     ms, n = ss.ss_timing_read()
     ss.ss_timing_reset()
     kms = ms / n
-    return {"entry_point": "ss_scan_bwd", "kernel_ms": round(kms, 5),
+    spt = algorithmic_slots_bwd_per_tokch(cfg.dstate)
+    ach = spt * cfg.tokch / (kms * 1e-3) / 1e12
+    return {"entry_point": "ss_scan_bwd", "kernel": "scan_bwd_kernel<16,4,2,%s> + reduce kernels" % cfg.io,
+            "roofline": {"bound": "alu", "achieved": round(ach, 3), "peak": round(VALU_PEAK_TOPS, 3),
+                         "unit": "T VALU-slot/s", "frac": round(ach / VALU_PEAK_TOPS, 4), "slots_per_tokch": spt},
+            "kernel_ms": round(kms, 5),
             "value": round(cfg.tokch / (kms * 1e-3) / 1e9, 3), "unit": "Gtok·ch/s",
             "ratio_to_forward": round(kms / fwd_kernel_ms, 3),
-            "workspace_bytes": ws.numel()}
+            "workspace_bytes": ws.numel(), "traffic": measured_traffic(cfg, "bwd")}
+
+
+def run_cp(ss, torch, cfg, t, A, dskip, bias, G, reps=10):
+    """One GPU's share of a context-parallel run over G shards (secondary): the
+    shard's aggregate, the combine over G shards and the shard's rescan from its
+    entering state, at the real shard shape (the all-gather of the pairs between
+    GPUs is not part of it)."""
+    L = cfg.seqlen // G
+    sh = {k: v[..., :L].contiguous() for k, v in t.items()}
+    dsum, h_end = ss.shard_state(sh["x"], sh["dt"], sh["B"], A, dt_bias=bias)
+    ds_all = dsum.unsqueeze(0).repeat(G, 1, 1).contiguous()
+    he_all = h_end.unsqueeze(0).repeat(G, 1, 1, 1).contiguous()
+    h_in, _ = ss.shard_combine(A, ds_all, he_all)
+    h0 = h_in[G - 1].contiguous()
+    ws = torch.empty(max(ss.workspace_bytes(cfg.batch, cfg.dim, cfg.dstate, L, t["x"].dtype), 256), dtype=torch.uint8,
+                     device=t["x"].device)
+    y = torch.empty_like(sh["x"])
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms_state = timed(lambda: ss.shard_state(sh["x"], sh["dt"], sh["B"], A, dt_bias=bias, workspace=ws))
+    ms_comb = timed(lambda: ss.shard_combine(A, ds_all, he_all))
+    ms_scan = timed(lambda: ss.scan_fwd(sh["x"], sh["dt"], sh["B"], sh["C"], A, z=sh["z"], Dskip=dskip, dt_bias=bias,
+                                        h0=h0, workspace=ws, y=y))
+    per_gpu = ms_state + ms_comb + ms_scan
+    return {"shards": G, "shard_tokens": L, "ms_shard_state": round(ms_state, 4), "ms_combine": round(ms_comb, 4),
+            "ms_shard_scan": round(ms_scan, 4), "ms_per_gpu": round(per_gpu, 4),
+            "projected_value": round(cfg.tokch / (per_gpu * 1e-3) / 1e9, 2), "unit": "Gtok·ch/s",
+            "exchange_bytes_per_gpu": G * cfg.batch * cfg.dim * (cfg.dstate + 1) * 4,
+            "note": "projection for G GPUs excludes the all-gather of the (dsum, h_end) pairs"}
 
 
 def main():
@@ -195,6 +255,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step timing")
     ap.add_argument("--no-zoh", action="store_true", help="skip the zero-order-hold scan timing")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward-pass timing")
+    ap.add_argument("--cp-shards", type=int, default=0,
+                    help="also time one GPU's share of a context-parallel run over this many shards")
     ap.add_argument("--copy-calib", type=int, default=0, help="only run a plain copy of this many bytes")
     args = ap.parse_args()
 
@@ -301,6 +363,8 @@ def main():
                       "value": round(tokch / (zms / zn * 1e-3) / 1e9, 3), "unit": "Gtok·ch/s"}
     if not args.no_bwd:
         out["bwd"] = run_bwd(ss, torch, dev, cfg, t, A, dskip, bias, kern_ms)
+    if args.cp_shards > 1:
+        out["context_parallel"] = run_cp(ss, torch, cfg, t, A, dskip, bias, args.cp_shards)
     if not args.no_decode:
         out["decode"] = run_decode(ss, torch, dev, 60, 60)
     if not args.no_cpu_baseline:
