@@ -255,6 +255,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step timing")
     ap.add_argument("--no-zoh", action="store_true", help="skip the zero-order-hold scan timing")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward-pass timing")
+    ap.add_argument("--no-dt-row", action="store_true", help="skip the dt-per-row scan timing")
     ap.add_argument("--cp-shards", type=int, default=0,
                     help="also time one GPU's share of a context-parallel run over this many shards")
     ap.add_argument("--copy-calib", type=int, default=0, help="only run a plain copy of this many bytes")
@@ -361,6 +362,29 @@ def main():
         ss.ss_timing_reset()
         out["zoh"] = {"entry_point": "ss_scan_fwd_zoh", "kernel_ms": round(zms / zn, 5),
                       "value": round(tokch / (zms / zn * 1e-3) / 1e9, 3), "unit": "Gtok·ch/s"}
+    if not args.no_dt_row:
+        # dt shared by a row's channels (SS_FLAG_DT_PER_ROW): the same workload with
+        # one dt row per batch row (secondary)
+        dtr = t["dt"][:, 0, :].contiguous()
+        for _ in range(20):
+            ss.scan_fwd(t["x"], dtr, t["B"], t["C"], A, z=t["z"], Dskip=dskip, dt_bias=bias, workspace=ws, y=y,
+                        h_final=hf)
+        torch.cuda.synchronize()
+        ss.ss_timing_reset()
+        ss.ss_timing_enable(True)
+        for _ in range(20):
+            ss.scan_fwd(t["x"], dtr, t["B"], t["C"], A, z=t["z"], Dskip=dskip, dt_bias=bias, workspace=ws, y=y,
+                        h_final=hf)
+        torch.cuda.synchronize()
+        ss.ss_timing_enable(False)
+        rms, rn = ss.ss_timing_read()
+        ss.ss_timing_reset()
+        eb = 2 if cfg.io == "bf16" else 4
+        rbytes = bpt * tokch - eb * tokch + eb * cfg.batch * cfg.seqlen
+        out["dt_per_row"] = {"entry_point": "ss_scan_fwd_ex (SS_FLAG_DT_PER_ROW)", "kernel_ms": round(rms / rn, 5),
+                             "value": round(tokch / (rms / rn * 1e-3) / 1e9, 3), "unit": "Gtok·ch/s",
+                             "algorithmic_bytes": int(rbytes),
+                             "hbm_gbs": round(rbytes / (rms / rn * 1e-3) / 1e9, 1)}
     if not args.no_bwd:
         out["bwd"] = run_bwd(ss, torch, dev, cfg, t, A, dskip, bias, kern_ms)
     if args.cp_shards > 1:

@@ -141,6 +141,34 @@ ss_status ss_state_update_zoh(int64_t batch, int64_t dim, int dstate, ss_dtype i
                               const float* Dskip, const float* dt_bias,
                               void* y, void* stream);
 
+/* The same two operations with options, as a bitwise OR of ss_flags:
+ *  SS_FLAG_ZOH         the zero-order-hold input term (as the _zoh entry points);
+ *  SS_FLAG_DT_PER_ROW  dt holds one value per (batch row, token), shared by the
+ *                      row's channels: (batch, seqlen) for the scan, (batch) for
+ *                      the decode step.  Delta = softplus(dt[b, t] + dt_bias[d]):
+ *                      the selective SSM's Delta is the softplus of a parameter
+ *                      plus a projection of the input broadcast over channels
+ *                      (reader's notes, kurisu.si, "What they did", Selective SSM
+ *                      item); dt is that projection, dt_bias the parameter.  It
+ *                      is the general form with dt[b, d, t] equal across d, and
+ *                      reads batch * seqlen values of dt instead of batch * dim
+ *                      * seqlen.
+ * Unknown bits return SS_ERR_UNSUPPORTED.  Everything else is as for ss_scan_fwd
+ * and ss_state_update. */
+typedef enum { SS_FLAG_ZOH = 1u, SS_FLAG_DT_PER_ROW = 2u } ss_flags;
+ss_status ss_scan_fwd_ex(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io, uint32_t flags,
+                         const void* x, const void* dt, const void* z,
+                         const void* B, const void* C, const float* A,
+                         const float* Dskip, const float* dt_bias, const float* h0,
+                         void* y, float* h_final,
+                         void* workspace, size_t workspace_bytes,
+                         const ss_scan_plan* plan, void* stream);
+ss_status ss_state_update_ex(int64_t batch, int64_t dim, int dstate, ss_dtype io, uint32_t flags, float* state,
+                             const void* x, const void* dt, const void* z,
+                             const void* B, const void* C, const float* A,
+                             const float* Dskip, const float* dt_bias,
+                             void* y, void* stream);
+
 /* Context (sequence) parallelism.  A sequence cut into shards, one per GPU,
  * needs a single exchange: the recurrence is linear in the state, so a shard
  * run from a zero state ends in h_end, and from a state h it ends in

@@ -69,6 +69,11 @@ def _load():
     lib.ss_scan_bwd_workspace_bytes.argtypes = [_i64, _i64, _int, _i64, _int]
     lib.ss_scan_bwd.restype = _int
     lib.ss_scan_bwd.argtypes = [_i64, _i64, _int, _i64, _int] + [_vp] * 21 + [ctypes.c_size_t, _vp]
+    lib.ss_scan_fwd_ex.restype = _int
+    lib.ss_scan_fwd_ex.argtypes = ([_i64, _i64, _int, _i64, _int, ctypes.c_uint32] + [_vp] * 11
+                                   + [_vp, ctypes.c_size_t, ctypes.POINTER(ss_scan_plan), _vp])
+    lib.ss_state_update_ex.restype = _int
+    lib.ss_state_update_ex.argtypes = [_i64, _i64, _int, _int, ctypes.c_uint32] + [_vp] * 11
     lib.ss_scan_shard_state.restype = _int
     lib.ss_scan_shard_state.argtypes = [_i64, _i64, _int, _i64, _int] + [_vp] * 7 + [_vp, ctypes.c_size_t, _vp]
     lib.ss_scan_shard_state_zoh.restype = _int
@@ -162,6 +167,21 @@ def ss_scan_bwd(batch, dim, dstate, seqlen, io, x, dt, z, B, C, A, Dskip, dt_bia
                 dx, ddt, dz, dB, dC, dA, dDskip, ddt_bias, dh0, workspace, workspace_bytes, stream=None):
     _check(lib.ss_scan_bwd(batch, dim, dstate, seqlen, io, x, dt, z, B, C, A, Dskip, dt_bias, h0, dy, dh_final,
                            dx, ddt, dz, dB, dC, dA, dDskip, ddt_bias, dh0, workspace, workspace_bytes, stream))
+
+
+SS_FLAG_ZOH = 1
+SS_FLAG_DT_PER_ROW = 2
+
+
+def ss_scan_fwd_ex(batch, dim, dstate, seqlen, io, flags, x, dt, z, B, C, A, Dskip, dt_bias, h0, y, h_final,
+                   workspace, workspace_bytes, plan=None, stream=None):
+    _check(lib.ss_scan_fwd_ex(batch, dim, dstate, seqlen, io, flags, x, dt, z, B, C, A, Dskip, dt_bias, h0, y,
+                              h_final, workspace, workspace_bytes, _plan_ptr(plan), stream))
+
+
+def ss_state_update_ex(batch, dim, dstate, io, flags, state, x, dt, z, B, C, A, Dskip, dt_bias, y, stream=None):
+    _check(lib.ss_state_update_ex(batch, dim, dstate, io, flags, state, x, dt, z, B, C, A, Dskip, dt_bias, y,
+                                  stream))
 
 
 def ss_scan_shard_state(batch, dim, dstate, seqlen, io, x, dt, B, A, dt_bias, dsum, h_end, workspace,

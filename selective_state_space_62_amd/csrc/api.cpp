@@ -264,7 +264,8 @@ namespace {
 ss_status scan_fwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io, const void* x,
                         const void* dt, const void* z, const void* B, const void* C, const float* A,
                         const float* Dskip, const float* dt_bias, const float* h0, void* y, float* h_final,
-                        void* workspace, size_t workspace_bytes, const ss_scan_plan* plan, void* stream, bool zoh) {
+                        void* workspace, size_t workspace_bytes, const ss_scan_plan* plan, void* stream, bool zoh,
+                        bool dt_row = false) {
   ss_status st = check_sizes(batch, dim, dstate, seqlen, io);
   if (st != SS_OK) return st;
   Plan p;
@@ -299,7 +300,8 @@ ss_status scan_fwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, 
   }
 
   // outputs must not overlap inputs, each other, or the workspace
-  const Range ins[] = {rng("x", x, seq_bytes), rng("dt", dt, seq_bytes), rng("z", z, seq_bytes),
+  const int64_t dt_bytes = dt_row ? batch * seqlen * eb : seq_bytes;
+  const Range ins[] = {rng("x", x, seq_bytes), rng("dt", dt, dt_bytes), rng("z", z, seq_bytes),
                        rng("B", B, bc_bytes), rng("C", C, bc_bytes), rng("A", A, dim * dstate * 4),
                        rng("Dskip", Dskip, dim * 4), rng("dt_bias", dt_bias, dim * 4), rng("h0", h0, st_bytes)};
   const Range outs[] = {rng("y", y, seq_bytes), rng("h_final", h_final, st_bytes),
@@ -332,6 +334,7 @@ ss_status scan_fwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, 
   dm.lanes = p.lanes;
   dm.io = io_code(io);
   dm.vec = (seqlen % ssscan::span_len(p.lanes, dm.io)) == 0 ? 1 : 0;
+  dm.dt_row = dt_row ? 1 : 0;
 
   const int64_t cpb = 64 / p.lanes;
   const int64_t nwg = ((dim + cpb - 1) / cpb) * batch * p.num_chunks;
@@ -387,7 +390,8 @@ ss_status scan_fwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, 
 
 ss_status state_update_impl(int64_t batch, int64_t dim, int dstate, ss_dtype io, float* state, const void* x,
                             const void* dt, const void* z, const void* B, const void* C, const float* A,
-                            const float* Dskip, const float* dt_bias, void* y, void* stream, bool zoh) {
+                            const float* Dskip, const float* dt_bias, void* y, void* stream, bool zoh,
+                            bool dt_row = false) {
   ss_status st = check_sizes(batch, dim, dstate, 1, io);
   if (st != SS_OK) return st;
   if ((__int128)batch * dim > ((__int128)1 << 34))
@@ -405,7 +409,7 @@ ss_status state_update_impl(int64_t batch, int64_t dim, int dstate, ss_dtype io,
   if (dt_bias && !aligned(dt_bias, 4)) return fail(SS_ERR_INVALID_ARG, "dt_bias is not 4-byte aligned");
   const int64_t eb = elem_bytes(io);
   const int64_t tok = batch * dim * eb;
-  const Range ins[] = {rng("x", x, tok), rng("dt", dt, tok), rng("z", z, tok),
+  const Range ins[] = {rng("x", x, tok), rng("dt", dt, dt_row ? batch * eb : tok), rng("z", z, tok),
                        rng("B", B, batch * dstate * eb), rng("C", C, batch * dstate * eb),
                        rng("A", A, dim * dstate * 4), rng("Dskip", Dskip, dim * 4),
                        rng("dt_bias", dt_bias, dim * 4)};
@@ -414,7 +418,7 @@ ss_status state_update_impl(int64_t batch, int64_t dim, int dstate, ss_dtype io,
     for (const Range& i : ins)
       if (overlap(o, i)) return fail(SS_ERR_INVALID_ARG, "%s overlaps input %s", o.name, i.name);
   if (overlap(outs[0], outs[1])) return fail(SS_ERR_INVALID_ARG, "state overlaps y");
-  hipError_t e = ssscan::launch_state_update(batch, dim, dstate, io_code(io), zoh, state, x, dt, z, B, C, A, Dskip,
+  hipError_t e = ssscan::launch_state_update(batch, dim, dstate, io_code(io), zoh, dt_row, state, x, dt, z, B, C, A, Dskip,
                                              dt_bias, y, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "state_update launch");
   return SS_OK;
@@ -693,6 +697,26 @@ ss_status ss_state_update_zoh(int64_t batch, int64_t dim, int dstate, ss_dtype i
                               const void* dt, const void* z, const void* B, const void* C, const float* A,
                               const float* Dskip, const float* dt_bias, void* y, void* stream) {
   return state_update_impl(batch, dim, dstate, io, state, x, dt, z, B, C, A, Dskip, dt_bias, y, stream, true);
+}
+
+ss_status ss_scan_fwd_ex(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io, uint32_t flags,
+                         const void* x, const void* dt, const void* z, const void* B, const void* C, const float* A,
+                         const float* Dskip, const float* dt_bias, const float* h0, void* y, float* h_final,
+                         void* workspace, size_t workspace_bytes, const ss_scan_plan* plan, void* stream) {
+  if (flags & ~(uint32_t)(SS_FLAG_ZOH | SS_FLAG_DT_PER_ROW))
+    return fail(SS_ERR_UNSUPPORTED, "unknown flags 0x%x", (unsigned)flags);
+  return scan_fwd_impl(batch, dim, dstate, seqlen, io, x, dt, z, B, C, A, Dskip, dt_bias, h0, y, h_final,
+                       workspace, workspace_bytes, plan, stream, (flags & SS_FLAG_ZOH) != 0,
+                       (flags & SS_FLAG_DT_PER_ROW) != 0);
+}
+
+ss_status ss_state_update_ex(int64_t batch, int64_t dim, int dstate, ss_dtype io, uint32_t flags, float* state,
+                             const void* x, const void* dt, const void* z, const void* B, const void* C,
+                             const float* A, const float* Dskip, const float* dt_bias, void* y, void* stream) {
+  if (flags & ~(uint32_t)(SS_FLAG_ZOH | SS_FLAG_DT_PER_ROW))
+    return fail(SS_ERR_UNSUPPORTED, "unknown flags 0x%x", (unsigned)flags);
+  return state_update_impl(batch, dim, dstate, io, state, x, dt, z, B, C, A, Dskip, dt_bias, y, stream,
+                           (flags & SS_FLAG_ZOH) != 0, (flags & SS_FLAG_DT_PER_ROW) != 0);
 }
 
 ss_status ss_scan_shard_state(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io, const void* x,

@@ -21,6 +21,7 @@ struct ScanDims {
   int32_t io;           // IoType
   int32_t vec;          // 1: every lane's span of a row is aligned for one vector access
   int32_t lanes;        // lanes per channel (1 or 2); each lane owns dstate/(groups*lanes) states
+  int32_t dt_row;       // 1: dt is (batch, seqlen), one value per token shared by a row's channels
 };
 
 struct ScanPtrs {
@@ -102,7 +103,7 @@ hipError_t launch_shard_combine(int64_t batch, int64_t dim, int dstate, int64_t 
                                 hipStream_t s);
 hipError_t launch_scan_bwd(const BwdDims& dm, const BwdPtrs& p, hipStream_t s);
 hipError_t launch_fill_zero(float* dst, int64_t n, hipStream_t s);
-hipError_t launch_state_update(int64_t batch, int64_t dim, int dstate, int io, bool zoh, float* state,
+hipError_t launch_state_update(int64_t batch, int64_t dim, int dstate, int io, bool zoh, bool dt_row, float* state,
                                const void* x, const void* dt, const void* z, const void* B, const void* C,
                                const float* A, const float* Dskip, const float* dt_bias, void* y,
                                hipStream_t s);

@@ -88,6 +88,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(5, 10)))
   const int64_t t1 = (t0 + dm.chunk_len < L) ? t0 + dm.chunk_len : L;
   const int64_t ch = b * dm.dim + dc;
   const int64_t row = ch * L;
+  const int64_t dt_row = dm.dt_row ? b * L : row;   // dt per (row, token) is shared by the row's channels
   const bool vec = dm.vec != 0;
   const bool has_z = z != nullptr;
 
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(5, 10)))
     const int64_t tf = own_first(t0);
     const int valid = own_valid(tf);
     load_span<IO, SPAN>(x, row + tf, valid, vec, cx);
-    load_span<IO, SPAN>(dt, row + tf, valid, vec, cdt);
+    load_span<IO, SPAN>(dt, dt_row + tf, valid, vec, cdt);
     if (has_z) load_span<IO, SPAN>(z, row + tf, valid, vec, cz);
     load_bc_tile(t0, t0 + T <= t1);
   }
@@ -166,14 +167,14 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(5, 10)))
     if (vec && ts + 2 * T <= t1) {
       const int64_t tn = tf + T;
       load_span<IO, SPAN>(x, row + tn, SPAN, true, cx);
-      load_span<IO, SPAN>(dt, row + tn, SPAN, true, cdt);
+      load_span<IO, SPAN>(dt, dt_row + tn, SPAN, true, cdt);
       if (has_z) load_span<IO, SPAN>(z, row + tn, SPAN, true, cz);
       load_bc_tile(ts + T, true);
     } else if (ts + T < t1) {
       const int64_t tn = tf + T;
       const int validn = own_valid(tn);
       load_span<IO, SPAN>(x, row + tn, validn, vec, cx);
-      load_span<IO, SPAN>(dt, row + tn, validn, vec, cdt);
+      load_span<IO, SPAN>(dt, dt_row + tn, validn, vec, cdt);
       if (has_z) load_span<IO, SPAN>(z, row + tn, validn, vec, cz);
       load_bc_tile(ts + T, ts + 2 * T <= t1);
     }

@@ -66,6 +66,7 @@ struct Item {
 template <int N, typename IO>
 struct Operands {
   int64_t dim, row_items;
+  bool dt_row;   // dt is (batch): one value per row, shared by its channels
   float* __restrict__ state;
   const typename IO::T* __restrict__ x;
   const typename IO::T* __restrict__ dt;
@@ -107,7 +108,7 @@ __device__ __forceinline__ Item<Q> fetch(const Operands<N, IO>& o, int64_t b, ui
   load_q<IO, Q>(o.B + b * N + r.j * Q, r.bq);
   load_q<IO, Q>(o.C + b * N + r.j * Q, r.cq);
   r.xv = load_one<IO>(o.x, r.ch);
-  r.dtv = load_one<IO>(o.dt, r.ch);
+  r.dtv = load_one<IO>(o.dt, o.dt_row ? b : r.ch);
   r.zl = load_one<IO>(o.z ? o.z : o.x, r.ch);
   r.bl = (o.dt_bias ? o.dt_bias : o.A)[d];
   r.sl = (o.Dskip ? o.Dskip : o.A)[d];
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(256) void state_update_kernel(int64_t batch, uint32
 }
 
 template <int N, typename IO, bool ZOH>
-hipError_t launch_t(int64_t batch, int64_t dim, float* state, const void* x, const void* dt, const void* z,
+hipError_t launch_t(int64_t batch, int64_t dim, bool dt_row, float* state, const void* x, const void* dt, const void* z,
                     const void* B, const void* C, const float* A, const float* Dskip, const float* dt_bias, void* y,
                     hipStream_t s) {
   using E = typename IO::T;
@@ -203,7 +204,7 @@ hipError_t launch_t(int64_t batch, int64_t dim, float* state, const void* x, con
   const int64_t grid_waves = blocks * kWavesPerBlock;
   const uint32_t stride_rows = (uint32_t)(grid_waves / pieces);
   const uint32_t stride_pieces = (uint32_t)(grid_waves % pieces);
-  const Operands<N, IO> o{dim, dim * K, state, (const E*)x, (const E*)dt, (const E*)z,
+  const Operands<N, IO> o{dim, dim * K, dt_row, state, (const E*)x, (const E*)dt, (const E*)z,
                           (const E*)B, (const E*)C, A, Dskip, dt_bias, (E*)y};
   hipLaunchKernelGGL((state_update_kernel<N, IO, ZOH>), dim3((unsigned)blocks),
                      dim3(64 * kWavesPerBlock), 0, s, batch, (uint32_t)pieces, stride_rows, stride_pieces, o);
@@ -211,30 +212,31 @@ hipError_t launch_t(int64_t batch, int64_t dim, float* state, const void* x, con
 }
 
 template <typename IO, bool ZOH>
-hipError_t launch_n(int64_t batch, int64_t dim, int dstate, float* state, const void* x, const void* dt, const void* z,
+hipError_t launch_n(int64_t batch, int64_t dim, bool dt_row, int dstate, float* state, const void* x, const void* dt,
+                    const void* z,
                     const void* B, const void* C, const float* A, const float* Dskip, const float* dt_bias, void* y,
                     hipStream_t s) {
   switch (dstate) {
-    case 1: return launch_t<1, IO, ZOH>(batch, dim, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
-    case 2: return launch_t<2, IO, ZOH>(batch, dim, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
-    case 4: return launch_t<4, IO, ZOH>(batch, dim, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
-    case 8: return launch_t<8, IO, ZOH>(batch, dim, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
-    case 16: return launch_t<16, IO, ZOH>(batch, dim, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
+    case 1: return launch_t<1, IO, ZOH>(batch, dim, dt_row, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
+    case 2: return launch_t<2, IO, ZOH>(batch, dim, dt_row, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
+    case 4: return launch_t<4, IO, ZOH>(batch, dim, dt_row, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
+    case 8: return launch_t<8, IO, ZOH>(batch, dim, dt_row, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
+    case 16: return launch_t<16, IO, ZOH>(batch, dim, dt_row, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_state_update(int64_t batch, int64_t dim, int dstate, int io, bool zoh, float* state,
+hipError_t launch_state_update(int64_t batch, int64_t dim, int dstate, int io, bool zoh, bool dt_row, float* state,
                                const void* x, const void* dt, const void* z, const void* B, const void* C,
                                const float* A, const float* Dskip, const float* dt_bias, void* y, hipStream_t s) {
   if (io == kIoBf16) {
-    return zoh ? launch_n<BF16, true>(batch, dim, dstate, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s)
-               : launch_n<BF16, false>(batch, dim, dstate, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
+    return zoh ? launch_n<BF16, true>(batch, dim, dt_row, dstate, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s)
+               : launch_n<BF16, false>(batch, dim, dt_row, dstate, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
   }
-  return zoh ? launch_n<F32, true>(batch, dim, dstate, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s)
-             : launch_n<F32, false>(batch, dim, dstate, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
+  return zoh ? launch_n<F32, true>(batch, dim, dt_row, dstate, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s)
+             : launch_n<F32, false>(batch, dim, dt_row, dstate, state, x, dt, z, B, C, A, Dskip, dt_bias, y, s);
 }
 
 }  // namespace ssscan

@@ -42,7 +42,8 @@ def scan_fwd(x, dt, B, C, A, z=None, Dskip=None, dt_bias=None, h0=None, *, plan=
              y=None, h_final=None, return_final_state=True, zoh=False):
     """Selective scan over full sequences (zoh=True: zero-order-hold input term).
 
-    x, dt, z: (batch, D, L); B, C: (batch, N, L) — all float32 or all bfloat16;
+    x, z: (batch, D, L); dt: (batch, D, L), or (batch, L) for one value per row and
+    token shared by the row's channels; B, C: (batch, N, L) — all float32 or all bfloat16;
     A: (D, N) float32; Dskip, dt_bias: (D,) float32; h0: (batch, D, N) float32.
     Returns (y, h_final); h_final is None when return_final_state is False.
     """
@@ -54,8 +55,9 @@ def scan_fwd(x, dt, B, C, A, z=None, Dskip=None, dt_bias=None, h0=None, *, plan=
     batch, dim, L = x.shape
     N = A.shape[1]
     io = _IO[x.dtype]
+    dt_row = dt.dim() == 2
     _need(x, "x", x.dtype, (batch, dim, L), dev)
-    _need(dt, "dt", x.dtype, (batch, dim, L), dev)
+    _need(dt, "dt", x.dtype, (batch, L) if dt_row else (batch, dim, L), dev)
     _need(z, "z", x.dtype, (batch, dim, L), dev)
     _need(B, "B", x.dtype, (batch, N, L), dev)
     _need(C, "C", x.dtype, (batch, N, L), dev)
@@ -74,10 +76,13 @@ def scan_fwd(x, dt, B, C, A, z=None, Dskip=None, dt_bias=None, h0=None, *, plan=
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
     if workspace.numel() < nbytes:
         raise ValueError("workspace has %d bytes, %d needed" % (workspace.numel(), nbytes))
-    fn = _b.ss_scan_fwd_zoh if zoh else _b.ss_scan_fwd
-    fn(batch, dim, N, L, io, _ptr(x), _ptr(dt), _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(Dskip),
-                   _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_final), _ptr(workspace), workspace.numel(),
-                   plan, _stream(dev))
+    args = (_ptr(x), _ptr(dt), _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(Dskip), _ptr(dt_bias), _ptr(h0), _ptr(y),
+            _ptr(h_final), _ptr(workspace), workspace.numel(), plan, _stream(dev))
+    if dt_row:
+        flags = _b.SS_FLAG_DT_PER_ROW | (_b.SS_FLAG_ZOH if zoh else 0)
+        _b.ss_scan_fwd_ex(batch, dim, N, L, io, flags, *args)
+    else:
+        (_b.ss_scan_fwd_zoh if zoh else _b.ss_scan_fwd)(batch, dim, N, L, io, *args)
     return y, h_final
 
 
@@ -85,7 +90,8 @@ def state_update(state, x, dt, B, C, A, z=None, Dskip=None, dt_bias=None, *, y=N
     """One decode step; ``state`` (batch, D, N) float32 is updated in place (zoh=True:
     zero-order-hold input term).
 
-    x, dt, z: (batch, D); B, C: (batch, N) in float32 or bfloat16.  Returns y (batch, D).
+    x, z: (batch, D); dt: (batch, D), or (batch,) shared by a row's channels;
+    B, C: (batch, N) in float32 or bfloat16.  Returns y (batch, D).
     """
     if x.dtype not in _IO:
         raise TypeError("x must be float32 or bfloat16")
@@ -95,7 +101,8 @@ def state_update(state, x, dt, B, C, A, z=None, Dskip=None, dt_bias=None, *, y=N
     batch, dim = x.shape
     N = A.shape[1]
     _need(state, "state", torch.float32, (batch, dim, N), dev)
-    _need(dt, "dt", x.dtype, (batch, dim), dev)
+    dt_row = dt.dim() == 1
+    _need(dt, "dt", x.dtype, (batch,) if dt_row else (batch, dim), dev)
     _need(z, "z", x.dtype, (batch, dim), dev)
     _need(B, "B", x.dtype, (batch, N), dev)
     _need(C, "C", x.dtype, (batch, N), dev)
@@ -105,9 +112,13 @@ def state_update(state, x, dt, B, C, A, z=None, Dskip=None, dt_bias=None, *, y=N
     if y is None:
         y = torch.empty((batch, dim), dtype=x.dtype, device=dev)
     _need(y, "y", x.dtype, (batch, dim), dev)
-    fn = _b.ss_state_update_zoh if zoh else _b.ss_state_update
-    fn(batch, dim, N, _IO[x.dtype], _ptr(state), _ptr(x), _ptr(dt), _ptr(z), _ptr(B), _ptr(C),
-                       _ptr(A), _ptr(Dskip), _ptr(dt_bias), _ptr(y), _stream(dev))
+    args = (_ptr(state), _ptr(x), _ptr(dt), _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(Dskip), _ptr(dt_bias), _ptr(y),
+            _stream(dev))
+    if dt_row:
+        flags = _b.SS_FLAG_DT_PER_ROW | (_b.SS_FLAG_ZOH if zoh else 0)
+        _b.ss_state_update_ex(batch, dim, N, _IO[x.dtype], flags, *args)
+    else:
+        (_b.ss_state_update_zoh if zoh else _b.ss_state_update)(batch, dim, N, _IO[x.dtype], *args)
     return y
 
 

@@ -249,6 +249,23 @@ def test_shard_combine_validation(case, status):
     assert st == status, (st, b.last_error())
 
 
+def test_flags_validation():
+    (batch, dim, N, L, io), p, plan = _scan_args()
+    args = [p[k] for k in ("x", "dt", "z", "B", "C", "A", "Dskip", "dt_bias", "h0", "y", "h_final")]
+    st = b.lib.ss_scan_fwd_ex(batch, dim, N, L, io, 4, *args, p["workspace"], p["workspace_bytes"],
+                              b._plan_ptr(plan), None)
+    assert st == b.SS_ERR_UNSUPPORTED and "flags" in b.last_error()
+    st = b.lib.ss_state_update_ex(4, 64, 16, b.SS_BF16, 8, ALIGNED, ALIGNED + (1 << 30), ALIGNED + (1 << 31), None,
+                                  ALIGNED + (1 << 32), ALIGNED + (1 << 33), ALIGNED + (1 << 34), None, None,
+                                  ALIGNED + (1 << 35), None)
+    assert st == b.SS_ERR_UNSUPPORTED
+    # an output inside the per-row dt (batch * L elements) is rejected
+    st = b.lib.ss_scan_fwd_ex(batch, dim, N, L, io, b.SS_FLAG_DT_PER_ROW,
+                              *[p[k] for k in ("x", "dt", "z", "B", "C", "A", "Dskip", "dt_bias", "h0")],
+                              p["dt"] + 64, p["h_final"], p["workspace"], p["workspace_bytes"], b._plan_ptr(plan), None)
+    assert st == b.SS_ERR_INVALID_ARG and "overlaps input dt" in b.last_error()
+
+
 def test_timing_record_empty():
     b.ss_timing_enable(False)
     b.ss_timing_reset()
