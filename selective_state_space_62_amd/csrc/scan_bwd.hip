@@ -63,7 +63,7 @@ __device__ __forceinline__ float sigmoid2(float v2) {
 // fit on a CU, so the 2.8B-shaped layer's 1280 workgroups are all resident at
 // once on 256 CUs.
 template <int N, int G, int K, typename IO>
-__global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(5, 10))) void scan_bwd_kernel(
+__global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10))) void scan_bwd_kernel(
     const BwdDims dm, const BwdPtrs p) {
   using T = typename IO::T;
   constexpr int CPB = 64 / K;          // channels per workgroup
@@ -216,12 +216,14 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(5, 10)))
     const int nj = FULL ? CK : (int)(t1 - t0);
     const int64_t tf = t0 + j_own;
     const int valid = FULL ? kSpan : own_valid(k);
-    float xv[kSpan], dl[kSpan], v2[kSpan], zv[kSpan], dyv[kSpan];
+    float xv[kSpan], dl[kSpan], v2[kSpan];
     stage(valid, f, xv, dl, v2);
+    // z and dy of the owned tokens stay raw until the owners use them
+    uint32_t cz[SW], cdy[SW];
 #pragma unroll
-    for (int i = 0; i < kSpan; ++i) {
-      zv[i] = span_elem<IO>(f.z, i);
-      dyv[i] = act ? span_elem<IO>(f.dy, i) : 0.0f;   // padding tokens load as zero
+    for (int q = 0; q < SW; ++q) {
+      cz[q] = f.z[q];
+      cdy[q] = f.dy[q];
     }
     float hs[CK + 1][NS];   // hs[j] = the state before chunk token j
 #pragma unroll
@@ -252,7 +254,6 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(5, 10)))
     __syncthreads();
 
     // owners: r, dr = dy silu(z), dz = dy r silu'(z)
-    float drv[kSpan];
     {
       float dzv[kSpan];
 #pragma unroll
@@ -264,16 +265,18 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(5, 10)))
           for (int g = 0; g < G; ++g) r += s_pp[j][g][c].x;
         }
         r = fmaf(skip, xv[i], r);
+        const float dyv = act ? span_elem<IO>(cdy, i) : 0.0f;   // padding tokens load as zero
         float gate = 1.0f;
         dzv[i] = 0.0f;
         if (has_z) {
-          const float sz = sigmoid2(zv[i] * kLog2e);
-          gate = zv[i] * sz;
-          dzv[i] = dyv[i] * r * (sz * fmaf(zv[i], 1.0f - sz, 1.0f));
+          const float zv = span_elem<IO>(cz, i);
+          const float sz = sigmoid2(zv * kLog2e);
+          gate = zv * sz;
+          dzv[i] = dyv * r * (sz * fmaf(zv, 1.0f - sz, 1.0f));
         }
-        drv[i] = dyv[i] * gate;
-        dD_acc = fmaf(drv[i], xv[i], dD_acc);
-        s_dr[j][c] = drv[i];
+        const float drv = dyv * gate;
+        dD_acc = fmaf(drv, xv[i], dD_acc);
+        s_dr[j][c] = drv;
       }
       if (has_z && act && (FULL || valid > 0)) store_span<IO, kSpan>(static_cast<T*>(p.dz), row + tf, valid, vec, dzv);
     }
@@ -359,7 +362,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(5, 10)))
             sB += pv.y;
           }
         }
-        dxv[i] = fmaf(sB, dl[i], drv[i] * skip);
+        dxv[i] = fmaf(sB, s_dd[j][c].x, s_dr[j][c] * skip);   // Delta and dr of the owned token from LDS
         const float dv = fmaf(sB, xv[i], ddp) * sigmoid2(v2[i]);
         ddtv[i] = dv;
         if (FULL || i < valid) dbias_acc += dv;
