@@ -63,6 +63,16 @@ def algorithmic_bytes_per_tokch(cfg) -> float:
     return per + shared / cfg.tokch
 
 
+def algorithmic_bytes_bwd(cfg) -> float:
+    """HBM bytes one backward call must move: x, dt, z and dy read once, dx, ddt and dz
+    written once; B and C read and dB, dC written once; the parameters, h0, dh_final
+    and their gradients once."""
+    eb = 4 if cfg.io == "f32" else 2
+    nbd, nbnl = cfg.batch * cfg.dim, cfg.batch * cfg.dstate * cfg.seqlen
+    return (7 * eb * cfg.tokch + 4 * eb * nbnl + 2 * 4 * cfg.dim * (cfg.dstate + 2)
+            + 3 * 4 * nbd * cfg.dstate)
+
+
 def algorithmic_slots_per_tokch(N: int) -> float:
     """VALU issue slots per (token, channel): per state component a multiply for
     Delta*A, the exponential, a multiply for Delta*x*B, the state FMA and the
@@ -201,6 +211,7 @@ def run_bwd(ss, torch, dev, cfg, t, A, dskip, bias, fwd_kernel_ms, calls=20):
             "kernel_ms": round(kms, 5),
             "value": round(cfg.tokch / (kms * 1e-3) / 1e9, 3), "unit": "Gtok·ch/s",
             "ratio_to_forward": round(kms / fwd_kernel_ms, 3),
+            "hbm_gbs": round(algorithmic_bytes_bwd(cfg) / (kms * 1e-3) / 1e9, 1),
             "workspace_bytes": ws.numel(), "traffic": measured_traffic(cfg, "bwd")}
 
 
@@ -345,28 +356,11 @@ def main():
         "roofline_hbm": {"achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "bytes_per_tokch": round(bpt, 4)},
     }
-    if not args.no_zoh:
-        # the same workload through the zero-order-hold entry point (secondary)
-        for _ in range(20):
-            ss.scan_fwd(t["x"], t["dt"], t["B"], t["C"], A, z=t["z"], Dskip=dskip, dt_bias=bias, workspace=ws, y=y,
-                        h_final=hf, zoh=True)
-        torch.cuda.synchronize()
-        ss.ss_timing_reset()
-        ss.ss_timing_enable(True)
-        for _ in range(20):
-            ss.scan_fwd(t["x"], t["dt"], t["B"], t["C"], A, z=t["z"], Dskip=dskip, dt_bias=bias, workspace=ws, y=y,
-                        h_final=hf, zoh=True)
-        torch.cuda.synchronize()
-        ss.ss_timing_enable(False)
-        zms, zn = ss.ss_timing_read()
-        ss.ss_timing_reset()
-        out["zoh"] = {"entry_point": "ss_scan_fwd_zoh", "kernel_ms": round(zms / zn, 5),
-                      "value": round(tokch / (zms / zn * 1e-3) / 1e9, 3), "unit": "Gtok·ch/s"}
     if not args.no_dt_row:
         # dt shared by a row's channels (SS_FLAG_DT_PER_ROW): the same workload with
         # one dt row per batch row (secondary)
         dtr = t["dt"][:, 0, :].contiguous()
-        for _ in range(20):
+        for _ in range(100):
             ss.scan_fwd(t["x"], dtr, t["B"], t["C"], A, z=t["z"], Dskip=dskip, dt_bias=bias, workspace=ws, y=y,
                         h_final=hf)
         torch.cuda.synchronize()
@@ -385,6 +379,23 @@ def main():
                              "value": round(tokch / (rms / rn * 1e-3) / 1e9, 3), "unit": "Gtok·ch/s",
                              "algorithmic_bytes": int(rbytes),
                              "hbm_gbs": round(rbytes / (rms / rn * 1e-3) / 1e9, 1)}
+    if not args.no_zoh:
+        # the same workload through the zero-order-hold entry point (secondary)
+        for _ in range(20):
+            ss.scan_fwd(t["x"], t["dt"], t["B"], t["C"], A, z=t["z"], Dskip=dskip, dt_bias=bias, workspace=ws, y=y,
+                        h_final=hf, zoh=True)
+        torch.cuda.synchronize()
+        ss.ss_timing_reset()
+        ss.ss_timing_enable(True)
+        for _ in range(20):
+            ss.scan_fwd(t["x"], t["dt"], t["B"], t["C"], A, z=t["z"], Dskip=dskip, dt_bias=bias, workspace=ws, y=y,
+                        h_final=hf, zoh=True)
+        torch.cuda.synchronize()
+        ss.ss_timing_enable(False)
+        zms, zn = ss.ss_timing_read()
+        ss.ss_timing_reset()
+        out["zoh"] = {"entry_point": "ss_scan_fwd_zoh", "kernel_ms": round(zms / zn, 5),
+                      "value": round(tokch / (zms / zn * 1e-3) / 1e9, 3), "unit": "Gtok·ch/s"}
     if not args.no_bwd:
         out["bwd"] = run_bwd(ss, torch, dev, cfg, t, A, dskip, bias, kern_ms)
     if args.cp_shards > 1:
