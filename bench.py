@@ -203,6 +203,37 @@ def run_bwd(ss, torch, dev, cfg, t, A, dskip, bias, fwd_kernel_ms, calls=20):
     ms, n = ss.ss_timing_read()
     ss.ss_timing_reset()
     kms = ms / n
+
+    # a training step's pair: the forward stores the checkpoints, the backward reads them
+    ck = torch.empty(ss.ckpt_numel(cfg.batch, cfg.dim, cfg.dstate, cfg.seqlen), dtype=torch.float32, device=dev)
+    fws = torch.empty(max(ss.workspace_bytes(cfg.batch, cfg.dim, cfg.dstate, cfg.seqlen, t["x"].dtype), 256),
+                      dtype=torch.uint8, device=dev)
+
+    def timed_pair(with_ckpt):
+        def fwd():
+            ss.scan_fwd(t["x"], t["dt"], t["B"], t["C"], A, z=t["z"], Dskip=dskip, dt_bias=bias, workspace=fws,
+                        ckpt=ck if with_ckpt else None)
+
+        def bwd():
+            ss.scan_bwd(t["x"], t["dt"], t["B"], t["C"], A, dy, z=t["z"], Dskip=dskip, dt_bias=bias, workspace=ws,
+                        ckpt=ck if with_ckpt else None)
+        out = []
+        for fn in (fwd, bwd):
+            for _ in range(calls):
+                fn()
+            torch.cuda.synchronize()
+            ss.ss_timing_reset()
+            ss.ss_timing_enable(True)
+            for _ in range(calls):
+                fn()
+            torch.cuda.synchronize()
+            ss.ss_timing_enable(False)
+            m, c = ss.ss_timing_read()
+            ss.ss_timing_reset()
+            out.append(m / c)
+        return out
+    f_ck, b_ck = timed_pair(True)
+    f_no, b_no = timed_pair(False)
     spt = algorithmic_slots_bwd_per_tokch(cfg.dstate)
     ach = spt * cfg.tokch / (kms * 1e-3) / 1e12
     return {"entry_point": "ss_scan_bwd", "kernel": "scan_bwd_kernel<16,4,2,%s> + reduce kernels" % cfg.io,
@@ -212,7 +243,12 @@ def run_bwd(ss, torch, dev, cfg, t, A, dskip, bias, fwd_kernel_ms, calls=20):
             "value": round(cfg.tokch / (kms * 1e-3) / 1e9, 3), "unit": "Gtok·ch/s",
             "ratio_to_forward": round(kms / fwd_kernel_ms, 3),
             "hbm_gbs": round(algorithmic_bytes_bwd(cfg) / (kms * 1e-3) / 1e9, 1),
-            "workspace_bytes": ws.numel(), "traffic": measured_traffic(cfg, "bwd")}
+            "workspace_bytes": ws.numel(), "traffic": measured_traffic(cfg, "bwd"),
+            "training_step": {"fwd_kernel_ms": round(f_no, 5), "bwd_kernel_ms": round(b_no, 5),
+                              "fwd_storing_checkpoints_kernel_ms": round(f_ck, 5),
+                              "bwd_from_checkpoints_kernel_ms": round(b_ck, 5),
+                              "step_ms": round(f_no + b_no, 5), "step_with_checkpoints_ms": round(f_ck + b_ck, 5),
+                              "checkpoint_bytes": ck.numel() * 4}}
 
 
 def run_cp(ss, torch, cfg, t, A, dskip, bias, G, reps=10):

@@ -156,13 +156,19 @@ ss_status ss_state_update_zoh(int64_t batch, int64_t dim, int dstate, ss_dtype i
  * Unknown bits return SS_ERR_UNSUPPORTED.  Everything else is as for ss_scan_fwd
  * and ss_state_update. */
 typedef enum { SS_FLAG_ZOH = 1u, SS_FLAG_DT_PER_ROW = 2u } ss_flags;
+/* ckpt (nullable, fp32, 16-byte aligned, ss_scan_ckpt_bytes long, no overlap
+ * with anything else) receives the state entering every chunk of the backward
+ * pass (16 tokens at dstate >= 8), laid out (batch, chunks, dim, dstate): a
+ * training step's forward hands them to ss_scan_bwd_ex, which then skips its own
+ * checkpoint sweep.  Not with SS_FLAG_ZOH (the backward is first-order). */
 ss_status ss_scan_fwd_ex(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io, uint32_t flags,
                          const void* x, const void* dt, const void* z,
                          const void* B, const void* C, const float* A,
                          const float* Dskip, const float* dt_bias, const float* h0,
-                         void* y, float* h_final,
+                         void* y, float* h_final, float* ckpt,
                          void* workspace, size_t workspace_bytes,
                          const ss_scan_plan* plan, void* stream);
+size_t ss_scan_ckpt_bytes(int64_t batch, int64_t dim, int dstate, int64_t seqlen);
 ss_status ss_state_update_ex(int64_t batch, int64_t dim, int dstate, ss_dtype io, uint32_t flags, float* state,
                              const void* x, const void* dt, const void* z,
                              const void* B, const void* C, const float* A,
@@ -241,6 +247,19 @@ ss_status ss_scan_bwd(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss
                       void* dx, void* ddt, void* dz, void* dB, void* dC,
                       float* dA, float* dDskip, float* ddt_bias, float* dh0,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* ss_scan_bwd with options: flags must be 0 (reserved); ckpt (nullable) holds
+ * the checkpoints a ss_scan_fwd_ex call stored for the same inputs (same x, dt,
+ * B, A, dt_bias, h0), and the backward then reads them instead of recomputing
+ * them.  Everything else is as for ss_scan_bwd; results are identical. */
+ss_status ss_scan_bwd_ex(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io, uint32_t flags,
+                         const void* x, const void* dt, const void* z,
+                         const void* B, const void* C, const float* A,
+                         const float* Dskip, const float* dt_bias, const float* h0,
+                         const void* dy, const float* dh_final, const float* ckpt,
+                         void* dx, void* ddt, void* dz, void* dB, void* dC,
+                         float* dA, float* dDskip, float* ddt_bias, float* dh0,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* Opt-in timing of the main scan kernels (for benchmarks).  While enabled, each
  * ss_scan_fwd call records HIP events around its scan kernel launches on its

@@ -70,8 +70,12 @@ def _load():
     lib.ss_scan_bwd.restype = _int
     lib.ss_scan_bwd.argtypes = [_i64, _i64, _int, _i64, _int] + [_vp] * 21 + [ctypes.c_size_t, _vp]
     lib.ss_scan_fwd_ex.restype = _int
-    lib.ss_scan_fwd_ex.argtypes = ([_i64, _i64, _int, _i64, _int, ctypes.c_uint32] + [_vp] * 11
+    lib.ss_scan_fwd_ex.argtypes = ([_i64, _i64, _int, _i64, _int, ctypes.c_uint32] + [_vp] * 12
                                    + [_vp, ctypes.c_size_t, ctypes.POINTER(ss_scan_plan), _vp])
+    lib.ss_scan_ckpt_bytes.restype = ctypes.c_size_t
+    lib.ss_scan_ckpt_bytes.argtypes = [_i64, _i64, _int, _i64]
+    lib.ss_scan_bwd_ex.restype = _int
+    lib.ss_scan_bwd_ex.argtypes = [_i64, _i64, _int, _i64, _int, ctypes.c_uint32] + [_vp] * 22 + [ctypes.c_size_t, _vp]
     lib.ss_state_update_ex.restype = _int
     lib.ss_state_update_ex.argtypes = [_i64, _i64, _int, _int, ctypes.c_uint32] + [_vp] * 11
     lib.ss_scan_shard_state.restype = _int
@@ -174,9 +178,20 @@ SS_FLAG_DT_PER_ROW = 2
 
 
 def ss_scan_fwd_ex(batch, dim, dstate, seqlen, io, flags, x, dt, z, B, C, A, Dskip, dt_bias, h0, y, h_final,
-                   workspace, workspace_bytes, plan=None, stream=None):
+                   ckpt, workspace, workspace_bytes, plan=None, stream=None):
     _check(lib.ss_scan_fwd_ex(batch, dim, dstate, seqlen, io, flags, x, dt, z, B, C, A, Dskip, dt_bias, h0, y,
-                              h_final, workspace, workspace_bytes, _plan_ptr(plan), stream))
+                              h_final, ckpt, workspace, workspace_bytes, _plan_ptr(plan), stream))
+
+
+def ss_scan_ckpt_bytes(batch, dim, dstate, seqlen) -> int:
+    return int(lib.ss_scan_ckpt_bytes(batch, dim, dstate, seqlen))
+
+
+def ss_scan_bwd_ex(batch, dim, dstate, seqlen, io, flags, x, dt, z, B, C, A, Dskip, dt_bias, h0, dy, dh_final, ckpt,
+                   dx, ddt, dz, dB, dC, dA, dDskip, ddt_bias, dh0, workspace, workspace_bytes, stream=None):
+    _check(lib.ss_scan_bwd_ex(batch, dim, dstate, seqlen, io, flags, x, dt, z, B, C, A, Dskip, dt_bias, h0, dy,
+                              dh_final, ckpt, dx, ddt, dz, dB, dC, dA, dDskip, ddt_bias, dh0, workspace,
+                              workspace_bytes, stream))
 
 
 def ss_state_update_ex(batch, dim, dstate, io, flags, state, x, dt, z, B, C, A, Dskip, dt_bias, y, stream=None):

@@ -265,7 +265,7 @@ ss_status scan_fwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, 
                         const void* dt, const void* z, const void* B, const void* C, const float* A,
                         const float* Dskip, const float* dt_bias, const float* h0, void* y, float* h_final,
                         void* workspace, size_t workspace_bytes, const ss_scan_plan* plan, void* stream, bool zoh,
-                        bool dt_row = false) {
+                        bool dt_row = false, float* ckpt = nullptr) {
   ss_status st = check_sizes(batch, dim, dstate, seqlen, io);
   if (st != SS_OK) return st;
   Plan p;
@@ -304,14 +304,21 @@ ss_status scan_fwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, 
   const Range ins[] = {rng("x", x, seq_bytes), rng("dt", dt, dt_bytes), rng("z", z, seq_bytes),
                        rng("B", B, bc_bytes), rng("C", C, bc_bytes), rng("A", A, dim * dstate * 4),
                        rng("Dskip", Dskip, dim * 4), rng("dt_bias", dt_bias, dim * 4), rng("h0", h0, st_bytes)};
+  if (ckpt) {
+    if (zoh) return fail(SS_ERR_UNSUPPORTED, "checkpoints are for the first-order backward pass (no ZOH)");
+    if (!aligned(ckpt, 16)) return fail(SS_ERR_INVALID_ARG, "ckpt is not 16-byte aligned");
+  }
+  const int64_t ck_len = ssscan::bwd_chunk_len(dstate);
+  const int64_t ck_count = (seqlen + ck_len - 1) / ck_len;
   const Range outs[] = {rng("y", y, seq_bytes), rng("h_final", h_final, st_bytes),
-                        rng("workspace", workspace, seqlen > 0 ? (int64_t)wl.total : 0)};
+                        rng("workspace", workspace, seqlen > 0 ? (int64_t)wl.total : 0),
+                        rng("ckpt", ckpt, batch * dim * ck_count * dstate * 4)};
   for (const Range& o : outs) {
     for (const Range& i : ins)
       if (overlap(o, i)) return fail(SS_ERR_INVALID_ARG, "%s overlaps input %s", o.name, i.name);
   }
-  for (int i = 0; i < 3; ++i)
-    for (int j = i + 1; j < 3; ++j)
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
       if (overlap(outs[i], outs[j])) return fail(SS_ERR_INVALID_ARG, "%s overlaps %s", outs[i].name, outs[j].name);
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -335,6 +342,7 @@ ss_status scan_fwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, 
   dm.io = io_code(io);
   dm.vec = (seqlen % ssscan::span_len(p.lanes, dm.io)) == 0 ? 1 : 0;
   dm.dt_row = dt_row ? 1 : 0;
+  dm.ck_count = ck_count;
 
   const int64_t cpb = 64 / p.lanes;
   const int64_t nwg = ((dim + cpb - 1) / cpb) * batch * p.num_chunks;
@@ -352,6 +360,7 @@ ss_status scan_fwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, 
   sp.h0 = h0;
   sp.y = y;
   sp.h_final = h_final;
+  sp.ckpt = ckpt;
   float* bcw = reinterpret_cast<float*>(ws + wl.bc);
 
   hipError_t e = ssscan::launch_prep_bc(dm, B, C, bcw, s);
@@ -533,10 +542,11 @@ ss_status scan_bwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, 
                         const float* Dskip, const float* dt_bias, const float* h0, const void* dy,
                         const float* dh_final, void* dx, void* ddt, void* dz, void* dB, void* dC, float* dA,
                         float* dDskip, float* ddt_bias, float* dh0, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+                        void* stream, const float* ckpt = nullptr) {
   ss_status st = check_sizes(batch, dim, dstate, seqlen, io);
   if (st != SS_OK) return st;
   if (!A) return fail(SS_ERR_INVALID_ARG, "A is NULL");
+  if (ckpt && !aligned(ckpt, 16)) return fail(SS_ERR_INVALID_ARG, "ckpt is not 16-byte aligned");
   if (seqlen > 0) {
     const char* names[] = {"x", "dt", "B", "C", "dy", "dx", "ddt", "dB", "dC"};
     const void* req[] = {x, dt, B, C, dy, dx, ddt, dB, dC};
@@ -570,7 +580,8 @@ ss_status scan_bwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, 
   const Range ins[] = {rng("x", x, seq_bytes), rng("dt", dt, seq_bytes), rng("z", z, seq_bytes),
                        rng("B", B, bc_bytes), rng("C", C, bc_bytes), rng("A", A, dim * dstate * 4),
                        rng("Dskip", Dskip, dim * 4), rng("dt_bias", dt_bias, dim * 4), rng("h0", h0, st_bytes),
-                       rng("dy", dy, seq_bytes), rng("dh_final", dh_final, st_bytes)};
+                       rng("dy", dy, seq_bytes), rng("dh_final", dh_final, st_bytes),
+                       rng("ckpt", ckpt, batch * dim * wl.chunks * dstate * 4)};
   const Range outs[] = {rng("dx", dx, seq_bytes), rng("ddt", ddt, seq_bytes), rng("dz", dz, seq_bytes),
                         rng("dB", dB, bc_bytes), rng("dC", dC, bc_bytes), rng("dA", dA, dim * dstate * 4),
                         rng("dDskip", dDskip, dim * 4), rng("ddt_bias", ddt_bias, dim * 4),
@@ -622,6 +633,7 @@ ss_status scan_bwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, 
   dm.dstate = dstate;
   dm.io = io_code(io);
   dm.vec = (seqlen % 2) == 0 ? 1 : 0;
+  dm.have_ckpt = ckpt ? 1 : 0;
   ssscan::BwdPtrs bp{};
   bp.x = x;
   bp.dt = dt;
@@ -642,7 +654,7 @@ ss_status scan_bwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, 
   bp.dDskip = dDskip;
   bp.ddt_bias = ddt_bias;
   bp.dh0 = dh0;
-  bp.ckpt = reinterpret_cast<float*>(ws + wl.ckpt);
+  bp.ckpt = ckpt ? const_cast<float*>(ckpt) : reinterpret_cast<float*>(ws + wl.ckpt);
   bp.part = reinterpret_cast<float*>(ws + wl.part);
   bp.dA_p = reinterpret_cast<float*>(ws + wl.dA_p);
   bp.dD_p = reinterpret_cast<float*>(ws + wl.dD_p);
@@ -702,12 +714,19 @@ ss_status ss_state_update_zoh(int64_t batch, int64_t dim, int dstate, ss_dtype i
 ss_status ss_scan_fwd_ex(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io, uint32_t flags,
                          const void* x, const void* dt, const void* z, const void* B, const void* C, const float* A,
                          const float* Dskip, const float* dt_bias, const float* h0, void* y, float* h_final,
-                         void* workspace, size_t workspace_bytes, const ss_scan_plan* plan, void* stream) {
+                         float* ckpt, void* workspace, size_t workspace_bytes, const ss_scan_plan* plan,
+                         void* stream) {
   if (flags & ~(uint32_t)(SS_FLAG_ZOH | SS_FLAG_DT_PER_ROW))
     return fail(SS_ERR_UNSUPPORTED, "unknown flags 0x%x", (unsigned)flags);
   return scan_fwd_impl(batch, dim, dstate, seqlen, io, x, dt, z, B, C, A, Dskip, dt_bias, h0, y, h_final,
                        workspace, workspace_bytes, plan, stream, (flags & SS_FLAG_ZOH) != 0,
-                       (flags & SS_FLAG_DT_PER_ROW) != 0);
+                       (flags & SS_FLAG_DT_PER_ROW) != 0, ckpt);
+}
+
+size_t ss_scan_ckpt_bytes(int64_t batch, int64_t dim, int dstate, int64_t seqlen) {
+  if (check_sizes(batch, dim, dstate, seqlen, SS_F32) != SS_OK) return 0;
+  const int64_t ck = ssscan::bwd_chunk_len(dstate);
+  return (size_t)batch * dim * ((seqlen + ck - 1) / ck) * dstate * sizeof(float);
 }
 
 ss_status ss_state_update_ex(int64_t batch, int64_t dim, int dstate, ss_dtype io, uint32_t flags, float* state,
@@ -775,6 +794,18 @@ ss_status ss_scan_bwd(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss
                       void* stream) {
   return scan_bwd_impl(batch, dim, dstate, seqlen, io, x, dt, z, B, C, A, Dskip, dt_bias, h0, dy, dh_final, dx,
                        ddt, dz, dB, dC, dA, dDskip, ddt_bias, dh0, workspace, workspace_bytes, stream);
+}
+
+ss_status ss_scan_bwd_ex(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io, uint32_t flags,
+                         const void* x, const void* dt, const void* z, const void* B, const void* C, const float* A,
+                         const float* Dskip, const float* dt_bias, const float* h0, const void* dy,
+                         const float* dh_final, const float* ckpt, void* dx, void* ddt, void* dz, void* dB, void* dC,
+                         float* dA, float* dDskip, float* ddt_bias, float* dh0, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (flags != 0) return fail(SS_ERR_UNSUPPORTED, "unknown flags 0x%x (the backward is first-order, per-channel dt)",
+                              (unsigned)flags);
+  return scan_bwd_impl(batch, dim, dstate, seqlen, io, x, dt, z, B, C, A, Dskip, dt_bias, h0, dy, dh_final, dx,
+                       ddt, dz, dB, dC, dA, dDskip, ddt_bias, dh0, workspace, workspace_bytes, stream, ckpt);
 }
 
 ss_status ss_timing_enable(int enable) {

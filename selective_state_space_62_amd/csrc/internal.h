@@ -22,6 +22,7 @@ struct ScanDims {
   int32_t vec;          // 1: every lane's span of a row is aligned for one vector access
   int32_t lanes;        // lanes per channel (1 or 2); each lane owns dstate/(groups*lanes) states
   int32_t dt_row;       // 1: dt is (batch, seqlen), one value per token shared by a row's channels
+  int64_t ck_count;     // with ScanPtrs::ckpt: checkpoints per channel, ceil(seqlen / bwd_chunk_tokens(dstate))
 };
 
 struct ScanPtrs {
@@ -38,6 +39,7 @@ struct ScanPtrs {
   float* h_final;       // nullable
   float* agg_h;         // chunk end states from zero (batch, dim, num_chunks, dstate)
   float* agg_s;         // chunk sums of Delta (batch, dim, num_chunks)
+  float* ckpt;          // nullable: (batch, ck_count, dim, dstate) state entering every backward chunk
 };
 
 // Shape of one backward launch.
@@ -49,6 +51,7 @@ struct BwdDims {
   int32_t dstate;
   int32_t io;
   int32_t vec;          // 1: every lane's 2-token span of a row is aligned for one vector access
+  int32_t have_ckpt;    // 1: BwdPtrs::ckpt already holds the checkpoints (stored by the forward)
 };
 
 struct BwdPtrs {
@@ -71,7 +74,7 @@ struct BwdPtrs {
   float* dDskip;          // nullable
   float* ddt_bias;        // nullable
   float* dh0;             // nullable
-  float* ckpt;            // workspace: (batch, dim, chunks, dstate) state at every chunk start
+  float* ckpt;            // workspace: (batch, chunks, dim, dstate) state at every chunk start
   float* part;            // workspace: (batch, cblocks, seqlen, 2 dstate) dB/dC partial sums
   float* dA_p;            // workspace: (batch, dim, dstate) per-row sums
   float* dD_p;            // workspace: (batch, dim)
@@ -79,6 +82,10 @@ struct BwdPtrs {
 };
 
 // Backward plan: lanes per channel and chunk length (tokens) for a state size.
+// The chunk length is also the interval of the forward's stored checkpoints.
+constexpr int bwd_chunk_tokens(int dstate) {
+  return 2 * (dstate >= 4 ? 4 : dstate) * (dstate >= 8 ? 2 : 1);
+}
 int bwd_lanes_per_channel(int dstate);
 int bwd_chunk_len(int dstate);
 

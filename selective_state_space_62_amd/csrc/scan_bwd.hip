@@ -77,6 +77,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10)))
   static_assert(NS >= 1 && N % SG == 0, "G * K must divide N");
   static_assert(K == 1 || K == 2, "one or two lanes per channel");
   static_assert(CK * N <= THREADS, "one B/C piece per thread");
+  static_assert(CK == bwd_chunk_tokens(N), "the chunk length the forward's checkpoints assume");
 
   __shared__ float2 s_dd[CK][CPB];     // (Delta, Delta x) per token and channel
   __shared__ float s_bc[CK][2 * N];    // B_n, C_n of the chunk's tokens
@@ -116,7 +117,9 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10)))
   const float bias2 = p.dt_bias ? p.dt_bias[dc] * kLog2e : 0.0f;
   const float skip = p.Dskip ? p.Dskip[dc] : 0.0f;
   const float* __restrict__ bc_row = p.bc + b * L * (2 * N);
-  float* __restrict__ ck_row = p.ckpt + ch * nck * N + sg * NS;
+  // checkpoints (batch, chunk, dim, N): a workgroup's channels are contiguous per chunk
+  float* __restrict__ ck_row = p.ckpt + (b * nck * dm.dim + dc) * N + sg * NS;
+  const int64_t ck_stride = dm.dim * N;
 
   const int j_own = sg * kSpan;   // first token of a chunk this lane owns
   auto chunk_end = [&](int64_t k) { return (k * CK + CK < L) ? k * CK + CK : L; };
@@ -156,8 +159,9 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10)))
     if (tid < CK * N) reinterpret_cast<float2*>(&s_bc[0][0])[tid] = f.bc;
   };
 
-  // ---- 1. forward sweep: the state at every chunk start ----
-  {
+  // ---- 1. forward sweep: the state at every chunk start (unless the forward
+  // pass already stored them) ----
+  if (!dm.have_ckpt) {
     float h[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) h[s] = p.h0 ? p.h0[ch * N + sg * NS + s] : 0.0f;
@@ -168,7 +172,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10)))
       constexpr bool FULL = decltype(full_tag)::value;
       if (act) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) ck_row[k * N + s] = h[s];
+        for (int s = 0; s < NS; ++s) ck_row[k * ck_stride + s] = h[s];
       }
       float xv[kSpan], dl[kSpan], v2[kSpan];
       stage(FULL ? kSpan : own_valid(k), f, xv, dl, v2);
@@ -207,7 +211,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10)))
   fetch(nck - 1, true, f);
   float ckn[NS];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) ckn[s] = act ? ck_row[(nck - 1) * N + s] : 0.0f;
+  for (int s = 0; s < NS; ++s) ckn[s] = act ? ck_row[(nck - 1) * ck_stride + s] : 0.0f;
 
   auto chunk = [&](auto full_tag, int64_t k) {
     constexpr bool FULL = decltype(full_tag)::value;
@@ -231,7 +235,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10)))
     if (k > 0) {
       fetch(k - 1, true, f);
 #pragma unroll
-      for (int s = 0; s < NS; ++s) ckn[s] = act ? ck_row[(k - 1) * N + s] : 0.0f;
+      for (int s = 0; s < NS; ++s) ckn[s] = act ? ck_row[(k - 1) * ck_stride + s] : 0.0f;
     }
     __syncthreads();
 
@@ -475,10 +479,7 @@ hipError_t launch_bwd_n(const BwdDims& dm, const BwdPtrs& p, hipStream_t s) {
 }  // namespace
 
 int bwd_lanes_per_channel(int dstate) { return dstate >= 8 ? 2 : 1; }
-int bwd_chunk_len(int dstate) {
-  const int groups = dstate >= 4 ? 4 : dstate;
-  return kSpan * groups * bwd_lanes_per_channel(dstate);
-}
+int bwd_chunk_len(int dstate) { return bwd_chunk_tokens(dstate); }
 
 hipError_t launch_scan_bwd(const BwdDims& dm, const BwdPtrs& p, hipStream_t s) {
   hipError_t e = (dm.io == kIoBf16) ? launch_bwd_n<BF16>(dm, p, s) : launch_bwd_n<F32>(dm, p, s);

@@ -36,13 +36,16 @@ struct BcPiece<1> {
 // At most 96 VGPRs (5 waves per SIMD): with 4 waves per workgroup and 28 KB of
 // LDS, five workgroups fit on a CU at once, which the two-lanes-per-channel plan
 // needs to keep every CU's share resident.
-template <int N, int G, int K, typename IO, bool AGG, bool ZOH>
+// CKPT (first-order, full pass only): also store the state entering every
+// backward-pass chunk, for a training step's backward.  It is a separate
+// instantiation so that the plain scan keeps its registers.
+template <int N, int G, int K, typename IO, bool AGG, bool ZOH, bool CKPT_K>
 __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(5, 10))) void scan_kernel(
     const ScanDims dm, const typename IO::T* __restrict__ x, const typename IO::T* __restrict__ dt,
     const typename IO::T* __restrict__ z, const float* __restrict__ bc, const float* __restrict__ A,
     const float* __restrict__ Dskip, const float* __restrict__ dt_bias, const float* __restrict__ h0,
     const float* __restrict__ h_in, typename IO::T* __restrict__ y, float* __restrict__ h_final,
-    float* __restrict__ agg_h, float* __restrict__ agg_s) {
+    float* __restrict__ agg_h, float* __restrict__ agg_s, float* __restrict__ ckpt) {
   constexpr int CPB = 64 / K;            // channels per workgroup (K adjacent lanes per channel)
   constexpr int SG = G * K;              // state groups (one per lane of a channel per wave)
   constexpr int NS = N / SG;             // state components per lane
@@ -109,6 +112,18 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(5, 10)))
     for (int s = 0; s < NS; ++s) h[s] = hi ? hi[s] : 0.0f;
   }
   float dsum = 0.0f;   // AGG: sum of Delta over the chunk
+  // checkpoints for the backward pass: the state entering every ck_len-token chunk
+  float* __restrict__ ck_row = nullptr;
+  if constexpr (CKPT_K) {
+    if (ckpt && act) ck_row = ckpt + (b * dm.ck_count * dm.dim + dc) * N + sg * NS;   // (batch, chunk, dim, N)
+  }
+  constexpr int CKL = bwd_chunk_tokens(N);   // checkpoint interval (a power of 2)
+  if constexpr (CKPT_K) {
+    if (ck_row && (t0 % CKL) == 0) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) ck_row[(t0 / CKL) * dm.dim * N + s] = h[s];
+    }
+  }
 
   // B/C of this batch row, re-laid out (token, n, {B, C}); pieces never straddle tokens
   const Piece* __restrict__ bc_row = reinterpret_cast<const Piece*>(bc + b * L * (2 * N));
@@ -143,8 +158,9 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(5, 10)))
 
   // One tile.  FULL (a compile-time tag) means all T tokens lie inside the chunk:
   // no per-token masks, no guards in the inner loop.
-  auto tile = [&](auto full_tag, int64_t ts) {
+  auto tile = [&](auto full_tag, auto ck_tag, int64_t ts) {
     constexpr bool FULL = decltype(full_tag)::value;
+    constexpr bool CKPT = decltype(ck_tag)::value && CKPT_K;
     const int64_t tf = own_first(ts);
     const int valid = FULL ? SPAN : own_valid(tf);
 
@@ -236,6 +252,8 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(5, 10)))
       }
     };
     const int nj = FULL ? T : (int)(t1 - ts);
+    constexpr int NMID = (T > CKL) ? T / CKL - 1 : 1;   // checkpoint positions inside the tile
+    float hmid[NMID][NS];
     Ops cur, nxt;
     fetch(0, cur);
 #pragma unroll
@@ -244,6 +262,35 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(5, 10)))
         if (j + 1 < T && (FULL || j + 1 < nj)) fetch(j + 1, nxt);
         compute(j, cur);
         cur = nxt;
+        if constexpr (CKPT && T > CKL) {
+          // the state after token ts + j enters checkpoint chunk (ts + j + 1) / CKL;
+          // tiles start at multiples of T, so inside a tile the positions are
+          // fixed: keep a copy (no branch here), stored after the tile
+          if ((j + 1) % CKL == 0 && j + 1 < T) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) hmid[(j + 1) / CKL - 1][s] = h[s];
+          }
+        }
+      }
+    }
+
+    if constexpr (CKPT) {
+      if (ck_row) {
+        if constexpr (T > CKL) {
+#pragma unroll
+          for (int m = 0; m < NMID; ++m) {
+            const int64_t tn = ts + (m + 1) * CKL;
+            if ((FULL || (m + 1) * CKL <= nj) && tn < L) {
+#pragma unroll
+              for (int s = 0; s < NS; ++s) ck_row[(tn / CKL) * dm.dim * N + s] = hmid[m][s];
+            }
+          }
+        }
+        const int64_t te = ts + nj;   // the state after the tile's last token
+        if (te % CKL == 0 && te < L) {
+#pragma unroll
+          for (int s = 0; s < NS; ++s) ck_row[(te / CKL) * dm.dim * N + s] = h[s];
+        }
       }
     }
 
@@ -274,8 +321,8 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(5, 10)))
   };
 
   for (int64_t ts = t0; ts < t1; ts += T) {
-    if (ts + T <= t1) tile(std::true_type{}, ts);
-    else tile(std::false_type{}, ts);
+    if (ts + T <= t1) tile(std::true_type{}, std::integral_constant<bool, CKPT_K>{}, ts);
+    else tile(std::false_type{}, std::integral_constant<bool, CKPT_K>{}, ts);
   }
 
   if (act) {
@@ -296,9 +343,17 @@ hipError_t launch_scan_t(const ScanDims& dm, const ScanPtrs& p, hipStream_t s) {
   using E = typename IO::T;
   const int64_t cblocks = (dm.dim + 64 / K - 1) / (64 / K);
   const int64_t nwg = cblocks * dm.batch * dm.num_chunks;
-  hipLaunchKernelGGL((scan_kernel<N, G, K, IO, AGG, ZOH>), dim3((unsigned)nwg), dim3(64 * G), 0, s, dm,
+  if constexpr (!AGG && !ZOH) {
+    if (p.ckpt) {
+      hipLaunchKernelGGL((scan_kernel<N, G, K, IO, false, false, true>), dim3((unsigned)nwg), dim3(64 * G), 0, s,
+                         dm, (const E*)p.x, (const E*)p.dt, (const E*)p.z, p.bc, p.A, p.Dskip, p.dt_bias, p.h0,
+                         p.h_in, (E*)p.y, p.h_final, p.agg_h, p.agg_s, p.ckpt);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((scan_kernel<N, G, K, IO, AGG, ZOH, false>), dim3((unsigned)nwg), dim3(64 * G), 0, s, dm,
                      (const E*)p.x, (const E*)p.dt, (const E*)p.z, p.bc, p.A, p.Dskip, p.dt_bias, p.h0, p.h_in,
-                     (E*)p.y, p.h_final, p.agg_h, p.agg_s);
+                     (E*)p.y, p.h_final, p.agg_h, p.agg_s, nullptr);
   return hipGetLastError();
 }
 

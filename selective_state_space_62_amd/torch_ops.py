@@ -38,9 +38,17 @@ def workspace_bytes(batch, dim, dstate, seqlen, dtype=torch.bfloat16, plan=None)
     return _b.ss_scan_fwd_workspace_bytes(batch, dim, dstate, seqlen, _IO[dtype], plan)
 
 
+def ckpt_numel(batch, dim, dstate, seqlen) -> int:
+    """float32 elements of the checkpoint buffer scan_fwd(ckpt=...) fills for scan_bwd."""
+    return _b.ss_scan_ckpt_bytes(batch, dim, dstate, seqlen) // 4
+
+
 def scan_fwd(x, dt, B, C, A, z=None, Dskip=None, dt_bias=None, h0=None, *, plan=None, workspace=None,
-             y=None, h_final=None, return_final_state=True, zoh=False):
+             y=None, h_final=None, return_final_state=True, zoh=False, ckpt=None):
     """Selective scan over full sequences (zoh=True: zero-order-hold input term).
+
+    ckpt: optional float32 tensor of ckpt_numel(...) elements that receives the
+    states the backward pass needs (pass it on to scan_bwd).
 
     x, z: (batch, D, L); dt: (batch, D, L), or (batch, L) for one value per row and
     token shared by the row's channels; B, C: (batch, N, L) — all float32 or all bfloat16;
@@ -76,13 +84,16 @@ def scan_fwd(x, dt, B, C, A, z=None, Dskip=None, dt_bias=None, h0=None, *, plan=
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
     if workspace.numel() < nbytes:
         raise ValueError("workspace has %d bytes, %d needed" % (workspace.numel(), nbytes))
-    args = (_ptr(x), _ptr(dt), _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(Dskip), _ptr(dt_bias), _ptr(h0), _ptr(y),
-            _ptr(h_final), _ptr(workspace), workspace.numel(), plan, _stream(dev))
-    if dt_row:
-        flags = _b.SS_FLAG_DT_PER_ROW | (_b.SS_FLAG_ZOH if zoh else 0)
-        _b.ss_scan_fwd_ex(batch, dim, N, L, io, flags, *args)
+    if ckpt is not None:
+        _need(ckpt, "ckpt", torch.float32, (ckpt_numel(batch, dim, N, L),), dev)
+    head = (_ptr(x), _ptr(dt), _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(Dskip), _ptr(dt_bias), _ptr(h0), _ptr(y),
+            _ptr(h_final))
+    tail = (_ptr(workspace), workspace.numel(), plan, _stream(dev))
+    if dt_row or ckpt is not None:
+        flags = (_b.SS_FLAG_DT_PER_ROW if dt_row else 0) | (_b.SS_FLAG_ZOH if zoh else 0)
+        _b.ss_scan_fwd_ex(batch, dim, N, L, io, flags, *head, _ptr(ckpt), *tail)
     else:
-        (_b.ss_scan_fwd_zoh if zoh else _b.ss_scan_fwd)(batch, dim, N, L, io, *args)
+        (_b.ss_scan_fwd_zoh if zoh else _b.ss_scan_fwd)(batch, dim, N, L, io, *head, *tail)
     return y, h_final
 
 
@@ -127,7 +138,7 @@ def bwd_workspace_bytes(batch, dim, dstate, seqlen, dtype=torch.bfloat16) -> int
 
 
 def scan_bwd(x, dt, B, C, A, dy, z=None, Dskip=None, dt_bias=None, h0=None, dh_final=None, *, workspace=None,
-             need_dA=True, need_dDskip=True, need_ddt_bias=True, need_dh0=True):
+             need_dA=True, need_dDskip=True, need_ddt_bias=True, need_dh0=True, ckpt=None):
     """Gradients of ``scan_fwd`` (first-order input term) for upstream gradients dy
     (batch, D, L) and dh_final (batch, D, N) float32 (None = 0).
 
@@ -162,10 +173,16 @@ def scan_bwd(x, dt, B, C, A, dy, z=None, Dskip=None, dt_bias=None, h0=None, dh_f
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
     if workspace.numel() < nbytes:
         raise ValueError("workspace has %d bytes, %d needed" % (workspace.numel(), nbytes))
-    _b.ss_scan_bwd(batch, dim, N, L, io, _ptr(x), _ptr(dt), _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(Dskip),
-                   _ptr(dt_bias), _ptr(h0), _ptr(dy), _ptr(dh_final), _ptr(out["dx"]), _ptr(out["ddt"]),
-                   _ptr(out["dz"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dA"]), _ptr(out["dDskip"]),
-                   _ptr(out["ddt_bias"]), _ptr(out["dh0"]), _ptr(workspace), workspace.numel(), _stream(dev))
+    ins = (_ptr(x), _ptr(dt), _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(Dskip), _ptr(dt_bias), _ptr(h0), _ptr(dy),
+           _ptr(dh_final))
+    outs = (_ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dz"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dA"]),
+            _ptr(out["dDskip"]), _ptr(out["ddt_bias"]), _ptr(out["dh0"]), _ptr(workspace), workspace.numel(),
+            _stream(dev))
+    if ckpt is not None:
+        _need(ckpt, "ckpt", torch.float32, (ckpt_numel(batch, dim, N, L),), dev)
+        _b.ss_scan_bwd_ex(batch, dim, N, L, io, 0, *ins, _ptr(ckpt), *outs)
+    else:
+        _b.ss_scan_bwd(batch, dim, N, L, io, *ins, *outs)
     return out
 
 

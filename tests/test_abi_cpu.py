@@ -252,9 +252,19 @@ def test_shard_combine_validation(case, status):
 def test_flags_validation():
     (batch, dim, N, L, io), p, plan = _scan_args()
     args = [p[k] for k in ("x", "dt", "z", "B", "C", "A", "Dskip", "dt_bias", "h0", "y", "h_final")]
-    st = b.lib.ss_scan_fwd_ex(batch, dim, N, L, io, 4, *args, p["workspace"], p["workspace_bytes"],
+    st = b.lib.ss_scan_fwd_ex(batch, dim, N, L, io, 4, *args, None, p["workspace"], p["workspace_bytes"],
                               b._plan_ptr(plan), None)
     assert st == b.SS_ERR_UNSUPPORTED and "flags" in b.last_error()
+    ck = ALIGNED + (1 << 38)
+    st = b.lib.ss_scan_fwd_ex(batch, dim, N, L, io, b.SS_FLAG_ZOH, *args, ck, p["workspace"], p["workspace_bytes"],
+                              b._plan_ptr(plan), None)
+    assert st == b.SS_ERR_UNSUPPORTED and "ZOH" in b.last_error()
+    st = b.lib.ss_scan_fwd_ex(batch, dim, N, L, io, 0, *args, ck + 4, p["workspace"], p["workspace_bytes"],
+                              b._plan_ptr(plan), None)
+    assert st == b.SS_ERR_INVALID_ARG and "ckpt" in b.last_error()
+    st = b.lib.ss_scan_fwd_ex(batch, dim, N, L, io, 0, *args, p["x"], p["workspace"], p["workspace_bytes"],
+                              b._plan_ptr(plan), None)
+    assert st == b.SS_ERR_INVALID_ARG and "overlaps" in b.last_error()
     st = b.lib.ss_state_update_ex(4, 64, 16, b.SS_BF16, 8, ALIGNED, ALIGNED + (1 << 30), ALIGNED + (1 << 31), None,
                                   ALIGNED + (1 << 32), ALIGNED + (1 << 33), ALIGNED + (1 << 34), None, None,
                                   ALIGNED + (1 << 35), None)
@@ -262,8 +272,22 @@ def test_flags_validation():
     # an output inside the per-row dt (batch * L elements) is rejected
     st = b.lib.ss_scan_fwd_ex(batch, dim, N, L, io, b.SS_FLAG_DT_PER_ROW,
                               *[p[k] for k in ("x", "dt", "z", "B", "C", "A", "Dskip", "dt_bias", "h0")],
-                              p["dt"] + 64, p["h_final"], p["workspace"], p["workspace_bytes"], b._plan_ptr(plan), None)
+                              p["dt"] + 64, p["h_final"], None, p["workspace"], p["workspace_bytes"], b._plan_ptr(plan),
+                              None)
     assert st == b.SS_ERR_INVALID_ARG and "overlaps input dt" in b.last_error()
+
+
+def test_ckpt_bytes_and_bwd_ex_flags():
+    # the state entering every 16-token chunk at N = 16, fp32
+    assert b.ss_scan_ckpt_bytes(8, 5120, 16, 2048) == 8 * 5120 * 128 * 16 * 4
+    assert b.ss_scan_ckpt_bytes(2, 64, 16, 17) == 2 * 64 * 2 * 16 * 4
+    assert b.ss_scan_ckpt_bytes(2, 64, 3, 17) == 0
+    names = list(_BWD_NAMES)
+    (batch, dim, N, L) = (2, 64, 16, 256)
+    a = {n: ALIGNED + i * (1 << 30) for i, n in enumerate(names)}
+    st = b.lib.ss_scan_bwd_ex(batch, dim, N, L, b.SS_F32, 1, *[a[n] for n in names[:11]], None,
+                              *[a[n] for n in names[11:]], ALIGNED + (1 << 36), 1 << 30, None)
+    assert st == b.SS_ERR_UNSUPPORTED and "flags" in b.last_error()
 
 
 def test_timing_record_empty():

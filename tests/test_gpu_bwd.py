@@ -197,3 +197,39 @@ def test_bwd_2p8b_layer_full(ss, o, dev):
     r = o.scan_bwd(f["x"], f["dt"], f["B"], f["C"], to_f64(A), to_f64(dy), z=f["z"], Dskip=to_f64(dskip),
                    dt_bias=to_f64(bias))
     _compare(g, r, "bf16", "bwd %s" % cfg.name)
+
+
+@pytest.mark.parametrize("case,io,plan", [((2, 77, 16, 37), "f32", None), ((2, 96, 16, 300), "bf16", None),
+                                          ((3, 33, 8, 50), "f32", None), ((2, 20, 4, 31), "f32", None),
+                                          ((2, 70, 2, 9), "f32", None), ((1, 130, 1, 13), "f32", None),
+                                          ((1, 64, 16, 20000), "bf16", (4, 2, 4096))],
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_forward_checkpoints_feed_backward(ss, dev, case, io, plan):
+    """The forward's stored checkpoints equal the backward's own sweep: a training
+    step that passes them gets identical gradients, and the forward's outputs do
+    not change when it stores them.  Under a chunked plan the forward's states at
+    chunk boundaries come from the cross-chunk combine, which rounds differently
+    from a sequential sweep, so there the gradients are checked against the
+    oracle instead of bit for bit."""
+    import torch
+    batch, D, N, L = case
+    rng = np.random.default_rng(zlib.crc32(repr(("ckpt", case, io)).encode()))
+    raw, par, f64 = _problem(rng, batch, D, N, L, io, True)
+    t = {k: to_dev(v, io, dev) for k, v in raw.items()}
+    p = {k: (torch.from_numpy(v).to(dev) if v is not None else None) for k, v in par.items()}
+    kw = dict(z=t["z"], Dskip=p["Dskip"], dt_bias=p["dt_bias"], h0=p["h0"])
+    ck = torch.full((ss.ckpt_numel(batch, D, N, L),), float("nan"), device=dev)
+    y0, h0f = ss.scan_fwd(t["x"], t["dt"], t["B"], t["C"], p["A"], plan=plan, **kw)
+    y1, h1f = ss.scan_fwd(t["x"], t["dt"], t["B"], t["C"], p["A"], plan=plan, ckpt=ck, **kw)
+    g0 = ss.scan_bwd(t["x"], t["dt"], t["B"], t["C"], p["A"], t["dy"], dh_final=p["dh_final"], **kw)
+    g1 = ss.scan_bwd(t["x"], t["dt"], t["B"], t["C"], p["A"], t["dy"], dh_final=p["dh_final"], ckpt=ck, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(h0f, h1f)
+    assert not torch.isnan(ck).any(), "every checkpoint is written"
+    if plan is None:
+        for k, v in g0.items():
+            if v is not None:
+                assert torch.equal(v, g1[k]), k
+        log("ckpt %s %s: forward checkpoints give identical gradients" % (case, io))
+    else:
+        _compare(g1, _run_oracle(oracle.default(), f64, par), io, "ckpt chunked %s" % (case,))
