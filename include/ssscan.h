@@ -77,10 +77,11 @@ typedef enum {
 /* Plan of one scan call: how the work is laid onto the GPU.
  *   state_groups:      waves per workgroup (1, 2 or 4); the state components are
  *                      split over the waves.
- *   lanes_per_channel: 1 or 2 (0 means 1).  With 2, two adjacent lanes share a
- *                      channel and split that wave's components again, so a
- *                      workgroup covers 32 channels instead of 64.
- *                      state_groups * lanes_per_channel must divide into dstate.
+ *   lanes_per_channel: 1, 2 or 4 (0 means 1; 4 only with 4 state groups).  With
+ *                      K > 1, K adjacent lanes share a channel and split that
+ *                      wave's components again, so a workgroup covers 64/K
+ *                      channels.  state_groups * lanes_per_channel must divide
+ *                      into dstate.
  *   chunk_len:         tokens per sequence chunk; chunk_len >= seqlen means one
  *                      chunk.  Chunks are scanned in parallel and joined by an
  *                      exclusive scan of their (decay, end state) pairs, then

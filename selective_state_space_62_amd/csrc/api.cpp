@@ -120,6 +120,14 @@ Plan auto_plan(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype 
     if (chunks > max_chunks) chunks = max_chunks;
     if (chunks < 1) chunks = 1;
   }
+  // Unchunked launches with fewer than two workgroups per CU (one wave per SIMD
+  // each) leave SIMDs idle; four lanes per channel (one state component each)
+  // halve the channels per workgroup and double the workgroups, for a little more
+  // VALU work per channel (130M-shaped layer: 384 -> 768 workgroups).
+  if (chunks == 1 && dstate >= 16 && wgs < 2 * (simds / 4)) {
+    p.lanes = 4;
+    p.tile = ssscan::tile_len(p.groups, io_code(io));
+  }
   int64_t cl = (seqlen + chunks - 1) / chunks;
   cl = ((cl + p.tile - 1) / p.tile) * p.tile;
   if (cl < p.tile) cl = p.tile;
@@ -140,9 +148,10 @@ ss_status make_plan(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_d
   if (!(p.groups == 1 || p.groups == 2 || p.groups == 4) || p.groups > dstate)
     return fail(SS_ERR_UNSUPPORTED, "plan.state_groups %d must be 1, 2 or 4 and at most dstate (%d)", p.groups,
                 dstate);
-  if (!(p.lanes == 1 || p.lanes == 2) || p.groups * p.lanes > dstate)
+  if (!(p.lanes == 1 || p.lanes == 2 || (p.lanes == 4 && p.groups == 4)) || p.groups * p.lanes > dstate)
     return fail(SS_ERR_UNSUPPORTED,
-                "plan.lanes_per_channel %d must be 1 or 2, with state_groups * lanes_per_channel <= dstate (%d)",
+                "plan.lanes_per_channel %d must be 1, 2 or 4 (4 with 4 state groups), with state_groups * "
+                "lanes_per_channel <= dstate (%d)",
                 in->lanes_per_channel, dstate);
   p.tile = ssscan::tile_len(p.groups, io_code(io));
   int64_t cl = in->chunk_len;

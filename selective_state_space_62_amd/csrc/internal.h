@@ -20,7 +20,7 @@ struct ScanDims {
   int32_t groups;       // waves per workgroup
   int32_t io;           // IoType
   int32_t vec;          // 1: every lane's span of a row is aligned for one vector access
-  int32_t lanes;        // lanes per channel (1 or 2); each lane owns dstate/(groups*lanes) states
+  int32_t lanes;        // lanes per channel (1, 2 or 4); each lane owns dstate/(groups*lanes) states
   int32_t dt_row;       // 1: dt is (batch, seqlen), one value per token shared by a row's channels
   int64_t ck_count;     // with ScanPtrs::ckpt: checkpoints per channel, ceil(seqlen / bwd_chunk_tokens(dstate))
 };

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(5, 10)))
   constexpr int BC_PER_THREAD = (BC_PIECES + THREADS - 1) / THREADS;
   constexpr int TOK_PIECES = 2 * N / PF;                         // pieces per token
   static_assert(NS >= 1 && N % SG == 0, "G * K must divide N");
-  static_assert(K == 1 || K == 2, "one or two lanes per channel");
+  static_assert(K == 1 || K == 2 || K == 4, "one, two or four lanes per channel");
   constexpr bool SHARE_DD = (G * K) > 1;   // Delta is computed once and shared through LDS
 
   __shared__ float2 s_dd[SHARE_DD ? T : 1][CPB];              // (Delta, Delta*x) per token and channel
@@ -246,7 +246,9 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(5, 10)))
         dsum += o.d;
       } else {
         // both lanes of a channel end with the channel's sum over this wave's components
-        if constexpr (K == 2) acc += __builtin_amdgcn_update_dpp(0.0f, acc, 0xB1, 0xf, 0xf, false);
+        // the K lanes of a channel (adjacent in a quad) end with the channel's sum
+        if constexpr (K >= 2) acc += __builtin_amdgcn_update_dpp(0.0f, acc, 0xB1, 0xf, 0xf, false);   // [1,0,3,2]
+        if constexpr (K == 4) acc += __builtin_amdgcn_update_dpp(0.0f, acc, 0x4E, 0xf, 0xf, false);   // [2,3,0,1]
         if constexpr (SHARE_DD) s_part[j][w][c] = acc;
         else yp[j] = acc;
       }
@@ -362,6 +364,9 @@ hipError_t launch_scan_k(const ScanDims& dm, const ScanPtrs& p, hipStream_t s) {
   if (dm.lanes == 1) return launch_scan_t<N, G, 1, IO, AGG, ZOH>(dm, p, s);
   if constexpr (N >= 2 * G) {
     if (dm.lanes == 2) return launch_scan_t<N, G, 2, IO, AGG, ZOH>(dm, p, s);
+  }
+  if constexpr (N >= 4 * G && G == 4) {
+    if (dm.lanes == 4) return launch_scan_t<N, G, 4, IO, AGG, ZOH>(dm, p, s);
   }
   return hipErrorInvalidValue;
 }

@@ -90,6 +90,8 @@ def _scan_status(**kw):
     (dict(shape=(2, 64, 2, 256), plan=(4, 256)), b.SS_ERR_UNSUPPORTED),   # more groups than states
     (dict(shape=(2, 64, 4, 256), plan=(4, 2, 256)), b.SS_ERR_UNSUPPORTED),  # 8 state groups > 4 states
     (dict(plan=(4, 3, 256)), b.SS_ERR_UNSUPPORTED),                        # 3 lanes per channel
+    (dict(plan=(2, 4, 256)), b.SS_ERR_UNSUPPORTED),                        # 4 lanes need 4 state groups
+    (dict(shape=(2, 64, 8, 256), plan=(4, 4, 256)), b.SS_ERR_UNSUPPORTED),  # 16 state groups > 8 states
     (dict(shape=(1 << 41, 64, 16, 256)), b.SS_ERR_INVALID_ARG),
 ])
 def test_scan_validation(case, status):
@@ -127,6 +129,8 @@ def test_plan_choice():
     assert g == 4 and cl < (1 << 20) and cl % 32 == 0      # few channels, long sequence: chunked
     g, k, cl = b.ss_scan_fwd_plan(1, 16, 2, 64, b.SS_F32)
     assert (g, k) == (2, 1)
+    g, k, cl = b.ss_scan_fwd_plan(8, 1536, 16, 2048, b.SS_F32)
+    assert (g, k) == (4, 4) and cl >= 2048                 # < 2 workgroups per CU with 2 lanes: 4 lanes
 
 
 @pytest.mark.parametrize("case,status", [

@@ -41,7 +41,8 @@ def test_chunked_equals_unchunked(ss, dev, io):
     raw, par, f64 = random_problem(rng, 2, 192, 16, 4096, io)
     t, p = _upload(raw, par, io, dev)
     outs = {}
-    for plan in [(4, 4096), (4, 1024), (4, 256), (2, 512), (1, 64), (4, 2, 4096), (4, 2, 512), (2, 2, 64)]:
+    for plan in [(4, 4096), (4, 1024), (4, 256), (2, 512), (1, 64), (4, 2, 4096), (4, 2, 512), (2, 2, 64),
+                 (4, 4, 4096), (4, 4, 256)]:
         log("chunked plan %s (%s)" % (plan, io))
         y, hf = ss.scan_fwd(t["x"], t["dt"], t["B"], t["C"], p["A"], z=t["z"], Dskip=p["Dskip"],
                             dt_bias=p["dt_bias"], h0=p["h0"], plan=plan)
@@ -166,7 +167,8 @@ def test_state_groups_agree_and_runs_are_deterministic(ss, dev):
     raw, par, _ = random_problem(rng, 2, 128, 16, 640, "bf16")
     t, p = _upload(raw, par, "bf16", dev)
     res = []
-    for plan in [(1, 640), (2, 640), (4, 2, 640), (4, 640), (4, 640), (2, 2, 640), (1, 2, 640)]:
+    for plan in [(1, 640), (2, 640), (4, 2, 640), (4, 640), (4, 640), (2, 2, 640), (1, 2, 640), (4, 4, 640),
+                 (4, 4, 640)]:
         y, hf = ss.scan_fwd(t["x"], t["dt"], t["B"], t["C"], p["A"], z=t["z"], Dskip=p["Dskip"],
                             dt_bias=p["dt_bias"], h0=p["h0"], plan=plan)
         torch.cuda.synchronize()

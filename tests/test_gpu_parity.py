@@ -96,6 +96,10 @@ RAGGED = [
     (1, 31, 16, 301, "bf16", True, True, True, True, (2, 2, 48)),
     (2, 64, 2, 77, "f32", True, True, True, True, (1, 2, 12)),
     (1, 33, 4, 1000, "bf16", False, True, False, True, (2, 2, 64)),
+    (2, 100, 16, 37, "f32", True, True, True, True, (4, 4, 1 << 20)),
+    (2, 70, 16, 515, "bf16", True, True, True, True, (4, 4, 1 << 20)),
+    (1, 40, 16, 1000, "bf16", True, False, True, True, (4, 4, 128)),
+    (3, 17, 16, 61, "f32", False, True, False, True, (4, 4, 32)),
 ]
 
 
