@@ -97,22 +97,28 @@ def algorithmic_slots_bwd_per_tokch(N: int) -> float:
 
 
 def cpu_baseline(cfg, budget_s: float):
-    """The oracle (as it stands) on host cores over whole batch rows of the workload,
-    row by row until ~budget_s of oracle time; inputs drawn on the host, untimed."""
+    """The oracle (as it stands) on host cores over the workload, 1024 channels per
+    call, passing over it again until ~budget_s of oracle time; inputs are drawn on
+    the host once per piece and kept (untimed).  A workload that one pass cannot
+    finish within the budget is cut at a piece boundary."""
     import numpy as np
     import oracle
     from workloads import inputs
     o = oracle.default()
     A, dskip, bias = inputs.params(cfg)
+    chans_per_call = 1024
+    pieces = [(b, d0) for b in range(cfg.batch) for d0 in range(0, cfg.dim, chans_per_call)]
+    cache = {}
     tokch = 0
     spent = 0.0
-    rows = 0
-    chans_per_call = 1024
-    for b in range(cfg.batch):
-        for d0 in range(0, cfg.dim, chans_per_call):
+    passes = 0
+    while spent < budget_s:
+        for b, d0 in pieces:
             ch = [(b, d) for d in range(d0, min(cfg.dim, d0 + chans_per_call))]
-            sub = inputs.scan_inputs(cfg, channels=ch)
-            f = {k: inputs.raw_to_f64(v, cfg.io) for k, v in sub.items()}
+            if (b, d0) not in cache:
+                sub = inputs.scan_inputs(cfg, channels=ch)
+                cache[(b, d0)] = {k: inputs.raw_to_f64(v, cfg.io) for k, v in sub.items()}
+            f = cache[(b, d0)]
             idx = np.array([d for _, d in ch])
             t0 = time.perf_counter()
             o.scan(f["x"][None], f["dt"][None], f["B"][b:b + 1], f["C"][b:b + 1], A[idx], z=f["z"][None],
@@ -121,12 +127,11 @@ def cpu_baseline(cfg, budget_s: float):
             tokch += len(ch) * cfg.seqlen
             if spent >= budget_s:
                 break
-        rows += 1
-        if spent >= budget_s:
-            break
+        passes += 1
+    whole = cfg.batch * cfg.dim * cfg.seqlen
     return {"value": tokch / spent / 1e9, "unit": "Gtok·ch/s", "cores": o.max_threads(), "kind": "oracle",
-            "sample": "%d channels x L=%d of the %s workload (%.1f s of oracle time, float64)"
-                      % (tokch // cfg.seqlen, cfg.seqlen, cfg.name, spent)}
+            "sample": "%.2f passes over the %s workload (%d channels x L=%d each), %.1f s of oracle time, float64"
+                      % (tokch / whole, cfg.name, cfg.batch * cfg.dim, cfg.seqlen, spent)}
 
 
 def measured_traffic(cfg, kind: str = "scan"):

@@ -21,3 +21,31 @@ def test_bench_algorithmic_counts():
     assert abs(bench.algorithmic_bytes_per_tokch(B28) - 8.048) < 1e-3
     assert bench.algorithmic_slots_per_tokch(16) == 112
     assert bench.algorithmic_slots_bwd_per_tokch(16) == 411
+
+
+def test_cpu_baseline_repeats_passes_until_budget():
+    """The oracle baseline keeps passing over the (tiny) workload until the time
+    budget is spent, and reports the fraction of the workload it covered."""
+    sys.path.insert(0, str(ROOT))
+    import bench
+    from workloads import TINY
+    r = bench.cpu_baseline(TINY, 0.3)
+    assert r["kind"] == "oracle" and r["unit"] == "Gtok·ch/s" and r["value"] > 0 and r["cores"] >= 1
+    passes = float(r["sample"].split(" passes")[0])
+    assert passes > 1.0, r["sample"]
+
+
+def test_measured_traffic_tracks_kernel_sources():
+    """Traffic comes from the committed counter summaries only while their kernel
+    hash matches the sources (else None); a different workload name gets None."""
+    sys.path.insert(0, str(ROOT))
+    import json
+    import bench
+    from workloads import B28, TINY
+    d = json.loads(bench.COUNTERS_FILES["scan"].read_text())
+    got = bench.measured_traffic(B28, "scan")
+    if d["kernel_hash"] == bench.kernel_hash("scan"):
+        assert got == d["hbm_bytes_per_launch"] > bench.algorithmic_bytes_per_tokch(B28) * B28.tokch * 0.9
+    else:
+        assert got is None
+    assert bench.measured_traffic(TINY, "scan") is None
