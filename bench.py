@@ -82,16 +82,19 @@ def algorithmic_slots_per_tokch(N: int) -> float:
     return 4 * N + 8 + TRANS_SLOTS * (N + 4)
 
 
-def algorithmic_slots_bwd_per_tokch(N: int) -> float:
+def algorithmic_slots_bwd_per_tokch(N: int, sweep: bool = True) -> float:
     """VALU issue slots per (token, channel) of the backward pass by recomputation:
-    per state component the checkpoint sweep (3 ops + exp), the chunk recompute with
-    the readout (4 ops + exp) and the adjoint step (10 ops + exp: adjoint update,
-    dC and dB terms, the decay's derivative for dDelta and dA, lam B for dx, the
-    adjoint decay, and Abar recomputed); per (token, channel) two softplus
-    evaluations (5 ops + 2 transcendentals each), sigmoid(dt + dt_bias) (2 + 2),
-    silu(z) and its derivative (7 + 2) and the six output formulas (8 ops).  A
-    transcendental costs TRANS_SLOTS slots."""
-    per_n = 17 + 3 * TRANS_SLOTS
+    per state component the checkpoint sweep (3 ops + exp; absent when the forward
+    stored the checkpoints), the chunk recompute with the readout (4 ops + exp,
+    keeping Abar) and the adjoint step (9 ops: adjoint update, dC and dB terms, the
+    decay's derivative for dDelta and dA, lam B for dx, and the adjoint decay by the
+    kept Abar); per (token, channel) two softplus evaluations (5 ops + 2
+    transcendentals each), sigmoid(dt + dt_bias) (2 + 2), silu(z) and its derivative
+    (7 + 2) and the six output formulas (8 ops).  A transcendental costs TRANS_SLOTS
+    slots."""
+    per_n = 4 + 9 + TRANS_SLOTS
+    if sweep:
+        per_n += 3 + TRANS_SLOTS
     per_tok = 10 + 2 + 7 + 8 + TRANS_SLOTS * (4 + 2 + 2)
     return per_n * N + per_tok
 
@@ -252,6 +255,9 @@ def run_bwd(ss, torch, dev, cfg, t, A, dskip, bias, fwd_kernel_ms, calls=20):
             "training_step": {"fwd_kernel_ms": round(f_no, 5), "bwd_kernel_ms": round(b_no, 5),
                               "fwd_storing_checkpoints_kernel_ms": round(f_ck, 5),
                               "bwd_from_checkpoints_kernel_ms": round(b_ck, 5),
+                              "bwd_from_checkpoints_frac": round(
+                                  algorithmic_slots_bwd_per_tokch(cfg.dstate, sweep=False) * cfg.tokch
+                                  / (b_ck * 1e-3) / 1e12 / VALU_PEAK_TOPS, 4),
                               "step_ms": round(f_no + b_no, 5), "step_with_checkpoints_ms": round(f_ck + b_ck, 5),
                               "checkpoint_bytes": ck.numel() * 4}}
 

@@ -534,8 +534,8 @@ BwdLayout bwd_layout(int64_t batch, int64_t dim, int dstate, int64_t seqlen) {
   off += round256((size_t)batch * seqlen * dstate * 2 * sizeof(float));
   w.ckpt = off;
   off += round256((size_t)batch * dim * w.chunks * dstate * sizeof(float));
-  w.part = off;
-  off += round256((size_t)batch * w.cblocks * seqlen * 2 * dstate * sizeof(float));
+  w.part = off;   // dB/dC partials (batch, channel block, output, token), tokens padded to whole chunks
+  off += round256((size_t)batch * w.cblocks * 2 * dstate * (w.chunks * ck) * sizeof(float));
   w.dA_p = off;
   off += round256((size_t)batch * dim * dstate * sizeof(float));
   w.dD_p = off;

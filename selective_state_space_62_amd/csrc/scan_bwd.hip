@@ -21,15 +21,18 @@
 // of a chunk for the per-(token, channel) work (Delta, the gate, dx, ddt, dz).
 //  1. A forward sweep over the sequence stores the state at every chunk start
 //     (the checkpoints, in the workspace).
-//  2. Chunks are then visited last to first.  The chunk's states are recomputed
-//     from its checkpoint into registers, with the readout (dz needs r_t); the
-//     owner of each token forms dr and dz; then every lane runs the adjoint state
-//     back through the chunk.  The sums over state components (for dx and
-//     dDelta) reach the token's owner through LDS, as the forward's readout does.
-// dB and dC are sums over channels.  In a workgroup the channels of each
-// 16-lane row are summed with DPP (a channel pair first, the even channel keeping
-// dB and the odd one dC, then rotations within the row), the rows' sums are added
-// in LDS in a fixed order, and one partial per (workgroup, token) goes to the
+//  2. Chunks are then visited last to first.  The chunk's states (and their
+//     decay factors Abar) are recomputed from its checkpoint into registers, with
+//     the readout (dz needs r_t); the owner of each token forms dr and dz; then
+//     every lane runs the adjoint state back through the chunk, reusing the
+//     recomputed Abar.  The sums over state components (for dx and dDelta) reach
+//     the token's owner through LDS, as the forward's readout does.
+// dB and dC are sums over channels.  Every wave holds all of the workgroup's
+// channels (for its own state components), so a wave forms the workgroup's sums
+// by itself: a swap of wave halves between two registers (v_permlane32_swap)
+// and an add, a swap of row pairs (v_permlane16_swap) and an add, then DPP adds
+// within the 16-lane rows.  A chunk's sums stay in registers and are written
+// token-contiguous, one partial per (workgroup, output, token), to the
 // workspace; bwd_reduce_bc_kernel adds a batch row's partials in a fixed order.
 // dA, dDskip and dt_bias's gradient are summed per (row, channel) in registers
 // and over rows by bwd_reduce_param_kernel.  All sums have a fixed order:
@@ -59,9 +62,41 @@ __device__ __forceinline__ float sigmoid2(float v2) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-v2));
 }
 
-// At most 96 VGPRs and 32 KB of LDS: five workgroups (one wave per SIMD each)
-// fit on a CU, so the 2.8B-shaped layer's 1280 workgroups are all resident at
-// once on 256 CUs.
+// dB and dC of one token summed over the channels of a wave (lane = K c + hk):
+// the result in row r (16 lanes) is, for NS == 2, dB[0], dC[0], dB[1], dC[1] for
+// r = 0..3, and for NS == 1, dB, dB, dC, dC; within a row, lanes with the same
+// hk (lane mod K) hold the same sum.  The order of the additions is fixed.
+template <int NS, int K>
+__device__ __forceinline__ float bc_channel_sum(const float (&dB)[NS], const float (&dC)[NS]) {
+  static_assert(NS == 1 || NS == 2, "one or two state components per lane");
+  auto swap32 = [](float a, float b) {   // ([a lower half, b lower half], [a upper half, b upper half])
+    return __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  };
+  auto swap16 = [](float a, float b) {   // ([a r0, b r0, a r2, b r2], [a r1, b r1, a r3, b r3])
+    return __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  };
+  float u;
+  if constexpr (NS == 2) {
+    const auto pb = swap32(dB[0], dB[1]);
+    const auto pc = swap32(dC[0], dC[1]);
+    const float sb = __uint_as_float(pb[0]) + __uint_as_float(pb[1]);   // lower half dB[0], upper dB[1]
+    const float sc = __uint_as_float(pc[0]) + __uint_as_float(pc[1]);
+    const auto q = swap16(sb, sc);
+    u = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+  } else {
+    const auto pv = swap32(dB[0], dC[0]);
+    const float sv = __uint_as_float(pv[0]) + __uint_as_float(pv[1]);   // lower half dB, upper dC
+    const auto q = swap16(sv, sv);
+    u = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+  }
+  u += __builtin_amdgcn_update_dpp(0.0f, u, 0x128, 0xf, 0xf, false);   // row_ror:8
+  u += __builtin_amdgcn_update_dpp(0.0f, u, 0x124, 0xf, 0xf, false);   // row_ror:4
+  u += __builtin_amdgcn_update_dpp(0.0f, u, 0x4E, 0xf, 0xf, false);    // lanes 2 apart
+  if constexpr (K == 1) u += __builtin_amdgcn_update_dpp(0.0f, u, 0xB1, 0xf, 0xf, false);   // neighbours
+  return u;
+}
+
+// 132 VGPRs (three waves per SIMD) and 32 KB of LDS per workgroup.
 template <int N, int G, int K, typename IO>
 __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10))) void scan_bwd_kernel(
     const BwdDims dm, const BwdPtrs p) {
@@ -72,7 +107,6 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10)))
   constexpr int CK = kSpan * SG;       // chunk length (tokens)
   constexpr int NOUT = 2 * N;          // dB and dC values per token
   constexpr int THREADS = 64 * G;
-  constexpr int RED = 4 * 2 * K * NS;  // floats per (token, wave) of 8- or 16-channel sums
   constexpr int SW = SpanT<IO, kSpan>::kWords;
   static_assert(NS >= 1 && N % SG == 0, "G * K must divide N");
   static_assert(K == 1 || K == 2, "one or two lanes per channel");
@@ -83,7 +117,6 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10)))
   __shared__ float s_bc[CK][2 * N];    // B_n, C_n of the chunk's tokens
   __shared__ float2 s_pp[CK][G][CPB];  // per-wave partial sums (readout; dDelta and sum lam B)
   __shared__ float s_dr[CK][CPB];      // dr per token and channel
-  __shared__ float s_red[CK][G][RED];  // per-row channel sums of dB (even) and dC (odd)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -205,7 +238,18 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10)))
     dAacc[s] = 0.0f;
   }
   float dD_acc = 0.0f, dbias_acc = 0.0f;
-  float* __restrict__ part_row = p.part + (b * dm.cblocks + cb) * L * NOUT;
+  // dB/dC partials (batch, channel block, output, token), tokens padded to whole chunks
+  const int64_t Lp = nck * CK;
+  float* __restrict__ part_row = p.part + (b * dm.cblocks + cb) * NOUT * Lp;
+  // the lanes that write them: the first K lanes of each row that holds a sum (all
+  // rows for NS == 2, rows 0 and 2 for NS == 1), and the output each one writes.
+  // The sums cover the whole workgroup (channels past dim add zeros), so a
+  // writing lane writes whether or not its own channel is active.
+  const int prow = lane >> 4;
+  const bool pw = (lane & 15) < K && (NS == 2 || (prow & 1) == 0);
+  const int pwhich = NS == 2 ? (prow & 1) : (prow >> 1);   // 0: dB, 1: dC
+  const int ps = NS == 2 ? (prow >> 1) : 0;
+  float* __restrict__ pdst = part_row + (int64_t)(pwhich * N + sg * NS + ps) * Lp;
 
   Fetch f;
   fetch(nck - 1, true, f);
@@ -230,6 +274,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10)))
       cdy[q] = f.dy[q];
     }
     float hs[CK + 1][NS];   // hs[j] = the state before chunk token j
+    float Es[CK][NS];       // Es[j] = Abar of chunk token j
 #pragma unroll
     for (int s = 0; s < NS; ++s) hs[0][s] = ckn[s];
     if (k > 0) {
@@ -248,6 +293,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10)))
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
           const float E = __builtin_amdgcn_exp2f(o.x * A2[s]);
+          Es[j][s] = E;
           hs[j + 1][s] = fmaf(E, hs[j][s], o.y * s_bc[j][2 * (sg * NS + s)]);
           acc = fmaf(s_bc[j][2 * (sg * NS + s) + 1], hs[j + 1][s], acc);
         }
@@ -287,6 +333,9 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10)))
     __syncthreads();
 
     // the adjoint state back through the chunk
+    float uo[CK];   // this lane's dB/dC sum per chunk token (kept by the writing lanes)
+#pragma unroll
+    for (int j = 0; j < CK; ++j) uo[j] = 0.0f;
 #pragma unroll
     for (int j = CK - 1; j >= 0; --j) {
       if (FULL || j < nj) {
@@ -300,7 +349,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10)))
           const float Cv = s_bc[j][2 * (sg * NS + s) + 1];
           lam[s] = fmaf(dr, Cv, lam[s]);
           dCv[s] = dr * hs[j + 1][s];
-          const float E = __builtin_amdgcn_exp2f(o.x * A2[s]);
+          const float E = Es[j][s];
           const float ga = lam[s] * hs[j][s] * E;
           ddp = fmaf(ga, A2[s], ddp);
           dAacc[s] = fmaf(ga, o.x, dAacc[s]);
@@ -313,43 +362,23 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10)))
           sB += __builtin_amdgcn_update_dpp(0.0f, sB, 0xB1, 0xf, 0xf, false);
         }
         s_pp[j][w][c] = make_float2(ddp * kLn2, sB);   // both lanes of a channel hold the sums
-        // dB and dC summed over the channels of each 16-lane row: the channel
-        // pair (c, c ^ 1) first, the even channel keeping dB and the odd one dC
-        // (lanes 2 apart for K == 2, 1 apart for K == 1), then rotations within
-        // the row; lanes (lane & 15) < 2K end with the row's sums
-        const bool odd = (c & 1) != 0;
-        float v[NS];
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const float give = odd ? dBv[s] : dCv[s];
-          const float keep = odd ? dCv[s] : dBv[s];
-          if constexpr (K == 2) v[s] = keep + __builtin_amdgcn_update_dpp(0.0f, give, 0x4E, 0xf, 0xf, false);
-          else v[s] = keep + __builtin_amdgcn_update_dpp(0.0f, give, 0xB1, 0xf, 0xf, false);
-          if constexpr (K == 1) v[s] += __builtin_amdgcn_update_dpp(0.0f, v[s], 0x4E, 0xf, 0xf, false);   // lanes 2 apart
-          v[s] += __builtin_amdgcn_update_dpp(0.0f, v[s], 0x124, 0xf, 0xf, false);   // row_ror:4
-          v[s] += __builtin_amdgcn_update_dpp(0.0f, v[s], 0x128, 0xf, 0xf, false);   // row_ror:8
-          __asm__ volatile("" : "+v"(v[s]));   // finish the sums here, not inside the store branch
-        }
-        const int l = lane & 15;
-        if (l < 2 * K) {
-#pragma unroll
-          for (int s = 0; s < NS; ++s) s_red[j][w][((lane >> 4) * 2 * K + l) * NS + s] = v[s];
-        }
+        uo[j] = bc_channel_sum<NS, K>(dBv, dCv);
       }
     }
     __syncthreads();
 
-    // the chunk's dB/dC partials: per (token, output) the 4 row sums of the wave
-    // that holds the component, in row order
-    for (int idx = tid; idx < CK * NOUT; idx += THREADS) {
-      const int j = idx / NOUT;
-      const int o = idx % NOUT;   // o < N: dB_n, else dC_n
-      const int which = o / N, n = o % N;
-      const int gsg = n / NS;
-      const int l = which * K + gsg % K;
-      const float* src = &s_red[j][gsg / K][l * NS + n % NS];
-      const float acc = ((src[0] + src[2 * K * NS]) + src[4 * K * NS]) + src[6 * K * NS];
-      if (FULL || t0 + j < t1) part_row[(t0 + j) * NOUT + o] = acc;
+    // the chunk's dB/dC partials, 16-byte stores of consecutive tokens (padding
+    // tokens of the ragged last chunk write zeros, which nothing reads)
+    if (pw) {
+      static_assert(CK % 2 == 0, "whole pairs of tokens");
+      if constexpr (CK % 4 == 0) {
+#pragma unroll
+        for (int q = 0; q < CK; q += 4)
+          *reinterpret_cast<float4*>(pdst + t0 + q) = make_float4(uo[q], uo[q + 1], uo[q + 2], uo[q + 3]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < CK; q += 2) *reinterpret_cast<float2*>(pdst + t0 + q) = make_float2(uo[q], uo[q + 1]);
+      }
     }
     // owners: dx = Delta sum lam B + dr Dskip, ddt = (dDelta) sigmoid(v)
     {
@@ -408,20 +437,22 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10)))
 }
 
 // dB[b, n, t] and dC[b, n, t]: the channel blocks' partials, in block order.
+// Partials are (batch, block, output, token) with Lp tokens per output; one
+// thread per (b, output, t), tokens fastest, so loads and stores are coalesced.
 template <typename IO>
 __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restrict__ part, int64_t batch,
-                                                            int64_t cblocks, int64_t L, int N,
+                                                            int64_t cblocks, int64_t L, int64_t Lp, int N,
                                                             typename IO::T* __restrict__ dB,
                                                             typename IO::T* __restrict__ dC) {
   const int64_t nout = 2 * (int64_t)N;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= batch * L * nout) return;
-  const int64_t o = i % nout;
-  const int64_t t = (i / nout) % L;
-  const int64_t b = i / (nout * L);
-  const float* src = part + (b * cblocks * L + t) * nout + o;
+  if (i >= batch * nout * L) return;
+  const int64_t t = i % L;
+  const int64_t o = (i / L) % nout;
+  const int64_t b = i / (L * nout);
+  const float* src = part + (b * cblocks * nout + o) * Lp + t;
   float acc = 0.0f;
-  for (int64_t q = 0; q < cblocks; ++q) acc += src[q * L * nout];
+  for (int64_t q = 0; q < cblocks; ++q) acc += src[q * nout * Lp];
   const int64_t n = o % N;
   store_one<IO>(o < N ? dB : dC, (b * N + n) * L + t, acc);
 }
@@ -487,12 +518,14 @@ hipError_t launch_scan_bwd(const BwdDims& dm, const BwdPtrs& p, hipStream_t s) {
   const int64_t nbc = dm.batch * dm.seqlen * 2 * dm.dstate;
   if (nbc > 0) {
     const unsigned blocks = (unsigned)((nbc + 255) / 256);
+    const int64_t ck = bwd_chunk_tokens(dm.dstate);
+    const int64_t Lp = (dm.seqlen + ck - 1) / ck * ck;
     if (dm.io == kIoBf16)
       hipLaunchKernelGGL((bwd_reduce_bc_kernel<BF16>), dim3(blocks), dim3(256), 0, s, p.part, dm.batch, dm.cblocks,
-                         dm.seqlen, dm.dstate, static_cast<uint16_t*>(p.dB), static_cast<uint16_t*>(p.dC));
+                         dm.seqlen, Lp, dm.dstate, static_cast<uint16_t*>(p.dB), static_cast<uint16_t*>(p.dC));
     else
       hipLaunchKernelGGL((bwd_reduce_bc_kernel<F32>), dim3(blocks), dim3(256), 0, s, p.part, dm.batch, dm.cblocks,
-                         dm.seqlen, dm.dstate, static_cast<float*>(p.dB), static_cast<float*>(p.dC));
+                         dm.seqlen, Lp, dm.dstate, static_cast<float*>(p.dB), static_cast<float*>(p.dC));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
