@@ -249,10 +249,16 @@ ss_status ss_scan_bwd(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss
                       float* dA, float* dDskip, float* ddt_bias, float* dh0,
                       void* workspace, size_t workspace_bytes, void* stream);
 
-/* ss_scan_bwd with options: flags must be 0 (reserved); ckpt (nullable) holds
- * the checkpoints a ss_scan_fwd_ex call stored for the same inputs (same x, dt,
- * B, A, dt_bias, h0), and the backward then reads them instead of recomputing
- * them.  Everything else is as for ss_scan_bwd; results are identical. */
+/* ss_scan_bwd with options.  flags: 0 or SS_FLAG_DT_PER_ROW, for the backward
+ * of the per-row form of ss_scan_fwd_ex: dt is (batch, seqlen), and ddt, also
+ * (batch, seqlen) in the I/O dtype, is the gradient of that shared dt, the sum
+ * over channels of the per-channel gradient (summed in a fixed order).
+ * SS_FLAG_ZOH returns SS_ERR_UNSUPPORTED (the backward differentiates the
+ * first-order input term only), as do unknown bits.  ckpt (nullable) holds the
+ * checkpoints a ss_scan_fwd_ex call stored for the same inputs (same x, dt, B,
+ * A, dt_bias, h0 and flags), and the backward then reads them instead of
+ * recomputing them.  Everything else is as for ss_scan_bwd; with flags 0,
+ * results are identical to ss_scan_bwd's. */
 ss_status ss_scan_bwd_ex(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io, uint32_t flags,
                          const void* x, const void* dt, const void* z,
                          const void* B, const void* C, const float* A,

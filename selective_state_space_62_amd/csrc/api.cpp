@@ -534,8 +534,8 @@ BwdLayout bwd_layout(int64_t batch, int64_t dim, int dstate, int64_t seqlen) {
   off += round256((size_t)batch * seqlen * dstate * 2 * sizeof(float));
   w.ckpt = off;
   off += round256((size_t)batch * dim * w.chunks * dstate * sizeof(float));
-  w.part = off;   // dB/dC partials (batch, channel block, output, token), tokens padded to whole chunks
-  off += round256((size_t)batch * w.cblocks * 2 * dstate * (w.chunks * ck) * sizeof(float));
+  w.part = off;   // partials (batch, channel block, output, token), tokens padded to whole chunks
+  off += round256((size_t)batch * w.cblocks * ssscan::bwd_part_outputs(dstate) * (w.chunks * ck) * sizeof(float));
   w.dA_p = off;
   off += round256((size_t)batch * dim * dstate * sizeof(float));
   w.dD_p = off;
@@ -551,7 +551,7 @@ ss_status scan_bwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, 
                         const float* Dskip, const float* dt_bias, const float* h0, const void* dy,
                         const float* dh_final, void* dx, void* ddt, void* dz, void* dB, void* dC, float* dA,
                         float* dDskip, float* ddt_bias, float* dh0, void* workspace, size_t workspace_bytes,
-                        void* stream, const float* ckpt = nullptr) {
+                        void* stream, const float* ckpt = nullptr, bool dt_row = false) {
   ss_status st = check_sizes(batch, dim, dstate, seqlen, io);
   if (st != SS_OK) return st;
   if (!A) return fail(SS_ERR_INVALID_ARG, "A is NULL");
@@ -584,14 +584,15 @@ ss_status scan_bwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, 
   }
   const int64_t eb = elem_bytes(io);
   const int64_t seq_bytes = batch * dim * seqlen * eb;
+  const int64_t dt_bytes = dt_row ? batch * seqlen * eb : seq_bytes;   // dt and ddt
   const int64_t bc_bytes = batch * dstate * seqlen * eb;
   const int64_t st_bytes = batch * dim * dstate * 4;
-  const Range ins[] = {rng("x", x, seq_bytes), rng("dt", dt, seq_bytes), rng("z", z, seq_bytes),
+  const Range ins[] = {rng("x", x, seq_bytes), rng("dt", dt, dt_bytes), rng("z", z, seq_bytes),
                        rng("B", B, bc_bytes), rng("C", C, bc_bytes), rng("A", A, dim * dstate * 4),
                        rng("Dskip", Dskip, dim * 4), rng("dt_bias", dt_bias, dim * 4), rng("h0", h0, st_bytes),
                        rng("dy", dy, seq_bytes), rng("dh_final", dh_final, st_bytes),
                        rng("ckpt", ckpt, batch * dim * wl.chunks * dstate * 4)};
-  const Range outs[] = {rng("dx", dx, seq_bytes), rng("ddt", ddt, seq_bytes), rng("dz", dz, seq_bytes),
+  const Range outs[] = {rng("dx", dx, seq_bytes), rng("ddt", ddt, dt_bytes), rng("dz", dz, seq_bytes),
                         rng("dB", dB, bc_bytes), rng("dC", dC, bc_bytes), rng("dA", dA, dim * dstate * 4),
                         rng("dDskip", dDskip, dim * 4), rng("ddt_bias", ddt_bias, dim * 4),
                         rng("dh0", dh0, st_bytes), rng("workspace", workspace, seqlen > 0 ? (int64_t)wl.total : 0)};
@@ -643,6 +644,7 @@ ss_status scan_bwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, 
   dm.io = io_code(io);
   dm.vec = (seqlen % 2) == 0 ? 1 : 0;
   dm.have_ckpt = ckpt ? 1 : 0;
+  dm.dt_row = dt_row ? 1 : 0;
   ssscan::BwdPtrs bp{};
   bp.x = x;
   bp.dt = dt;
@@ -811,10 +813,11 @@ ss_status ss_scan_bwd_ex(int64_t batch, int64_t dim, int dstate, int64_t seqlen,
                          const float* dh_final, const float* ckpt, void* dx, void* ddt, void* dz, void* dB, void* dC,
                          float* dA, float* dDskip, float* ddt_bias, float* dh0, void* workspace,
                          size_t workspace_bytes, void* stream) {
-  if (flags != 0) return fail(SS_ERR_UNSUPPORTED, "unknown flags 0x%x (the backward is first-order, per-channel dt)",
-                              (unsigned)flags);
+  if (flags & SS_FLAG_ZOH) return fail(SS_ERR_UNSUPPORTED, "the backward pass has no zero-order-hold form");
+  if (flags & ~(uint32_t)SS_FLAG_DT_PER_ROW) return fail(SS_ERR_UNSUPPORTED, "unknown flags 0x%x", (unsigned)flags);
   return scan_bwd_impl(batch, dim, dstate, seqlen, io, x, dt, z, B, C, A, Dskip, dt_bias, h0, dy, dh_final, dx,
-                       ddt, dz, dB, dC, dA, dDskip, ddt_bias, dh0, workspace, workspace_bytes, stream, ckpt);
+                       ddt, dz, dB, dC, dA, dDskip, ddt_bias, dh0, workspace, workspace_bytes, stream, ckpt,
+                       (flags & SS_FLAG_DT_PER_ROW) != 0);
 }
 
 ss_status ss_timing_enable(int enable) {

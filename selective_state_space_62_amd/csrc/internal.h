@@ -52,7 +52,12 @@ struct BwdDims {
   int32_t io;
   int32_t vec;          // 1: every lane's 2-token span of a row is aligned for one vector access
   int32_t have_ckpt;    // 1: BwdPtrs::ckpt already holds the checkpoints (stored by the forward)
+  int32_t dt_row;       // 1: dt (and ddt) hold one value per (batch row, token), shared by the channels
 };
+
+// dB/dC partials per (batch row, channel block): 2 N outputs plus one for the
+// per-row dt gradient, each over the tokens padded to whole backward chunks
+constexpr int bwd_part_outputs(int dstate) { return 2 * dstate + 1; }
 
 struct BwdPtrs {
   const void* x;
@@ -75,7 +80,7 @@ struct BwdPtrs {
   float* ddt_bias;        // nullable
   float* dh0;             // nullable
   float* ckpt;            // workspace: (batch, chunks, dim, dstate) state at every chunk start
-  float* part;            // workspace: (batch, cblocks, seqlen, 2 dstate) dB/dC partial sums
+  float* part;            // workspace: (batch, cblocks, bwd_part_outputs, padded seqlen) partial sums
   float* dA_p;            // workspace: (batch, dim, dstate) per-row sums
   float* dD_p;            // workspace: (batch, dim)
   float* dbias_p;         // workspace: (batch, dim)

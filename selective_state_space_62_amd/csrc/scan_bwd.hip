@@ -106,6 +106,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10)))
   constexpr int NS = N / SG;           // state components per lane
   constexpr int CK = kSpan * SG;       // chunk length (tokens)
   constexpr int NOUT = 2 * N;          // dB and dC values per token
+  constexpr int NPART = bwd_part_outputs(N);   // partial outputs: dB, dC, then the per-row ddt
   constexpr int THREADS = 64 * G;
   constexpr int SW = SpanT<IO, kSpan>::kWords;
   static_assert(NS >= 1 && N % SG == 0, "G * K must divide N");
@@ -135,6 +136,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10)))
   const int64_t L = dm.seqlen;
   const int64_t ch = b * dm.dim + dc;
   const int64_t row = ch * L;
+  const int64_t dt_row = dm.dt_row ? b * L : row;   // dt per (row, token) is shared by the row's channels
   const bool vec = dm.vec != 0;
   const bool has_z = p.z != nullptr;
   const int64_t nck = (L + CK - 1) / CK;
@@ -170,7 +172,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10)))
     const int64_t t0 = k * CK;
     const int valid = own_valid(k);
     load_span<IO, kSpan>(x, row + t0 + j_own, valid, vec, f.x);
-    load_span<IO, kSpan>(dt, row + t0 + j_own, valid, vec, f.dt);
+    load_span<IO, kSpan>(dt, dt_row + t0 + j_own, valid, vec, f.dt);
     if (grads) {
       if (has_z) load_span<IO, kSpan>(z, row + t0 + j_own, valid, vec, f.z);
       load_span<IO, kSpan>(dy, row + t0 + j_own, valid, vec, f.dy);
@@ -240,7 +242,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10)))
   float dD_acc = 0.0f, dbias_acc = 0.0f;
   // dB/dC partials (batch, channel block, output, token), tokens padded to whole chunks
   const int64_t Lp = nck * CK;
-  float* __restrict__ part_row = p.part + (b * dm.cblocks + cb) * NOUT * Lp;
+  float* __restrict__ part_row = p.part + (b * dm.cblocks + cb) * NPART * Lp;
   // the lanes that write them: the first K lanes of each row that holds a sum (all
   // rows for NS == 2, rows 0 and 2 for NS == 1), and the output each one writes.
   // The sums cover the whole workgroup (channels past dim add zeros), so a
@@ -364,22 +366,16 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10)))
         s_pp[j][w][c] = make_float2(ddp * kLn2, sB);   // both lanes of a channel hold the sums
         uo[j] = bc_channel_sum<NS, K>(dBv, dCv);
       }
-    }
-    __syncthreads();
-
-    // the chunk's dB/dC partials, 16-byte stores of consecutive tokens (padding
-    // tokens of the ragged last chunk write zeros, which nothing reads)
-    if (pw) {
-      static_assert(CK % 2 == 0, "whole pairs of tokens");
-      if constexpr (CK % 4 == 0) {
-#pragma unroll
-        for (int q = 0; q < CK; q += 4)
-          *reinterpret_cast<float4*>(pdst + t0 + q) = make_float4(uo[q], uo[q + 1], uo[q + 2], uo[q + 3]);
-      } else {
-#pragma unroll
-        for (int q = 0; q < CK; q += 2) *reinterpret_cast<float2*>(pdst + t0 + q) = make_float2(uo[q], uo[q + 1]);
+      // the dB/dC partials of a group of consecutive tokens, stored once the
+      // group is done (padding tokens of the ragged last chunk write zeros,
+      // which nothing reads)
+      constexpr int SV = (CK % 4 == 0) ? 4 : 2;
+      if (j % SV == 0 && pw) {
+        if constexpr (SV == 4) *reinterpret_cast<float4*>(pdst + t0 + j) = make_float4(uo[j], uo[j + 1], uo[j + 2], uo[j + 3]);
+        else *reinterpret_cast<float2*>(pdst + t0 + j) = make_float2(uo[j], uo[j + 1]);
       }
     }
+    __syncthreads();
     // owners: dx = Delta sum lam B + dr Dskip, ddt = (dDelta) sigmoid(v)
     {
       float dxv[kSpan], ddtv[kSpan];
@@ -397,12 +393,23 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10)))
         }
         dxv[i] = fmaf(sB, s_dd[j][c].x, s_dr[j][c] * skip);   // Delta and dr of the owned token from LDS
         const float dv = fmaf(sB, xv[i], ddp) * sigmoid2(v2[i]);
-        ddtv[i] = dv;
+        ddtv[i] = dv;   // zero for padding tokens and inactive channels
         if (FULL || i < valid) dbias_acc += dv;
       }
       if (act && (FULL || valid > 0)) {
         store_span<IO, kSpan>(static_cast<T*>(p.dx), row + tf, valid, vec, dxv);
-        store_span<IO, kSpan>(static_cast<T*>(p.ddt), row + tf, valid, vec, ddtv);
+        if (!dm.dt_row) store_span<IO, kSpan>(static_cast<T*>(p.ddt), row + tf, valid, vec, ddtv);
+      }
+      if (dm.dt_row) {
+        // a shared dt's gradient is the sum over channels: every owner of this
+        // lane's two tokens sits in this wave (one lane per channel), so the
+        // channel sum is formed in the wave; row 0 of the result holds the first
+        // owned token's sum and row 2 the second's, for each lane parity hk
+        static_assert(kSpan == 2, "two owned tokens per lane");
+        const float d0[1] = {ddtv[0]}, d1[1] = {ddtv[1]};
+        const float u = bc_channel_sum<1, K>(d0, d1);
+        if ((lane & 15) < K && (prow & 1) == 0 && (FULL || t0 + j_own + (prow >> 1) < t1))
+          part_row[(int64_t)NOUT * Lp + t0 + j_own + (prow >> 1)] = u;
       }
     }
     __syncthreads();
@@ -436,25 +443,27 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4, 10)))
   }
 }
 
-// dB[b, n, t] and dC[b, n, t]: the channel blocks' partials, in block order.
-// Partials are (batch, block, output, token) with Lp tokens per output; one
-// thread per (b, output, t), tokens fastest, so loads and stores are coalesced.
+// dB[b, n, t], dC[b, n, t] and, for a per-row dt, ddt[b, t]: the channel
+// blocks' partials, in block order.  Partials are (batch, block, output, token)
+// with bwd_part_outputs(N) outputs of Lp tokens; one thread per (b, output, t),
+// tokens fastest, so loads and stores are coalesced.
 template <typename IO>
 __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restrict__ part, int64_t batch,
                                                             int64_t cblocks, int64_t L, int64_t Lp, int N,
-                                                            typename IO::T* __restrict__ dB,
-                                                            typename IO::T* __restrict__ dC) {
-  const int64_t nout = 2 * (int64_t)N;
+                                                            int nred, typename IO::T* __restrict__ dB,
+                                                            typename IO::T* __restrict__ dC,
+                                                            typename IO::T* __restrict__ ddt_row) {
+  const int64_t npart = bwd_part_outputs(N);
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= batch * nout * L) return;
+  if (i >= batch * nred * L) return;
   const int64_t t = i % L;
-  const int64_t o = (i / L) % nout;
-  const int64_t b = i / (L * nout);
-  const float* src = part + (b * cblocks * nout + o) * Lp + t;
+  const int64_t o = (i / L) % nred;
+  const int64_t b = i / (L * nred);
+  const float* src = part + (b * cblocks * npart + o) * Lp + t;
   float acc = 0.0f;
-  for (int64_t q = 0; q < cblocks; ++q) acc += src[q * nout * Lp];
-  const int64_t n = o % N;
-  store_one<IO>(o < N ? dB : dC, (b * N + n) * L + t, acc);
+  for (int64_t q = 0; q < cblocks; ++q) acc += src[q * npart * Lp];
+  if (o == 2 * N) store_one<IO>(ddt_row, b * L + t, acc);
+  else store_one<IO>(o < N ? dB : dC, (b * N + o % N) * L + t, acc);
 }
 
 // dA, dDskip and dt_bias's gradient: sums over batch rows, in row order.
@@ -515,17 +524,20 @@ int bwd_chunk_len(int dstate) { return bwd_chunk_tokens(dstate); }
 hipError_t launch_scan_bwd(const BwdDims& dm, const BwdPtrs& p, hipStream_t s) {
   hipError_t e = (dm.io == kIoBf16) ? launch_bwd_n<BF16>(dm, p, s) : launch_bwd_n<F32>(dm, p, s);
   if (e != hipSuccess) return e;
-  const int64_t nbc = dm.batch * dm.seqlen * 2 * dm.dstate;
+  const int nred = 2 * dm.dstate + (dm.dt_row ? 1 : 0);   // outputs to reduce
+  const int64_t nbc = dm.batch * dm.seqlen * nred;
   if (nbc > 0) {
     const unsigned blocks = (unsigned)((nbc + 255) / 256);
     const int64_t ck = bwd_chunk_tokens(dm.dstate);
     const int64_t Lp = (dm.seqlen + ck - 1) / ck * ck;
     if (dm.io == kIoBf16)
       hipLaunchKernelGGL((bwd_reduce_bc_kernel<BF16>), dim3(blocks), dim3(256), 0, s, p.part, dm.batch, dm.cblocks,
-                         dm.seqlen, Lp, dm.dstate, static_cast<uint16_t*>(p.dB), static_cast<uint16_t*>(p.dC));
+                         dm.seqlen, Lp, dm.dstate, nred, static_cast<uint16_t*>(p.dB), static_cast<uint16_t*>(p.dC),
+                         static_cast<uint16_t*>(p.ddt));
     else
       hipLaunchKernelGGL((bwd_reduce_bc_kernel<F32>), dim3(blocks), dim3(256), 0, s, p.part, dm.batch, dm.cblocks,
-                         dm.seqlen, Lp, dm.dstate, static_cast<float*>(p.dB), static_cast<float*>(p.dC));
+                         dm.seqlen, Lp, dm.dstate, nred, static_cast<float*>(p.dB), static_cast<float*>(p.dC),
+                         static_cast<float*>(p.ddt));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -140,11 +140,13 @@ def bwd_workspace_bytes(batch, dim, dstate, seqlen, dtype=torch.bfloat16) -> int
 def scan_bwd(x, dt, B, C, A, dy, z=None, Dskip=None, dt_bias=None, h0=None, dh_final=None, *, workspace=None,
              need_dA=True, need_dDskip=True, need_ddt_bias=True, need_dh0=True, ckpt=None):
     """Gradients of ``scan_fwd`` (first-order input term) for upstream gradients dy
-    (batch, D, L) and dh_final (batch, D, N) float32 (None = 0).
+    (batch, D, L) and dh_final (batch, D, N) float32 (None = 0).  dt may be
+    (batch, L): one value per token shared by the channels (SS_FLAG_DT_PER_ROW);
+    its gradient is then (batch, L), the sum over channels.
 
-    Returns a dict: dx, ddt, dz (None without z) in the I/O dtype, shaped like x;
-    dB, dC shaped like B; dA (D, N), dDskip (D,), ddt_bias (D,), dh0 (batch, D, N)
-    in float32 (None where not requested).
+    Returns a dict: dx, ddt, dz (None without z) in the I/O dtype, shaped like x
+    (ddt like dt); dB, dC shaped like B; dA (D, N), dDskip (D,), ddt_bias (D,),
+    dh0 (batch, D, N) in float32 (None where not requested).
     """
     if x.dtype not in _IO:
         raise TypeError("x must be float32 or bfloat16")
@@ -154,15 +156,17 @@ def scan_bwd(x, dt, B, C, A, dy, z=None, Dskip=None, dt_bias=None, h0=None, dh_f
     batch, dim, L = x.shape
     N = A.shape[1]
     io = _IO[x.dtype]
-    for t, name, shape in ((x, "x", (batch, dim, L)), (dt, "dt", (batch, dim, L)), (z, "z", (batch, dim, L)),
-                           (dy, "dy", (batch, dim, L)), (B, "B", (batch, N, L)), (C, "C", (batch, N, L))):
+    dt_row = dt is not None and dt.dim() == 2
+    for t, name, shape in ((x, "x", (batch, dim, L)), (dt, "dt", (batch, L) if dt_row else (batch, dim, L)),
+                           (z, "z", (batch, dim, L)), (dy, "dy", (batch, dim, L)), (B, "B", (batch, N, L)),
+                           (C, "C", (batch, N, L))):
         _need(t, name, x.dtype, shape, dev)
     _need(A, "A", torch.float32, (dim, N), dev)
     _need(Dskip, "Dskip", torch.float32, (dim,), dev)
     _need(dt_bias, "dt_bias", torch.float32, (dim,), dev)
     _need(h0, "h0", torch.float32, (batch, dim, N), dev)
     _need(dh_final, "dh_final", torch.float32, (batch, dim, N), dev)
-    out = dict(dx=torch.empty_like(x), ddt=torch.empty_like(x), dz=torch.empty_like(x) if z is not None else None,
+    out = dict(dx=torch.empty_like(x), ddt=torch.empty_like(dt), dz=torch.empty_like(x) if z is not None else None,
                dB=torch.empty_like(B), dC=torch.empty_like(C),
                dA=torch.empty((dim, N), dtype=torch.float32, device=dev) if need_dA else None,
                dDskip=torch.empty(dim, dtype=torch.float32, device=dev) if need_dDskip else None,
@@ -178,9 +182,10 @@ def scan_bwd(x, dt, B, C, A, dy, z=None, Dskip=None, dt_bias=None, h0=None, dh_f
     outs = (_ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dz"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dA"]),
             _ptr(out["dDskip"]), _ptr(out["ddt_bias"]), _ptr(out["dh0"]), _ptr(workspace), workspace.numel(),
             _stream(dev))
-    if ckpt is not None:
-        _need(ckpt, "ckpt", torch.float32, (ckpt_numel(batch, dim, N, L),), dev)
-        _b.ss_scan_bwd_ex(batch, dim, N, L, io, 0, *ins, _ptr(ckpt), *outs)
+    if ckpt is not None or dt_row:
+        if ckpt is not None:
+            _need(ckpt, "ckpt", torch.float32, (ckpt_numel(batch, dim, N, L),), dev)
+        _b.ss_scan_bwd_ex(batch, dim, N, L, io, _b.SS_FLAG_DT_PER_ROW if dt_row else 0, *ins, _ptr(ckpt), *outs)
     else:
         _b.ss_scan_bwd(batch, dim, N, L, io, *ins, *outs)
     return out

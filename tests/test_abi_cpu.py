@@ -205,11 +205,15 @@ def test_bwd_validation(case, status):
 
 
 def test_bwd_workspace_bytes():
-    # (batch, L, N, 2) B/C re-layout + (batch, D, L/16, N) checkpoints + (batch, D/32, L, 2N) dB/dC partials
-    # + (batch, D, N) + 2 (batch, D) per-row sums, each rounded to 256 bytes
+    # (batch, L, N, 2) B/C re-layout + (batch, D, L/16, N) checkpoints + (batch, D/32, 2N + 1, L) partials
+    # (dB, dC and a per-row ddt) + (batch, D, N) + 2 (batch, D) per-row sums, each rounded to 256 bytes
     n = b.ss_scan_bwd_workspace_bytes(8, 5120, 16, 2048, b.SS_BF16)
-    expect = 8 * 2048 * 32 * 4 + 8 * 5120 * 128 * 16 * 4 + 8 * 160 * 2048 * 32 * 4 + 8 * 5120 * 16 * 4 + 2 * 8 * 5120 * 4
+    expect = 8 * 2048 * 32 * 4 + 8 * 5120 * 128 * 16 * 4 + 8 * 160 * 33 * 2048 * 4 + 8 * 5120 * 16 * 4 + 2 * 8 * 5120 * 4
     assert n == expect
+    # a ragged length pads the partials' tokens to whole 16-token chunks
+    r = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    n = b.ss_scan_bwd_workspace_bytes(1, 64, 16, 17, b.SS_F32)
+    assert n == r(17 * 32 * 4) + r(64 * 2 * 16 * 4) + r(2 * 33 * 32 * 4) + r(64 * 16 * 4) + 2 * r(64 * 4)
     assert b.ss_scan_bwd_workspace_bytes(2, 64, 16, 0, b.SS_F32) == 0
     assert b.ss_scan_bwd_workspace_bytes(2, 64, 3, 16, b.SS_F32) == 0
 
@@ -289,9 +293,17 @@ def test_ckpt_bytes_and_bwd_ex_flags():
     names = list(_BWD_NAMES)
     (batch, dim, N, L) = (2, 64, 16, 256)
     a = {n: ALIGNED + i * (1 << 30) for i, n in enumerate(names)}
-    st = b.lib.ss_scan_bwd_ex(batch, dim, N, L, b.SS_F32, 1, *[a[n] for n in names[:11]], None,
-                              *[a[n] for n in names[11:]], ALIGNED + (1 << 36), 1 << 30, None)
-    assert st == b.SS_ERR_UNSUPPORTED and "flags" in b.last_error()
+    def call(flags, **over):
+        v = dict(a, **over)
+        return b.lib.ss_scan_bwd_ex(batch, dim, N, L, b.SS_F32, flags, *[v[n] for n in names[:11]], None,
+                                    *[v[n] for n in names[11:]], ALIGNED + (1 << 36), 1 << 30, None)
+    assert call(b.SS_FLAG_ZOH) == b.SS_ERR_UNSUPPORTED and "zero-order-hold" in b.last_error()
+    assert call(4) == b.SS_ERR_UNSUPPORTED and "flags" in b.last_error()
+    # with one dt per (row, token), dt and ddt are batch * seqlen long: a ddt that
+    # starts inside that span overlaps dt
+    row_bytes = batch * L * 4
+    assert call(b.SS_FLAG_DT_PER_ROW, ddt=a["dt"] + row_bytes - 16) == b.SS_ERR_INVALID_ARG
+    assert "ddt overlaps input dt" in b.last_error()
 
 
 def test_timing_record_empty():
