@@ -160,8 +160,8 @@ typedef enum { SS_FLAG_ZOH = 1u, SS_FLAG_DT_PER_ROW = 2u } ss_flags;
 /* ckpt (nullable, fp32, 16-byte aligned, ss_scan_ckpt_bytes long, no overlap
  * with anything else) receives the state entering every chunk of the backward
  * pass (16 tokens at dstate >= 8), laid out (batch, chunks, dim, dstate): a
- * training step's forward hands them to ss_scan_bwd_ex, which then skips its own
- * checkpoint sweep.  Not with SS_FLAG_ZOH (the backward is first-order). */
+ * training step's forward hands them to ss_scan_bwd_ex (with the same flags),
+ * which then skips its own checkpoint sweep. */
 ss_status ss_scan_fwd_ex(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io, uint32_t flags,
                          const void* x, const void* dt, const void* z,
                          const void* B, const void* C, const float* A,
@@ -213,7 +213,8 @@ ss_status ss_scan_shard_combine(int64_t batch, int64_t dim, int dstate, int64_t 
                                 const float* A, const float* dsum, const float* h_end,
                                 const float* h0, float* h_in, float* h_final, void* stream);
 
-/* Backward pass of ss_scan_fwd (first-order input term): the gradients of a
+/* Backward pass of ss_scan_fwd (first-order input term; ss_scan_bwd_ex with
+ * SS_FLAG_ZOH is that of ss_scan_fwd_zoh): the gradients of a
  * loss with respect to every input of the scan, given dy = dLoss/dy and
  * dh_final = dLoss/dh_final.  Training differentiates the scan, and the state
  * is recomputed in the backward pass instead of being stored (reader's notes on
@@ -249,12 +250,15 @@ ss_status ss_scan_bwd(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss
                       float* dA, float* dDskip, float* ddt_bias, float* dh0,
                       void* workspace, size_t workspace_bytes, void* stream);
 
-/* ss_scan_bwd with options.  flags: 0 or SS_FLAG_DT_PER_ROW, for the backward
- * of the per-row form of ss_scan_fwd_ex: dt is (batch, seqlen), and ddt, also
- * (batch, seqlen) in the I/O dtype, is the gradient of that shared dt, the sum
- * over channels of the per-channel gradient (summed in a fixed order).
- * SS_FLAG_ZOH returns SS_ERR_UNSUPPORTED (the backward differentiates the
- * first-order input term only), as do unknown bits.  ckpt (nullable) holds the
+/* ss_scan_bwd with options, the backward of ss_scan_fwd_ex with the same flags:
+ *  SS_FLAG_ZOH         the zero-order-hold input term c = (e^(Delta A) - 1)/A
+ *                      (Delta when A = 0) in place of Delta, whose derivatives
+ *                      are dc/dDelta = e^(Delta A) and dc/dA = Delta^2 psi(Delta A),
+ *                      psi(u) = (u e^u - e^u + 1)/u^2;
+ *  SS_FLAG_DT_PER_ROW  dt is (batch, seqlen), and ddt, also (batch, seqlen) in the
+ *                      I/O dtype, is the gradient of that shared dt, the sum over
+ *                      channels of the per-channel gradient (in a fixed order).
+ * Unknown bits return SS_ERR_UNSUPPORTED.  ckpt (nullable) holds the
  * checkpoints a ss_scan_fwd_ex call stored for the same inputs (same x, dt, B,
  * A, dt_bias, h0 and flags), and the backward then reads them instead of
  * recomputing them.  Everything else is as for ss_scan_bwd; with flags 0,

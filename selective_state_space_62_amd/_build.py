@@ -15,7 +15,7 @@ BUILD = PKG / "_build"
 LIB = PKG / "libssscan.so"
 
 SOURCES = ["api.cpp", "scan_fwd.hip", "scan_bf16_euler.hip", "scan_bf16_zoh.hip", "scan_f32_euler.hip",
-           "scan_f32_zoh.hip", "scan_bwd.hip", "state_update.hip"]
+           "scan_f32_zoh.hip", "scan_bwd.hip", "scan_bwd_zoh.hip", "state_update.hip"]
 ARCH = "gfx950"
 
 # Packed-FP32 VALU ops are disabled for all device code; see the design notes.

@@ -313,10 +313,7 @@ ss_status scan_fwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, 
   const Range ins[] = {rng("x", x, seq_bytes), rng("dt", dt, dt_bytes), rng("z", z, seq_bytes),
                        rng("B", B, bc_bytes), rng("C", C, bc_bytes), rng("A", A, dim * dstate * 4),
                        rng("Dskip", Dskip, dim * 4), rng("dt_bias", dt_bias, dim * 4), rng("h0", h0, st_bytes)};
-  if (ckpt) {
-    if (zoh) return fail(SS_ERR_UNSUPPORTED, "checkpoints are for the first-order backward pass (no ZOH)");
-    if (!aligned(ckpt, 16)) return fail(SS_ERR_INVALID_ARG, "ckpt is not 16-byte aligned");
-  }
+  if (ckpt && !aligned(ckpt, 16)) return fail(SS_ERR_INVALID_ARG, "ckpt is not 16-byte aligned");
   const int64_t ck_len = ssscan::bwd_chunk_len(dstate);
   const int64_t ck_count = (seqlen + ck_len - 1) / ck_len;
   const Range outs[] = {rng("y", y, seq_bytes), rng("h_final", h_final, st_bytes),
@@ -551,7 +548,7 @@ ss_status scan_bwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, 
                         const float* Dskip, const float* dt_bias, const float* h0, const void* dy,
                         const float* dh_final, void* dx, void* ddt, void* dz, void* dB, void* dC, float* dA,
                         float* dDskip, float* ddt_bias, float* dh0, void* workspace, size_t workspace_bytes,
-                        void* stream, const float* ckpt = nullptr, bool dt_row = false) {
+                        void* stream, const float* ckpt = nullptr, bool dt_row = false, bool zoh = false) {
   ss_status st = check_sizes(batch, dim, dstate, seqlen, io);
   if (st != SS_OK) return st;
   if (!A) return fail(SS_ERR_INVALID_ARG, "A is NULL");
@@ -645,6 +642,7 @@ ss_status scan_bwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, 
   dm.vec = (seqlen % 2) == 0 ? 1 : 0;
   dm.have_ckpt = ckpt ? 1 : 0;
   dm.dt_row = dt_row ? 1 : 0;
+  dm.zoh = zoh ? 1 : 0;
   ssscan::BwdPtrs bp{};
   bp.x = x;
   bp.dt = dt;
@@ -813,11 +811,11 @@ ss_status ss_scan_bwd_ex(int64_t batch, int64_t dim, int dstate, int64_t seqlen,
                          const float* dh_final, const float* ckpt, void* dx, void* ddt, void* dz, void* dB, void* dC,
                          float* dA, float* dDskip, float* ddt_bias, float* dh0, void* workspace,
                          size_t workspace_bytes, void* stream) {
-  if (flags & SS_FLAG_ZOH) return fail(SS_ERR_UNSUPPORTED, "the backward pass has no zero-order-hold form");
-  if (flags & ~(uint32_t)SS_FLAG_DT_PER_ROW) return fail(SS_ERR_UNSUPPORTED, "unknown flags 0x%x", (unsigned)flags);
+  if (flags & ~(uint32_t)(SS_FLAG_ZOH | SS_FLAG_DT_PER_ROW))
+    return fail(SS_ERR_UNSUPPORTED, "unknown flags 0x%x", (unsigned)flags);
   return scan_bwd_impl(batch, dim, dstate, seqlen, io, x, dt, z, B, C, A, Dskip, dt_bias, h0, dy, dh_final, dx,
                        ddt, dz, dB, dC, dA, dDskip, ddt_bias, dh0, workspace, workspace_bytes, stream, ckpt,
-                       (flags & SS_FLAG_DT_PER_ROW) != 0);
+                       (flags & SS_FLAG_DT_PER_ROW) != 0, (flags & SS_FLAG_ZOH) != 0);
 }
 
 ss_status ss_timing_enable(int enable) {

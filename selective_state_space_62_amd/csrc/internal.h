@@ -53,6 +53,7 @@ struct BwdDims {
   int32_t vec;          // 1: every lane's 2-token span of a row is aligned for one vector access
   int32_t have_ckpt;    // 1: BwdPtrs::ckpt already holds the checkpoints (stored by the forward)
   int32_t dt_row;       // 1: dt (and ddt) hold one value per (batch row, token), shared by the channels
+  int32_t zoh;          // 1: zero-order-hold input term
 };
 
 // dB/dC partials per (batch row, channel block): 2 N outputs plus one for the
@@ -114,6 +115,8 @@ hipError_t launch_shard_combine(int64_t batch, int64_t dim, int dstate, int64_t 
                                 const float* dsum, const float* h_end, const float* h0, float* h_in, float* h_final,
                                 hipStream_t s);
 hipError_t launch_scan_bwd(const BwdDims& dm, const BwdPtrs& p, hipStream_t s);
+// the main backward kernel alone, zero-order-hold form (scan_bwd_zoh.hip)
+hipError_t launch_scan_bwd_zoh_main(const BwdDims& dm, const BwdPtrs& p, hipStream_t s);
 hipError_t launch_fill_zero(float* dst, int64_t n, hipStream_t s);
 hipError_t launch_state_update(int64_t batch, int64_t dim, int dstate, int io, bool zoh, bool dt_row, float* state,
                                const void* x, const void* dt, const void* z, const void* B, const void* C,

@@ -1,0 +1,523 @@
+// Backward pass of the selective scan (ss_scan_bwd) for gfx950: the main kernel
+// template and its launch dispatch, instantiated by scan_bwd.hip (first-order
+// input term) and scan_bwd_zoh.hip (zero-order hold).
+//
+// Training runs the scan forward and then backward; the pages' fused kernel
+// keeps the expanded state on-chip and recomputes it in the backward pass
+// instead of storing it (reader's notes, kurisu.si, "What they did", Selective
+// SSM item).  The gradients are those of the forward definition
+//   Delta_t = softplus(dt_t + dt_bias),  Abar = exp(Delta_t A_n),
+//   h_t[n] = Abar h_(t-1)[n] + Delta_t B_t[n] x_t,
+//   y_t = r_t silu(z_t),  r_t = C_t . h_t + Dskip x_t,
+// taken in reverse token order with the adjoint state lam_t = dLoss/dh_t:
+//   dr_t = dy_t silu(z_t),  dz_t = dy_t r_t silu'(z_t),
+//   lam_t = Abar_(t+1) lam_(t+1) + dr_t C_t  (lam_L = dh_final),
+//   dC_t[n] += dr_t h_t[n],  dB_t[n] += lam_t[n] Delta_t x_t   (summed over channels),
+//   with dAbar = lam_t h_(t-1):  dDelta += dAbar Abar A,  dA += dAbar Abar Delta,
+//   dDelta += x_t sum_n lam_t[n] B_t[n],  dx_t = Delta_t sum_n lam_t[n] B_t[n] + dr_t Dskip,
+//   ddt_t = dDelta sigmoid(dt_t + dt_bias),  dh0 = Abar_0 lam_0.
+//
+// One workgroup owns 64/K channels of one batch row, laid out like the forward
+// kernel: G waves, K adjacent lanes per channel, each lane NS = N/(G K) state
+// components.  Work goes in chunks of CK = 2 G K tokens; each lane owns 2 tokens
+// of a chunk for the per-(token, channel) work (Delta, the gate, dx, ddt, dz).
+//  1. A forward sweep over the sequence stores the state at every chunk start
+//     (the checkpoints, in the workspace).
+//  2. Chunks are then visited last to first.  The chunk's states (and their
+//     decay factors Abar) are recomputed from its checkpoint into registers, with
+//     the readout (dz needs r_t); the owner of each token forms dr and dz; then
+//     every lane runs the adjoint state back through the chunk, reusing the
+//     recomputed Abar.  The sums over state components (for dx and dDelta) reach
+//     the token's owner through LDS, as the forward's readout does.
+// dB and dC are sums over channels.  Every wave holds all of the workgroup's
+// channels (for its own state components), so a wave forms the workgroup's sums
+// by itself: a swap of wave halves between two registers (v_permlane32_swap)
+// and an add, a swap of row pairs (v_permlane16_swap) and an add, then DPP adds
+// within the 16-lane rows.  A chunk's sums stay in registers and are written
+// token-contiguous, one partial per (workgroup, output, token), to the
+// workspace; bwd_reduce_bc_kernel adds a batch row's partials in a fixed order.
+// dA, dDskip and dt_bias's gradient are summed per (row, channel) in registers
+// and over rows by bwd_reduce_param_kernel.  All sums have a fixed order:
+// results are deterministic.  The next chunk's global operands are fetched while
+// the current one computes, and whole chunks run without per-token guards.
+#pragma once
+
+#include <type_traits>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace ssscan {
+namespace bwd_detail {
+
+using namespace dev;
+
+constexpr int kSpan = 2;   // tokens of a chunk owned per lane
+
+// Workgroup index -> logical block so that the channel blocks of one batch row
+// share an XCD (workgroups are dealt to the 8 XCDs round-robin).
+__device__ __forceinline__ int64_t bwd_logical_block(int64_t wg, int64_t nwg) {
+  if ((nwg & 7) != 0) return wg;
+  return (wg & 7) * (nwg >> 3) + (wg >> 3);
+}
+
+// sigmoid(v) given v2 = v log2(e); 0 when e^-v overflows
+__device__ __forceinline__ float sigmoid2(float v2) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-v2));
+}
+
+// dB and dC of one token summed over the channels of a wave (lane = K c + hk):
+// the result in row r (16 lanes) is, for NS == 2, dB[0], dC[0], dB[1], dC[1] for
+// r = 0..3, and for NS == 1, dB, dB, dC, dC; within a row, lanes with the same
+// hk (lane mod K) hold the same sum.  The order of the additions is fixed.
+template <int NS, int K>
+__device__ __forceinline__ float bc_channel_sum(const float (&dB)[NS], const float (&dC)[NS]) {
+  static_assert(NS == 1 || NS == 2, "one or two state components per lane");
+  auto swap32 = [](float a, float b) {   // ([a lower half, b lower half], [a upper half, b upper half])
+    return __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  };
+  auto swap16 = [](float a, float b) {   // ([a r0, b r0, a r2, b r2], [a r1, b r1, a r3, b r3])
+    return __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  };
+  float u;
+  if constexpr (NS == 2) {
+    const auto pb = swap32(dB[0], dB[1]);
+    const auto pc = swap32(dC[0], dC[1]);
+    const float sb = __uint_as_float(pb[0]) + __uint_as_float(pb[1]);   // lower half dB[0], upper dB[1]
+    const float sc = __uint_as_float(pc[0]) + __uint_as_float(pc[1]);
+    const auto q = swap16(sb, sc);
+    u = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+  } else {
+    const auto pv = swap32(dB[0], dC[0]);
+    const float sv = __uint_as_float(pv[0]) + __uint_as_float(pv[1]);   // lower half dB, upper dC
+    const auto q = swap16(sv, sv);
+    u = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+  }
+  u += __builtin_amdgcn_update_dpp(0.0f, u, 0x128, 0xf, 0xf, false);   // row_ror:8
+  u += __builtin_amdgcn_update_dpp(0.0f, u, 0x124, 0xf, 0xf, false);   // row_ror:4
+  u += __builtin_amdgcn_update_dpp(0.0f, u, 0x4E, 0xf, 0xf, false);    // lanes 2 apart
+  if constexpr (K == 1) u += __builtin_amdgcn_update_dpp(0.0f, u, 0xB1, 0xf, 0xf, false);   // neighbours
+  return u;
+}
+
+// psi(u) = (u e^u - e^u + 1) / u^2: the zero-order-hold input coefficient
+// c = (e^(Delta A) - 1) / A has dc/dA = Delta^2 psi(Delta A).  Takes u2 = u
+// log2(e) and E = e^u.  |u| < 1: the series sum_k (k + 1) u^k / (k + 2)! to
+// degree 9 (the first dropped term is below 1e-7 relative); otherwise
+// ((u - 1) E + 1) / u^2 with one fma, whose rounding is ~1e-7 / u^2 relative.
+__device__ __forceinline__ float zoh_psi(float u2, float E) {
+  const float u = u2 * kLn2;
+  float p = fmaf(u, 1.0f / 3991680.0f, 1.0f / 403200.0f);
+  p = fmaf(p, u, 1.0f / 45360.0f);
+  p = fmaf(p, u, 1.0f / 5760.0f);
+  p = fmaf(p, u, 1.0f / 840.0f);
+  p = fmaf(p, u, 1.0f / 144.0f);
+  p = fmaf(p, u, 1.0f / 30.0f);
+  p = fmaf(p, u, 1.0f / 8.0f);
+  p = fmaf(p, u, 1.0f / 3.0f);
+  p = fmaf(p, u, 0.5f);
+  const float q = fmaf(u - 1.0f, E, 1.0f) * __builtin_amdgcn_rcpf(u * u);
+  return fabsf(u) < 1.0f ? p : q;
+}
+
+// Three waves per SIMD at N = 16 (about 160 VGPRs); at most 32 KB of LDS.
+// ZOH: the zero-order-hold input term, c = Delta phi(Delta A) in place of Delta.
+template <int N, int G, int K, typename IO, bool ZOH>
+__global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(ZOH ? 3 : 4, 10))) void scan_bwd_kernel(
+    const BwdDims dm, const BwdPtrs p) {
+  using T = typename IO::T;
+  // per token and channel in LDS: (Delta, Delta x), and for ZOH also (x, x Delta^2)
+  using DD = std::conditional_t<ZOH, float4, float2>;
+  constexpr int CPB = 64 / K;          // channels per workgroup
+  constexpr int SG = G * K;            // state groups
+  constexpr int NS = N / SG;           // state components per lane
+  constexpr int CK = kSpan * SG;       // chunk length (tokens)
+  constexpr int NOUT = 2 * N;          // dB and dC values per token
+  constexpr int NPART = bwd_part_outputs(N);   // partial outputs: dB, dC, then the per-row ddt
+  constexpr int THREADS = 64 * G;
+  constexpr int SW = SpanT<IO, kSpan>::kWords;
+  static_assert(NS >= 1 && N % SG == 0, "G * K must divide N");
+  static_assert(K == 1 || K == 2, "one or two lanes per channel");
+  static_assert(CK * N <= THREADS, "one B/C piece per thread");
+  static_assert(CK == bwd_chunk_tokens(N), "the chunk length the forward's checkpoints assume");
+
+  __shared__ DD s_dd[CK][CPB];         // (Delta, Delta x[, x, x Delta^2]) per token and channel
+  __shared__ float s_bc[CK][2 * N];    // B_n, C_n of the chunk's tokens
+  __shared__ float2 s_pp[CK][G][CPB];  // per-wave partial sums (readout; dDelta and sum lam B)
+  __shared__ float s_dr[CK][CPB];      // dr per token and channel
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int c = lane / K;
+  const int hk = lane % K;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int sg = w * K + hk;
+
+  const int64_t nwg = dm.cblocks * dm.batch;
+  const int64_t lb = bwd_logical_block(blockIdx.x, nwg);
+  const int64_t cb = lb % dm.cblocks;
+  const int64_t b = lb / dm.cblocks;
+  const int64_t d = cb * CPB + c;
+  const bool act = d < dm.dim;
+  const int64_t dc = act ? d : dm.dim - 1;   // inactive lanes run a valid row with zero gradients
+  const int64_t L = dm.seqlen;
+  const int64_t ch = b * dm.dim + dc;
+  const int64_t row = ch * L;
+  const int64_t dt_row = dm.dt_row ? b * L : row;   // dt per (row, token) is shared by the row's channels
+  const bool vec = dm.vec != 0;
+  const bool has_z = p.z != nullptr;
+  const int64_t nck = (L + CK - 1) / CK;
+
+  const T* __restrict__ x = static_cast<const T*>(p.x);
+  const T* __restrict__ dt = static_cast<const T*>(p.dt);
+  const T* __restrict__ z = static_cast<const T*>(p.z);
+  const T* __restrict__ dy = static_cast<const T*>(p.dy);
+
+  float A2[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) A2[s] = p.A[dc * N + sg * NS + s] * kLog2e;
+  const float bias2 = p.dt_bias ? p.dt_bias[dc] * kLog2e : 0.0f;
+  const float skip = p.Dskip ? p.Dskip[dc] : 0.0f;
+  const float* __restrict__ bc_row = p.bc + b * L * (2 * N);
+  // checkpoints (batch, chunk, dim, N): a workgroup's channels are contiguous per chunk
+  float* __restrict__ ck_row = p.ckpt + (b * nck * dm.dim + dc) * N + sg * NS;
+  const int64_t ck_stride = dm.dim * N;
+
+  const int j_own = sg * kSpan;   // first token of a chunk this lane owns
+  auto chunk_end = [&](int64_t k) { return (k * CK + CK < L) ? k * CK + CK : L; };
+  auto own_valid = [&](int64_t k) {
+    const int64_t v = chunk_end(k) - (k * CK + j_own);
+    return (int)(v < 0 ? 0 : (v < kSpan ? v : kSpan));
+  };
+
+  // A chunk's global operands, fetched one chunk ahead of their use.
+  struct Fetch {
+    uint32_t x[SW], dt[SW], z[SW], dy[SW];
+    float2 bc;
+  };
+  auto fetch = [&](int64_t k, bool grads, Fetch& f) {
+    const int64_t t0 = k * CK;
+    const int valid = own_valid(k);
+    load_span<IO, kSpan>(x, row + t0 + j_own, valid, vec, f.x);
+    load_span<IO, kSpan>(dt, dt_row + t0 + j_own, valid, vec, f.dt);
+    if (grads) {
+      if (has_z) load_span<IO, kSpan>(z, row + t0 + j_own, valid, vec, f.z);
+      load_span<IO, kSpan>(dy, row + t0 + j_own, valid, vec, f.dy);
+    }
+    f.bc = make_float2(0.0f, 0.0f);
+    if (tid < CK * N && t0 + tid / N < chunk_end(k))
+      f.bc = reinterpret_cast<const float2*>(bc_row + t0 * (2 * N))[tid];
+  };
+  // Delta and Delta x of the owned tokens into LDS (zero Delta for padding
+  // tokens), and the chunk's B and C
+  auto stage = [&](int valid, const Fetch& f, float (&xv)[kSpan], float (&dl)[kSpan], float (&v2)[kSpan]) {
+#pragma unroll
+    for (int i = 0; i < kSpan; ++i) {
+      xv[i] = span_elem<IO>(f.x, i);
+      v2[i] = fmaf(span_elem<IO>(f.dt, i), kLog2e, bias2);
+      dl[i] = (i < valid) ? softplus_dt(span_elem<IO>(f.dt, i), bias2) : 0.0f;
+      if constexpr (ZOH) s_dd[j_own + i][c] = make_float4(dl[i], dl[i] * xv[i], xv[i], dl[i] * dl[i] * xv[i]);
+      else s_dd[j_own + i][c] = make_float2(dl[i], dl[i] * xv[i]);
+    }
+    if (tid < CK * N) reinterpret_cast<float2*>(&s_bc[0][0])[tid] = f.bc;
+  };
+
+  // ---- 1. forward sweep: the state at every chunk start (unless the forward
+  // pass already stored them) ----
+  if (!dm.have_ckpt) {
+    float h[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) h[s] = p.h0 ? p.h0[ch * N + sg * NS + s] : 0.0f;
+    Fetch f;
+    fetch(0, false, f);
+    // FULL (a compile-time tag): all CK tokens of the chunk lie inside the sequence
+    auto sweep = [&](auto full_tag, int64_t k) {
+      constexpr bool FULL = decltype(full_tag)::value;
+      if (act) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) ck_row[k * ck_stride + s] = h[s];
+      }
+      float xv[kSpan], dl[kSpan], v2[kSpan];
+      stage(FULL ? kSpan : own_valid(k), f, xv, dl, v2);
+      if (k + 1 < nck) fetch(k + 1, false, f);
+      __syncthreads();
+      const int nj = FULL ? CK : (int)(chunk_end(k) - k * CK);
+#pragma unroll
+      for (int j = 0; j < CK; ++j) {
+        if (FULL || j < nj) {
+          const DD o = s_dd[j][c];
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            float u2 = o.x * A2[s];
+            if constexpr (ZOH) __asm__ volatile("" : "+v"(u2) : "v"(h[s]));   // token by token (registers)
+            const float E = __builtin_amdgcn_exp2f(u2);
+            float in = o.y * s_bc[j][2 * (sg * NS + s)];
+            if constexpr (ZOH) in *= zoh_phi(u2, E);
+            h[s] = fmaf(E, h[s], in);
+          }
+        }
+      }
+      __syncthreads();
+    };
+    const int64_t nfull = L / CK;
+    for (int64_t k = 0; k < nfull; ++k) sweep(std::true_type{}, k);
+    if (nfull < nck) sweep(std::false_type{}, nfull);
+  }
+
+  // ---- 2. chunks last to first ----
+  float lam[NS], dAacc[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    lam[s] = (act && p.dh_final) ? p.dh_final[ch * N + sg * NS + s] : 0.0f;
+    dAacc[s] = 0.0f;
+  }
+  float dD_acc = 0.0f, dbias_acc = 0.0f;
+  // dB/dC partials (batch, channel block, output, token), tokens padded to whole chunks
+  const int64_t Lp = nck * CK;
+  float* __restrict__ part_row = p.part + (b * dm.cblocks + cb) * NPART * Lp;
+  // the lanes that write them: the first K lanes of each row that holds a sum (all
+  // rows for NS == 2, rows 0 and 2 for NS == 1), and the output each one writes.
+  // The sums cover the whole workgroup (channels past dim add zeros), so a
+  // writing lane writes whether or not its own channel is active.
+  const int prow = lane >> 4;
+  const bool pw = (lane & 15) < K && (NS == 2 || (prow & 1) == 0);
+  const int pwhich = NS == 2 ? (prow & 1) : (prow >> 1);   // 0: dB, 1: dC
+  const int ps = NS == 2 ? (prow >> 1) : 0;
+  float* __restrict__ pdst = part_row + (int64_t)(pwhich * N + sg * NS + ps) * Lp;
+
+  Fetch f;
+  fetch(nck - 1, true, f);
+  float ckn[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) ckn[s] = act ? ck_row[(nck - 1) * ck_stride + s] : 0.0f;
+
+  auto chunk = [&](auto full_tag, int64_t k) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    const int64_t t0 = k * CK;
+    const int64_t t1 = chunk_end(k);
+    const int nj = FULL ? CK : (int)(t1 - t0);
+    const int64_t tf = t0 + j_own;
+    const int valid = FULL ? kSpan : own_valid(k);
+    float xv[kSpan], dl[kSpan], v2[kSpan];
+    stage(valid, f, xv, dl, v2);
+    // z and dy of the owned tokens stay raw until the owners use them
+    uint32_t cz[SW], cdy[SW];
+#pragma unroll
+    for (int q = 0; q < SW; ++q) {
+      cz[q] = f.z[q];
+      cdy[q] = f.dy[q];
+    }
+    float hs[CK + 1][NS];   // hs[j] = the state before chunk token j
+    // Es[j] = Abar of chunk token j, kept for the adjoint step (first order; the
+    // zero-order-hold form needs the registers for phi and psi and recomputes it)
+    float Es[ZOH ? 1 : CK][NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) hs[0][s] = ckn[s];
+    if (k > 0) {
+      fetch(k - 1, true, f);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) ckn[s] = act ? ck_row[(k - 1) * ck_stride + s] : 0.0f;
+    }
+    __syncthreads();
+
+    // recompute the chunk's states, with the readout
+#pragma unroll
+    for (int j = 0; j < CK; ++j) {
+      if (FULL || j < nj) {
+        const DD o = s_dd[j][c];
+        float acc = 0.0f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          float u2 = o.x * A2[s];
+          if constexpr (ZOH) __asm__ volatile("" : "+v"(u2) : "v"(hs[j][s]));   // token by token (registers)
+          const float E = __builtin_amdgcn_exp2f(u2);
+          if constexpr (!ZOH) Es[j][s] = E;
+          float in = o.y * s_bc[j][2 * (sg * NS + s)];
+          if constexpr (ZOH) in *= zoh_phi(u2, E);
+          hs[j + 1][s] = fmaf(E, hs[j][s], in);
+          acc = fmaf(s_bc[j][2 * (sg * NS + s) + 1], hs[j + 1][s], acc);
+        }
+        if constexpr (K == 2) acc += __builtin_amdgcn_update_dpp(0.0f, acc, 0xB1, 0xf, 0xf, false);
+        s_pp[j][w][c].x = acc;   // both lanes of a channel hold the sum and store it
+      }
+    }
+    __syncthreads();
+
+    // owners: r, dr = dy silu(z), dz = dy r silu'(z)
+    {
+      float dzv[kSpan];
+#pragma unroll
+      for (int i = 0; i < kSpan; ++i) {
+        const int j = j_own + i;
+        float r = 0.0f;
+        if (FULL || i < valid) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) r += s_pp[j][g][c].x;
+        }
+        r = fmaf(skip, xv[i], r);
+        const float dyv = act ? span_elem<IO>(cdy, i) : 0.0f;   // padding tokens load as zero
+        float gate = 1.0f;
+        dzv[i] = 0.0f;
+        if (has_z) {
+          const float zv = span_elem<IO>(cz, i);
+          const float sz = sigmoid2(zv * kLog2e);
+          gate = zv * sz;
+          dzv[i] = dyv * r * (sz * fmaf(zv, 1.0f - sz, 1.0f));
+        }
+        const float drv = dyv * gate;
+        dD_acc = fmaf(drv, xv[i], dD_acc);
+        s_dr[j][c] = drv;
+      }
+      if (has_z && act && (FULL || valid > 0)) store_span<IO, kSpan>(static_cast<T*>(p.dz), row + tf, valid, vec, dzv);
+    }
+    __syncthreads();
+
+    // the adjoint state back through the chunk
+    float uo[CK];   // this lane's dB/dC sum per chunk token (kept by the writing lanes)
+#pragma unroll
+    for (int j = 0; j < CK; ++j) uo[j] = 0.0f;
+#pragma unroll
+    for (int j = CK - 1; j >= 0; --j) {
+      if constexpr (ZOH) __builtin_amdgcn_sched_barrier(0);   // token by token (registers)
+      if (FULL || j < nj) {
+        const float dr = s_dr[j][c];
+        const DD o = s_dd[j][c];
+        float ddp = 0.0f, sB = 0.0f;   // ddp in units of A log2(e)
+        float sE = 0.0f;               // ZOH: sum lam e^u B, the input term's dDelta factor
+        float dBv[NS], dCv[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const float Bv = s_bc[j][2 * (sg * NS + s)];
+          const float Cv = s_bc[j][2 * (sg * NS + s) + 1];
+          lam[s] = fmaf(dr, Cv, lam[s]);
+          dCv[s] = dr * hs[j + 1][s];
+          float u2 = o.x * A2[s];
+          if constexpr (ZOH) __asm__ volatile("" : "+v"(u2) : "v"(lam[s]));   // token by token (registers)
+          const float E = ZOH ? __builtin_amdgcn_exp2f(u2) : Es[ZOH ? 0 : j][s];
+          const float ga = lam[s] * hs[j][s] * E;
+          ddp = fmaf(ga, A2[s], ddp);
+          dAacc[s] = fmaf(ga, o.x, dAacc[s]);
+          if constexpr (ZOH) {
+            // c = Delta phi: dx and dB carry phi; dc/dDelta = e^u; dc/dA = Delta^2 psi
+            const float lp = lam[s] * zoh_phi(u2, E);
+            const float lB = lam[s] * Bv;
+            sB = fmaf(lp, Bv, sB);
+            dBv[s] = lp * o.y;
+            sE = fmaf(lB, E, sE);
+            dAacc[s] = fmaf(lB, o.w * zoh_psi(u2, E), dAacc[s]);
+            // keep the update here: sunk to the end of the chunk, it would hold
+            // every token's u and Abar in registers until then
+            __asm__ volatile("" : "+v"(dAacc[s]));
+          } else {
+            sB = fmaf(lam[s], Bv, sB);
+            dBv[s] = lam[s] * o.y;
+          }
+          lam[s] *= E;
+        }
+        if constexpr (ZOH) ddp = fmaf(ddp, kLn2, o.z * sE);   // the whole dDelta, in natural units
+        if constexpr (K == 2) {
+          ddp += __builtin_amdgcn_update_dpp(0.0f, ddp, 0xB1, 0xf, 0xf, false);
+          sB += __builtin_amdgcn_update_dpp(0.0f, sB, 0xB1, 0xf, 0xf, false);
+        }
+        s_pp[j][w][c] = make_float2(ZOH ? ddp : ddp * kLn2, sB);   // both lanes of a channel hold the sums
+        uo[j] = bc_channel_sum<NS, K>(dBv, dCv);
+      }
+      // the dB/dC partials of a group of consecutive tokens, stored once the
+      // group is done (padding tokens of the ragged last chunk write zeros,
+      // which nothing reads)
+      constexpr int SV = (CK % 4 == 0) ? 4 : 2;
+      if (j % SV == 0 && pw) {
+        if constexpr (SV == 4) *reinterpret_cast<float4*>(pdst + t0 + j) = make_float4(uo[j], uo[j + 1], uo[j + 2], uo[j + 3]);
+        else *reinterpret_cast<float2*>(pdst + t0 + j) = make_float2(uo[j], uo[j + 1]);
+      }
+    }
+    __syncthreads();
+    // owners: dx = Delta sum lam B + dr Dskip, ddt = (dDelta) sigmoid(v)
+    {
+      float dxv[kSpan], ddtv[kSpan];
+#pragma unroll
+      for (int i = 0; i < kSpan; ++i) {
+        const int j = j_own + i;
+        float ddp = 0.0f, sB = 0.0f;
+        if (FULL || i < valid) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const float2 pv = s_pp[j][g][c];
+            ddp += pv.x;
+            sB += pv.y;
+          }
+        }
+        dxv[i] = fmaf(sB, s_dd[j][c].x, s_dr[j][c] * skip);   // Delta and dr of the owned token from LDS
+        // Euler: dDelta = (decay part) + x sum lam B; ZOH: the lanes already added x sum lam e^u B
+        const float dv = (ZOH ? ddp : fmaf(sB, xv[i], ddp)) * sigmoid2(v2[i]);
+        ddtv[i] = dv;   // zero for padding tokens and inactive channels
+        if (FULL || i < valid) dbias_acc += dv;
+      }
+      if (act && (FULL || valid > 0)) {
+        store_span<IO, kSpan>(static_cast<T*>(p.dx), row + tf, valid, vec, dxv);
+        if (!dm.dt_row) store_span<IO, kSpan>(static_cast<T*>(p.ddt), row + tf, valid, vec, ddtv);
+      }
+      if (dm.dt_row) {
+        // a shared dt's gradient is the sum over channels: every owner of this
+        // lane's two tokens sits in this wave (one lane per channel), so the
+        // channel sum is formed in the wave; row 0 of the result holds the first
+        // owned token's sum and row 2 the second's, for each lane parity hk
+        static_assert(kSpan == 2, "two owned tokens per lane");
+        const float d0[1] = {ddtv[0]}, d1[1] = {ddtv[1]};
+        const float u = bc_channel_sum<1, K>(d0, d1);
+        if ((lane & 15) < K && (prow & 1) == 0 && (FULL || t0 + j_own + (prow >> 1) < t1))
+          part_row[(int64_t)NOUT * Lp + t0 + j_own + (prow >> 1)] = u;
+      }
+    }
+    __syncthreads();
+  };
+  {
+    int64_t k = nck - 1;
+    if (L % CK != 0) chunk(std::false_type{}, k--);   // the ragged last chunk comes first
+    for (; k >= 0; --k) chunk(std::true_type{}, k);
+  }
+
+  // dh0 = Abar_0 lam_0 (lam already carries the factor); per-(row, channel) sums
+  if (act) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (p.dh0) p.dh0[ch * N + sg * NS + s] = lam[s];
+      p.dA_p[ch * N + sg * NS + s] = dAacc[s];
+    }
+  }
+  s_pp[sg][0][c] = make_float2(dD_acc, dbias_acc);   // CK >= SG rows
+  __syncthreads();
+  if (sg == 0 && act) {
+    float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+    for (int g = 0; g < SG; ++g) {
+      const float2 v = s_pp[g][0][c];
+      a0 += v.x;
+      a1 += v.y;
+    }
+    p.dD_p[ch] = a0;
+    p.dbias_p[ch] = a1;
+  }
+}
+
+template <int N, int G, int K, typename IO, bool ZOH>
+hipError_t launch_bwd_t(const BwdDims& dm, const BwdPtrs& p, hipStream_t s) {
+  const int64_t nwg = dm.cblocks * dm.batch;
+  hipLaunchKernelGGL((scan_bwd_kernel<N, G, K, IO, ZOH>), dim3((unsigned)nwg), dim3(64 * G), 0, s, dm, p);
+  return hipGetLastError();
+}
+
+template <typename IO, bool ZOH>
+hipError_t launch_bwd_n(const BwdDims& dm, const BwdPtrs& p, hipStream_t s) {
+  switch (dm.dstate) {
+    case 1: return launch_bwd_t<1, 1, 1, IO, ZOH>(dm, p, s);
+    case 2: return launch_bwd_t<2, 2, 1, IO, ZOH>(dm, p, s);
+    case 4: return launch_bwd_t<4, 4, 1, IO, ZOH>(dm, p, s);
+    case 8: return launch_bwd_t<8, 4, 2, IO, ZOH>(dm, p, s);
+    case 16: return launch_bwd_t<16, 4, 2, IO, ZOH>(dm, p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace bwd_detail
+}  // namespace ssscan

@@ -36,9 +36,9 @@ struct BcPiece<1> {
 // At most 96 VGPRs (5 waves per SIMD): with 4 waves per workgroup and 28 KB of
 // LDS, five workgroups fit on a CU at once, which the two-lanes-per-channel plan
 // needs to keep every CU's share resident.
-// CKPT (first-order, full pass only): also store the state entering every
-// backward-pass chunk, for a training step's backward.  It is a separate
-// instantiation so that the plain scan keeps its registers.
+// CKPT_K (full pass only): also store the state entering every backward-pass
+// chunk, for a training step's backward.  It is a separate instantiation so
+// that the plain scan keeps its registers.
 template <int N, int G, int K, typename IO, bool AGG, bool ZOH, bool CKPT_K>
 __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(5, 10))) void scan_kernel(
     const ScanDims dm, const typename IO::T* __restrict__ x, const typename IO::T* __restrict__ dt,
@@ -345,9 +345,9 @@ hipError_t launch_scan_t(const ScanDims& dm, const ScanPtrs& p, hipStream_t s) {
   using E = typename IO::T;
   const int64_t cblocks = (dm.dim + 64 / K - 1) / (64 / K);
   const int64_t nwg = cblocks * dm.batch * dm.num_chunks;
-  if constexpr (!AGG && !ZOH) {
+  if constexpr (!AGG) {
     if (p.ckpt) {
-      hipLaunchKernelGGL((scan_kernel<N, G, K, IO, false, false, true>), dim3((unsigned)nwg), dim3(64 * G), 0, s,
+      hipLaunchKernelGGL((scan_kernel<N, G, K, IO, false, ZOH, true>), dim3((unsigned)nwg), dim3(64 * G), 0, s,
                          dm, (const E*)p.x, (const E*)p.dt, (const E*)p.z, p.bc, p.A, p.Dskip, p.dt_bias, p.h0,
                          p.h_in, (E*)p.y, p.h_final, p.agg_h, p.agg_s, p.ckpt);
       return hipGetLastError();

@@ -138,9 +138,9 @@ def bwd_workspace_bytes(batch, dim, dstate, seqlen, dtype=torch.bfloat16) -> int
 
 
 def scan_bwd(x, dt, B, C, A, dy, z=None, Dskip=None, dt_bias=None, h0=None, dh_final=None, *, workspace=None,
-             need_dA=True, need_dDskip=True, need_ddt_bias=True, need_dh0=True, ckpt=None):
-    """Gradients of ``scan_fwd`` (first-order input term) for upstream gradients dy
-    (batch, D, L) and dh_final (batch, D, N) float32 (None = 0).  dt may be
+             need_dA=True, need_dDskip=True, need_ddt_bias=True, need_dh0=True, ckpt=None, zoh=False):
+    """Gradients of ``scan_fwd`` (zoh=True: of ``scan_fwd(..., zoh=True)``) for upstream
+    gradients dy (batch, D, L) and dh_final (batch, D, N) float32 (None = 0).  dt may be
     (batch, L): one value per token shared by the channels (SS_FLAG_DT_PER_ROW);
     its gradient is then (batch, L), the sum over channels.
 
@@ -182,10 +182,11 @@ def scan_bwd(x, dt, B, C, A, dy, z=None, Dskip=None, dt_bias=None, h0=None, dh_f
     outs = (_ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dz"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dA"]),
             _ptr(out["dDskip"]), _ptr(out["ddt_bias"]), _ptr(out["dh0"]), _ptr(workspace), workspace.numel(),
             _stream(dev))
-    if ckpt is not None or dt_row:
+    if ckpt is not None or dt_row or zoh:
         if ckpt is not None:
             _need(ckpt, "ckpt", torch.float32, (ckpt_numel(batch, dim, N, L),), dev)
-        _b.ss_scan_bwd_ex(batch, dim, N, L, io, _b.SS_FLAG_DT_PER_ROW if dt_row else 0, *ins, _ptr(ckpt), *outs)
+        flags = (_b.SS_FLAG_DT_PER_ROW if dt_row else 0) | (_b.SS_FLAG_ZOH if zoh else 0)
+        _b.ss_scan_bwd_ex(batch, dim, N, L, io, flags, *ins, _ptr(ckpt), *outs)
     else:
         _b.ss_scan_bwd(batch, dim, N, L, io, *ins, *outs)
     return out

@@ -264,9 +264,11 @@ def test_flags_validation():
                               b._plan_ptr(plan), None)
     assert st == b.SS_ERR_UNSUPPORTED and "flags" in b.last_error()
     ck = ALIGNED + (1 << 38)
-    st = b.lib.ss_scan_fwd_ex(batch, dim, N, L, io, b.SS_FLAG_ZOH, *args, ck, p["workspace"], p["workspace_bytes"],
-                              b._plan_ptr(plan), None)
-    assert st == b.SS_ERR_UNSUPPORTED and "ZOH" in b.last_error()
+    # checkpoints are stored under ZOH too (the backward has that form): a ZOH call
+    # with a checkpoint buffer gets as far as the overlap checks
+    st = b.lib.ss_scan_fwd_ex(batch, dim, N, L, io, b.SS_FLAG_ZOH, *args, p["x"], p["workspace"],
+                              p["workspace_bytes"], b._plan_ptr(plan), None)
+    assert st == b.SS_ERR_INVALID_ARG and "overlaps" in b.last_error()
     st = b.lib.ss_scan_fwd_ex(batch, dim, N, L, io, 0, *args, ck + 4, p["workspace"], p["workspace_bytes"],
                               b._plan_ptr(plan), None)
     assert st == b.SS_ERR_INVALID_ARG and "ckpt" in b.last_error()
@@ -297,7 +299,9 @@ def test_ckpt_bytes_and_bwd_ex_flags():
         v = dict(a, **over)
         return b.lib.ss_scan_bwd_ex(batch, dim, N, L, b.SS_F32, flags, *[v[n] for n in names[:11]], None,
                                     *[v[n] for n in names[11:]], ALIGNED + (1 << 36), 1 << 30, None)
-    assert call(b.SS_FLAG_ZOH) == b.SS_ERR_UNSUPPORTED and "zero-order-hold" in b.last_error()
+    # ZOH is accepted: such a call reaches the argument checks
+    assert call(b.SS_FLAG_ZOH, dx=a["x"]) == b.SS_ERR_INVALID_ARG and "dx overlaps input x" in b.last_error()
+    assert call(b.SS_FLAG_ZOH | b.SS_FLAG_DT_PER_ROW, dx=a["x"]) == b.SS_ERR_INVALID_ARG
     assert call(4) == b.SS_ERR_UNSUPPORTED and "flags" in b.last_error()
     # with one dt per (row, token), dt and ddt are batch * seqlen long: a ddt that
     # starts inside that span overlaps dt

@@ -1,0 +1,169 @@
+"""The zero-order-hold backward (ss_scan_bwd_ex with SS_FLAG_ZOH) on the GPU
+against the oracle's gradients.
+
+With the zero-order hold the input coefficient is c = (e^(Delta A) - 1)/A, the
+discretisation under which Theorem 1 of the reader's notes holds exactly
+(kurisu.si, "Main results (verified)"); its derivatives dc/dDelta = e^(Delta A)
+and dc/dA = Delta^2 psi(Delta A) are pinned in the oracle by finite differences
+(tests/pins.py).  The GPU evaluates phi = c / Delta and psi by series near
+u = Delta A = 0 and by their closed forms elsewhere; the cases below span both
+regions.  Tolerances as for the first-order backward (tests/test_gpu_bwd.py).
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import log, random_problem, rel_l2, to_dev, to_f64
+from workloads import inputs
+
+pytestmark = pytest.mark.gpu
+
+ELEMENT = ("dx", "ddt", "dz", "dh0")
+SUMS = ("dA", "dDskip", "ddt_bias", "dB", "dC")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def ss():
+    import selective_state_space_62_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def o():
+    return oracle.default()
+
+
+def _tol(io, name):
+    if io == "bf16":
+        return 2e-2
+    return 1e-5 if name in ELEMENT else 5e-5
+
+
+def _problem(rng, batch, D, N, L, io, optional=True, a_range=None, dt_shift=0.0):
+    raw, par, f64 = random_problem(rng, batch, D, N, L, io, with_z=optional, with_skip=optional,
+                                   with_bias=optional, with_h0=optional)
+    if a_range is not None:
+        par["A"] = -rng.uniform(a_range[0], a_range[1], (D, N)).astype(np.float32)
+    if dt_shift:
+        v = inputs.raw_to_f64(raw["dt"], io).astype(np.float32) + np.float32(dt_shift)
+        raw["dt"] = v if io == "f32" else inputs.f32_to_bf16_bits(v)
+        f64["dt"] = inputs.raw_to_f64(raw["dt"], io)
+    dy = rng.standard_normal((batch, D, L)).astype(np.float32)
+    raw["dy"] = dy if io == "f32" else inputs.f32_to_bf16_bits(dy)
+    f64["dy"] = inputs.raw_to_f64(raw["dy"], io)
+    par["dh_final"] = rng.standard_normal((batch, D, N)).astype(np.float32) if optional else None
+    return raw, par, f64
+
+
+def _run(ss, raw, par, io, dev, **kw):
+    import torch
+    t = {k: to_dev(v, io, dev) for k, v in raw.items()}
+    p = {k: (torch.from_numpy(v).to(dev) if v is not None else None) for k, v in par.items()}
+    g = ss.scan_bwd(t["x"], t["dt"], t["B"], t["C"], p["A"], t["dy"], z=t.get("z"), Dskip=p["Dskip"],
+                    dt_bias=p["dt_bias"], h0=p["h0"], dh_final=p["dh_final"], zoh=True, **kw)
+    torch.cuda.synchronize()
+    return g, t, p
+
+
+def _oracle(o, f64, par):
+    return o.scan_bwd(f64["x"], f64["dt"], f64["B"], f64["C"], par["A"], f64["dy"], z=f64.get("z"),
+                      Dskip=par["Dskip"], dt_bias=par["dt_bias"], h0=par["h0"], dh_final=par["dh_final"], zoh=True)
+
+
+def _compare(g, r, io, what):
+    errs = {k: rel_l2(to_f64(g[k]), r[k]) for k in ELEMENT + SUMS if g.get(k) is not None and r.get(k) is not None}
+    log("%s: %s" % (what, ", ".join("%s %.2e" % kv for kv in errs.items())))
+    for k, e in errs.items():
+        assert e <= _tol(io, k), (what, k, e, errs)
+
+
+CASES = [(2, 77, 16, 37), (1, 64, 16, 64), (3, 33, 8, 50), (2, 20, 4, 31), (2, 70, 2, 9), (1, 130, 1, 13),
+         (2, 40, 16, 1), (2, 64, 16, 17)]
+
+
+@pytest.mark.parametrize("case", CASES, ids=["x".join(map(str, c)) for c in CASES])
+@pytest.mark.parametrize("optional", [True, False], ids=["all-inputs", "no-optional"])
+def test_bwd_zoh_f32_matches_oracle(ss, o, dev, case, optional):
+    batch, D, N, L = case
+    log("bwd zoh f32 %s optional=%s" % (case, optional))
+    rng = np.random.default_rng(zlib.crc32(repr(("zoh", case, optional)).encode()))
+    raw, par, f64 = _problem(rng, batch, D, N, L, "f32", optional)
+    g, _, _ = _run(ss, raw, par, "f32", dev)
+    _compare(g, _oracle(o, f64, par), "f32", "bwd zoh %s" % (case,))
+
+
+@pytest.mark.parametrize("what,a_range,dt_shift", [
+    ("series region: A near zero", (1e-4, 2e-2), 0.0),
+    ("closed-form region: large Delta", (0.5, 8.0), 2.5),
+    ("both regions in every wave", (1e-3, 40.0), 1.0),
+], ids=["small-u", "large-u", "mixed-u"])
+def test_bwd_zoh_u_regions(ss, o, dev, what, a_range, dt_shift):
+    """u = Delta A in the series region of phi and psi (|u| below 1/4 and 1), in
+    the closed-form region, and mixed within every wave."""
+    rng = np.random.default_rng(zlib.crc32(repr(("zoh-u", what)).encode()))
+    raw, par, f64 = _problem(rng, 2, 96, 16, 70, "f32", True, a_range=a_range, dt_shift=dt_shift)
+    g, _, _ = _run(ss, raw, par, "f32", dev)
+    _compare(g, _oracle(o, f64, par), "f32", "bwd zoh %s" % what)
+
+
+def test_bwd_zoh_bf16(ss, o, dev):
+    rng = np.random.default_rng(zlib.crc32(b"zoh-bf16"))
+    raw, par, f64 = _problem(rng, 2, 512, 16, 600, "bf16", True)
+    g, _, _ = _run(ss, raw, par, "bf16", dev)
+    _compare(g, _oracle(o, f64, par), "bf16", "bwd zoh bf16 2x512x16x600")
+
+
+def test_bwd_zoh_checkpoints_and_determinism(ss, o, dev):
+    """A ZOH forward that stores checkpoints feeds the ZOH backward to identical
+    gradients; two runs give identical bits."""
+    import torch
+    batch, D, N, L = 2, 96, 16, 130
+    rng = np.random.default_rng(zlib.crc32(b"zoh-ckpt"))
+    raw, par, f64 = _problem(rng, batch, D, N, L, "f32", True)
+    g1, t, p = _run(ss, raw, par, "f32", dev)
+    g2, _, _ = _run(ss, raw, par, "f32", dev)
+    ck = torch.full((ss.ckpt_numel(batch, D, N, L),), float("nan"), device=dev)
+    y0, h0f = ss.scan_fwd(t["x"], t["dt"], t["B"], t["C"], p["A"], z=t["z"], Dskip=p["Dskip"], dt_bias=p["dt_bias"],
+                          h0=p["h0"], zoh=True)
+    y1, h1f = ss.scan_fwd(t["x"], t["dt"], t["B"], t["C"], p["A"], z=t["z"], Dskip=p["Dskip"], dt_bias=p["dt_bias"],
+                          h0=p["h0"], zoh=True, ckpt=ck)
+    g3, _, _ = _run(ss, raw, par, "f32", dev, ckpt=ck)
+    assert torch.equal(y0, y1) and torch.equal(h0f, h1f)
+    assert not torch.isnan(ck).any()
+    for k, v in g1.items():
+        if v is not None:
+            assert torch.equal(v, g2[k]), k
+            assert torch.equal(v, g3[k]), k
+    _compare(g1, _oracle(o, f64, par), "f32", "bwd zoh ckpt")
+
+
+def test_bwd_zoh_dt_per_row(ss, o, dev):
+    """ZOH with one dt per (row, token): the shared dt's gradient is the channel
+    sum of the oracle's per-channel gradient with dt repeated."""
+    import torch
+    batch, D, N, L = 2, 77, 16, 45
+    rng = np.random.default_rng(zlib.crc32(b"zoh-row"))
+    raw, par, f64 = _problem(rng, batch, D, N, L, "f32", True)
+    dt_row = (0.5 * rng.standard_normal((batch, L))).astype(np.float32)
+    raw["dt"] = np.ascontiguousarray(np.broadcast_to(dt_row[:, None, :], (batch, D, L)))
+    f64["dt"] = raw["dt"].astype(np.float64)
+    g_full, t, p = _run(ss, raw, par, "f32", dev)
+    g_row = ss.scan_bwd(t["x"], torch.from_numpy(dt_row).to(dev), t["B"], t["C"], p["A"], t["dy"], z=t["z"],
+                        Dskip=p["Dskip"], dt_bias=p["dt_bias"], h0=p["h0"], dh_final=p["dh_final"], zoh=True)
+    torch.cuda.synchronize()
+    for k in ("dx", "dz", "dB", "dC", "dA", "dDskip", "ddt_bias", "dh0"):
+        assert torch.equal(g_row[k], g_full[k]), k
+    r = _oracle(o, f64, par)
+    e = rel_l2(to_f64(g_row["ddt"]), r["ddt"].sum(axis=1))
+    log("bwd zoh dt per row: shared dt gradient rel-L2 %.2e" % e)
+    assert e <= 5e-5
+    _compare(g_full, r, "f32", "bwd zoh (dt repeated)")
