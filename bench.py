@@ -36,7 +36,7 @@ _CSRC = "selective_state_space_62_amd/csrc/"
 KERNEL_SOURCES = {
     "scan": [_CSRC + f for f in ("scan_kernel.h", "scan_bf16_euler.hip", "scan_f32_euler.hip", "device_common.h")],
     "decode": [_CSRC + f for f in ("state_update.hip", "device_common.h")],
-    "bwd": [_CSRC + f for f in ("scan_bwd.hip", "device_common.h")],
+    "bwd": [_CSRC + f for f in ("scan_bwd_kernel.h", "scan_bwd.hip", "device_common.h")],
 }
 COUNTERS_FILES = {
     "scan": ROOT / "profiles" / "scan_2.8b_bf16_counters.json",
@@ -242,9 +242,30 @@ def run_bwd(ss, torch, dev, cfg, t, A, dskip, bias, fwd_kernel_ms, calls=20):
         return out
     f_ck, b_ck = timed_pair(True)
     f_no, b_no = timed_pair(False)
+
+    def timed(fn):
+        for _ in range(calls):
+            fn()
+        torch.cuda.synchronize()
+        ss.ss_timing_reset()
+        ss.ss_timing_enable(True)
+        for _ in range(calls):
+            fn()
+        torch.cuda.synchronize()
+        ss.ss_timing_enable(False)
+        m, c = ss.ss_timing_read()
+        ss.ss_timing_reset()
+        return m / c
+    # the other forms of the backward on the same workload: zero-order hold, and one
+    # dt per (row, token) (the first channel's dt row shared by all channels)
+    zoh_ms = timed(lambda: ss.scan_bwd(t["x"], t["dt"], t["B"], t["C"], A, dy, z=t["z"], Dskip=dskip,
+                                       dt_bias=bias, workspace=ws, zoh=True))
+    dt_row = t["dt"][:, 0, :].contiguous()
+    row_ms = timed(lambda: ss.scan_bwd(t["x"], dt_row, t["B"], t["C"], A, dy, z=t["z"], Dskip=dskip,
+                                       dt_bias=bias, workspace=ws))
     spt = algorithmic_slots_bwd_per_tokch(cfg.dstate)
     ach = spt * cfg.tokch / (kms * 1e-3) / 1e12
-    return {"entry_point": "ss_scan_bwd", "kernel": "scan_bwd_kernel<16,4,2,%s> + reduce kernels" % cfg.io,
+    return {"entry_point": "ss_scan_bwd", "kernel": "scan_bwd_kernel<16,4,2,%s,euler> + reduce kernels" % cfg.io,
             "roofline": {"bound": "alu", "achieved": round(ach, 3), "peak": round(VALU_PEAK_TOPS, 3),
                          "unit": "T VALU-slot/s", "frac": round(ach / VALU_PEAK_TOPS, 4), "slots_per_tokch": spt},
             "kernel_ms": round(kms, 5),
@@ -252,6 +273,10 @@ def run_bwd(ss, torch, dev, cfg, t, A, dskip, bias, fwd_kernel_ms, calls=20):
             "ratio_to_forward": round(kms / fwd_kernel_ms, 3),
             "hbm_gbs": round(algorithmic_bytes_bwd(cfg) / (kms * 1e-3) / 1e9, 1),
             "workspace_bytes": ws.numel(), "traffic": measured_traffic(cfg, "bwd"),
+            "zoh": {"entry_point": "ss_scan_bwd_ex (SS_FLAG_ZOH)", "kernel_ms": round(zoh_ms, 5),
+                    "value": round(cfg.tokch / (zoh_ms * 1e-3) / 1e9, 3)},
+            "dt_per_row": {"entry_point": "ss_scan_bwd_ex (SS_FLAG_DT_PER_ROW)", "kernel_ms": round(row_ms, 5),
+                           "value": round(cfg.tokch / (row_ms * 1e-3) / 1e9, 3)},
             "training_step": {"fwd_kernel_ms": round(f_no, 5), "bwd_kernel_ms": round(b_no, 5),
                               "fwd_storing_checkpoints_kernel_ms": round(f_ck, 5),
                               "bwd_from_checkpoints_kernel_ms": round(b_ck, 5),
