@@ -378,7 +378,6 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(ZOH ? 3 
     for (int j = 0; j < CK; ++j) uo[j] = 0.0f;
 #pragma unroll
     for (int j = CK - 1; j >= 0; --j) {
-      if constexpr (ZOH) __builtin_amdgcn_sched_barrier(0);   // token by token (registers)
       if (FULL || j < nj) {
         const float dr = s_dr[j][c];
         const DD o = s_dd[j][c];
