@@ -190,14 +190,17 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(ZOH ? 3 
     return (int)(v < 0 ? 0 : (v < kSpan ? v : kSpan));
   };
 
-  // A chunk's global operands, fetched one chunk ahead of their use.
+  // A chunk's global operands, fetched one chunk ahead of their use.  WHOLE (a
+  // compile-time tag): every token of chunk k lies inside the sequence, so the
+  // loads need no per-lane bounds.
   struct Fetch {
     uint32_t x[SW], dt[SW], z[SW], dy[SW];
     float2 bc;
   };
-  auto fetch = [&](int64_t k, bool grads, Fetch& f) {
+  auto fetch = [&](auto whole_tag, int64_t k, bool grads, Fetch& f) {
+    constexpr bool WHOLE = decltype(whole_tag)::value;
     const int64_t t0 = k * CK;
-    const int valid = own_valid(k);
+    const int valid = WHOLE ? kSpan : own_valid(k);
     load_span<IO, kSpan>(x, row + t0 + j_own, valid, vec, f.x);
     load_span<IO, kSpan>(dt, dt_row + t0 + j_own, valid, vec, f.dt);
     if (grads) {
@@ -205,7 +208,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(ZOH ? 3 
       load_span<IO, kSpan>(dy, row + t0 + j_own, valid, vec, f.dy);
     }
     f.bc = make_float2(0.0f, 0.0f);
-    if (tid < CK * N && t0 + tid / N < chunk_end(k))
+    if (tid < CK * N && (WHOLE || t0 + tid / N < chunk_end(k)))
       f.bc = reinterpret_cast<const float2*>(bc_row + t0 * (2 * N))[tid];
   };
   // Delta and Delta x of the owned tokens into LDS (zero Delta for padding
@@ -228,8 +231,10 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(ZOH ? 3 
     float h[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) h[s] = p.h0 ? p.h0[ch * N + sg * NS + s] : 0.0f;
+    const int64_t nfull = L / CK;   // whole chunks
     Fetch f;
-    fetch(0, false, f);
+    if (nfull > 0) fetch(std::true_type{}, 0, false, f);
+    else fetch(std::false_type{}, 0, false, f);
     // FULL (a compile-time tag): all CK tokens of the chunk lie inside the sequence
     auto sweep = [&](auto full_tag, int64_t k) {
       constexpr bool FULL = decltype(full_tag)::value;
@@ -239,7 +244,8 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(ZOH ? 3 
       }
       float xv[kSpan], dl[kSpan], v2[kSpan];
       stage(FULL ? kSpan : own_valid(k), f, xv, dl, v2);
-      if (k + 1 < nck) fetch(k + 1, false, f);
+      if (k + 1 < nfull) fetch(std::true_type{}, k + 1, false, f);
+      else if (k + 1 < nck) fetch(std::false_type{}, k + 1, false, f);
       __syncthreads();
       const int nj = FULL ? CK : (int)(chunk_end(k) - k * CK);
 #pragma unroll
@@ -259,7 +265,6 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(ZOH ? 3 
       }
       __syncthreads();
     };
-    const int64_t nfull = L / CK;
     for (int64_t k = 0; k < nfull; ++k) sweep(std::true_type{}, k);
     if (nfull < nck) sweep(std::false_type{}, nfull);
   }
@@ -286,7 +291,8 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(ZOH ? 3 
   float* __restrict__ pdst = part_row + (int64_t)(pwhich * N + sg * NS + ps) * Lp;
 
   Fetch f;
-  fetch(nck - 1, true, f);
+  if (L % CK == 0) fetch(std::true_type{}, nck - 1, true, f);
+  else fetch(std::false_type{}, nck - 1, true, f);
   float ckn[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) ckn[s] = act ? ck_row[(nck - 1) * ck_stride + s] : 0.0f;
@@ -314,7 +320,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(ZOH ? 3 
 #pragma unroll
     for (int s = 0; s < NS; ++s) hs[0][s] = ckn[s];
     if (k > 0) {
-      fetch(k - 1, true, f);
+      fetch(std::true_type{}, k - 1, true, f);   // every chunk before the last is whole
 #pragma unroll
       for (int s = 0; s < NS; ++s) ckn[s] = act ? ck_row[(k - 1) * ck_stride + s] : 0.0f;
     }
