@@ -99,6 +99,83 @@ def algorithmic_slots_bwd_per_tokch(N: int, sweep: bool = True) -> float:
     return per_n * N + per_tok
 
 
+def ceilings(cfg, kernel_gtokch: float) -> dict:
+    """The scan's three throughput ceilings in Gtok·ch/s and the kernel's fraction
+    of each: HBM (algorithmic bytes at 8 TB/s); transcendentals alone (N + 4 per
+    token-channel at the half-rate issue of gfx950, as if the other VALU work
+    co-issued); and the VALU issue slots of all the algorithmic work (the bound
+    that applies, since transcendentals and FMAs share the issue port)."""
+    hbm = HBM_PEAK_GBS / algorithmic_bytes_per_tokch(cfg)
+    exp_only = VALU_PEAK_TOPS * 1e3 / TRANS_SLOTS / (cfg.dstate + 4)
+    slots = VALU_PEAK_TOPS * 1e3 / algorithmic_slots_per_tokch(cfg.dstate)
+    return {"unit": "Gtok·ch/s", "hbm": round(hbm, 1), "transcendentals_only": round(exp_only, 1),
+            "valu_issue_slots": round(slots, 1), "kernel": round(kernel_gtokch, 1),
+            "frac_of_min_hbm_transcendentals": round(kernel_gtokch / min(hbm, exp_only), 4),
+            "frac_of_valu_issue_slots": round(kernel_gtokch / slots, 4)}
+
+
+def run_l_sweep(ss, torch, dev, cfg, lengths=(512, 1024, 2048, 4096, 8192, 16384), calls=20):
+    """The scan at several sequence lengths with the workload's batch and channels
+    (the pages claim linear scaling in L): kernel time per call and per token."""
+    import dataclasses
+    from workloads import device as wdev
+    A, dskip, bias = wdev.params(cfg, dev)
+    rows = []
+    for L in lengths:
+        c = dataclasses.replace(cfg, seqlen=L, name="%s-L%d" % (cfg.name, L))
+        t = wdev.scan_inputs(c, dev)
+        ws = torch.empty(max(ss.workspace_bytes(c.batch, c.dim, c.dstate, L, t["x"].dtype), 256), dtype=torch.uint8,
+                         device=dev)
+
+        def call():
+            ss.scan_fwd(t["x"], t["dt"], t["B"], t["C"], A, z=t["z"], Dskip=dskip, dt_bias=bias, workspace=ws)
+        for _ in range(calls):
+            call()
+        torch.cuda.synchronize()
+        ss.ss_timing_reset()
+        ss.ss_timing_enable(True)
+        for _ in range(calls):
+            call()
+        torch.cuda.synchronize()
+        ss.ss_timing_enable(False)
+        ms, n = ss.ss_timing_read()
+        ss.ss_timing_reset()
+        ms /= n
+        plan = ss.ss_scan_fwd_plan(c.batch, c.dim, c.dstate, L, ss.SS_BF16 if c.io == "bf16" else ss.SS_F32)
+        rows.append({"seq_len": L, "kernel_ms": round(ms, 5), "us_per_1k_tokens": round(ms * 1e3 * 1024 / L, 3),
+                     "value": round(c.tokch / (ms * 1e-3) / 1e9, 2), "plan": list(plan)})
+        del t, ws
+        torch.cuda.empty_cache()
+    return rows
+
+
+def cpu_single_thread(budget_s: float = 2.0):
+    """The oracle on one host thread over the 130M-shaped workload (fp32 I/O),
+    256 channels per call until ~budget_s of oracle time."""
+    import numpy as np
+    import oracle
+    from workloads import M130, inputs
+    o = oracle.default()
+    A, dskip, bias = inputs.params(M130)
+    tokch, spent = 0, 0.0
+    pieces = [(b, d0) for b in range(M130.batch) for d0 in range(0, M130.dim, 256)]
+    for b, d0 in pieces:
+        if spent >= budget_s:
+            break
+        ch = [(b, d) for d in range(d0, min(M130.dim, d0 + 256))]
+        sub = inputs.scan_inputs(M130, channels=ch)
+        f = {k: inputs.raw_to_f64(v, M130.io) for k, v in sub.items()}
+        idx = np.array([d for _, d in ch])
+        t0 = time.perf_counter()
+        o.scan(f["x"][None], f["dt"][None], f["B"][b:b + 1], f["C"][b:b + 1], A[idx], z=f["z"][None],
+               Dskip=dskip[idx], dt_bias=bias[idx], nthreads=1)
+        spent += time.perf_counter() - t0
+        tokch += len(ch) * M130.seqlen
+    return {"value": tokch / spent / 1e9, "unit": "Gtok·ch/s", "cores": 1, "kind": "oracle",
+            "sample": "%d channels x L=%d of the %s workload, one thread (%.1f s)" % (tokch // M130.seqlen,
+                                                                                   M130.seqlen, M130.name, spent)}
+
+
 def cpu_baseline(cfg, budget_s: float):
     """The oracle (as it stands) on host cores over the workload, 1024 channels per
     call, passing over it again until ~budget_s of oracle time; inputs are drawn on
@@ -342,6 +419,8 @@ def main():
     ap.add_argument("--cp-shards", type=int, default=0,
                     help="also time one GPU's share of a context-parallel run over this many shards")
     ap.add_argument("--copy-calib", type=int, default=0, help="only run a plain copy of this many bytes")
+    ap.add_argument("--l-sweep", action="store_true",
+                    help="also time the scan at L = 512 ... 16384 with the workload's batch and channels")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -427,6 +506,7 @@ def main():
                      "slots_per_tokch": spt},
         "roofline_hbm": {"achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "bytes_per_tokch": round(bpt, 4)},
+        "ceilings": ceilings(cfg, tokch / (kern_ms * 1e-3) / 1e9),
     }
     if not args.no_dt_row:
         # dt shared by a row's channels (SS_FLAG_DT_PER_ROW): the same workload with
@@ -472,10 +552,14 @@ def main():
         out["bwd"] = run_bwd(ss, torch, dev, cfg, t, A, dskip, bias, kern_ms)
     if args.cp_shards > 1:
         out["context_parallel"] = run_cp(ss, torch, cfg, t, A, dskip, bias, args.cp_shards)
+    if args.l_sweep:
+        out["l_sweep"] = run_l_sweep(ss, torch, dev, cfg)
     if not args.no_decode:
         out["decode"] = run_decode(ss, torch, dev, 60, 60)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
+        out["cpu_baseline"]["host_cpus_in_affinity"] = len(os.sched_getaffinity(0))
+        out["cpu_baseline"]["single_thread"] = cpu_single_thread()
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out))
