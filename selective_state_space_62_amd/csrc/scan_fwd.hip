@@ -8,11 +8,12 @@
 //
 // Mapping onto CDNA4:
 //  * One workgroup = 64/K channels of one batch row and G waves; each channel
-//    has K adjacent lanes (K = 1 or 2) in every wave.  The N state components are
-//    split into G*K groups: lane k of a channel in wave w owns group w K + k.
+//    has K adjacent lanes (K = 1, 2 or 4) in every wave.  The N state components
+//    are split into G*K groups: lane k of a channel in wave w owns group w K + k.
 //    K = 2 halves the channels per workgroup, so there are twice as many equal
 //    workgroups (for the 2.8B-shaped layer 1280, exactly 5 per CU, where 640
-//    leave half the CUs with one more than the rest).
+//    leave half the CUs with one more than the rest); K = 4 (one component per
+//    lane) doubles them again for layers with too few channels to fill the chip.
 //  * Tiles of T = G * 16B/elem tokens.  Each wave loads 16 bytes of x, dt, z per
 //    channel for its own T/G tokens (16/K bytes per lane), computes Delta and
 //    Delta*x once per (token, channel), and shares them through LDS.  The
@@ -24,7 +25,8 @@
 //    for all outstanding scalar and LDS accesses).  All global loads of the next
 //    tile are issued one tile ahead.
 //  * Every lane runs its state components through all T tokens of the tile; the
-//    K lanes of a channel add their readouts with one DPP add, and each wave
+//    K lanes of a channel add their readouts with DPP adds (one for K = 2, two
+//    for K = 4), and each wave
 //    writes one partial readout per (token, channel) to LDS.  The owner of a
 //    token sums the G partials in a fixed order (deterministic results), adds the
 //    skip term, applies the gate and writes its span of y.
@@ -36,6 +38,11 @@
 //    discretisation under which the notes' Theorem 1 (selection is gating) holds
 //    exactly.  The kernels are instantiated per I/O dtype and discretisation in
 //    scan_{bf16,f32}_{euler,zoh}.hip from scan_kernel.h.
+//  * dt may hold one value per (batch row, token), shared by the row's channels
+//    (the broadcast Delta of the notes); the kernel then reads it by row.
+//  * For a training step the forward can also store the state entering every
+//    backward chunk (a separate instantiation, CKPT_K, so the plain scan keeps
+//    its registers); the backward then skips its own checkpoint sweep.
 //  * Long sequences with few channels are cut into chunks: an aggregate pass
 //    (AGG = true) gives each chunk's end state from a zero start and its sum of
 //    Delta; combine_kernel runs the exclusive scan of (exp(A sum Delta), h_end)
