@@ -50,3 +50,16 @@ def test_measured_traffic_tracks_kernel_sources():
     else:
         assert got is None
     assert bench.measured_traffic(TINY, "scan") is None
+
+
+def test_ceilings_at_the_2p8b_shape():
+    """HBM 8 TB/s over 8.048 B, 20 transcendentals at half rate alone, and all
+    112 issue slots: 994, 983 and 351 Gtok·ch/s; the kernel's fraction of each."""
+    sys.path.insert(0, str(ROOT))
+    import bench
+    from workloads import B28
+    c = bench.ceilings(B28, 245.0)
+    assert abs(c["hbm"] - 994.0) < 0.5 and abs(c["transcendentals_only"] - 983.0) < 0.5
+    assert abs(c["valu_issue_slots"] - 351.1) < 0.1
+    assert abs(c["frac_of_valu_issue_slots"] - 245.0 / 351.08) < 1e-3
+    assert abs(c["frac_of_min_hbm_transcendentals"] - 245.0 / 983.0) < 1e-3
