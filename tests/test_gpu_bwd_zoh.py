@@ -167,3 +167,15 @@ def test_bwd_zoh_dt_per_row(ss, o, dev):
     log("bwd zoh dt per row: shared dt gradient rel-L2 %.2e" % e)
     assert e <= 5e-5
     _compare(g_full, r, "f32", "bwd zoh (dt repeated)")
+
+
+def test_bwd_zoh_a_zero(ss, o, dev):
+    """Entries of A exactly zero: the ZOH coefficient's limit Delta (dc/dDelta = 1,
+    dc/dA = Delta^2 / 2) comes from the series branches, as in the oracle."""
+    rng = np.random.default_rng(zlib.crc32(b"zoh-a0"))
+    raw, par, f64 = _problem(rng, 2, 64, 16, 40, "f32", True)
+    A = par["A"].copy()
+    A[rng.random(A.shape) < 0.25] = 0.0
+    par["A"] = A
+    g, _, _ = _run(ss, raw, par, "f32", dev)
+    _compare(g, _oracle(o, f64, par), "f32", "bwd zoh with A = 0 entries")
