@@ -1,8 +1,8 @@
 /*
  * CPU oracle for the selective state-space (S6) scan.
  *
- * TEST INFRASTRUCTURE ONLY.  Nothing but the tests, the smoke check of the
- * graft entry point and the benchmark's cpu_baseline leg may load or call this
+ * TEST INFRASTRUCTURE ONLY.  Nothing but the tests, the smoke check in
+ * __graft_entry__.py and the benchmark's cpu_baseline leg may load or call this
  * library.  It shares no source, header or helper with the GPU library, and the
  * GPU library never calls it.
  *
