@@ -123,7 +123,7 @@ __device__ __forceinline__ float zoh_psi(float u2, float E) {
 // Three waves per SIMD at N = 16 (about 160 VGPRs); at most 32 KB of LDS.
 // ZOH: the zero-order-hold input term, c = Delta phi(Delta A) in place of Delta.
 template <int N, int G, int K, typename IO, bool ZOH>
-__global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(ZOH ? 3 : 4, 10))) void scan_bwd_kernel(
+__global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10))) void scan_bwd_kernel(
     const BwdDims dm, const BwdPtrs p) {
   using T = typename IO::T;
   // per token and channel in LDS: (Delta, Delta x), and for ZOH also (x, x Delta^2)

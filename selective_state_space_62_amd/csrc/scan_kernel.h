@@ -33,14 +33,17 @@ struct BcPiece<1> {
   static constexpr int kFloats = 2;
 };
 
-// At most 96 VGPRs (5 waves per SIMD): with 4 waves per workgroup and 28 KB of
-// LDS, five workgroups fit on a CU at once, which the two-lanes-per-channel plan
-// needs to keep every CU's share resident.
+// At most 96 VGPRs (5 waves per SIMD) for the plans with two or four lanes per
+// channel and up to 2 state components per lane: with 4 waves per workgroup and
+// 28 KB of LDS, five workgroups fit on a CU at once, which the two-lanes-per-
+// channel plan needs to keep every CU's share resident.  One-lane plans (each
+// lane owns 8 or 4 tokens of the per-token work) and plans with more components
+// per lane get no occupancy target.
 // CKPT_K (full pass only): also store the state entering every backward-pass
 // chunk, for a training step's backward.  It is a separate instantiation so
 // that the plain scan keeps its registers.
 template <int N, int G, int K, typename IO, bool AGG, bool ZOH, bool CKPT_K>
-__global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(5, 10))) void scan_kernel(
+__global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 && N / (G * K) <= 2 ? 5 : 1, 10))) void scan_kernel(
     const ScanDims dm, const typename IO::T* __restrict__ x, const typename IO::T* __restrict__ dt,
     const typename IO::T* __restrict__ z, const float* __restrict__ bc, const float* __restrict__ A,
     const float* __restrict__ Dskip, const float* __restrict__ dt_bias, const float* __restrict__ h0,
