@@ -16,9 +16,12 @@
 // (it is touched once per step).  All of an item's loads are issued together,
 // and no lane divides: a grid of up to DECODE_BLOCKS workgroups strides over
 // (batch row, 64-item piece) pairs advanced by a host-computed quotient and
-// remainder.  At the 256 x 5120 x 16 decode shape the cap of 16384 workgroups
-// gives most waves a single item, which measured faster than fewer, longer-
-// lived waves (8192 blocks: +4%, 2048 blocks: +13%).
+// remainder.  A wave advances the same piece of two batch rows: A, dt_bias and
+// Dskip are read once for both and twice as many independent loads are in
+// flight per wave (30.98 -> 29.53 us at the 256 x 5120 x 16 decode shape; four
+// rows per wave 29.93 us, eight 33.2 us).  At that shape every wave then has a
+// single pair of items: more, short-lived waves measured faster than fewer,
+// longer-lived ones.
 #include "device_common.h"
 #include "internal.h"
 
@@ -158,8 +161,8 @@ __device__ __forceinline__ void finish(const Operands<N, IO>& o, Item<Q>& r) {
 // Work decomposition: lane items are (channel, group of Q state components),
 // K = N / Q items per channel, laid out row by row (one row per batch entry,
 // dim * K items, padded to whole waves of 64).  Each wave owns one 64-item
-// piece of one row per iteration and strides over pieces by the grid's wave
-// count; the (row, piece) pair is advanced with a quotient and remainder the
+// piece of a pair of rows per iteration and strides over (row pair, piece) by
+// the grid's wave count; the (row, piece) pair is advanced with a quotient and remainder the
 // host precomputes, so no lane divides.  Row and piece are wave-uniform, so all
 // K lanes of a channel are active together for the DPP sum.
 template <int N, typename IO, bool ZOH>
@@ -181,9 +184,20 @@ __global__ __launch_bounds__(256) void state_update_kernel(int64_t batch, uint32
       ++bb;
     }
   };
-  for (; b < batch; advance(b, piece)) {
-    Item<Q> it = fetch<N, IO, Q, K>(o, b, piece, lane);
-    finish<N, IO, Q, K, ZOH>(o, it);
+  // b counts pairs of batch rows: a wave advances the same channels of two rows
+  // (A, dt_bias and Dskip are loaded once for both, and both rows' loads are in
+  // flight together); an odd batch's last row is a pair of one
+  const int64_t pairs = (batch + 1) / 2;
+  for (; b < pairs; advance(b, piece)) {
+    const int64_t r = 2 * b;
+    Item<Q> i0 = fetch<N, IO, Q, K>(o, r, piece, lane);
+    if (r + 1 < batch) {
+      Item<Q> i1 = fetch<N, IO, Q, K>(o, r + 1, piece, lane);
+      finish<N, IO, Q, K, ZOH>(o, i0);
+      finish<N, IO, Q, K, ZOH>(o, i1);
+    } else {
+      finish<N, IO, Q, K, ZOH>(o, i0);
+    }
   }
 }
 
@@ -195,7 +209,7 @@ hipError_t launch_t(int64_t batch, int64_t dim, bool dt_row, float* state, const
   constexpr int K = N < 4 ? 1 : N / 4;
   constexpr int64_t kWavesPerBlock = 4;
   const int64_t pieces = (dim * K + 63) / 64;
-  const int64_t total_waves = batch * pieces;
+  const int64_t total_waves = (batch + 1) / 2 * pieces;   // waves over (row pair, piece)
   // wave indices and pieces are 32-bit in the kernel
   if (pieces >= (int64_t(1) << 31) || total_waves >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   // a bounded grid (DECODE_BLOCKS workgroups); the grid-stride loop covers the rest

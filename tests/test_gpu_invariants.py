@@ -121,7 +121,13 @@ def test_decode_grid_stride_ragged(ss, dev, dstate, optional):
     64), and the optional z, Dskip and dt_bias present or absent."""
     import torch
     rng = np.random.default_rng(40 + dstate + 100 * optional)
-    batch, D = 2100, 77
+    # waves cover (pair of batch rows, 64-item piece); the grid holds at most
+    # 16384 x 4 waves, so an odd batch above 2 x 65536 / pieces makes the loop wrap
+    # and ends on a pair of one row
+    D = 77
+    lanes = dstate // min(dstate, 4)
+    pieces = (D * lanes + 63) // 64
+    batch = 2 * (65536 // pieces + 50) + 1
     raw, par, f64 = random_problem(rng, batch, D, dstate, 1, "f32", with_z=optional, with_skip=optional,
                                    with_bias=optional)
     t, p = _upload(raw, par, "f32", dev)
