@@ -86,13 +86,14 @@ def algorithmic_slots_bwd_per_tokch(N: int, sweep: bool = True) -> float:
     """VALU issue slots per (token, channel) of the backward pass by recomputation:
     per state component the checkpoint sweep (3 ops + exp; absent when the forward
     stored the checkpoints), the chunk recompute with the readout (4 ops + exp,
-    keeping Abar) and the adjoint step (9 ops: adjoint update, dC and dB terms, the
-    decay's derivative for dDelta and dA, lam B for dx, and the adjoint decay by the
-    kept Abar); per (token, channel) two softplus evaluations (5 ops + 2
+    keeping Abar) and the adjoint step (8 ops: adjoint update, dC and dB terms, the
+    adjoint decayed by the kept Abar, which also scales h for the decay's
+    derivative, that derivative's dDelta and dA terms, and lam B for dx); per
+    (token, channel) two softplus evaluations (5 ops + 2
     transcendentals each), sigmoid(dt + dt_bias) (2 + 2), silu(z) and its derivative
     (7 + 2) and the six output formulas (8 ops).  A transcendental costs TRANS_SLOTS
     slots."""
-    per_n = 4 + 9 + TRANS_SLOTS
+    per_n = 4 + 8 + TRANS_SLOTS
     if sweep:
         per_n += 3 + TRANS_SLOTS
     per_tok = 10 + 2 + 7 + 8 + TRANS_SLOTS * (4 + 2 + 2)

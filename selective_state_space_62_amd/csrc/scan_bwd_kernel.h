@@ -97,6 +97,9 @@ __device__ __forceinline__ float bc_channel_sum(const float (&dB)[NS], const flo
   u += __builtin_amdgcn_update_dpp(0.0f, u, 0x124, 0xf, 0xf, false);   // row_ror:4
   u += __builtin_amdgcn_update_dpp(0.0f, u, 0x4E, 0xf, 0xf, false);    // lanes 2 apart
   if constexpr (K == 1) u += __builtin_amdgcn_update_dpp(0.0f, u, 0xB1, 0xf, 0xf, false);   // neighbours
+  // formed by every lane here: only some lanes store the sums, and an add sunk
+  // into their branch would split the last DPP add into three instructions
+  __asm__ volatile("" : "+v"(u));
   return u;
 }
 
@@ -387,7 +390,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
       if (FULL || j < nj) {
         const float dr = s_dr[j][c];
         const DD o = s_dd[j][c];
-        float ddp = 0.0f, sB = 0.0f;   // ddp in units of A log2(e)
+        float ddp = 0.0f, sB = 0.0f;   // first order: ddp in units of A log2(e), scaled by ln 2 by the owner
         float sE = 0.0f;               // ZOH: sum lam e^u B, the input term's dDelta factor
         float dBv[NS], dCv[NS];
 #pragma unroll
@@ -399,7 +402,8 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
           float u2 = o.x * A2[s];
           if constexpr (ZOH) __asm__ volatile("" : "+v"(u2) : "v"(lam[s]));   // token by token (registers)
           const float E = ZOH ? __builtin_amdgcn_exp2f(u2) : Es[ZOH ? 0 : j][s];
-          const float ga = lam[s] * hs[j][s] * E;
+          const float lamE = lam[s] * E;   // the next token's adjoint before its dr C term
+          const float ga = lamE * hs[j][s];
           ddp = fmaf(ga, A2[s], ddp);
           dAacc[s] = fmaf(ga, o.x, dAacc[s]);
           if constexpr (ZOH) {
@@ -417,14 +421,14 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
             sB = fmaf(lam[s], Bv, sB);
             dBv[s] = lam[s] * o.y;
           }
-          lam[s] *= E;
+          lam[s] = lamE;
         }
         if constexpr (ZOH) ddp = fmaf(ddp, kLn2, o.z * sE);   // the whole dDelta, in natural units
         if constexpr (K == 2) {
           ddp += __builtin_amdgcn_update_dpp(0.0f, ddp, 0xB1, 0xf, 0xf, false);
           sB += __builtin_amdgcn_update_dpp(0.0f, sB, 0xB1, 0xf, 0xf, false);
         }
-        s_pp[j][w][c] = make_float2(ZOH ? ddp : ddp * kLn2, sB);   // both lanes of a channel hold the sums
+        s_pp[j][w][c] = make_float2(ddp, sB);   // both lanes of a channel hold the sums
         uo[j] = bc_channel_sum<NS, K>(dBv, dCv);
       }
       // the dB/dC partials of a group of consecutive tokens, stored once the
@@ -453,8 +457,8 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
           }
         }
         dxv[i] = fmaf(sB, s_dd[j][c].x, s_dr[j][c] * skip);   // Delta and dr of the owned token from LDS
-        // Euler: dDelta = (decay part) + x sum lam B; ZOH: the lanes already added x sum lam e^u B
-        const float dv = (ZOH ? ddp : fmaf(sB, xv[i], ddp)) * sigmoid2(v2[i]);
+        // Euler: dDelta = (decay part) ln 2 + x sum lam B; ZOH: the lanes already added x sum lam e^u B
+        const float dv = (ZOH ? ddp : fmaf(ddp, kLn2, sB * xv[i])) * sigmoid2(v2[i]);
         ddtv[i] = dv;   // zero for padding tokens and inactive channels
         if (FULL || i < valid) dbias_acc += dv;
       }

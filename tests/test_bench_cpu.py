@@ -20,8 +20,8 @@ def test_bench_algorithmic_counts():
     # x, dt, z read and y written in bf16 (8 B), plus B/C, parameters and h_final amortised
     assert abs(bench.algorithmic_bytes_per_tokch(B28) - 8.048) < 1e-3
     assert bench.algorithmic_slots_per_tokch(16) == 112
-    assert bench.algorithmic_slots_bwd_per_tokch(16) == 363
-    assert bench.algorithmic_slots_bwd_per_tokch(16, sweep=False) == 283
+    assert bench.algorithmic_slots_bwd_per_tokch(16) == 347
+    assert bench.algorithmic_slots_bwd_per_tokch(16, sweep=False) == 267
 
 
 def test_cpu_baseline_repeats_passes_until_budget():
