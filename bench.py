@@ -150,6 +150,49 @@ def run_l_sweep(ss, torch, dev, cfg, lengths=(512, 1024, 2048, 4096, 8192, 16384
     return rows
 
 
+def run_long_bwd(ss, torch, dev, calls=3):
+    """The backward on the million-token workload (batch 1, D 2048, N 16, bf16),
+    device-generated inputs and dy: the library's automatic split into sequence
+    segments against the same backward run whole (one segment).  Kernel time from
+    the library's events around each call's kernels."""
+    from workloads import LONG, inputs
+    from workloads import device as wdev
+    cfg = LONG
+    b, d, n, L = cfg.batch, cfg.dim, cfg.dstate, cfg.seqlen
+    t = wdev.scan_inputs(cfg, dev)
+    A, dskip, bias = wdev.params(cfg, dev)
+    dy = wdev.fill(torch.empty((b, d, L), dtype=torch.bfloat16, device=dev), cfg, inputs.STREAM_DY)
+    seg = ss.ss_scan_bwd_segment_len(b, d, n, L, ss.SS_BF16)
+    ws = torch.empty(max(ss.bwd_workspace_bytes(b, d, n, L, torch.bfloat16, 0),
+                         ss.bwd_workspace_bytes(b, d, n, L, torch.bfloat16, L)), dtype=torch.uint8, device=dev)
+
+    def timed(segment_len):
+        def call():
+            return ss.scan_bwd(t["x"], t["dt"], t["B"], t["C"], A, dy, z=t["z"], Dskip=dskip, dt_bias=bias,
+                               workspace=ws, segment_len=segment_len)
+        call()
+        torch.cuda.synchronize()
+        ss.ss_timing_reset()
+        ss.ss_timing_enable(True)
+        for _ in range(calls):
+            call()
+        torch.cuda.synchronize()
+        ss.ss_timing_enable(False)
+        ms, k = ss.ss_timing_read()
+        ss.ss_timing_reset()
+        return ms / k
+
+    split_ms = timed(0)
+    whole_ms = timed(L)
+    del t, dy, ws
+    torch.cuda.empty_cache()
+    return {"workload": cfg.name, "entry_point": "ss_scan_bwd (automatic split) vs ss_scan_bwd_seg (whole)",
+            "segment_len": seg, "segments": (L + seg - 1) // seg, "split_ms": round(split_ms, 3),
+            "whole_ms": round(whole_ms, 3), "value_split": round(cfg.tokch / (split_ms * 1e-3) / 1e9, 2),
+            "value_whole": round(cfg.tokch / (whole_ms * 1e-3) / 1e9, 2), "unit": "Gtok·ch/s",
+            "speedup": round(whole_ms / split_ms, 2), "calls": calls}
+
+
 def cpu_single_thread(budget_s: float = 2.0):
     """The oracle on one host thread over the 130M-shaped workload (fp32 I/O),
     256 channels per call until ~budget_s of oracle time."""
@@ -422,6 +465,8 @@ def main():
     ap.add_argument("--copy-calib", type=int, default=0, help="only run a plain copy of this many bytes")
     ap.add_argument("--l-sweep", action="store_true",
                     help="also time the scan at L = 512 ... 16384 with the workload's batch and channels")
+    ap.add_argument("--long-bwd", action="store_true",
+                    help="also time the backward on the million-token workload, split into segments and whole")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -555,6 +600,8 @@ def main():
         out["context_parallel"] = run_cp(ss, torch, cfg, t, A, dskip, bias, args.cp_shards)
     if args.l_sweep:
         out["l_sweep"] = run_l_sweep(ss, torch, dev, cfg)
+    if args.long_bwd:
+        out["long_bwd"] = run_long_bwd(ss, torch, dev)
     if not args.no_decode:
         out["decode"] = run_decode(ss, torch, dev, 60, 60)
     if not args.no_cpu_baseline:

@@ -272,6 +272,43 @@ ss_status ss_scan_bwd_ex(int64_t batch, int64_t dim, int dstate, int64_t seqlen,
                          float* dA, float* dDskip, float* ddt_bias, float* dh0,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* Splitting a long sequence in the backward pass.  The backward takes each
+ * (batch row, channel block) through all of its tokens in one workgroup, so a
+ * long sequence with few rows and channels would leave most of the GPU idle.
+ * It is then cut into segments run by separate workgroups, the backward
+ * counterpart of the forward's chunks (the pages evaluate the recurrence with a
+ * parallel scan; reader's notes on the Mamba paper, kurisu.si, "What they did").
+ * Each segment starts from the state entering it (the forward's chunk
+ * aggregates and their combine, or the checkpoints in ckpt) and from the
+ * adjoint carried in from the tokens after it.  That adjoint follows from the
+ * same linearity run backwards: a segment passes on exp(A sum Delta) times what
+ * enters it plus its own aggregate sum_t (prod of Abar up to t) dr_t C_t, with
+ * dr = dy silu(z), which needs no state; a combine from dh_final chains them.
+ * The gradients equal the unsplit ones up to rounding (across a segment the
+ * decay is applied as one exponential rather than a product of per-token
+ * factors).
+ *   ss_scan_bwd_segment_len: the segment length ss_scan_bwd and ss_scan_bwd_ex
+ *     use for this shape on the current device: seqlen when they run the
+ *     sequence whole (sequences shorter than 8192 tokens, or with at least two
+ *     workgroups of 64/lanes channels per CU), 0 for invalid arguments.
+ *   ss_scan_bwd_seg: ss_scan_bwd_ex with an explicit segment_len: 0 for the
+ *     automatic choice, else a positive multiple of 64 (SS_ERR_INVALID_ARG
+ *     otherwise, or beyond 2^20 segments); a length of at least seqlen runs the
+ *     sequence whole.  Its workspace size is ss_scan_bwd_seg_workspace_bytes
+ *     with the same segment_len (0 for invalid arguments). */
+int64_t ss_scan_bwd_segment_len(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io);
+size_t ss_scan_bwd_seg_workspace_bytes(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io,
+                                       int64_t segment_len);
+ss_status ss_scan_bwd_seg(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io, uint32_t flags,
+                          int64_t segment_len,
+                          const void* x, const void* dt, const void* z,
+                          const void* B, const void* C, const float* A,
+                          const float* Dskip, const float* dt_bias, const float* h0,
+                          const void* dy, const float* dh_final, const float* ckpt,
+                          void* dx, void* ddt, void* dz, void* dB, void* dC,
+                          float* dA, float* dDskip, float* ddt_bias, float* dh0,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Opt-in timing of the main scan kernels (for benchmarks).  While enabled, each
  * ss_scan_fwd call records HIP events around its scan kernel launches on its
  * stream, and each ss_scan_bwd call around its backward kernels.  ss_timing_read synchronises on the recorded events and returns the

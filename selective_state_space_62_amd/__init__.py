@@ -5,7 +5,8 @@
 """
 from . import binding  # noqa: F401  (raises ImportError if libssscan.so is missing)
 from .binding import (SS_BF16, SS_F32, SS_FLAG_DT_PER_ROW, SS_FLAG_ZOH, SsError, ss_abi_version,  # noqa: F401
-                      ss_scan_bwd, ss_scan_bwd_ex, ss_scan_bwd_workspace_bytes, ss_scan_ckpt_bytes, ss_scan_fwd,
+                      ss_scan_bwd, ss_scan_bwd_ex, ss_scan_bwd_seg, ss_scan_bwd_seg_workspace_bytes,
+                      ss_scan_bwd_segment_len, ss_scan_bwd_workspace_bytes, ss_scan_ckpt_bytes, ss_scan_fwd,
                       ss_scan_fwd_ex, ss_scan_fwd_plan, ss_scan_fwd_workspace_bytes, ss_scan_fwd_zoh,
                       ss_scan_shard_combine, ss_scan_shard_state, ss_scan_shard_state_zoh, ss_state_update,
                       ss_state_update_ex, ss_state_update_zoh, ss_timing_enable, ss_timing_read, ss_timing_reset)
@@ -18,4 +19,4 @@ __all__ = ["ss_scan_fwd", "ss_state_update", "ss_scan_fwd_zoh", "ss_state_update
            "workspace_bytes", "bwd_workspace_bytes", "ss_scan_shard_state", "ss_scan_shard_state_zoh",
            "ss_scan_shard_combine", "shard_state", "shard_combine", "ss_scan_fwd_ex", "ss_state_update_ex",
            "SS_FLAG_ZOH", "SS_FLAG_DT_PER_ROW", "ss_scan_bwd_ex", "ss_scan_ckpt_bytes", "ckpt_numel", "SsError",
-           "SS_F32", "SS_BF16"]
+           "SS_F32", "SS_BF16", "ss_scan_bwd_seg", "ss_scan_bwd_seg_workspace_bytes", "ss_scan_bwd_segment_len"]

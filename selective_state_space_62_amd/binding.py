@@ -76,6 +76,13 @@ def _load():
     lib.ss_scan_ckpt_bytes.argtypes = [_i64, _i64, _int, _i64]
     lib.ss_scan_bwd_ex.restype = _int
     lib.ss_scan_bwd_ex.argtypes = [_i64, _i64, _int, _i64, _int, ctypes.c_uint32] + [_vp] * 22 + [ctypes.c_size_t, _vp]
+    lib.ss_scan_bwd_segment_len.restype = _i64
+    lib.ss_scan_bwd_segment_len.argtypes = [_i64, _i64, _int, _i64, _int]
+    lib.ss_scan_bwd_seg_workspace_bytes.restype = ctypes.c_size_t
+    lib.ss_scan_bwd_seg_workspace_bytes.argtypes = [_i64, _i64, _int, _i64, _int, _i64]
+    lib.ss_scan_bwd_seg.restype = _int
+    lib.ss_scan_bwd_seg.argtypes = ([_i64, _i64, _int, _i64, _int, ctypes.c_uint32, _i64] + [_vp] * 22
+                                    + [ctypes.c_size_t, _vp])
     lib.ss_state_update_ex.restype = _int
     lib.ss_state_update_ex.argtypes = [_i64, _i64, _int, _int, ctypes.c_uint32] + [_vp] * 11
     lib.ss_scan_shard_state.restype = _int
@@ -192,6 +199,22 @@ def ss_scan_bwd_ex(batch, dim, dstate, seqlen, io, flags, x, dt, z, B, C, A, Dsk
     _check(lib.ss_scan_bwd_ex(batch, dim, dstate, seqlen, io, flags, x, dt, z, B, C, A, Dskip, dt_bias, h0, dy,
                               dh_final, ckpt, dx, ddt, dz, dB, dC, dA, dDskip, ddt_bias, dh0, workspace,
                               workspace_bytes, stream))
+
+
+def ss_scan_bwd_segment_len(batch, dim, dstate, seqlen, io) -> int:
+    return int(lib.ss_scan_bwd_segment_len(batch, dim, dstate, seqlen, io))
+
+
+def ss_scan_bwd_seg_workspace_bytes(batch, dim, dstate, seqlen, io, segment_len) -> int:
+    return int(lib.ss_scan_bwd_seg_workspace_bytes(batch, dim, dstate, seqlen, io, segment_len))
+
+
+def ss_scan_bwd_seg(batch, dim, dstate, seqlen, io, flags, segment_len, x, dt, z, B, C, A, Dskip, dt_bias, h0, dy,
+                    dh_final, ckpt, dx, ddt, dz, dB, dC, dA, dDskip, ddt_bias, dh0, workspace, workspace_bytes,
+                    stream=None):
+    _check(lib.ss_scan_bwd_seg(batch, dim, dstate, seqlen, io, flags, segment_len, x, dt, z, B, C, A, Dskip, dt_bias,
+                               h0, dy, dh_final, ckpt, dx, ddt, dz, dB, dC, dA, dDskip, ddt_bias, dh0, workspace,
+                               workspace_bytes, stream))
 
 
 def ss_state_update_ex(batch, dim, dstate, io, flags, state, x, dt, z, B, C, A, Dskip, dt_bias, y, stream=None):

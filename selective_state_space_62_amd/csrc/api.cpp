@@ -515,12 +515,65 @@ ss_status shard_state_impl(int64_t batch, int64_t dim, int dstate, int64_t seqle
   return e == hipSuccess ? SS_OK : hip_fail(e, "shard reduce launch");
 }
 
+// Segments of a split backward.  The backward takes a (batch row, channel
+// block) through all its tokens in one workgroup, so a long sequence with few
+// rows and channels would leave most CUs idle; it is then cut into segments run
+// by separate workgroups, whose incoming state and adjoint come from aggregate
+// passes and combines (about a third of the main pass's work again).
+// Automatic, as the forward's chunks: sequences of at least 8192 tokens whose
+// unsplit launch has fewer than two workgroups per CU get about 64 workgroups
+// per CU, in segments of at least 2048 tokens (million-token workload: 7
+// segments 132 ms, 24 segments 96.6 ms, 128 segments 83.2 ms, 512 segments
+// 80.2 ms).  Segment lengths are multiples of 64 tokens: whole backward chunks
+// and whole forward tiles.
+constexpr int64_t kBwdSegAlign = 64;
+
+struct BwdSeg {
+  int64_t len;   // tokens per segment; when n == 1, the sequence padded to whole chunks
+  int64_t n;     // segments
+};
+
+BwdSeg bwd_seg_of_len(int64_t seqlen, int dstate, int64_t len) {
+  const int64_t ck = ssscan::bwd_chunk_len(dstate);
+  if (len <= 0 || len >= seqlen) return BwdSeg{(seqlen + ck - 1) / ck * ck, 1};
+  return BwdSeg{len, (seqlen + len - 1) / len};
+}
+
+BwdSeg bwd_auto_segments(int64_t batch, int64_t dim, int dstate, int64_t seqlen) {
+  const int64_t cpb = 64 / ssscan::bwd_lanes_per_channel(dstate);
+  const int64_t wgs = ((dim + cpb - 1) / cpb) * batch;
+  const int64_t cus = device_cus();
+  int64_t n = 1;
+  if (seqlen >= 8192 && wgs < 2 * cus) {
+    n = (64 * cus + wgs - 1) / wgs;
+    const int64_t nmax = seqlen / 2048;
+    if (n > nmax) n = nmax;
+  }
+  if (n <= 1) return bwd_seg_of_len(seqlen, dstate, 0);
+  int64_t len = (seqlen + n - 1) / n;
+  len = (len + kBwdSegAlign - 1) / kBwdSegAlign * kBwdSegAlign;
+  return bwd_seg_of_len(seqlen, dstate, len);
+}
+
+// requested: 0 = automatic, else the segment length (a positive multiple of 64)
+ss_status bwd_plan_segments(int64_t batch, int64_t dim, int dstate, int64_t seqlen, int64_t requested,
+                            BwdSeg* out) {
+  if (requested < 0 || requested % kBwdSegAlign != 0)
+    return fail(SS_ERR_INVALID_ARG, "segment_len %lld must be 0 (automatic) or a positive multiple of %lld",
+                (long long)requested, (long long)kBwdSegAlign);
+  *out = requested == 0 ? bwd_auto_segments(batch, dim, dstate, seqlen) : bwd_seg_of_len(seqlen, dstate, requested);
+  if (out->n > (1 << 20))
+    return fail(SS_ERR_INVALID_ARG, "segment_len %lld gives %lld segments (limit 2^20)", (long long)requested,
+                (long long)out->n);
+  return SS_OK;
+}
+
 struct BwdLayout {
-  size_t bc, ckpt, part, dA_p, dD_p, dbias_p, total;
+  size_t bc, ckpt, part, dA_p, dD_p, dbias_p, h_seg, agg_h, agg_s, lam_seg, adj_m, adj_s, total;
   int64_t cblocks, chunks;
 };
 
-BwdLayout bwd_layout(int64_t batch, int64_t dim, int dstate, int64_t seqlen) {
+BwdLayout bwd_layout(int64_t batch, int64_t dim, int dstate, int64_t seqlen, const BwdSeg& sg) {
   BwdLayout w{};
   const int64_t cpb = 64 / ssscan::bwd_lanes_per_channel(dstate);
   const int64_t ck = ssscan::bwd_chunk_len(dstate);
@@ -533,12 +586,28 @@ BwdLayout bwd_layout(int64_t batch, int64_t dim, int dstate, int64_t seqlen) {
   off += round256((size_t)batch * dim * w.chunks * dstate * sizeof(float));
   w.part = off;   // partials (batch, channel block, output, token), tokens padded to whole chunks
   off += round256((size_t)batch * w.cblocks * ssscan::bwd_part_outputs(dstate) * (w.chunks * ck) * sizeof(float));
-  w.dA_p = off;
-  off += round256((size_t)batch * dim * dstate * sizeof(float));
+  w.dA_p = off;   // per-(segment, row) sums
+  off += round256((size_t)sg.n * batch * dim * dstate * sizeof(float));
   w.dD_p = off;
-  off += round256((size_t)batch * dim * sizeof(float));
+  off += round256((size_t)sg.n * batch * dim * sizeof(float));
   w.dbias_p = off;
-  off += round256((size_t)batch * dim * sizeof(float));
+  off += round256((size_t)sg.n * batch * dim * sizeof(float));
+  if (sg.n > 1) {
+    const size_t st = (size_t)batch * dim * sg.n * dstate * sizeof(float);
+    const size_t sc = (size_t)batch * dim * sg.n * sizeof(float);
+    w.h_seg = off;
+    off += round256(st);
+    w.agg_h = off;
+    off += round256(st);
+    w.agg_s = off;
+    off += round256(sc);
+    w.lam_seg = off;
+    off += round256(st);
+    w.adj_m = off;
+    off += round256(st);
+    w.adj_s = off;
+    off += round256(sc);
+  }
   w.total = off;
   return w;
 }
@@ -548,8 +617,12 @@ ss_status scan_bwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, 
                         const float* Dskip, const float* dt_bias, const float* h0, const void* dy,
                         const float* dh_final, void* dx, void* ddt, void* dz, void* dB, void* dC, float* dA,
                         float* dDskip, float* ddt_bias, float* dh0, void* workspace, size_t workspace_bytes,
-                        void* stream, const float* ckpt = nullptr, bool dt_row = false, bool zoh = false) {
+                        void* stream, const float* ckpt = nullptr, bool dt_row = false, bool zoh = false,
+                        int64_t seg_req = 0) {
   ss_status st = check_sizes(batch, dim, dstate, seqlen, io);
+  if (st != SS_OK) return st;
+  BwdSeg sgm;
+  st = bwd_plan_segments(batch, dim, dstate, seqlen, seg_req, &sgm);
   if (st != SS_OK) return st;
   if (!A) return fail(SS_ERR_INVALID_ARG, "A is NULL");
   if (ckpt && !aligned(ckpt, 16)) return fail(SS_ERR_INVALID_ARG, "ckpt is not 16-byte aligned");
@@ -572,7 +645,7 @@ ss_status scan_bwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, 
   for (int i = 0; i < 4; ++i)
     if (a4[i] && !aligned(a4[i], 4)) return fail(SS_ERR_INVALID_ARG, "%s is not 4-byte aligned", n4[i]);
 
-  const BwdLayout wl = bwd_layout(batch, dim, dstate, seqlen);
+  const BwdLayout wl = bwd_layout(batch, dim, dstate, seqlen, sgm);
   if (seqlen > 0) {
     if (!workspace) return fail(SS_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", wl.total);
     if (!aligned(workspace, 256)) return fail(SS_ERR_WORKSPACE, "workspace is not 256-byte aligned");
@@ -618,7 +691,7 @@ ss_status scan_bwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, 
     }
     return SS_OK;
   }
-  const int64_t nwg = wl.cblocks * batch;
+  const int64_t nwg = wl.cblocks * batch * sgm.n;
   if (nwg > 0x7fffffffLL) return fail(SS_ERR_INVALID_ARG, "launch needs %lld workgroups (limit 2^31-1)", (long long)nwg);
 
   char* ws = static_cast<char*>(workspace);
@@ -643,6 +716,8 @@ ss_status scan_bwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, 
   dm.have_ckpt = ckpt ? 1 : 0;
   dm.dt_row = dt_row ? 1 : 0;
   dm.zoh = zoh ? 1 : 0;
+  dm.nseg = (int32_t)sgm.n;
+  dm.seg_len = sgm.len;
   ssscan::BwdPtrs bp{};
   bp.x = x;
   bp.dt = dt;
@@ -668,6 +743,12 @@ ss_status scan_bwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, 
   bp.dA_p = reinterpret_cast<float*>(ws + wl.dA_p);
   bp.dD_p = reinterpret_cast<float*>(ws + wl.dD_p);
   bp.dbias_p = reinterpret_cast<float*>(ws + wl.dbias_p);
+  if (sgm.n > 1) {
+    bp.h_seg = reinterpret_cast<const float*>(ws + wl.h_seg);
+    bp.lam_seg = reinterpret_cast<const float*>(ws + wl.lam_seg);
+    bp.adj_m = reinterpret_cast<float*>(ws + wl.adj_m);
+    bp.adj_s = reinterpret_cast<float*>(ws + wl.adj_s);
+  }
 
   const bool timed = timing_on();
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
@@ -676,6 +757,37 @@ ss_status scan_bwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, 
     if (st != SS_OK) return st;
     e = hipEventRecord(ev0, s);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  if (sgm.n > 1) {
+    if (!ckpt) {
+      // the state entering every segment: the forward's aggregate pass over the
+      // segments and its combine
+      const Plan fp = auto_plan(batch, dim, dstate, seqlen, io);
+      ssscan::ScanDims fd = pd;
+      fd.chunk_len = sgm.len;   // a multiple of every forward tile length
+      fd.num_chunks = (int32_t)sgm.n;
+      fd.groups = fp.groups;
+      fd.lanes = fp.lanes;
+      fd.vec = (seqlen % ssscan::span_len(fp.lanes, fd.io)) == 0 ? 1 : 0;
+      fd.dt_row = dt_row ? 1 : 0;
+      ssscan::ScanPtrs sp{};
+      sp.x = x;
+      sp.dt = dt;
+      sp.bc = bcw;
+      sp.A = A;
+      sp.dt_bias = dt_bias;
+      sp.agg_h = reinterpret_cast<float*>(ws + wl.agg_h);
+      sp.agg_s = reinterpret_cast<float*>(ws + wl.agg_s);
+      e = ssscan::launch_scan(fd, sp, /*aggregate=*/true, zoh, s);
+      if (e != hipSuccess) return hip_fail(e, "scan (aggregate) launch");
+      e = ssscan::launch_combine(fd, A, sp.agg_h, sp.agg_s, h0, reinterpret_cast<float*>(ws + wl.h_seg), s);
+      if (e != hipSuccess) return hip_fail(e, "combine launch");
+    }
+    e = ssscan::launch_bwd_adjoint_agg(dm, bp, s);
+    if (e != hipSuccess) return hip_fail(e, "adjoint aggregate launch");
+    e = ssscan::launch_bwd_adjoint_combine(dm, A, dh_final, bp.adj_m, bp.adj_s, reinterpret_cast<float*>(ws + wl.lam_seg),
+                                           s);
+    if (e != hipSuccess) return hip_fail(e, "adjoint combine launch");
   }
   e = ssscan::launch_scan_bwd(dm, bp, s);
   if (e != hipSuccess) return hip_fail(e, "scan_bwd launch");
@@ -790,9 +902,22 @@ ss_status ss_scan_shard_combine(int64_t batch, int64_t dim, int dstate, int64_t 
 }
 
 size_t ss_scan_bwd_workspace_bytes(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io) {
+  return ss_scan_bwd_seg_workspace_bytes(batch, dim, dstate, seqlen, io, 0);
+}
+
+int64_t ss_scan_bwd_segment_len(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io) {
+  if (check_sizes(batch, dim, dstate, seqlen, io) != SS_OK) return 0;
+  const BwdSeg sg = bwd_auto_segments(batch, dim, dstate, seqlen);
+  return sg.n > 1 ? sg.len : seqlen;
+}
+
+size_t ss_scan_bwd_seg_workspace_bytes(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io,
+                                       int64_t segment_len) {
   if (check_sizes(batch, dim, dstate, seqlen, io) != SS_OK) return 0;
   if (seqlen == 0) return 0;
-  return bwd_layout(batch, dim, dstate, seqlen).total;
+  BwdSeg sg;
+  if (bwd_plan_segments(batch, dim, dstate, seqlen, segment_len, &sg) != SS_OK) return 0;
+  return bwd_layout(batch, dim, dstate, seqlen, sg).total;
 }
 
 ss_status ss_scan_bwd(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io, const void* x,
@@ -816,6 +941,19 @@ ss_status ss_scan_bwd_ex(int64_t batch, int64_t dim, int dstate, int64_t seqlen,
   return scan_bwd_impl(batch, dim, dstate, seqlen, io, x, dt, z, B, C, A, Dskip, dt_bias, h0, dy, dh_final, dx,
                        ddt, dz, dB, dC, dA, dDskip, ddt_bias, dh0, workspace, workspace_bytes, stream, ckpt,
                        (flags & SS_FLAG_DT_PER_ROW) != 0, (flags & SS_FLAG_ZOH) != 0);
+}
+
+ss_status ss_scan_bwd_seg(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io, uint32_t flags,
+                          int64_t segment_len, const void* x, const void* dt, const void* z, const void* B,
+                          const void* C, const float* A, const float* Dskip, const float* dt_bias, const float* h0,
+                          const void* dy, const float* dh_final, const float* ckpt, void* dx, void* ddt, void* dz,
+                          void* dB, void* dC, float* dA, float* dDskip, float* ddt_bias, float* dh0, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (flags & ~(uint32_t)(SS_FLAG_ZOH | SS_FLAG_DT_PER_ROW))
+    return fail(SS_ERR_UNSUPPORTED, "unknown flags 0x%x", (unsigned)flags);
+  return scan_bwd_impl(batch, dim, dstate, seqlen, io, x, dt, z, B, C, A, Dskip, dt_bias, h0, dy, dh_final, dx,
+                       ddt, dz, dB, dC, dA, dDskip, ddt_bias, dh0, workspace, workspace_bytes, stream, ckpt,
+                       (flags & SS_FLAG_DT_PER_ROW) != 0, (flags & SS_FLAG_ZOH) != 0, segment_len);
 }
 
 ss_status ss_timing_enable(int enable) {

@@ -54,6 +54,8 @@ struct BwdDims {
   int32_t have_ckpt;    // 1: BwdPtrs::ckpt already holds the checkpoints (stored by the forward)
   int32_t dt_row;       // 1: dt (and ddt) hold one value per (batch row, token), shared by the channels
   int32_t zoh;          // 1: zero-order-hold input term
+  int32_t nseg;         // sequence segments run by separate workgroups (1: the whole sequence)
+  int64_t seg_len;      // tokens per segment (a multiple of the chunk length; >= seqlen when nseg == 1)
 };
 
 // dB/dC partials per (batch row, channel block): 2 N outputs plus one for the
@@ -82,9 +84,14 @@ struct BwdPtrs {
   float* dh0;             // nullable
   float* ckpt;            // workspace: (batch, chunks, dim, dstate) state at every chunk start
   float* part;            // workspace: (batch, cblocks, bwd_part_outputs, padded seqlen) partial sums
-  float* dA_p;            // workspace: (batch, dim, dstate) per-row sums
-  float* dD_p;            // workspace: (batch, dim)
-  float* dbias_p;         // workspace: (batch, dim)
+  float* dA_p;            // workspace: (nseg, batch, dim, dstate) per-(segment, row) sums
+  float* dD_p;            // workspace: (nseg, batch, dim)
+  float* dbias_p;         // workspace: (nseg, batch, dim)
+  // split sequences (nseg > 1), each (batch, dim, nseg, dstate) or (batch, dim, nseg):
+  const float* h_seg;     // the state entering each segment (unless ckpt holds the checkpoints)
+  const float* lam_seg;   // the adjoint carried into each segment from the tokens after it
+  float* adj_m;           // workspace: each segment's adjoint aggregate from a zero start
+  float* adj_s;           // workspace: each segment's sum of Delta
 };
 
 // Backward plan: lanes per channel and chunk length (tokens) for a state size.
@@ -115,6 +122,11 @@ hipError_t launch_shard_combine(int64_t batch, int64_t dim, int dstate, int64_t 
                                 const float* dsum, const float* h_end, const float* h0, float* h_in, float* h_final,
                                 hipStream_t s);
 hipError_t launch_scan_bwd(const BwdDims& dm, const BwdPtrs& p, hipStream_t s);
+// split sequences: the adjoint aggregates of segments 1 .. nseg-1 (adj_m, adj_s),
+// then the adjoint carried into every segment (lam_seg) from dh_final
+hipError_t launch_bwd_adjoint_agg(const BwdDims& dm, const BwdPtrs& p, hipStream_t s);
+hipError_t launch_bwd_adjoint_combine(const BwdDims& dm, const float* A, const float* dh_final, const float* adj_m,
+                                      const float* adj_s, float* lam_seg, hipStream_t s);
 // the main backward kernel alone, zero-order-hold form (scan_bwd_zoh.hip)
 hipError_t launch_scan_bwd_zoh_main(const BwdDims& dm, const BwdPtrs& p, hipStream_t s);
 hipError_t launch_fill_zero(float* dst, int64_t n, hipStream_t s);

@@ -31,10 +31,11 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restr
   else store_one<IO>(o < N ? dB : dC, (b * N + o % N) * L + t, acc);
 }
 
-// dA, dDskip and dt_bias's gradient: sums over batch rows, in row order.
+// dA, dDskip and dt_bias's gradient: sums over the (segment, batch row) rows of
+// the partials, in row order.
 __global__ __launch_bounds__(256) void bwd_reduce_param_kernel(const float* __restrict__ dA_p,
                                                                const float* __restrict__ dD_p,
-                                                               const float* __restrict__ dbias_p, int64_t batch,
+                                                               const float* __restrict__ dbias_p, int64_t rows,
                                                                int64_t dim, int N, float* __restrict__ dA,
                                                                float* __restrict__ dD, float* __restrict__ dbias) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -42,18 +43,42 @@ __global__ __launch_bounds__(256) void bwd_reduce_param_kernel(const float* __re
   if (i < na) {
     if (dA) {
       float acc = 0.0f;
-      for (int64_t b = 0; b < batch; ++b) acc += dA_p[b * na + i];
+      for (int64_t b = 0; b < rows; ++b) acc += dA_p[b * na + i];
       dA[i] = acc;
     }
   } else if (i < na + dim) {
     const int64_t dd = i - na;
     float a0 = 0.0f, a1 = 0.0f;
-    for (int64_t b = 0; b < batch; ++b) {
+    for (int64_t b = 0; b < rows; ++b) {
       a0 += dD_p[b * dim + dd];
       a1 += dbias_p[b * dim + dd];
     }
     if (dD) dD[dd] = a0;
     if (dbias) dbias[dd] = a1;
+  }
+}
+
+// The adjoint carried into every segment of a split sequence, one lane per
+// (b, d, n), from the last segment back: lam_seg[nseg-1] = dh_final (or zero),
+// lam_seg[s-1] = exp(A sum Delta_s) lam_seg[s] + M_s.  The decay factor is the
+// product of the segment's Abar, as in the forward's combine.
+__global__ __launch_bounds__(256) void bwd_adjoint_combine_kernel(int64_t nstate, int64_t dim, int dstate, int nseg,
+                                                                  const float* __restrict__ A,
+                                                                  const float* __restrict__ dh_final,
+                                                                  const float* __restrict__ adj_m,
+                                                                  const float* __restrict__ adj_s,
+                                                                  float* __restrict__ lam_seg) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nstate) return;
+  const int64_t ch = i / dstate;
+  const int n = (int)(i - ch * dstate);
+  const int64_t d = ch % dim;
+  const float a2 = A[d * dstate + n] * kLog2e;
+  float mu = dh_final ? dh_final[i] : 0.0f;
+  for (int sgi = nseg - 1; sgi >= 0; --sgi) {
+    const int64_t k = (ch * nseg + sgi) * dstate + n;
+    lam_seg[k] = mu;
+    if (sgi > 0) mu = fmaf(__builtin_amdgcn_exp2f(a2 * adj_s[ch * nseg + sgi]), mu, adj_m[k]);
   }
 }
 
@@ -91,7 +116,21 @@ hipError_t launch_scan_bwd(const BwdDims& dm, const BwdPtrs& p, hipStream_t s) {
   }
   const int64_t npar = dm.dim * dm.dstate + dm.dim;
   hipLaunchKernelGGL(bwd_reduce_param_kernel, dim3((unsigned)((npar + 255) / 256)), dim3(256), 0, s, p.dA_p, p.dD_p,
-                     p.dbias_p, dm.batch, dm.dim, dm.dstate, p.dA, p.dDskip, p.ddt_bias);
+                     p.dbias_p, dm.batch * dm.nseg, dm.dim, dm.dstate, p.dA, p.dDskip, p.ddt_bias);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_adjoint_agg(const BwdDims& dm, const BwdPtrs& p, hipStream_t s) {
+  if (dm.nseg < 2) return hipSuccess;
+  return dm.io == kIoBf16 ? bwd_detail::launch_adjoint_agg_n<BF16>(dm, p, s)
+                          : bwd_detail::launch_adjoint_agg_n<F32>(dm, p, s);
+}
+
+hipError_t launch_bwd_adjoint_combine(const BwdDims& dm, const float* A, const float* dh_final, const float* adj_m,
+                                      const float* adj_s, float* lam_seg, hipStream_t s) {
+  const int64_t nstate = dm.batch * dm.dim * dm.dstate;
+  hipLaunchKernelGGL(bwd_adjoint_combine_kernel, dim3((unsigned)((nstate + 255) / 256)), dim3(256), 0, s, nstate,
+                     dm.dim, dm.dstate, dm.nseg, A, dh_final, adj_m, adj_s, lam_seg);
   return hipGetLastError();
 }
 

@@ -156,10 +156,12 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int sg = w * K + hk;
 
-  const int64_t nwg = dm.cblocks * dm.batch;
+  // logical block -> (segment, batch row, channel block), channel block fastest
+  const int64_t nwg = dm.cblocks * dm.batch * dm.nseg;
   const int64_t lb = bwd_logical_block(blockIdx.x, nwg);
   const int64_t cb = lb % dm.cblocks;
-  const int64_t b = lb / dm.cblocks;
+  const int64_t b = (lb / dm.cblocks) % dm.batch;
+  const int64_t seg = lb / (dm.cblocks * dm.batch);
   const int64_t d = cb * CPB + c;
   const bool act = d < dm.dim;
   const int64_t dc = act ? d : dm.dim - 1;   // inactive lanes run a valid row with zero gradients
@@ -169,7 +171,11 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
   const int64_t dt_row = dm.dt_row ? b * L : row;   // dt per (row, token) is shared by the row's channels
   const bool vec = dm.vec != 0;
   const bool has_z = p.z != nullptr;
-  const int64_t nck = (L + CK - 1) / CK;
+  const int64_t nck = (L + CK - 1) / CK;   // chunks of the whole sequence
+  // this workgroup's chunks [kb, ke): its segment of the sequence
+  const int64_t kb = seg * dm.seg_len / CK;
+  const int64_t ke = (seg + 1) * dm.seg_len / CK < nck ? (seg + 1) * dm.seg_len / CK : nck;
+  const int64_t kfull = ke < L / CK ? ke : L / CK;   // chunks below kfull lie wholly inside the sequence
 
   const T* __restrict__ x = static_cast<const T*>(p.x);
   const T* __restrict__ dt = static_cast<const T*>(p.dt);
@@ -232,12 +238,13 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
   // pass already stored them) ----
   if (!dm.have_ckpt) {
     float h[NS];
+    // the state entering the segment: h0 for the first, else from the segments' combine
+    const float* hs0 = seg > 0 ? p.h_seg + (ch * dm.nseg + seg) * N : (p.h0 ? p.h0 + ch * N : nullptr);
 #pragma unroll
-    for (int s = 0; s < NS; ++s) h[s] = p.h0 ? p.h0[ch * N + sg * NS + s] : 0.0f;
-    const int64_t nfull = L / CK;   // whole chunks
+    for (int s = 0; s < NS; ++s) h[s] = hs0 ? hs0[sg * NS + s] : 0.0f;
     Fetch f;
-    if (nfull > 0) fetch(std::true_type{}, 0, false, f);
-    else fetch(std::false_type{}, 0, false, f);
+    if (kb < kfull) fetch(std::true_type{}, kb, false, f);
+    else fetch(std::false_type{}, kb, false, f);
     // FULL (a compile-time tag): all CK tokens of the chunk lie inside the sequence
     auto sweep = [&](auto full_tag, int64_t k) {
       constexpr bool FULL = decltype(full_tag)::value;
@@ -247,8 +254,8 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
       }
       float xv[kSpan], dl[kSpan], v2[kSpan];
       stage(FULL ? kSpan : own_valid(k), f, xv, dl, v2);
-      if (k + 1 < nfull) fetch(std::true_type{}, k + 1, false, f);
-      else if (k + 1 < nck) fetch(std::false_type{}, k + 1, false, f);
+      if (k + 1 < kfull) fetch(std::true_type{}, k + 1, false, f);
+      else if (k + 1 < ke) fetch(std::false_type{}, k + 1, false, f);
       __syncthreads();
       const int nj = FULL ? CK : (int)(chunk_end(k) - k * CK);
 #pragma unroll
@@ -268,15 +275,18 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
       }
       __syncthreads();
     };
-    for (int64_t k = 0; k < nfull; ++k) sweep(std::true_type{}, k);
-    if (nfull < nck) sweep(std::false_type{}, nfull);
+    for (int64_t k = kb; k < kfull; ++k) sweep(std::true_type{}, k);
+    if (kfull < ke) sweep(std::false_type{}, kfull);
   }
 
   // ---- 2. chunks last to first ----
   float lam[NS], dAacc[NS];
+  // the adjoint carried in from the tokens after the segment: dh_final for the
+  // last, else from the segments' combine
+  const float* lam0 = p.lam_seg ? p.lam_seg + (ch * dm.nseg + seg) * N : (p.dh_final ? p.dh_final + ch * N : nullptr);
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    lam[s] = (act && p.dh_final) ? p.dh_final[ch * N + sg * NS + s] : 0.0f;
+    lam[s] = (act && lam0) ? lam0[sg * NS + s] : 0.0f;
     dAacc[s] = 0.0f;
   }
   float dD_acc = 0.0f, dbias_acc = 0.0f;
@@ -294,11 +304,11 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
   float* __restrict__ pdst = part_row + (int64_t)(pwhich * N + sg * NS + ps) * Lp;
 
   Fetch f;
-  if (L % CK == 0) fetch(std::true_type{}, nck - 1, true, f);
-  else fetch(std::false_type{}, nck - 1, true, f);
+  if (ke == kfull) fetch(std::true_type{}, ke - 1, true, f);
+  else fetch(std::false_type{}, ke - 1, true, f);
   float ckn[NS];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) ckn[s] = act ? ck_row[(nck - 1) * ck_stride + s] : 0.0f;
+  for (int s = 0; s < NS; ++s) ckn[s] = act ? ck_row[(ke - 1) * ck_stride + s] : 0.0f;
 
   auto chunk = [&](auto full_tag, int64_t k) {
     constexpr bool FULL = decltype(full_tag)::value;
@@ -322,7 +332,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
     float Es[ZOH ? 1 : CK][NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) hs[0][s] = ckn[s];
-    if (k > 0) {
+    if (k > kb) {
       fetch(std::true_type{}, k - 1, true, f);   // every chunk before the last is whole
 #pragma unroll
       for (int s = 0; s < NS; ++s) ckn[s] = act ? ck_row[(k - 1) * ck_stride + s] : 0.0f;
@@ -481,17 +491,19 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
     __syncthreads();
   };
   {
-    int64_t k = nck - 1;
-    if (L % CK != 0) chunk(std::false_type{}, k--);   // the ragged last chunk comes first
-    for (; k >= 0; --k) chunk(std::true_type{}, k);
+    int64_t k = ke - 1;
+    if (ke > kfull) chunk(std::false_type{}, k--);   // the sequence's ragged last chunk comes first
+    for (; k >= kb; --k) chunk(std::true_type{}, k);
   }
 
-  // dh0 = Abar_0 lam_0 (lam already carries the factor); per-(row, channel) sums
+  // dh0 = Abar_0 lam_0 (lam already carries the factor; the first segment's
+  // workgroups); per-(segment, row, channel) sums
+  const int64_t pch = seg * dm.batch * dm.dim + ch;
   if (act) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      if (p.dh0) p.dh0[ch * N + sg * NS + s] = lam[s];
-      p.dA_p[ch * N + sg * NS + s] = dAacc[s];
+      if (p.dh0 && seg == 0) p.dh0[ch * N + sg * NS + s] = lam[s];
+      p.dA_p[pch * N + sg * NS + s] = dAacc[s];
     }
   }
   s_pp[sg][0][c] = make_float2(dD_acc, dbias_acc);   // CK >= SG rows
@@ -504,14 +516,149 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
       a0 += v.x;
       a1 += v.y;
     }
-    p.dD_p[ch] = a0;
-    p.dbias_p[ch] = a1;
+    p.dD_p[pch] = a0;
+    p.dbias_p[pch] = a1;
+  }
+}
+
+// A split sequence's adjoint aggregates.  Going back through segment s (tokens
+// t0 .. t1-1) the carried adjoint obeys mu <- Abar_t (mu + dr_t C_t), so what
+// leaves the segment is exp(A sum Delta) mu_in + M_s, with
+//   M_s = sum_t (prod_{t0 <= t' <= t} Abar_t') dr_t C_t
+// the value that leaves when nothing enters.  dr = dy silu(z) needs no state,
+// so every segment's (M_s, sum Delta) is computed independently here, for the
+// segments after the first (the first one's is never used); a combine then
+// gives the adjoint entering every segment.  Same lane layout and chunking as
+// the main kernel: the owner of each token stages Delta and dr, and every lane
+// runs its state components back through the chunk.
+template <int N, int G, int K, typename IO>
+__global__ __launch_bounds__(64 * G) void bwd_adjoint_agg_kernel(const BwdDims dm, const BwdPtrs p) {
+  using T = typename IO::T;
+  constexpr int CPB = 64 / K;
+  constexpr int SG = G * K;
+  constexpr int NS = N / SG;
+  constexpr int CK = kSpan * SG;
+  constexpr int SW = SpanT<IO, kSpan>::kWords;
+  static_assert(CK * N <= 64 * G, "one B/C piece per thread");
+  __shared__ float2 s_dr[CK][CPB];   // (Delta, dr) per token and channel
+  __shared__ float s_c[CK][N];       // C_n of the chunk's tokens
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int c = lane / K;
+  const int hk = lane % K;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int sg = w * K + hk;
+
+  // logical block -> (segment 1 .. nseg-1, batch row, channel block)
+  const int64_t nwg = dm.cblocks * dm.batch * (dm.nseg - 1);
+  const int64_t lb = bwd_logical_block(blockIdx.x, nwg);
+  const int64_t cb = lb % dm.cblocks;
+  const int64_t b = (lb / dm.cblocks) % dm.batch;
+  const int64_t seg = 1 + lb / (dm.cblocks * dm.batch);
+  const int64_t d = cb * CPB + c;
+  const bool act = d < dm.dim;
+  const int64_t dc = act ? d : dm.dim - 1;
+  const int64_t L = dm.seqlen;
+  const int64_t ch = b * dm.dim + dc;
+  const int64_t row = ch * L;
+  const int64_t dt_row = dm.dt_row ? b * L : row;
+  const bool vec = dm.vec != 0;
+  const bool has_z = p.z != nullptr;
+  const int64_t nck = (L + CK - 1) / CK;
+  const int64_t kb = seg * dm.seg_len / CK;
+  const int64_t ke = (seg + 1) * dm.seg_len / CK < nck ? (seg + 1) * dm.seg_len / CK : nck;
+  const int j_own = sg * kSpan;
+
+  const T* __restrict__ dt = static_cast<const T*>(p.dt);
+  const T* __restrict__ z = static_cast<const T*>(p.z);
+  const T* __restrict__ dy = static_cast<const T*>(p.dy);
+  float A2[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) A2[s] = p.A[dc * N + sg * NS + s] * kLog2e;
+  const float bias2 = p.dt_bias ? p.dt_bias[dc] * kLog2e : 0.0f;
+  const float* __restrict__ bc_row = p.bc + b * L * (2 * N);
+
+  auto chunk_end = [&](int64_t k) { return (k * CK + CK < L) ? k * CK + CK : L; };
+  struct Fetch {
+    uint32_t dt[SW], z[SW], dy[SW];
+    float c;
+  };
+  auto fetch = [&](int64_t k, Fetch& f) {
+    const int64_t t0 = k * CK;
+    const int64_t v = chunk_end(k) - (t0 + j_own);
+    const int valid = (int)(v < 0 ? 0 : (v < kSpan ? v : kSpan));
+    load_span<IO, kSpan>(dt, dt_row + t0 + j_own, valid, vec, f.dt);
+    if (has_z) load_span<IO, kSpan>(z, row + t0 + j_own, valid, vec, f.z);
+    load_span<IO, kSpan>(dy, row + t0 + j_own, valid, vec, f.dy);
+    f.c = 0.0f;
+    if (tid < CK * N && t0 + tid / N < chunk_end(k)) f.c = bc_row[(t0 * N + tid) * 2 + 1];
+  };
+
+  float mu[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) mu[s] = 0.0f;
+  float dsum = 0.0f;
+  Fetch f;
+  fetch(ke - 1, f);
+  for (int64_t k = ke - 1; k >= kb; --k) {
+    const int64_t t0 = k * CK;
+    const int nj = (int)(chunk_end(k) - t0);
+#pragma unroll
+    for (int i = 0; i < kSpan; ++i) {
+      const float dl = (j_own + i < nj) ? softplus_dt(span_elem<IO>(f.dt, i), bias2) : 0.0f;
+      const float dyv = act ? span_elem<IO>(f.dy, i) : 0.0f;   // padding tokens load as zero
+      float gate = 1.0f;
+      if (has_z) {
+        const float zv = span_elem<IO>(f.z, i);
+        gate = zv * sigmoid2(zv * kLog2e);
+      }
+      s_dr[j_own + i][c] = make_float2(dl, dyv * gate);
+    }
+    if (tid < CK * N) s_c[tid / N][tid % N] = f.c;
+    if (k > kb) fetch(k - 1, f);
+    __syncthreads();
+#pragma unroll
+    for (int j = CK - 1; j >= 0; --j) {
+      const float2 o = s_dr[j][c];   // zero Delta and dr past the sequence's end
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const float lam = fmaf(o.y, s_c[j][sg * NS + s], mu[s]);
+        mu[s] = __builtin_amdgcn_exp2f(o.x * A2[s]) * lam;
+      }
+      dsum += o.x;
+    }
+    __syncthreads();
+  }
+  if (act) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) p.adj_m[(ch * dm.nseg + seg) * N + sg * NS + s] = mu[s];
+    if (sg == 0) p.adj_s[ch * dm.nseg + seg] = dsum;
+  }
+}
+
+template <int N, int G, int K, typename IO>
+hipError_t launch_adjoint_agg_t(const BwdDims& dm, const BwdPtrs& p, hipStream_t s) {
+  const int64_t nwg = dm.cblocks * dm.batch * (dm.nseg - 1);
+  hipLaunchKernelGGL((bwd_adjoint_agg_kernel<N, G, K, IO>), dim3((unsigned)nwg), dim3(64 * G), 0, s, dm, p);
+  return hipGetLastError();
+}
+
+template <typename IO>
+hipError_t launch_adjoint_agg_n(const BwdDims& dm, const BwdPtrs& p, hipStream_t s) {
+  switch (dm.dstate) {
+    case 1: return launch_adjoint_agg_t<1, 1, 1, IO>(dm, p, s);
+    case 2: return launch_adjoint_agg_t<2, 2, 1, IO>(dm, p, s);
+    case 4: return launch_adjoint_agg_t<4, 4, 1, IO>(dm, p, s);
+    case 8: return launch_adjoint_agg_t<8, 4, 2, IO>(dm, p, s);
+    case 16: return launch_adjoint_agg_t<16, 4, 2, IO>(dm, p, s);
+    default: return hipErrorInvalidValue;
   }
 }
 
 template <int N, int G, int K, typename IO, bool ZOH>
 hipError_t launch_bwd_t(const BwdDims& dm, const BwdPtrs& p, hipStream_t s) {
-  const int64_t nwg = dm.cblocks * dm.batch;
+  const int64_t nwg = dm.cblocks * dm.batch * dm.nseg;
   hipLaunchKernelGGL((scan_bwd_kernel<N, G, K, IO, ZOH>), dim3((unsigned)nwg), dim3(64 * G), 0, s, dm, p);
   return hipGetLastError();
 }

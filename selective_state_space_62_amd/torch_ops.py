@@ -133,16 +133,19 @@ def state_update(state, x, dt, B, C, A, z=None, Dskip=None, dt_bias=None, *, y=N
     return y
 
 
-def bwd_workspace_bytes(batch, dim, dstate, seqlen, dtype=torch.bfloat16) -> int:
-    return _b.ss_scan_bwd_workspace_bytes(batch, dim, dstate, seqlen, _IO[dtype])
+def bwd_workspace_bytes(batch, dim, dstate, seqlen, dtype=torch.bfloat16, segment_len=None) -> int:
+    return _b.ss_scan_bwd_seg_workspace_bytes(batch, dim, dstate, seqlen, _IO[dtype], int(segment_len or 0))
 
 
 def scan_bwd(x, dt, B, C, A, dy, z=None, Dskip=None, dt_bias=None, h0=None, dh_final=None, *, workspace=None,
-             need_dA=True, need_dDskip=True, need_ddt_bias=True, need_dh0=True, ckpt=None, zoh=False):
+             need_dA=True, need_dDskip=True, need_ddt_bias=True, need_dh0=True, ckpt=None, zoh=False,
+             segment_len=None):
     """Gradients of ``scan_fwd`` (zoh=True: of ``scan_fwd(..., zoh=True)``) for upstream
     gradients dy (batch, D, L) and dh_final (batch, D, N) float32 (None = 0).  dt may be
     (batch, L): one value per token shared by the channels (SS_FLAG_DT_PER_ROW);
-    its gradient is then (batch, L), the sum over channels.
+    its gradient is then (batch, L), the sum over channels.  segment_len (None or 0:
+    the library's choice; else a multiple of 64) cuts the sequence into segments
+    run in parallel (ss_scan_bwd_seg).
 
     Returns a dict: dx, ddt, dz (None without z) in the I/O dtype, shaped like x
     (ddt like dt); dB, dC shaped like B; dA (D, N), dDskip (D,), ddt_bias (D,),
@@ -172,7 +175,8 @@ def scan_bwd(x, dt, B, C, A, dy, z=None, Dskip=None, dt_bias=None, h0=None, dh_f
                dDskip=torch.empty(dim, dtype=torch.float32, device=dev) if need_dDskip else None,
                ddt_bias=torch.empty(dim, dtype=torch.float32, device=dev) if need_ddt_bias else None,
                dh0=torch.empty((batch, dim, N), dtype=torch.float32, device=dev) if need_dh0 else None)
-    nbytes = _b.ss_scan_bwd_workspace_bytes(batch, dim, N, L, io)
+    seg = int(segment_len or 0)
+    nbytes = _b.ss_scan_bwd_seg_workspace_bytes(batch, dim, N, L, io, seg)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
     if workspace.numel() < nbytes:
@@ -182,10 +186,12 @@ def scan_bwd(x, dt, B, C, A, dy, z=None, Dskip=None, dt_bias=None, h0=None, dh_f
     outs = (_ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dz"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dA"]),
             _ptr(out["dDskip"]), _ptr(out["ddt_bias"]), _ptr(out["dh0"]), _ptr(workspace), workspace.numel(),
             _stream(dev))
-    if ckpt is not None or dt_row or zoh:
-        if ckpt is not None:
-            _need(ckpt, "ckpt", torch.float32, (ckpt_numel(batch, dim, N, L),), dev)
-        flags = (_b.SS_FLAG_DT_PER_ROW if dt_row else 0) | (_b.SS_FLAG_ZOH if zoh else 0)
+    if ckpt is not None:
+        _need(ckpt, "ckpt", torch.float32, (ckpt_numel(batch, dim, N, L),), dev)
+    flags = (_b.SS_FLAG_DT_PER_ROW if dt_row else 0) | (_b.SS_FLAG_ZOH if zoh else 0)
+    if seg:
+        _b.ss_scan_bwd_seg(batch, dim, N, L, io, flags, seg, *ins, _ptr(ckpt), *outs)
+    elif ckpt is not None or flags:
         _b.ss_scan_bwd_ex(batch, dim, N, L, io, flags, *ins, _ptr(ckpt), *outs)
     else:
         _b.ss_scan_bwd(batch, dim, N, L, io, *ins, *outs)

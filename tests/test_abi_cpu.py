@@ -310,6 +310,31 @@ def test_ckpt_bytes_and_bwd_ex_flags():
     assert "ddt overlaps input dt" in b.last_error()
 
 
+def test_bwd_segment_plan_and_workspace():
+    r = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    # explicit lengths are multiples of 64; a length of at least seqlen runs the sequence whole
+    assert b.ss_scan_bwd_seg_workspace_bytes(1, 64, 16, 17, b.SS_F32, 64) == b.ss_scan_bwd_workspace_bytes(
+        1, 64, 16, 17, b.SS_F32)
+    assert b.ss_scan_bwd_seg_workspace_bytes(1, 64, 16, 300, b.SS_F32, 100) == 0
+    assert b.ss_scan_bwd_seg_workspace_bytes(1, 64, 16, 300, b.SS_F32, -64) == 0
+    # five segments of 64 tokens: the per-(segment, row) sums grow fivefold, and the
+    # segments' entering states, their forward aggregates (end states and Delta sums),
+    # the carried adjoints and the adjoint aggregates (values and Delta sums) are added
+    n5 = b.ss_scan_bwd_seg_workspace_bytes(1, 64, 16, 300, b.SS_F32, 64)
+    n1 = b.ss_scan_bwd_seg_workspace_bytes(1, 64, 16, 300, b.SS_F32, 1 << 20)
+    st, sc = 64 * 5 * 16 * 4, 64 * 5 * 4
+    assert n5 - n1 == (r(5 * 64 * 16 * 4) - r(64 * 16 * 4)) + 2 * (r(5 * 64 * 4) - r(64 * 4)) + 4 * r(st) + 2 * r(sc)
+    # the automatic choice: the 2.8B shape runs whole; one channel block over 8192 tokens is split
+    assert b.ss_scan_bwd_segment_len(8, 5120, 16, 2048, b.SS_BF16) == 2048
+    assert b.ss_scan_bwd_segment_len(1, 32, 16, 8192, b.SS_F32) == 2048
+    assert b.ss_scan_bwd_segment_len(1, 32, 3, 8192, b.SS_F32) == 0
+    # an invalid length is rejected before the pointers are looked at
+    st_ = b.lib.ss_scan_bwd_seg(1, 64, 16, 300, b.SS_F32, 0, 100, *([None] * 22), 0, None)
+    assert st_ == b.SS_ERR_INVALID_ARG and "segment_len" in b.last_error()
+    assert b.lib.ss_scan_bwd_seg(1, 64, 16, 300, b.SS_F32, 8, 64, *([None] * 22), 0, None) == \
+        b.SS_ERR_UNSUPPORTED
+
+
 def test_timing_record_empty():
     b.ss_timing_enable(False)
     b.ss_timing_reset()

@@ -1,0 +1,252 @@
+"""The backward pass with the sequence cut into segments (ss_scan_bwd_seg, and
+the automatic split of long sequences) on the GPU against the oracle.
+
+Each segment runs from the state entering it (the forward's chunk aggregates
+and their combine, or forward-saved checkpoints) and from the adjoint carried in
+from the tokens after it (per-segment adjoint aggregates and a reverse
+combine).  The gradients are those of the whole sequence, so the oracle's
+backward (pinned in tests/pins.py by finite differences and adjoint identities)
+is the reference, at the tolerances of tests/test_gpu_bwd.py.  Segment lengths
+are multiples of 64 tokens; the cases cut sequences into 2 to 10 segments, most
+with a ragged last one, and cover every state size, both I/O types, the
+zero-order hold, one dt per (row, token) and forward-saved checkpoints.  The
+million-token workload runs in the automatic split, the oracle checking 64
+channels over every token.
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import log, random_problem, rel_l2, to_dev, to_f64
+from workloads import LONG, inputs
+
+pytestmark = pytest.mark.gpu
+
+ELEMENT = ("dx", "ddt", "dz", "dh0")
+SUMS = ("dA", "dDskip", "ddt_bias", "dB", "dC")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def ss():
+    import selective_state_space_62_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def o():
+    return oracle.default()
+
+
+def _tol(io, name):
+    if io == "bf16":
+        return 2e-2
+    return 1e-5 if name in ELEMENT else 5e-5
+
+
+def _problem(rng, batch, D, N, L, io, optional=True):
+    raw, par, f64 = random_problem(rng, batch, D, N, L, io, with_z=optional, with_skip=optional,
+                                   with_bias=optional, with_h0=optional)
+    dy = rng.standard_normal((batch, D, L)).astype(np.float32)
+    raw["dy"] = dy if io == "f32" else inputs.f32_to_bf16_bits(dy)
+    f64["dy"] = inputs.raw_to_f64(raw["dy"], io)
+    par["dh_final"] = rng.standard_normal((batch, D, N)).astype(np.float32) if optional else None
+    return raw, par, f64
+
+
+def _upload(raw, par, io, dev):
+    import torch
+    t = {k: to_dev(v, io, dev) for k, v in raw.items()}
+    p = {k: (torch.from_numpy(v).to(dev) if v is not None else None) for k, v in par.items()}
+    return t, p
+
+
+def _bwd(ss, t, p, **kw):
+    import torch
+    g = ss.scan_bwd(t["x"], t["dt"], t["B"], t["C"], p["A"], t["dy"], z=t.get("z"), Dskip=p["Dskip"],
+                    dt_bias=p["dt_bias"], h0=p["h0"], dh_final=p["dh_final"], **kw)
+    torch.cuda.synchronize()
+    return g
+
+
+def _oracle(o, f64, par, zoh=False):
+    return o.scan_bwd(f64["x"], f64["dt"], f64["B"], f64["C"], par["A"], f64["dy"], z=f64.get("z"),
+                      Dskip=par["Dskip"], dt_bias=par["dt_bias"], h0=par["h0"], dh_final=par["dh_final"], zoh=zoh)
+
+
+def _compare(g, r, io, what, skip=()):
+    errs = {k: rel_l2(to_f64(g[k]), r[k]) for k in ELEMENT + SUMS
+            if k not in skip and g.get(k) is not None and r.get(k) is not None}
+    log("%s: %s" % (what, ", ".join("%s %.2e" % kv for kv in errs.items())))
+    for k, e in errs.items():
+        assert e <= _tol(io, k), (what, k, e, errs)
+
+
+# (batch, D, N, L, segment length)
+CASES = [
+    (1, 77, 16, 300, 64),     # 5 segments, the last ragged (44 tokens, not a whole chunk)
+    (2, 33, 16, 256, 128),    # 2 whole segments
+    (2, 40, 8, 257, 64),      # 5 segments, a 1-token last one
+    (1, 20, 4, 130, 64),      # 3 segments
+    (2, 70, 2, 129, 64),      # 3 segments
+    (1, 130, 1, 577, 64),     # 10 segments
+    (1, 32, 16, 64, 64),      # one segment: the unsplit path
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=["x".join(map(str, c)) for c in CASES])
+@pytest.mark.parametrize("optional", [True, False], ids=["all-inputs", "no-optional"])
+def test_bwd_seg_f32_matches_oracle(ss, o, dev, case, optional):
+    batch, D, N, L, seg = case
+    log("bwd seg f32 %s optional=%s" % (case, optional))
+    rng = np.random.default_rng(zlib.crc32(repr(("seg", case, optional)).encode()))
+    raw, par, f64 = _problem(rng, batch, D, N, L, "f32", optional)
+    t, p = _upload(raw, par, "f32", dev)
+    g = _bwd(ss, t, p, segment_len=seg)
+    _compare(g, _oracle(o, f64, par), "f32", "bwd seg %s" % (case,))
+
+
+@pytest.mark.parametrize("case", [(2, 96, 16, 520, 128), (1, 50, 8, 300, 64)], ids=lambda c: "x".join(map(str, c)))
+def test_bwd_seg_bf16_matches_oracle(ss, o, dev, case):
+    batch, D, N, L, seg = case
+    log("bwd seg bf16 %s" % (case,))
+    rng = np.random.default_rng(zlib.crc32(repr(("seg-bf16", case)).encode()))
+    raw, par, f64 = _problem(rng, batch, D, N, L, "bf16")
+    t, p = _upload(raw, par, "bf16", dev)
+    g = _bwd(ss, t, p, segment_len=seg)
+    _compare(g, _oracle(o, f64, par), "bf16", "bwd seg bf16 %s" % (case,))
+
+
+@pytest.mark.parametrize("case", [(2, 77, 16, 300, 64), (1, 40, 4, 200, 64)], ids=lambda c: "x".join(map(str, c)))
+def test_bwd_seg_zoh_matches_oracle(ss, o, dev, case):
+    """Zero-order hold: the segments' incoming states come from the ZOH forward
+    aggregates; the adjoint's decay is the same Abar."""
+    batch, D, N, L, seg = case
+    log("bwd seg zoh %s" % (case,))
+    rng = np.random.default_rng(zlib.crc32(repr(("seg-zoh", case)).encode()))
+    raw, par, f64 = _problem(rng, batch, D, N, L, "f32")
+    t, p = _upload(raw, par, "f32", dev)
+    g = _bwd(ss, t, p, segment_len=seg, zoh=True)
+    _compare(g, _oracle(o, f64, par, zoh=True), "f32", "bwd seg zoh %s" % (case,))
+
+
+def test_bwd_seg_dt_per_row(ss, o, dev):
+    """One dt per (row, token): the shared dt's gradient, summed over channels,
+    against the oracle's general backward with dt repeated over the channels."""
+    import torch
+    batch, D, N, L, seg = 2, 64, 16, 300, 64
+    rng = np.random.default_rng(zlib.crc32(b"seg-dt-row"))
+    raw, par, f64 = _problem(rng, batch, D, N, L, "f32")
+    dt_row = (0.5 * rng.standard_normal((batch, L))).astype(np.float32)
+    dt_full = np.ascontiguousarray(np.broadcast_to(dt_row[:, None, :], (batch, D, L)))
+    raw["dt"], f64["dt"] = dt_full, dt_full.astype(np.float64)
+    t, p = _upload(raw, par, "f32", dev)
+    t["dt"] = torch.from_numpy(dt_row).to(dev)
+    log("bwd seg dt per row %s" % ((batch, D, N, L, seg),))
+    g = _bwd(ss, t, p, segment_len=seg)
+    r = _oracle(o, f64, par)
+    e = rel_l2(to_f64(g["ddt"]), r["ddt"].sum(axis=1))
+    log("  shared dt gradient rel-L2 %.3e" % e)
+    assert e <= 5e-5
+    _compare(g, r, "f32", "bwd seg dt per row", skip=("ddt",))
+
+
+def test_bwd_seg_from_checkpoints(ss, o, dev):
+    """Forward-saved checkpoints give the segments their states (no aggregate pass)."""
+    import torch
+    batch, D, N, L, seg = 2, 45, 16, 333, 128
+    rng = np.random.default_rng(zlib.crc32(b"seg-ckpt"))
+    raw, par, f64 = _problem(rng, batch, D, N, L, "f32")
+    t, p = _upload(raw, par, "f32", dev)
+    ck = torch.full((ss.ckpt_numel(batch, D, N, L),), float("nan"), device=dev)
+    ss.scan_fwd(t["x"], t["dt"], t["B"], t["C"], p["A"], z=t["z"], Dskip=p["Dskip"], dt_bias=p["dt_bias"],
+                h0=p["h0"], ckpt=ck)
+    log("bwd seg from checkpoints %s" % ((batch, D, N, L, seg),))
+    g = _bwd(ss, t, p, segment_len=seg, ckpt=ck)
+    _compare(g, _oracle(o, f64, par), "f32", "bwd seg ckpt")
+
+
+def test_bwd_seg_agrees_with_whole_and_is_deterministic(ss, dev):
+    """The split backward equals the unsplit one up to fp32 rounding (the decay
+    across a segment is one exponential of the summed Delta), and repeats bit for
+    bit."""
+    import torch
+    batch, D, N, L = 2, 96, 16, 1000
+    rng = np.random.default_rng(zlib.crc32(b"seg-vs-whole"))
+    raw, par, f64 = _problem(rng, batch, D, N, L, "f32")
+    t, p = _upload(raw, par, "f32", dev)
+    log("bwd seg vs whole %s" % ((batch, D, N, L),))
+    whole = _bwd(ss, t, p, segment_len=1024)     # at least seqlen: one segment
+    s1 = _bwd(ss, t, p, segment_len=192)
+    s2 = _bwd(ss, t, p, segment_len=192)
+    for k, v in s1.items():
+        if v is None:
+            continue
+        assert torch.equal(v, s2[k]), k
+        e = rel_l2(to_f64(v), to_f64(whole[k]))
+        log("  %s rel-L2 vs whole %.2e" % (k, e))
+        assert e <= (2e-6 if k in ELEMENT else 1e-5), (k, e)
+
+
+def test_bwd_automatic_split(ss, o, dev):
+    """A long sequence on few channels is split automatically (one workgroup's
+    worth of channels, 8192 tokens: four segments of 2048), and still matches."""
+    batch, D, N, L = 1, 32, 16, 8192
+    seg = ss.ss_scan_bwd_segment_len(batch, D, N, L, ss.SS_F32)
+    log("bwd automatic split %s: segment_len %d" % ((batch, D, N, L), seg))
+    assert 0 < seg < L and seg % 64 == 0
+    rng = np.random.default_rng(zlib.crc32(b"seg-auto"))
+    raw, par, f64 = _problem(rng, batch, D, N, L, "f32")
+    t, p = _upload(raw, par, "f32", dev)
+    g = _bwd(ss, t, p)
+    _compare(g, _oracle(o, f64, par), "f32", "bwd auto split")
+
+
+def test_bwd_long_1m_sampled(ss, o, dev):
+    """The million-token workload (1 x 2048 x 16, bf16) in the automatic split,
+    with device-generated inputs and dy; the oracle recomputes 64 sampled channels
+    over all 2^20 tokens.  dB and dC sum over all channels and are not checked
+    here (the smaller cases check them)."""
+    import torch
+    from workloads import device as wdev
+    cfg = LONG
+    B_, D, N, L = cfg.batch, cfg.dim, cfg.dstate, cfg.seqlen
+    seg = ss.ss_scan_bwd_segment_len(B_, D, N, L, ss.SS_BF16)
+    log("bwd long context 1M, bf16, segment_len %d" % seg)
+    assert seg < L
+    t = wdev.scan_inputs(cfg, dev)
+    A, dskip, bias = wdev.params(cfg, dev)
+    dy = wdev.fill(torch.empty((B_, D, L), dtype=torch.bfloat16, device=dev), cfg, inputs.STREAM_DY)
+    g = ss.scan_bwd(t["x"], t["dt"], t["B"], t["C"], A, dy, z=t["z"], Dskip=dskip, dt_bias=bias)
+    torch.cuda.synchronize()
+    chans = inputs.sample_channels(cfg, cfg.check_channels)
+    assert all(b == 0 for b, _ in chans)
+    ds = np.array([d for _, d in chans])
+    idx = torch.from_numpy(ds).to(dev)
+    got = {k: to_f64(g[k][0, idx]) for k in ("dx", "ddt", "dz")}
+    got.update(dA=to_f64(g["dA"][idx]), dDskip=to_f64(g["dDskip"][idx]), ddt_bias=to_f64(g["ddt_bias"][idx]),
+               dh0=to_f64(g["dh0"][0, idx]))
+    del g, t, dy
+    torch.cuda.empty_cache()
+    sub = inputs.scan_inputs(cfg, channels=chans)
+    f = {k: inputs.raw_to_f64(v, cfg.io) for k, v in sub.items()}
+    dyh = np.stack([inputs.raw_to_f64(inputs.draw(cfg, inputs.STREAM_DY, d * L, L), cfg.io) for d in ds])
+    An, dn, bn = inputs.params(cfg)
+    r = o.scan_bwd(f["x"][None], f["dt"][None], f["B"], f["C"], An[ds], dyh[None], z=f["z"][None], Dskip=dn[ds],
+                   dt_bias=bn[ds])
+    errs = {}
+    for k in ("dx", "ddt", "dz", "dh0"):
+        errs[k] = rel_l2(got[k], r[k][0])
+    for k in ("dA", "dDskip", "ddt_bias"):
+        errs[k] = rel_l2(got[k], r[k])
+    log("  64 channels x 1M tokens: %s" % ", ".join("%s %.2e" % kv for kv in errs.items()))
+    for k, e in errs.items():
+        assert e <= 2e-2, (k, e)

@@ -29,6 +29,7 @@ from .configs import ScanConfig
 
 # Philox stream ids, one per tensor
 STREAM_X, STREAM_DT, STREAM_Z, STREAM_B, STREAM_C, STREAM_H0 = 1, 2, 3, 4, 5, 6
+STREAM_DY = 7  # the upstream gradient dy of a backward workload, N(0, 1) like x
 KEY1 = 0x53533632  # second key word, fixed for all workloads
 
 
