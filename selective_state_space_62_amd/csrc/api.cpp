@@ -584,7 +584,7 @@ BwdLayout bwd_layout(int64_t batch, int64_t dim, int dstate, int64_t seqlen, con
   off += round256((size_t)batch * seqlen * dstate * 2 * sizeof(float));
   w.ckpt = off;
   off += round256((size_t)batch * dim * w.chunks * dstate * sizeof(float));
-  w.part = off;   // partials (batch, channel block, output, token), tokens padded to whole chunks
+  w.part = off;   // partials (batch, channel block, chunk, output, chunk token)
   off += round256((size_t)batch * w.cblocks * ssscan::bwd_part_outputs(dstate) * (w.chunks * ck) * sizeof(float));
   w.dA_p = off;   // per-(segment, row) sums
   off += round256((size_t)sg.n * batch * dim * dstate * sizeof(float));

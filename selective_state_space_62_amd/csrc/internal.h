@@ -59,7 +59,7 @@ struct BwdDims {
 };
 
 // dB/dC partials per (batch row, channel block): 2 N outputs plus one for the
-// per-row dt gradient, each over the tokens padded to whole backward chunks
+// per-row dt gradient, for every token of whole backward chunks
 constexpr int bwd_part_outputs(int dstate) { return 2 * dstate + 1; }
 
 struct BwdPtrs {
@@ -83,7 +83,7 @@ struct BwdPtrs {
   float* ddt_bias;        // nullable
   float* dh0;             // nullable
   float* ckpt;            // workspace: (batch, chunks, dim, dstate) state at every chunk start
-  float* part;            // workspace: (batch, cblocks, bwd_part_outputs, padded seqlen) partial sums
+  float* part;            // workspace: (batch, cblocks, chunk, bwd_part_outputs, chunk token) partial sums
   float* dA_p;            // workspace: (nseg, batch, dim, dstate) per-(segment, row) sums
   float* dD_p;            // workspace: (nseg, batch, dim)
   float* dbias_p;         // workspace: (nseg, batch, dim)

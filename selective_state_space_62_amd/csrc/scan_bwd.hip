@@ -9,12 +9,13 @@ namespace {
 using namespace dev;
 
 // dB[b, n, t], dC[b, n, t] and, for a per-row dt, ddt[b, t]: the channel
-// blocks' partials, in block order.  Partials are (batch, block, output, token)
-// with bwd_part_outputs(N) outputs of Lp tokens; one thread per (b, output, t),
-// tokens fastest, so loads and stores are coalesced.
+// blocks' partials, in block order.  Partials are (batch, block, chunk, output,
+// chunk token) with bwd_part_outputs(N) outputs per chunk of ck tokens; one
+// thread per (b, output, t), tokens fastest, so the stores are coalesced and
+// the loads come in runs of ck tokens.
 template <typename IO>
 __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restrict__ part, int64_t batch,
-                                                            int64_t cblocks, int64_t L, int64_t Lp, int N,
+                                                            int64_t cblocks, int64_t L, int64_t nck, int ck, int N,
                                                             int nred, typename IO::T* __restrict__ dB,
                                                             typename IO::T* __restrict__ dC,
                                                             typename IO::T* __restrict__ ddt_row) {
@@ -24,9 +25,10 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restr
   const int64_t t = i % L;
   const int64_t o = (i / L) % nred;
   const int64_t b = i / (L * nred);
-  const float* src = part + (b * cblocks * npart + o) * Lp + t;
+  const int64_t blk = nck * npart * ck;   // one block's partials
+  const float* src = part + b * cblocks * blk + ((t / ck) * npart + o) * ck + t % ck;
   float acc = 0.0f;
-  for (int64_t q = 0; q < cblocks; ++q) acc += src[q * npart * Lp];
+  for (int64_t q = 0; q < cblocks; ++q) acc += src[q * blk];
   if (o == 2 * N) store_one<IO>(ddt_row, b * L + t, acc);
   else store_one<IO>(o < N ? dB : dC, (b * N + o % N) * L + t, acc);
 }
@@ -101,15 +103,15 @@ hipError_t launch_scan_bwd(const BwdDims& dm, const BwdPtrs& p, hipStream_t s) {
   const int64_t nbc = dm.batch * dm.seqlen * nred;
   if (nbc > 0) {
     const unsigned blocks = (unsigned)((nbc + 255) / 256);
-    const int64_t ck = bwd_chunk_tokens(dm.dstate);
-    const int64_t Lp = (dm.seqlen + ck - 1) / ck * ck;
+    const int ck = bwd_chunk_tokens(dm.dstate);
+    const int64_t nck = (dm.seqlen + ck - 1) / ck;
     if (dm.io == kIoBf16)
       hipLaunchKernelGGL((bwd_reduce_bc_kernel<BF16>), dim3(blocks), dim3(256), 0, s, p.part, dm.batch, dm.cblocks,
-                         dm.seqlen, Lp, dm.dstate, nred, static_cast<uint16_t*>(p.dB), static_cast<uint16_t*>(p.dC),
-                         static_cast<uint16_t*>(p.ddt));
+                         dm.seqlen, nck, ck, dm.dstate, nred, static_cast<uint16_t*>(p.dB),
+                         static_cast<uint16_t*>(p.dC), static_cast<uint16_t*>(p.ddt));
     else
       hipLaunchKernelGGL((bwd_reduce_bc_kernel<F32>), dim3(blocks), dim3(256), 0, s, p.part, dm.batch, dm.cblocks,
-                         dm.seqlen, Lp, dm.dstate, nred, static_cast<float*>(p.dB), static_cast<float*>(p.dC),
+                         dm.seqlen, nck, ck, dm.dstate, nred, static_cast<float*>(p.dB), static_cast<float*>(p.dC),
                          static_cast<float*>(p.ddt));
     e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -34,10 +34,11 @@
 // by itself: a swap of wave halves between two registers (v_permlane32_swap)
 // and an add, a swap of row pairs (v_permlane16_swap) and an add, then DPP adds
 // within the 16-lane rows.  A chunk's sums stay in registers and are written
-// token-contiguous, one partial per (workgroup, output, token), to the
-// workspace; bwd_reduce_bc_kernel adds a batch row's partials in a fixed order.
-// dA, dDskip and dt_bias's gradient are summed per (row, channel) in registers
-// and over rows by bwd_reduce_param_kernel.  All sums have a fixed order:
+// to the workspace, one partial per (workgroup, output, token), each chunk's
+// outputs in one contiguous block (token fastest); bwd_reduce_bc_kernel adds a
+// batch row's partials in a fixed order.  dA, dDskip and dt_bias's gradient
+// are summed per (segment, row, channel) in registers and over segments and
+// rows by bwd_reduce_param_kernel.  All sums have a fixed order:
 // results are deterministic.  The next chunk's global operands are fetched while
 // the current one computes, and whole chunks run without per-token guards.
 #pragma once
@@ -291,8 +292,9 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
   }
   float dD_acc = 0.0f, dbias_acc = 0.0f;
   // dB/dC partials (batch, channel block, output, token), tokens padded to whole chunks
-  const int64_t Lp = nck * CK;
-  float* __restrict__ part_row = p.part + (b * dm.cblocks + cb) * NPART * Lp;
+  // dB/dC partials (batch, channel block, chunk, output, chunk token): a chunk's
+  // outputs are contiguous, one block per chunk
+  float* __restrict__ part_blk = p.part + (b * dm.cblocks + cb) * nck * (NPART * CK);
   // the lanes that write them: the first K lanes of each row that holds a sum (all
   // rows for NS == 2, rows 0 and 2 for NS == 1), and the output each one writes.
   // The sums cover the whole workgroup (channels past dim add zeros), so a
@@ -301,7 +303,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
   const bool pw = (lane & 15) < K && (NS == 2 || (prow & 1) == 0);
   const int pwhich = NS == 2 ? (prow & 1) : (prow >> 1);   // 0: dB, 1: dC
   const int ps = NS == 2 ? (prow >> 1) : 0;
-  float* __restrict__ pdst = part_row + (int64_t)(pwhich * N + sg * NS + ps) * Lp;
+  float* __restrict__ pdst = part_blk + (int64_t)(pwhich * N + sg * NS + ps) * CK;
 
   Fetch f;
   if (ke == kfull) fetch(std::true_type{}, ke - 1, true, f);
@@ -446,8 +448,9 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
       // which nothing reads)
       constexpr int SV = (CK % 4 == 0) ? 4 : 2;
       if (j % SV == 0 && pw) {
-        if constexpr (SV == 4) *reinterpret_cast<float4*>(pdst + t0 + j) = make_float4(uo[j], uo[j + 1], uo[j + 2], uo[j + 3]);
-        else *reinterpret_cast<float2*>(pdst + t0 + j) = make_float2(uo[j], uo[j + 1]);
+        float* const q = pdst + k * (NPART * CK) + j;
+        if constexpr (SV == 4) *reinterpret_cast<float4*>(q) = make_float4(uo[j], uo[j + 1], uo[j + 2], uo[j + 3]);
+        else *reinterpret_cast<float2*>(q) = make_float2(uo[j], uo[j + 1]);
       }
     }
     __syncthreads();
@@ -485,7 +488,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
         const float d0[1] = {ddtv[0]}, d1[1] = {ddtv[1]};
         const float u = bc_channel_sum<1, K>(d0, d1);
         if ((lane & 15) < K && (prow & 1) == 0 && (FULL || t0 + j_own + (prow >> 1) < t1))
-          part_row[(int64_t)NOUT * Lp + t0 + j_own + (prow >> 1)] = u;
+          part_blk[(k * NPART + NOUT) * CK + j_own + (prow >> 1)] = u;
       }
     }
     __syncthreads();
