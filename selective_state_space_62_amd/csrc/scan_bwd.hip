@@ -10,9 +10,10 @@ using namespace dev;
 
 // dB[b, n, t], dC[b, n, t] and, for a per-row dt, ddt[b, t]: the channel
 // blocks' partials, in block order.  Partials are (batch, block, chunk, output,
-// chunk token) with bwd_part_outputs(N) outputs per chunk of ck tokens; one
-// thread per (b, output, t), tokens fastest, so the stores are coalesced and
-// the loads come in runs of ck tokens.
+// chunk token) with bwd_part_outputs(N) outputs per chunk of ck tokens.  One
+// thread per (b, chunk, output, chunk token) of the nred outputs reduced, in
+// that order, so a wave reads a contiguous run of each block's chunk and
+// writes runs of ck tokens.
 template <typename IO>
 __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restrict__ part, int64_t batch,
                                                             int64_t cblocks, int64_t L, int64_t nck, int ck, int N,
@@ -21,12 +22,15 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restr
                                                             typename IO::T* __restrict__ ddt_row) {
   const int64_t npart = bwd_part_outputs(N);
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= batch * nred * L) return;
-  const int64_t t = i % L;
-  const int64_t o = (i / L) % nred;
-  const int64_t b = i / (L * nred);
+  if (i >= batch * nck * nred * ck) return;
+  const int j = (int)(i % ck);
+  const int64_t o = (i / ck) % nred;
+  const int64_t k = (i / (ck * nred)) % nck;
+  const int64_t b = i / (ck * nred * nck);
+  const int64_t t = k * ck + j;
+  if (t >= L) return;   // padding tokens of the last chunk
   const int64_t blk = nck * npart * ck;   // one block's partials
-  const float* src = part + b * cblocks * blk + ((t / ck) * npart + o) * ck + t % ck;
+  const float* src = part + b * cblocks * blk + (k * npart + o) * ck + j;
   float acc = 0.0f;
   for (int64_t q = 0; q < cblocks; ++q) acc += src[q * blk];
   if (o == 2 * N) store_one<IO>(ddt_row, b * L + t, acc);
@@ -100,11 +104,11 @@ hipError_t launch_scan_bwd(const BwdDims& dm, const BwdPtrs& p, hipStream_t s) {
                                      : bwd_detail::launch_bwd_n<F32, false>(dm, p, s);
   if (e != hipSuccess) return e;
   const int nred = 2 * dm.dstate + (dm.dt_row ? 1 : 0);   // outputs to reduce
-  const int64_t nbc = dm.batch * dm.seqlen * nred;
+  const int ck = bwd_chunk_tokens(dm.dstate);
+  const int64_t nck = (dm.seqlen + ck - 1) / ck;
+  const int64_t nbc = dm.batch * nck * nred * ck;
   if (nbc > 0) {
     const unsigned blocks = (unsigned)((nbc + 255) / 256);
-    const int ck = bwd_chunk_tokens(dm.dstate);
-    const int64_t nck = (dm.seqlen + ck - 1) / ck;
     if (dm.io == kIoBf16)
       hipLaunchKernelGGL((bwd_reduce_bc_kernel<BF16>), dim3(blocks), dim3(256), 0, s, p.part, dm.batch, dm.cblocks,
                          dm.seqlen, nck, ck, dm.dstate, nred, static_cast<uint16_t*>(p.dB),

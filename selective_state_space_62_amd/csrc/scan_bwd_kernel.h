@@ -531,20 +531,25 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
 // the value that leaves when nothing enters.  dr = dy silu(z) needs no state,
 // so every segment's (M_s, sum Delta) is computed independently here, for the
 // segments after the first (the first one's is never used); a combine then
-// gives the adjoint entering every segment.  Same lane layout and chunking as
-// the main kernel: the owner of each token stages Delta and dr, and every lane
-// runs its state components back through the chunk.
+// gives the adjoint entering every segment.  Same lanes as the main kernel
+// (G waves, K lanes per channel, NS state components per lane); work goes in
+// stages of 16 bytes of every operand row per lane (AS tokens, AS * G * K per
+// stage, which divides every segment length): the owner of each token stages
+// Delta and dr, and every lane runs its components back through the stage.
 template <int N, int G, int K, typename IO>
 __global__ __launch_bounds__(64 * G) void bwd_adjoint_agg_kernel(const BwdDims dm, const BwdPtrs p) {
   using T = typename IO::T;
   constexpr int CPB = 64 / K;
   constexpr int SG = G * K;
   constexpr int NS = N / SG;
-  constexpr int CK = kSpan * SG;
-  constexpr int SW = SpanT<IO, kSpan>::kWords;
-  static_assert(CK * N <= 64 * G, "one B/C piece per thread");
-  __shared__ float2 s_dr[CK][CPB];   // (Delta, dr) per token and channel
-  __shared__ float s_c[CK][N];       // C_n of the chunk's tokens
+  constexpr int AS = IO::kPerSpan;            // tokens per lane and stage
+  constexpr int ST = AS * SG;                 // tokens per stage (at most 64)
+  constexpr int SW = SpanT<IO, AS>::kWords;
+  constexpr int THREADS = 64 * G;
+  constexpr int CPT = (ST * N + THREADS - 1) / THREADS;   // C values each thread stages
+  static_assert(64 % ST == 0, "a stage divides every segment length");
+  __shared__ float2 s_dr[ST][CPB];   // (Delta, dr) per token and channel
+  __shared__ float s_c[ST][N];       // C_n of the stage's tokens
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -566,12 +571,13 @@ __global__ __launch_bounds__(64 * G) void bwd_adjoint_agg_kernel(const BwdDims d
   const int64_t ch = b * dm.dim + dc;
   const int64_t row = ch * L;
   const int64_t dt_row = dm.dt_row ? b * L : row;
-  const bool vec = dm.vec != 0;
+  const bool vec = (L % AS) == 0;   // every lane's span is 16-byte aligned
   const bool has_z = p.z != nullptr;
-  const int64_t nck = (L + CK - 1) / CK;
-  const int64_t kb = seg * dm.seg_len / CK;
-  const int64_t ke = (seg + 1) * dm.seg_len / CK < nck ? (seg + 1) * dm.seg_len / CK : nck;
-  const int j_own = sg * kSpan;
+  const int64_t t_begin = seg * dm.seg_len;
+  const int64_t t_end = t_begin + dm.seg_len < L ? t_begin + dm.seg_len : L;
+  const int64_t sb = t_begin / ST;
+  const int64_t se = (t_end + ST - 1) / ST;
+  const int j_own = sg * AS;
 
   const T* __restrict__ dt = static_cast<const T*>(p.dt);
   const T* __restrict__ z = static_cast<const T*>(p.z);
@@ -582,20 +588,22 @@ __global__ __launch_bounds__(64 * G) void bwd_adjoint_agg_kernel(const BwdDims d
   const float bias2 = p.dt_bias ? p.dt_bias[dc] * kLog2e : 0.0f;
   const float* __restrict__ bc_row = p.bc + b * L * (2 * N);
 
-  auto chunk_end = [&](int64_t k) { return (k * CK + CK < L) ? k * CK + CK : L; };
   struct Fetch {
     uint32_t dt[SW], z[SW], dy[SW];
-    float c;
+    float c[CPT];
   };
   auto fetch = [&](int64_t k, Fetch& f) {
-    const int64_t t0 = k * CK;
-    const int64_t v = chunk_end(k) - (t0 + j_own);
-    const int valid = (int)(v < 0 ? 0 : (v < kSpan ? v : kSpan));
-    load_span<IO, kSpan>(dt, dt_row + t0 + j_own, valid, vec, f.dt);
-    if (has_z) load_span<IO, kSpan>(z, row + t0 + j_own, valid, vec, f.z);
-    load_span<IO, kSpan>(dy, row + t0 + j_own, valid, vec, f.dy);
-    f.c = 0.0f;
-    if (tid < CK * N && t0 + tid / N < chunk_end(k)) f.c = bc_row[(t0 * N + tid) * 2 + 1];
+    const int64_t t0 = k * ST;
+    const int64_t v = t_end - (t0 + j_own);
+    const int valid = (int)(v < 0 ? 0 : (v < AS ? v : AS));
+    load_span<IO, AS>(dt, dt_row + t0 + j_own, valid, vec, f.dt);
+    if (has_z) load_span<IO, AS>(z, row + t0 + j_own, valid, vec, f.z);
+    load_span<IO, AS>(dy, row + t0 + j_own, valid, vec, f.dy);
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int idx = tid + q * THREADS;
+      f.c[q] = (idx < ST * N && t0 + idx / N < t_end) ? bc_row[(t0 * N + idx) * 2 + 1] : 0.0f;
+    }
   };
 
   float mu[NS];
@@ -603,12 +611,11 @@ __global__ __launch_bounds__(64 * G) void bwd_adjoint_agg_kernel(const BwdDims d
   for (int s = 0; s < NS; ++s) mu[s] = 0.0f;
   float dsum = 0.0f;
   Fetch f;
-  fetch(ke - 1, f);
-  for (int64_t k = ke - 1; k >= kb; --k) {
-    const int64_t t0 = k * CK;
-    const int nj = (int)(chunk_end(k) - t0);
+  fetch(se - 1, f);
+  for (int64_t k = se - 1; k >= sb; --k) {
+    const int64_t nj = t_end - k * ST;   // tokens of the stage inside the segment (ST or fewer)
 #pragma unroll
-    for (int i = 0; i < kSpan; ++i) {
+    for (int i = 0; i < AS; ++i) {
       const float dl = (j_own + i < nj) ? softplus_dt(span_elem<IO>(f.dt, i), bias2) : 0.0f;
       const float dyv = act ? span_elem<IO>(f.dy, i) : 0.0f;   // padding tokens load as zero
       float gate = 1.0f;
@@ -618,12 +625,16 @@ __global__ __launch_bounds__(64 * G) void bwd_adjoint_agg_kernel(const BwdDims d
       }
       s_dr[j_own + i][c] = make_float2(dl, dyv * gate);
     }
-    if (tid < CK * N) s_c[tid / N][tid % N] = f.c;
-    if (k > kb) fetch(k - 1, f);
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int idx = tid + q * THREADS;
+      if (idx < ST * N) s_c[idx / N][idx % N] = f.c[q];
+    }
+    if (k > sb) fetch(k - 1, f);
     __syncthreads();
 #pragma unroll
-    for (int j = CK - 1; j >= 0; --j) {
-      const float2 o = s_dr[j][c];   // zero Delta and dr past the sequence's end
+    for (int j = ST - 1; j >= 0; --j) {
+      const float2 o = s_dr[j][c];   // zero Delta and dr past the segment's end
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const float lam = fmaf(o.y, s_c[j][sg * NS + s], mu[s]);
