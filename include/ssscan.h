@@ -290,7 +290,9 @@ ss_status ss_scan_bwd_ex(int64_t batch, int64_t dim, int dstate, int64_t seqlen,
  *   ss_scan_bwd_segment_len: the segment length ss_scan_bwd and ss_scan_bwd_ex
  *     use for this shape on the current device: seqlen when they run the
  *     sequence whole (sequences shorter than 8192 tokens, or with at least two
- *     workgroups of 64/lanes channels per CU), 0 for invalid arguments.
+ *     workgroups per CU, a workgroup taking 32 channels of a batch row at
+ *     dstate >= 8 and 64 below; 0 when seqlen is 0), and 0 for invalid
+ *     arguments.
  *   ss_scan_bwd_seg: ss_scan_bwd_ex with an explicit segment_len: 0 for the
  *     automatic choice, else a positive multiple of 64 (SS_ERR_INVALID_ARG
  *     otherwise, or beyond 2^20 segments); a length of at least seqlen runs the
