@@ -184,13 +184,43 @@ def run_long_bwd(ss, torch, dev, calls=3):
 
     split_ms = timed(0)
     whole_ms = timed(L)
-    del t, dy, ws
+
+    # the training-step pair: the forward (chunked plan) storing checkpoints, then
+    # the split backward reading them instead of running its own aggregate pass
+    ck = torch.empty(ss.ckpt_numel(b, d, n, L), dtype=torch.float32, device=dev)
+    fws = torch.empty(max(ss.workspace_bytes(b, d, n, L, torch.bfloat16), 256), dtype=torch.uint8, device=dev)
+
+    def lib_ms(fn):
+        fn()
+        torch.cuda.synchronize()
+        ss.ss_timing_reset()
+        ss.ss_timing_enable(True)
+        for _ in range(calls):
+            fn()
+        torch.cuda.synchronize()
+        ss.ss_timing_enable(False)
+        ms, k = ss.ss_timing_read()
+        ss.ss_timing_reset()
+        return ms / k
+
+    fwd_ms = lib_ms(lambda: ss.scan_fwd(t["x"], t["dt"], t["B"], t["C"], A, z=t["z"], Dskip=dskip, dt_bias=bias,
+                                        workspace=fws))
+    fwd_ck_ms = lib_ms(lambda: ss.scan_fwd(t["x"], t["dt"], t["B"], t["C"], A, z=t["z"], Dskip=dskip, dt_bias=bias,
+                                           workspace=fws, ckpt=ck))
+    bwd_ck_ms = lib_ms(lambda: ss.scan_bwd(t["x"], t["dt"], t["B"], t["C"], A, dy, z=t["z"], Dskip=dskip,
+                                           dt_bias=bias, workspace=ws, ckpt=ck))
+    del t, dy, ws, ck, fws
     torch.cuda.empty_cache()
     return {"workload": cfg.name, "entry_point": "ss_scan_bwd (automatic split) vs ss_scan_bwd_seg (whole)",
             "segment_len": seg, "segments": (L + seg - 1) // seg, "split_ms": round(split_ms, 3),
             "whole_ms": round(whole_ms, 3), "value_split": round(cfg.tokch / (split_ms * 1e-3) / 1e9, 2),
             "value_whole": round(cfg.tokch / (whole_ms * 1e-3) / 1e9, 2), "unit": "Gtok·ch/s",
-            "speedup": round(whole_ms / split_ms, 2), "calls": calls}
+            "speedup": round(whole_ms / split_ms, 2), "calls": calls,
+            "training_step": {"fwd_ms": round(fwd_ms, 3), "fwd_storing_checkpoints_ms": round(fwd_ck_ms, 3),
+                              "bwd_from_checkpoints_ms": round(bwd_ck_ms, 3),
+                              "step_ms": round(fwd_ms + split_ms, 3),
+                              "step_with_checkpoints_ms": round(fwd_ck_ms + bwd_ck_ms, 3),
+                              "checkpoint_bytes": ss.ckpt_numel(b, d, n, L) * 4}}
 
 
 def cpu_single_thread(budget_s: float = 2.0):
