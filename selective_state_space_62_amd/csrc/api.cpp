@@ -569,7 +569,7 @@ ss_status bwd_plan_segments(int64_t batch, int64_t dim, int dstate, int64_t seql
 }
 
 struct BwdLayout {
-  size_t bc, ckpt, part, dA_p, dD_p, dbias_p, h_seg, agg_h, agg_s, lam_seg, adj_m, adj_s, total;
+  size_t bc, ckpt, part, dA_p, dD_p, dbias_p, h_seg, agg_h, lam_seg, adj_m, adj_s, total;
   int64_t cblocks, chunks;
 };
 
@@ -595,17 +595,15 @@ BwdLayout bwd_layout(int64_t batch, int64_t dim, int dstate, int64_t seqlen, con
   if (sg.n > 1) {
     const size_t st = (size_t)batch * dim * sg.n * dstate * sizeof(float);
     const size_t sc = (size_t)batch * dim * sg.n * sizeof(float);
-    w.h_seg = off;
+    w.h_seg = off;   // state entering each segment
     off += round256(st);
-    w.agg_h = off;
+    w.agg_h = off;   // each segment's end state from zero
     off += round256(st);
-    w.agg_s = off;
-    off += round256(sc);
-    w.lam_seg = off;
+    w.lam_seg = off;   // adjoint entering each segment
     off += round256(st);
-    w.adj_m = off;
+    w.adj_m = off;   // each segment's adjoint aggregate
     off += round256(st);
-    w.adj_s = off;
+    w.adj_s = off;   // each segment's sum of Delta (the exponent of both decays)
     off += round256(sc);
   }
   w.total = off;
@@ -748,6 +746,7 @@ ss_status scan_bwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, 
     bp.lam_seg = reinterpret_cast<const float*>(ws + wl.lam_seg);
     bp.adj_m = reinterpret_cast<float*>(ws + wl.adj_m);
     bp.adj_s = reinterpret_cast<float*>(ws + wl.adj_s);
+    bp.agg_h = reinterpret_cast<float*>(ws + wl.agg_h);
   }
 
   const bool timed = timing_on();
@@ -759,32 +758,20 @@ ss_status scan_bwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, 
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   }
   if (sgm.n > 1) {
+    // the segments' aggregates in one pass (their states only when no checkpoints
+    // give them), then the combines: the state entering every segment (from h0)
+    // and the adjoint entering it from the tokens after it (from dh_final)
+    e = ssscan::launch_bwd_segment_agg(dm, bp, /*states=*/!ckpt, s);
+    if (e != hipSuccess) return hip_fail(e, "segment aggregate launch");
     if (!ckpt) {
-      // the state entering every segment: the forward's aggregate pass over the
-      // segments and its combine
-      const Plan fp = auto_plan(batch, dim, dstate, seqlen, io);
-      ssscan::ScanDims fd = pd;
-      fd.chunk_len = sgm.len;   // a multiple of every forward tile length
-      fd.num_chunks = (int32_t)sgm.n;
-      fd.groups = fp.groups;
-      fd.lanes = fp.lanes;
-      fd.vec = (seqlen % ssscan::span_len(fp.lanes, fd.io)) == 0 ? 1 : 0;
-      fd.dt_row = dt_row ? 1 : 0;
-      ssscan::ScanPtrs sp{};
-      sp.x = x;
-      sp.dt = dt;
-      sp.bc = bcw;
-      sp.A = A;
-      sp.dt_bias = dt_bias;
-      sp.agg_h = reinterpret_cast<float*>(ws + wl.agg_h);
-      sp.agg_s = reinterpret_cast<float*>(ws + wl.agg_s);
-      e = ssscan::launch_scan(fd, sp, /*aggregate=*/true, zoh, s);
-      if (e != hipSuccess) return hip_fail(e, "scan (aggregate) launch");
-      e = ssscan::launch_combine(fd, A, sp.agg_h, sp.agg_s, h0, reinterpret_cast<float*>(ws + wl.h_seg), s);
+      ssscan::ScanDims cd{};
+      cd.batch = batch;
+      cd.dim = dim;
+      cd.dstate = dstate;
+      cd.num_chunks = (int32_t)sgm.n;
+      e = ssscan::launch_combine(cd, A, bp.agg_h, bp.adj_s, h0, reinterpret_cast<float*>(ws + wl.h_seg), s);
       if (e != hipSuccess) return hip_fail(e, "combine launch");
     }
-    e = ssscan::launch_bwd_adjoint_agg(dm, bp, s);
-    if (e != hipSuccess) return hip_fail(e, "adjoint aggregate launch");
     e = ssscan::launch_bwd_adjoint_combine(dm, A, dh_final, bp.adj_m, bp.adj_s, reinterpret_cast<float*>(ws + wl.lam_seg),
                                            s);
     if (e != hipSuccess) return hip_fail(e, "adjoint combine launch");

@@ -92,6 +92,7 @@ struct BwdPtrs {
   const float* lam_seg;   // the adjoint carried into each segment from the tokens after it
   float* adj_m;           // workspace: each segment's adjoint aggregate from a zero start
   float* adj_s;           // workspace: each segment's sum of Delta
+  float* agg_h;           // workspace: each segment's end state from a zero start (no ckpt)
 };
 
 // Backward plan: lanes per channel and chunk length (tokens) for a state size.
@@ -122,9 +123,10 @@ hipError_t launch_shard_combine(int64_t batch, int64_t dim, int dstate, int64_t 
                                 const float* dsum, const float* h_end, const float* h0, float* h_in, float* h_final,
                                 hipStream_t s);
 hipError_t launch_scan_bwd(const BwdDims& dm, const BwdPtrs& p, hipStream_t s);
-// split sequences: the adjoint aggregates of segments 1 .. nseg-1 (adj_m, adj_s),
-// then the adjoint carried into every segment (lam_seg) from dh_final
-hipError_t launch_bwd_adjoint_agg(const BwdDims& dm, const BwdPtrs& p, hipStream_t s);
+// split sequences: the segments' aggregates in one pass (adj_m for segments
+// 1 .. nseg-1, adj_s, and with states also agg_h for every segment), then the
+// adjoint carried into every segment (lam_seg) from dh_final
+hipError_t launch_bwd_segment_agg(const BwdDims& dm, const BwdPtrs& p, bool states, hipStream_t s);
 hipError_t launch_bwd_adjoint_combine(const BwdDims& dm, const float* A, const float* dh_final, const float* adj_m,
                                       const float* adj_s, float* lam_seg, hipStream_t s);
 // the main backward kernel alone, zero-order-hold form (scan_bwd_zoh.hip)

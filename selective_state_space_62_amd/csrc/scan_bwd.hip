@@ -126,10 +126,13 @@ hipError_t launch_scan_bwd(const BwdDims& dm, const BwdPtrs& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_adjoint_agg(const BwdDims& dm, const BwdPtrs& p, hipStream_t s) {
+hipError_t launch_bwd_segment_agg(const BwdDims& dm, const BwdPtrs& p, bool states, hipStream_t s) {
+  using namespace bwd_detail;
   if (dm.nseg < 2) return hipSuccess;
-  return dm.io == kIoBf16 ? bwd_detail::launch_adjoint_agg_n<BF16>(dm, p, s)
-                          : bwd_detail::launch_adjoint_agg_n<F32>(dm, p, s);
+  const bool bf = dm.io == kIoBf16;
+  if (!states) return bf ? launch_segment_agg_n<BF16, false, false>(dm, p, s) : launch_segment_agg_n<F32, false, false>(dm, p, s);
+  if (dm.zoh) return bf ? launch_segment_agg_n<BF16, true, true>(dm, p, s) : launch_segment_agg_n<F32, true, true>(dm, p, s);
+  return bf ? launch_segment_agg_n<BF16, false, true>(dm, p, s) : launch_segment_agg_n<F32, false, true>(dm, p, s);
 }
 
 hipError_t launch_bwd_adjoint_combine(const BwdDims& dm, const float* A, const float* dh_final, const float* adj_m,

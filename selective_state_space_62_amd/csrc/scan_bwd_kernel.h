@@ -524,20 +524,28 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
   }
 }
 
-// A split sequence's adjoint aggregates.  Going back through segment s (tokens
-// t0 .. t1-1) the carried adjoint obeys mu <- Abar_t (mu + dr_t C_t), so what
-// leaves the segment is exp(A sum Delta) mu_in + M_s, with
-//   M_s = sum_t (prod_{t0 <= t' <= t} Abar_t') dr_t C_t
-// the value that leaves when nothing enters.  dr = dy silu(z) needs no state,
-// so every segment's (M_s, sum Delta) is computed independently here, for the
-// segments after the first (the first one's is never used); a combine then
-// gives the adjoint entering every segment.  Same lanes as the main kernel
-// (G waves, K lanes per channel, NS state components per lane); work goes in
-// stages of 16 bytes of every operand row per lane (AS tokens, AS * G * K per
-// stage, which divides every segment length): the owner of each token stages
-// Delta and dr, and every lane runs its components back through the stage.
-template <int N, int G, int K, typename IO>
-__global__ __launch_bounds__(64 * G) void bwd_adjoint_agg_kernel(const BwdDims dm, const BwdPtrs p) {
+// A split sequence's aggregates, in one pass back through each segment (tokens
+// t0 .. t1-1):
+//  - the adjoint: going back through the segment the carried adjoint obeys
+//    mu <- Abar_t (mu + dr_t C_t), so what leaves the segment is
+//    exp(A sum Delta) mu_in + M_s, with M_s = sum_t (prod_{t0 <= t' <= t}
+//    Abar_t') dr_t C_t the value that leaves when nothing enters;
+//  - with FWD (no forward-saved checkpoints), the state: from a zero start the
+//    segment ends in H_s = sum_t (prod_{t < t' < t1} Abar_t') c_t B_t x_t, the
+//    forward's chunk aggregate, summed here from the last token with a running
+//    product of Abar (c_t = Delta_t, or Delta_t phi(Delta_t A) for ZOH);
+//  - the segment's sum of Delta, the exponent of both decay factors.
+// dr = dy silu(z) needs no state, so every segment is independent; combines
+// then give the state and the adjoint entering every segment.  Segments 1 ..
+// nseg-1 need M_s and 0 .. nseg-2 need H_s, so the pass covers all of them
+// with FWD and the segments after the first without.  Same lanes as the main
+// kernel (G waves, K lanes per channel, NS state components per lane); work
+// goes in stages of 16 bytes of every operand row per lane (AS tokens, AS * G
+// * K per stage, which divides every segment length): the owner of each token
+// stages Delta, dr (and Delta x), and every lane runs its components back
+// through the stage.
+template <int N, int G, int K, typename IO, bool ZOH, bool FWD>
+__global__ __launch_bounds__(64 * G) void bwd_segment_agg_kernel(const BwdDims dm, const BwdPtrs p) {
   using T = typename IO::T;
   constexpr int CPB = 64 / K;
   constexpr int SG = G * K;
@@ -546,10 +554,13 @@ __global__ __launch_bounds__(64 * G) void bwd_adjoint_agg_kernel(const BwdDims d
   constexpr int ST = AS * SG;                 // tokens per stage (at most 64)
   constexpr int SW = SpanT<IO, AS>::kWords;
   constexpr int THREADS = 64 * G;
-  constexpr int CPT = (ST * N + THREADS - 1) / THREADS;   // C values each thread stages
+  constexpr int CPT = (ST * N + THREADS - 1) / THREADS;   // (B, C) pairs (C alone without FWD) each thread stages
   static_assert(64 % ST == 0, "a stage divides every segment length");
-  __shared__ float2 s_dr[ST][CPB];   // (Delta, dr) per token and channel
-  __shared__ float s_c[ST][N];       // C_n of the stage's tokens
+  static_assert(FWD || !ZOH, "the discretisation only enters the state's aggregate");
+  using BCV = std::conditional_t<FWD, float2, float>;
+  __shared__ float2 s_dr[ST][CPB];               // (Delta, dr) per token and channel
+  __shared__ float s_dx[FWD ? ST : 1][CPB];      // Delta x per token and channel
+  __shared__ BCV s_bc[ST][N];                    // (B_n, C_n), or C_n, of the stage's tokens
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -558,12 +569,14 @@ __global__ __launch_bounds__(64 * G) void bwd_adjoint_agg_kernel(const BwdDims d
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int sg = w * K + hk;
 
-  // logical block -> (segment 1 .. nseg-1, batch row, channel block)
-  const int64_t nwg = dm.cblocks * dm.batch * (dm.nseg - 1);
+  // logical block -> (segment, batch row, channel block): every segment with
+  // FWD, else segments 1 .. nseg-1
+  const int64_t seg0 = FWD ? 0 : 1;
+  const int64_t nwg = dm.cblocks * dm.batch * (dm.nseg - seg0);
   const int64_t lb = bwd_logical_block(blockIdx.x, nwg);
   const int64_t cb = lb % dm.cblocks;
   const int64_t b = (lb / dm.cblocks) % dm.batch;
-  const int64_t seg = 1 + lb / (dm.cblocks * dm.batch);
+  const int64_t seg = seg0 + lb / (dm.cblocks * dm.batch);
   const int64_t d = cb * CPB + c;
   const bool act = d < dm.dim;
   const int64_t dc = act ? d : dm.dim - 1;
@@ -579,6 +592,7 @@ __global__ __launch_bounds__(64 * G) void bwd_adjoint_agg_kernel(const BwdDims d
   const int64_t se = (t_end + ST - 1) / ST;
   const int j_own = sg * AS;
 
+  const T* __restrict__ x = static_cast<const T*>(p.x);
   const T* __restrict__ dt = static_cast<const T*>(p.dt);
   const T* __restrict__ z = static_cast<const T*>(p.z);
   const T* __restrict__ dy = static_cast<const T*>(p.dy);
@@ -586,29 +600,36 @@ __global__ __launch_bounds__(64 * G) void bwd_adjoint_agg_kernel(const BwdDims d
 #pragma unroll
   for (int s = 0; s < NS; ++s) A2[s] = p.A[dc * N + sg * NS + s] * kLog2e;
   const float bias2 = p.dt_bias ? p.dt_bias[dc] * kLog2e : 0.0f;
-  const float* __restrict__ bc_row = p.bc + b * L * (2 * N);
+  const float* __restrict__ bc_row = p.bc + b * L * (2 * N);   // (token, n, {B, C})
 
   struct Fetch {
-    uint32_t dt[SW], z[SW], dy[SW];
-    float c[CPT];
+    uint32_t x[FWD ? SW : 1], dt[SW], z[SW], dy[SW];
+    BCV bc[CPT];
   };
   auto fetch = [&](int64_t k, Fetch& f) {
     const int64_t t0 = k * ST;
     const int64_t v = t_end - (t0 + j_own);
     const int valid = (int)(v < 0 ? 0 : (v < AS ? v : AS));
+    if constexpr (FWD) load_span<IO, AS>(x, row + t0 + j_own, valid, vec, f.x);
     load_span<IO, AS>(dt, dt_row + t0 + j_own, valid, vec, f.dt);
     if (has_z) load_span<IO, AS>(z, row + t0 + j_own, valid, vec, f.z);
     load_span<IO, AS>(dy, row + t0 + j_own, valid, vec, f.dy);
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
       const int idx = tid + q * THREADS;
-      f.c[q] = (idx < ST * N && t0 + idx / N < t_end) ? bc_row[(t0 * N + idx) * 2 + 1] : 0.0f;
+      const bool in = idx < ST * N && t0 + idx / N < t_end;
+      if constexpr (FWD) f.bc[q] = in ? reinterpret_cast<const float2*>(bc_row)[t0 * N + idx] : make_float2(0.0f, 0.0f);
+      else f.bc[q] = in ? bc_row[(t0 * N + idx) * 2 + 1] : 0.0f;
     }
   };
 
-  float mu[NS];
+  float mu[NS], hf[NS], qd[NS];   // the adjoint; the state from zero and its pending decay
 #pragma unroll
-  for (int s = 0; s < NS; ++s) mu[s] = 0.0f;
+  for (int s = 0; s < NS; ++s) {
+    mu[s] = 0.0f;
+    hf[s] = 0.0f;
+    qd[s] = 1.0f;
+  }
   float dsum = 0.0f;
   Fetch f;
   fetch(se - 1, f);
@@ -624,21 +645,38 @@ __global__ __launch_bounds__(64 * G) void bwd_adjoint_agg_kernel(const BwdDims d
         gate = zv * sigmoid2(zv * kLog2e);
       }
       s_dr[j_own + i][c] = make_float2(dl, dyv * gate);
+      if constexpr (FWD) s_dx[j_own + i][c] = dl * span_elem<IO>(f.x, i);
     }
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
       const int idx = tid + q * THREADS;
-      if (idx < ST * N) s_c[idx / N][idx % N] = f.c[q];
+      if (idx < ST * N) s_bc[idx / N][idx % N] = f.bc[q];
     }
     if (k > sb) fetch(k - 1, f);
     __syncthreads();
 #pragma unroll
     for (int j = ST - 1; j >= 0; --j) {
-      const float2 o = s_dr[j][c];   // zero Delta and dr past the segment's end
+      const float2 o = s_dr[j][c];   // zero Delta, dr and Delta x past the segment's end
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const float lam = fmaf(o.y, s_c[j][sg * NS + s], mu[s]);
-        mu[s] = __builtin_amdgcn_exp2f(o.x * A2[s]) * lam;
+        const BCV bcv = s_bc[j][sg * NS + s];
+        const float u2 = o.x * A2[s];
+        const float E = __builtin_amdgcn_exp2f(u2);
+        float Cv, Bv = 0.0f;
+        if constexpr (FWD) {
+          Bv = bcv.x;
+          Cv = bcv.y;
+        } else {
+          Cv = bcv;
+        }
+        const float lam = fmaf(o.y, Cv, mu[s]);
+        mu[s] = E * lam;
+        if constexpr (FWD) {
+          float in = s_dx[j][c] * Bv;
+          if constexpr (ZOH) in *= zoh_phi(u2, E);
+          hf[s] = fmaf(qd[s], in, hf[s]);
+          qd[s] *= E;
+        }
       }
       dsum += o.x;
     }
@@ -646,26 +684,31 @@ __global__ __launch_bounds__(64 * G) void bwd_adjoint_agg_kernel(const BwdDims d
   }
   if (act) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) p.adj_m[(ch * dm.nseg + seg) * N + sg * NS + s] = mu[s];
+    for (int s = 0; s < NS; ++s) {
+      const int64_t k = (ch * dm.nseg + seg) * N + sg * NS + s;
+      if (seg > 0) p.adj_m[k] = mu[s];
+      if constexpr (FWD) p.agg_h[k] = hf[s];
+    }
     if (sg == 0) p.adj_s[ch * dm.nseg + seg] = dsum;
   }
 }
 
-template <int N, int G, int K, typename IO>
-hipError_t launch_adjoint_agg_t(const BwdDims& dm, const BwdPtrs& p, hipStream_t s) {
-  const int64_t nwg = dm.cblocks * dm.batch * (dm.nseg - 1);
-  hipLaunchKernelGGL((bwd_adjoint_agg_kernel<N, G, K, IO>), dim3((unsigned)nwg), dim3(64 * G), 0, s, dm, p);
+template <int N, int G, int K, typename IO, bool ZOH, bool FWD>
+hipError_t launch_segment_agg_t(const BwdDims& dm, const BwdPtrs& p, hipStream_t s) {
+  const int64_t nwg = dm.cblocks * dm.batch * (dm.nseg - (FWD ? 0 : 1));
+  hipLaunchKernelGGL((bwd_segment_agg_kernel<N, G, K, IO, ZOH, FWD>), dim3((unsigned)nwg), dim3(64 * G), 0, s, dm, p);
   return hipGetLastError();
 }
 
-template <typename IO>
-hipError_t launch_adjoint_agg_n(const BwdDims& dm, const BwdPtrs& p, hipStream_t s) {
+// FWD: also the segments' state aggregates (no forward-saved checkpoints)
+template <typename IO, bool ZOH, bool FWD>
+hipError_t launch_segment_agg_n(const BwdDims& dm, const BwdPtrs& p, hipStream_t s) {
   switch (dm.dstate) {
-    case 1: return launch_adjoint_agg_t<1, 1, 1, IO>(dm, p, s);
-    case 2: return launch_adjoint_agg_t<2, 2, 1, IO>(dm, p, s);
-    case 4: return launch_adjoint_agg_t<4, 4, 1, IO>(dm, p, s);
-    case 8: return launch_adjoint_agg_t<8, 4, 2, IO>(dm, p, s);
-    case 16: return launch_adjoint_agg_t<16, 4, 2, IO>(dm, p, s);
+    case 1: return launch_segment_agg_t<1, 1, 1, IO, ZOH, FWD>(dm, p, s);
+    case 2: return launch_segment_agg_t<2, 2, 1, IO, ZOH, FWD>(dm, p, s);
+    case 4: return launch_segment_agg_t<4, 4, 1, IO, ZOH, FWD>(dm, p, s);
+    case 8: return launch_segment_agg_t<8, 4, 2, IO, ZOH, FWD>(dm, p, s);
+    case 16: return launch_segment_agg_t<16, 4, 2, IO, ZOH, FWD>(dm, p, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -318,12 +318,12 @@ def test_bwd_segment_plan_and_workspace():
     assert b.ss_scan_bwd_seg_workspace_bytes(1, 64, 16, 300, b.SS_F32, 100) == 0
     assert b.ss_scan_bwd_seg_workspace_bytes(1, 64, 16, 300, b.SS_F32, -64) == 0
     # five segments of 64 tokens: the per-(segment, row) sums grow fivefold, and the
-    # segments' entering states, their forward aggregates (end states and Delta sums),
-    # the carried adjoints and the adjoint aggregates (values and Delta sums) are added
+    # segments' entering states, their end states from zero, the carried adjoints,
+    # the adjoint aggregates and the Delta sums (shared by both) are added
     n5 = b.ss_scan_bwd_seg_workspace_bytes(1, 64, 16, 300, b.SS_F32, 64)
     n1 = b.ss_scan_bwd_seg_workspace_bytes(1, 64, 16, 300, b.SS_F32, 1 << 20)
     st, sc = 64 * 5 * 16 * 4, 64 * 5 * 4
-    assert n5 - n1 == (r(5 * 64 * 16 * 4) - r(64 * 16 * 4)) + 2 * (r(5 * 64 * 4) - r(64 * 4)) + 4 * r(st) + 2 * r(sc)
+    assert n5 - n1 == (r(5 * 64 * 16 * 4) - r(64 * 16 * 4)) + 2 * (r(5 * 64 * 4) - r(64 * 4)) + 4 * r(st) + r(sc)
     # the automatic choice: the 2.8B shape runs whole; one channel block over 8192 tokens is split
     assert b.ss_scan_bwd_segment_len(8, 5120, 16, 2048, b.SS_BF16) == 2048
     assert b.ss_scan_bwd_segment_len(1, 32, 16, 8192, b.SS_F32) == 2048
