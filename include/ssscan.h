@@ -278,12 +278,13 @@ ss_status ss_scan_bwd_ex(int64_t batch, int64_t dim, int dstate, int64_t seqlen,
  * It is then cut into segments run by separate workgroups, the backward
  * counterpart of the forward's chunks (the pages evaluate the recurrence with a
  * parallel scan; reader's notes on the Mamba paper, kurisu.si, "What they did").
- * Each segment starts from the state entering it (the forward's chunk
- * aggregates and their combine, or the checkpoints in ckpt) and from the
- * adjoint carried in from the tokens after it.  That adjoint follows from the
+ * Each segment starts from the state entering it (every segment's end state
+ * from a zero start, chained by the forward's combine; or the checkpoints in
+ * ckpt) and from the adjoint carried in from the tokens after it.  That adjoint follows from the
  * same linearity run backwards: a segment passes on exp(A sum Delta) times what
  * enters it plus its own aggregate sum_t (prod of Abar up to t) dr_t C_t, with
  * dr = dy silu(z), which needs no state; a combine from dh_final chains them.
+ * One reverse pass over each segment gives both aggregates.
  * The gradients equal the unsplit ones up to rounding (across a segment the
  * decay is applied as one exponential rather than a product of per-token
  * factors).
