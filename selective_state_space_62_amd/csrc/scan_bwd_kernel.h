@@ -393,7 +393,10 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
     }
     __syncthreads();
 
-    // the adjoint state back through the chunk
+    // the adjoint state back through the chunk, at a raised wave priority
+    // (back to the default for the owners' phase): a SIMD's issue then favours
+    // the waves in this, the longest phase (about 4% faster at the 2.8B shape)
+    __builtin_amdgcn_s_setprio(2);
     float uo[CK];   // this lane's dB/dC sum per chunk token (kept by the writing lanes)
 #pragma unroll
     for (int j = 0; j < CK; ++j) uo[j] = 0.0f;
@@ -455,6 +458,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
     }
     __syncthreads();
     // owners: dx = Delta sum lam B + dr Dskip, ddt = (dDelta) sigmoid(v)
+    __builtin_amdgcn_s_setprio(0);
     {
       float dxv[kSpan], ddtv[kSpan];
 #pragma unroll
