@@ -31,8 +31,19 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restr
   if (t >= L) return;   // padding tokens of the last chunk
   const int64_t blk = nck * npart * ck;   // one block's partials
   const float* src = part + b * cblocks * blk + (k * npart + o) * ck + j;
+  // eight loads in flight per thread (a single chain of dependent load-add
+  // pairs left each thread waiting on one load at a time); the sum keeps the
+  // block order
   float acc = 0.0f;
-  for (int64_t q = 0; q < cblocks; ++q) acc += src[q * blk];
+  int64_t q = 0;
+  for (; q + 8 <= cblocks; q += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(src + (q + u) * blk);   // read once
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u];
+  }
+  for (; q < cblocks; ++q) acc += src[q * blk];
   if (o == 2 * N) store_one<IO>(ddt_row, b * L + t, acc);
   else store_one<IO>(o < N ? dB : dC, (b * N + o % N) * L + t, acc);
 }
