@@ -130,9 +130,13 @@ def run_l_sweep(ss, torch, dev, cfg, lengths=(512, 1024, 2048, 4096, 8192, 16384
 
         def call():
             ss.scan_fwd(t["x"], t["dt"], t["B"], t["C"], A, z=t["z"], Dskip=dskip, dt_bias=bias, workspace=ws)
-        for _ in range(calls):
-            call()
-        torch.cuda.synchronize()
+        # warm up for at least 100 ms at every length (as the main measurement's
+        # warm-up steps do), so that short sequences are not timed while the clock ramps
+        t_warm = time.perf_counter() + 0.1
+        while time.perf_counter() < t_warm:
+            for _ in range(10):
+                call()
+            torch.cuda.synchronize()
         ss.ss_timing_reset()
         ss.ss_timing_enable(True)
         for _ in range(calls):
