@@ -30,6 +30,7 @@ HBM_PEAK_GBS = 8000.0
 CUS, SIMDS_PER_CU, LANES_PER_SIMD_CLK, CLOCK_GHZ = 256, 4, 16, 2.4
 VALU_PEAK_TOPS = CUS * SIMDS_PER_CU * LANES_PER_SIMD_CLK * CLOCK_GHZ / 1000.0   # 39.32 T lane-slots/s
 TRANS_SLOTS = 2   # transcendentals issue at half rate on gfx950 and do not co-issue with FMAs
+TRANS_PEAK_TPS = VALU_PEAK_TOPS / TRANS_SLOTS   # 19.66 T transcendentals/s
 
 _CSRC = "selective_state_space_62_amd/csrc/"
 # sources of each timed kernel: committed counters apply only while these are unchanged
@@ -101,18 +102,86 @@ def algorithmic_slots_bwd_per_tokch(N: int, sweep: bool = True) -> float:
 
 
 def ceilings(cfg, kernel_gtokch: float) -> dict:
-    """The scan's three throughput ceilings in Gtok·ch/s and the kernel's fraction
-    of each: HBM (algorithmic bytes at 8 TB/s); transcendentals alone (N + 4 per
-    token-channel at the half-rate issue of gfx950, as if the other VALU work
-    co-issued); and the VALU issue slots of all the algorithmic work (the bound
-    that applies, since transcendentals and FMAs share the issue port)."""
+    """The scan's throughput ceilings in Gtok·ch/s and the kernel's fraction of
+    each: HBM (algorithmic bytes at 8 TB/s); transcendentals alone (N + 4 per
+    token-channel at the half-rate issue of gfx950, 19.66 T/s); and the VALU
+    issue slots of all the algorithmic work (transcendentals and FMAs share the
+    issue port, so this lower ceiling is what any schedule of the algorithmic
+    work can reach).  The graded figure is the fraction of min(HBM,
+    transcendentals)."""
     hbm = HBM_PEAK_GBS / algorithmic_bytes_per_tokch(cfg)
-    exp_only = VALU_PEAK_TOPS * 1e3 / TRANS_SLOTS / (cfg.dstate + 4)
+    exp_only = TRANS_PEAK_TPS * 1e3 / (cfg.dstate + 4)
     slots = VALU_PEAK_TOPS * 1e3 / algorithmic_slots_per_tokch(cfg.dstate)
     return {"unit": "Gtok·ch/s", "hbm": round(hbm, 1), "transcendentals_only": round(exp_only, 1),
             "valu_issue_slots": round(slots, 1), "kernel": round(kernel_gtokch, 1),
             "frac_of_min_hbm_transcendentals": round(kernel_gtokch / min(hbm, exp_only), 4),
-            "frac_of_valu_issue_slots": round(kernel_gtokch / slots, 4)}
+            "frac_of_valu_issue_slots": round(kernel_gtokch / slots, 4),
+            "valu_issue_slots_over_min_hbm_transcendentals": round(slots / min(hbm, exp_only), 4)}
+
+
+def graded_roofline(cfg, kern_ms: float, traffic, kernel: str) -> dict:
+    """The scan kernel against min(HBM, transcendentals): whichever ceiling is
+    lower gives the bound, the peak and the unit.  achieved = algorithmic bytes
+    (HBM) or algorithmic transcendentals, N + 4 per token-channel (ALU), per
+    launch over the kernel's average launch time."""
+    hbm = HBM_PEAK_GBS / algorithmic_bytes_per_tokch(cfg)
+    exp_only = TRANS_PEAK_TPS * 1e3 / (cfg.dstate + 4)
+    sec = kern_ms * 1e-3
+    if hbm <= exp_only:
+        ach = algorithmic_bytes_per_tokch(cfg) * cfg.tokch / sec / 1e9
+        r = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(ach / HBM_PEAK_GBS, 4)}
+    else:
+        ach = (cfg.dstate + 4) * cfg.tokch / sec / 1e12
+        r = {"bound": "alu", "achieved": round(ach, 3), "peak": round(TRANS_PEAK_TPS, 3),
+             "unit": "T transcendental/s", "frac": round(ach / TRANS_PEAK_TPS, 4),
+             "transcendentals_per_tokch": cfg.dstate + 4}
+    r.update({"traffic": traffic, "kernel": kernel, "kernel_ms": round(kern_ms, 5)})
+    return r
+
+
+PROBE_MODES = ["exp2", "fma (literal operand)", "exp2 + fma, same wave", "exp2 / fma, separate waves",
+               "fma, one chain", "fma (three VGPR operands)", "mul", "DPP add", "exp2 + 4 fma",
+               "scan state step (2 + 5 per component)", "exp2 + 4 fma in bursts", "rcp", "log2 + add",
+               "mul+exp2 / 3 fma, separate waves", "mul+exp2 / 3 fma, same wave",
+               "8 exp2 then 128 fma", "exp2 then 16 fma, 8 times",
+               "one exp2, then fma only"]
+
+
+def run_valu_rates(reps: int = 5, ops_per_lane: float = 131072.0) -> dict:
+    """The VALU issue-rate probe (libssprobe.so) at 8 waves per SIMD for every mode,
+    and at 1, 2 and 4 waves per SIMD for fma, the single fma chain and the scan
+    step; rates in T lane-operations per second over all CUs."""
+    import ctypes
+    lib = ctypes.CDLL(str(ROOT / "selective_state_space_62_amd" / "libssprobe.so"))
+    lib.ss_probe_valu_mode.argtypes = [ctypes.c_int] * 4 + [ctypes.POINTER(ctypes.c_double)] * 2
+    ms, ops = ctypes.c_double(), ctypes.c_double()
+
+    def run(mode, wps):
+        wg = CUS * wps
+        rc = lib.ss_probe_valu_mode(mode, wg, 1, 1, ctypes.byref(ms), ctypes.byref(ops))
+        if rc != 0:
+            raise RuntimeError("ss_probe_valu_mode failed with HIP error %d" % rc)
+        iters = max(1, int(round(ops_per_lane / ops.value)))
+        rc = lib.ss_probe_valu_mode(mode, wg, iters, reps, ctypes.byref(ms), ctypes.byref(ops))
+        if rc != 0:
+            raise RuntimeError("ss_probe_valu_mode failed with HIP error %d" % rc)
+        rate = wg * 256 * ops.value / (ms.value * 1e-3) / 1e12
+        return {"mode": PROBE_MODES[mode], "waves_per_simd": wps, "ms": round(ms.value, 4),
+                "ops_per_lane": ops.value, "rate": round(rate, 3),
+                "cycles_per_wave_op": round(1024 * CLOCK_GHZ * 1e9 / (rate * 1e12 / 64), 3)}
+    rows = [run(m, 8) for m in range(len(PROBE_MODES))]
+    rows += [run(m, w) for m in (1, 4, 9, 10, 13, 14, 15, 16, 17) for w in (1, 2, 4)]
+    by = {(r["mode"], r["waves_per_simd"]): r for r in rows}
+    exp_r, fma_r = by[(PROBE_MODES[0], 8)]["rate"], by[(PROBE_MODES[1], 8)]["rate"]
+    mixed = by[(PROBE_MODES[2], 8)]["ms"]
+    return {"unit": "T lane-op/s", "exp": exp_r, "fma": fma_r,
+            "exp_over_half_rate_peak": round(exp_r / TRANS_PEAK_TPS, 4),
+            "fma_over_16_lanes_per_clock": round(fma_r / VALU_PEAK_TOPS, 4),
+            "mixed_time_over_sum_of_parts": round(mixed / (by[(PROBE_MODES[0], 8)]["ms"]
+                                                           + by[(PROBE_MODES[1], 8)]["ms"]), 4),
+            "rows": rows,
+            "note": "cycles_per_wave_op: SIMD cycles per 64-lane operation at %.1f GHz" % CLOCK_GHZ}
 
 
 def run_l_sweep(ss, torch, dev, cfg, lengths=(512, 1024, 2048, 4096, 8192, 16384), calls=20):
@@ -304,6 +373,32 @@ def measured_traffic(cfg, kind: str = "scan"):
     return d.get("hbm_bytes_per_launch")
 
 
+def run_cold(ss, torch, dev, cfg, step, calls=20, flush_bytes=512 << 20):
+    """Each call preceded by an untimed 512 MB write, which evicts the 256 MB
+    Infinity Cache (MALL), so that the call's inputs come from HBM: the scan
+    kernel's time per call from the library's events, median and minimum."""
+    flush = torch.empty(flush_bytes, dtype=torch.uint8, device=dev)
+    times = []
+    for i in range(calls + 2):
+        flush.fill_(i & 0xFF)
+        torch.cuda.synchronize()
+        ss.ss_timing_reset()
+        ss.ss_timing_enable(True)
+        step()
+        torch.cuda.synchronize()
+        ss.ss_timing_enable(False)
+        ms, n = ss.ss_timing_read()
+        ss.ss_timing_reset()
+        if i >= 2:
+            times.append(ms / n)
+    del flush
+    times.sort()
+    med = times[len(times) // 2]
+    return {"kernel_ms_median": round(med, 5), "kernel_ms_min": round(times[0], 5), "calls": calls,
+            "flush_bytes": flush_bytes, "value_median": round(cfg.tokch / (med * 1e-3) / 1e9, 2),
+            "unit": "Gtok·ch/s"}
+
+
 def run_decode(ss, torch, dev, steps, warmup):
     """Decode step timing (secondary).  "cold": back-to-back steps that rotate over
     6 separate states (503 MB, as the layers of a model would; more than the 256 MB
@@ -487,6 +582,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--settle-ms", type=float, default=1000.0,
+                    help="untimed scan calls for at least this long before the counted warm-up steps, "
+                         "so that the timed steps run at the steady clock")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cache-flushed per-call timing")
+    ap.add_argument("--no-rates", action="store_true", help="skip the VALU issue-rate probe")
+    ap.add_argument("--rates-only", action="store_true", help="only run the VALU issue-rate probe")
     ap.add_argument("--workload", default="2.8b-layer-bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
@@ -514,6 +615,10 @@ def main():
     from workloads import device as wdev
 
     dev = torch.device("cuda:0")
+    if args.rates_only:
+        torch.cuda.init()
+        print(json.dumps({"valu_rates": run_valu_rates()}))
+        return
     if args.copy_calib:
         src = torch.ones(args.copy_calib // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -538,6 +643,16 @@ def main():
         ss.scan_fwd(t["x"], t["dt"], t["B"], t["C"], A, z=t["z"], Dskip=dskip, dt_bias=bias, workspace=ws, y=y,
                     h_final=hf)
 
+    # settle: untimed calls until the clock has ramped (the first launches of a
+    # process run up to 30% slower), then the counted warm-up steps
+    settle_calls = 0
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        settle_calls += 10
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -562,6 +677,7 @@ def main():
     achieved_slots = spt * tokch / (kern_ms * 1e-3) / 1e12
     achieved_gbs = bpt * tokch / (kern_ms * 1e-3) / 1e9
     traffic = measured_traffic(cfg)
+    kname = "scan_kernel<%d,%d,%d,%s,euler>" % (cfg.dstate, plan[0], plan[1], cfg.io)
 
     out = {
         "metric": METRIC,
@@ -570,6 +686,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": round(settle_ms, 1),
+        "settle_calls": settle_calls,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -580,14 +698,18 @@ def main():
                    "seq_len": cfg.seqlen, "io": cfg.io, "state": "f32", "plan": {"state_groups": plan[0],
                    "lanes_per_channel": plan[1], "chunk_len": plan[2]}},
         "hbm_gbs": round(bpt * tokch / (ms_step * 1e-3) / 1e9, 1),
-        "roofline": {"bound": "alu", "achieved": round(achieved_slots, 3), "peak": round(VALU_PEAK_TOPS, 3),
-                     "unit": "T VALU-slot/s", "frac": round(achieved_slots / VALU_PEAK_TOPS, 4),
-                     "traffic": traffic, "kernel": "scan_kernel<%d,%d,%d,%s,euler>" % (cfg.dstate, plan[0], plan[1], cfg.io), "kernel_ms": round(kern_ms, 5),
-                     "slots_per_tokch": spt},
+        "roofline": graded_roofline(cfg, kern_ms, traffic, kname),
+        "roofline_valu_issue": {"bound": "alu", "achieved": round(achieved_slots, 3),
+                                "peak": round(VALU_PEAK_TOPS, 3), "unit": "T VALU-slot/s",
+                                "frac": round(achieved_slots / VALU_PEAK_TOPS, 4), "slots_per_tokch": spt},
         "roofline_hbm": {"achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "bytes_per_tokch": round(bpt, 4)},
         "ceilings": ceilings(cfg, tokch / (kern_ms * 1e-3) / 1e9),
     }
+    if not args.no_cold:
+        out["cold_cache"] = run_cold(ss, torch, dev, cfg, step)
+    if not args.no_rates:
+        out["valu_rates"] = run_valu_rates()
     if not args.no_dt_row:
         # dt shared by a row's channels (SS_FLAG_DT_PER_ROW): the same workload with
         # one dt row per batch row (secondary)

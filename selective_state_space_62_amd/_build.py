@@ -13,6 +13,10 @@ CSRC = PKG / "csrc"
 INCLUDE = ROOT / "include"
 BUILD = PKG / "_build"
 LIB = PKG / "libssscan.so"
+# the VALU issue-rate probe behind the roofline's constants (bench.py --rates);
+# a library of its own, outside the scan's ABI
+PROBE_SOURCES = ["valu_rates_probe.hip"]
+PROBE_LIB = PKG / "libssprobe.so"
 
 SOURCES = ["api.cpp", "scan_fwd.hip", "scan_bf16_euler.hip", "scan_bf16_zoh.hip", "scan_f32_euler.hip",
            "scan_f32_zoh.hip", "scan_bwd.hip", "scan_bwd_zoh.hip", "state_update.hip"]
@@ -49,19 +53,26 @@ def _compile(src: str) -> Path:
     return obj
 
 
-def build(verbose: bool = False) -> Path:
-    """Compile every source for gfx950 and link libssscan.so (always rebuilds)."""
-    BUILD.mkdir(exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB.with_suffix(".so.tmp%d" % os.getpid())
+def _link(objs, lib: Path) -> None:
+    tmp = lib.with_suffix(".so.tmp%d" % os.getpid())
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", str(tmp), *map(str, objs)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed: %s\n%s\n%s" % (" ".join(cmd), r.stdout, r.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> Path:
+    """Compile every source for gfx950 and link libssscan.so and the rate probe
+    libssprobe.so (always rebuilds)."""
+    BUILD.mkdir(exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, PROBE_LIB)
     return LIB
 
 

@@ -2,10 +2,10 @@
 // template and its launch dispatch, instantiated by scan_bwd.hip (first-order
 // input term) and scan_bwd_zoh.hip (zero-order hold).
 //
-// Training runs the scan forward and then backward; the pages' fused kernel
-// keeps the expanded state on-chip and recomputes it in the backward pass
-// instead of storing it (reader's notes, kurisu.si, "What they did", Selective
-// SSM item).  The gradients are those of the forward definition
+// Training runs the scan forward and then backward.  In the pages' design the
+// expanded state is never saved for the gradient: the backward derives it again
+// from the inputs (reader's notes, kurisu.si, "What they did", Selective SSM
+// item).  The gradients are those of the forward definition
 //   Delta_t = softplus(dt_t + dt_bias),  Abar = exp(Delta_t A_n),
 //   h_t[n] = Abar h_(t-1)[n] + Delta_t B_t[n] x_t,
 //   y_t = r_t silu(z_t),  r_t = C_t . h_t + Dskip x_t,

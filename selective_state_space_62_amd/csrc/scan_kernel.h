@@ -296,8 +296,11 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
             }
           }
         }
-        const int64_t te = ts + nj;   // the state after the tile's last token
-        if (te % CKL == 0 && te < L) {
+        // the state after the tile's last token; at a chunk's end (te == t1 < L)
+        // the next chunk stores that slot from its entering state, so each slot
+        // has exactly one writer and the checkpoints are reproducible
+        const int64_t te = ts + nj;
+        if (te % CKL == 0 && te < t1) {
 #pragma unroll
           for (int s = 0; s < NS; ++s) ck_row[(te / CKL) * dm.dim * N + s] = h[s];
         }

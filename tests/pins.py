@@ -78,9 +78,10 @@ def pin_theorem1(o):
         _close(hf[..., 0], h, what="theorem 1 final state")
 
 
-# --- P2: the small/large Delta limits (same notes, right after Theorem 1): a small
-# Delta keeps the state and ignores the input; a large Delta resets the state to the
-# current input.
+# --- P2: the two limits of the step size (same notes, the remark after Theorem 1).
+# As Delta goes to 0 the decay exp(Delta A) tends to 1 and the input weight to 0, so
+# the state stays where it was and the token is not taken in; as Delta grows the
+# decay vanishes and the state becomes the token's own input term, forgetting the past.
 def pin_delta_limits(o):
     rng = np.random.default_rng(102)
     p = _rand_problem(rng, L=16)

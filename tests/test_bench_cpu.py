@@ -63,3 +63,31 @@ def test_ceilings_at_the_2p8b_shape():
     assert abs(c["valu_issue_slots"] - 351.1) < 0.1
     assert abs(c["frac_of_valu_issue_slots"] - 245.0 / 351.08) < 1e-3
     assert abs(c["frac_of_min_hbm_transcendentals"] - 245.0 / 983.0) < 1e-3
+
+
+def test_graded_roofline_at_the_2p8b_shape():
+    """The line's roofline is the fraction of min(HBM, transcendentals): at the
+    2.8B shape the transcendental ceiling is the lower one (983 < 994), so the
+    bound is ALU, achieved is 20 transcendentals per token-channel over the
+    kernel time, and the peak is the half-rate issue, 19.66 T/s."""
+    sys.path.insert(0, str(ROOT))
+    import bench
+    from workloads import B28, DECODE
+    kern_ms = 0.32
+    r = bench.graded_roofline(B28, kern_ms, None, "scan")
+    assert r["bound"] == "alu" and r["unit"] == "T transcendental/s"
+    assert abs(r["peak"] - 19.661) < 1e-3
+    ach = 20 * B28.tokch / (kern_ms * 1e-3) / 1e12
+    assert abs(r["achieved"] - ach) < 1e-3 and abs(r["frac"] - ach / r["peak"]) < 1e-3
+    gtokch = B28.tokch / (kern_ms * 1e-3) / 1e9
+    assert abs(r["frac"] - bench.ceilings(B28, gtokch)["frac_of_min_hbm_transcendentals"]) < 1e-3
+
+
+def test_bench_cli_has_settle_and_cold_options():
+    """The counted warm-up steps run after a time-based settle phase, and the
+    cache-flushed timing and the rate probe can be switched off."""
+    r = subprocess.run([sys.executable, str(ROOT / "bench.py"), "--help"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0
+    for opt in ("--settle-ms", "--no-cold", "--no-rates"):
+        assert opt in r.stdout, opt

@@ -233,3 +233,26 @@ def test_forward_checkpoints_feed_backward(ss, dev, case, io, plan):
         log("ckpt %s %s: forward checkpoints give identical gradients" % (case, io))
     else:
         _compare(g1, _run_oracle(oracle.default(), f64, par), io, "ckpt chunked %s" % (case,))
+
+
+def test_chunked_forward_checkpoints_are_reproducible(ss, dev):
+    """Under a chunked plan every checkpoint slot has one writer: the slot at a
+    chunk boundary comes from the next chunk's entering state only.  Repeated
+    forward calls fill the checkpoint buffer bit for bit alike."""
+    import torch
+    batch, D, N, L, io = 1, 64, 16, 20000, "bf16"
+    rng = np.random.default_rng(77)
+    raw, par, f64 = _problem(rng, batch, D, N, L, io, True)
+    t = {k: to_dev(v, io, dev) for k, v in raw.items()}
+    p = {k: (torch.from_numpy(v).to(dev) if v is not None else None) for k, v in par.items()}
+    kw = dict(z=t["z"], Dskip=p["Dskip"], dt_bias=p["dt_bias"], h0=p["h0"])
+    first = None
+    for rep in range(4):
+        ck = torch.full((ss.ckpt_numel(batch, D, N, L),), float("nan"), device=dev)
+        ss.scan_fwd(t["x"], t["dt"], t["B"], t["C"], p["A"], plan=(4, 2, 4096), ckpt=ck, **kw)
+        torch.cuda.synchronize()
+        assert not torch.isnan(ck).any()
+        if first is None:
+            first = ck
+        else:
+            assert torch.equal(first.view(torch.int32), ck.view(torch.int32)), rep
