@@ -312,6 +312,30 @@ ss_status ss_scan_bwd_seg(int64_t batch, int64_t dim, int dstate, int64_t seqlen
                           float* dA, float* dDskip, float* ddt_bias, float* dh0,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* Size of the static device scratch array behind ss_scan_fwd_noalloc (32 MiB per GPU). */
+#define SS_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* ss_scan_fwd_noalloc — for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * operation, arguments, layouts and errors are those of ss_scan_fwd_ex without
+ * the workspace; nothing is allocated.  The scratch space (the B/C re-layout, and
+ * on chunked plans the chunk aggregates and entering states) is a static device
+ * array of SS_NOALLOC_SCRATCH_BYTES that every GPU the library runs on holds until
+ * the process ends; its device address is looked up on the first call on each
+ * device.  A call whose ss_scan_fwd_workspace_bytes() exceeds that size (at
+ * dstate 16, more than 262,144 batch x sequence tokens unchunked) returns
+ * SS_ERR_WORKSPACE before any device work.  Every call on one GPU shares that
+ * GPU's array: calls that overlap in time on one GPU (other streams, other host
+ * threads) race, and the caller must order them.  The array keeps the last
+ * call's contents; a call reads no scratch byte it has not written itself. */
+size_t ss_scan_fwd_noalloc_max_bytes(void);
+ss_status ss_scan_fwd_noalloc(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype io, uint32_t flags,
+                              const void* x, const void* dt, const void* z,
+                              const void* B, const void* C, const float* A,
+                              const float* Dskip, const float* dt_bias, const float* h0,
+                              void* y, float* h_final, float* ckpt,
+                              const ss_scan_plan* plan, void* stream);
+
 /* Opt-in timing of the main scan kernels (for benchmarks).  While enabled, each
  * ss_scan_fwd call records HIP events around its scan kernel launches on its
  * stream, and each ss_scan_bwd call around its backward kernels.  ss_timing_read synchronises on the recorded events and returns the

@@ -19,7 +19,7 @@ PROBE_SOURCES = ["valu_rates_probe.hip"]
 PROBE_LIB = PKG / "libssprobe.so"
 
 SOURCES = ["api.cpp", "scan_fwd.hip", "scan_bf16_euler.hip", "scan_bf16_zoh.hip", "scan_f32_euler.hip",
-           "scan_f32_zoh.hip", "scan_bwd.hip", "scan_bwd_zoh.hip", "state_update.hip"]
+           "scan_f32_zoh.hip", "scan_bwd.hip", "scan_bwd_zoh.hip", "state_update.hip", "scan_fwd_noalloc.hip"]
 ARCH = "gfx950"
 
 # Packed-FP32 VALU ops are disabled for all device code; see the design notes.

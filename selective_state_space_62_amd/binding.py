@@ -91,6 +91,11 @@ def _load():
     lib.ss_scan_shard_state_zoh.argtypes = lib.ss_scan_shard_state.argtypes
     lib.ss_scan_shard_combine.restype = _int
     lib.ss_scan_shard_combine.argtypes = [_i64, _i64, _int, _i64] + [_vp] * 6 + [_vp]
+    lib.ss_scan_fwd_noalloc_max_bytes.restype = ctypes.c_size_t
+    lib.ss_scan_fwd_noalloc_max_bytes.argtypes = []
+    lib.ss_scan_fwd_noalloc.restype = _int
+    lib.ss_scan_fwd_noalloc.argtypes = ([_i64, _i64, _int, _i64, _int, ctypes.c_uint32] + [_vp] * 12
+                                        + [ctypes.POINTER(ss_scan_plan), _vp])
     lib.ss_timing_enable.restype = _int
     lib.ss_timing_enable.argtypes = [_int]
     lib.ss_timing_reset.restype = _int
@@ -188,6 +193,16 @@ def ss_scan_fwd_ex(batch, dim, dstate, seqlen, io, flags, x, dt, z, B, C, A, Dsk
                    ckpt, workspace, workspace_bytes, plan=None, stream=None):
     _check(lib.ss_scan_fwd_ex(batch, dim, dstate, seqlen, io, flags, x, dt, z, B, C, A, Dskip, dt_bias, h0, y,
                               h_final, ckpt, workspace, workspace_bytes, _plan_ptr(plan), stream))
+
+
+def ss_scan_fwd_noalloc_max_bytes() -> int:
+    return int(lib.ss_scan_fwd_noalloc_max_bytes())
+
+
+def ss_scan_fwd_noalloc(batch, dim, dstate, seqlen, io, flags, x, dt, z, B, C, A, Dskip, dt_bias, h0, y, h_final,
+                        ckpt, plan=None, stream=None):
+    _check(lib.ss_scan_fwd_noalloc(batch, dim, dstate, seqlen, io, flags, x, dt, z, B, C, A, Dskip, dt_bias, h0, y,
+                                   h_final, ckpt, _plan_ptr(plan), stream))
 
 
 def ss_scan_ckpt_bytes(batch, dim, dstate, seqlen) -> int:

@@ -31,6 +31,26 @@ ss_status hip_fail(hipError_t e, const char* what) {
   return fail(SS_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
 }
 
+}  // namespace
+
+namespace ssscan {
+
+ss_status record_error(ss_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+ss_status record_hip_error(hipError_t e, const char* what) { return hip_fail(e, what); }
+
+}  // namespace ssscan
+
+namespace {
+
 bool valid_dstate(int n) { return n == 1 || n == 2 || n == 4 || n == 8 || n == 16; }
 
 int elem_bytes(ss_dtype io) { return io == SS_BF16 ? 2 : 4; }

@@ -5,7 +5,14 @@
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
+#include "ssscan.h"
+
 namespace ssscan {
+
+// Records the per-thread message that ss_last_error() returns and passes the
+// status through (printf-style message).
+ss_status record_error(ss_status st, const char* fmt, ...);
+ss_status record_hip_error(hipError_t e, const char* what);
 
 enum IoType : int32_t { kIoF32 = 0, kIoBf16 = 1 };
 

@@ -345,3 +345,19 @@ def test_python_errors_carry_message():
     with pytest.raises(b.SsError) as e:
         b.ss_scan_fwd(1, 16, 3, 64, b.SS_F32, *([None] * 11), None, 0)
     assert e.value.status == b.SS_ERR_UNSUPPORTED and "dstate" in str(e.value)
+
+
+def test_noalloc_scan_refuses_shapes_beyond_its_static_scratch():
+    """ss_scan_fwd_noalloc checks the scratch it needs against its static array
+    before any device work: a shape that needs more is refused with
+    SS_ERR_WORKSPACE and a message naming both sizes."""
+    assert b.ss_scan_fwd_noalloc_max_bytes() == 32 * MB
+    batch, dim, N, L = 4, 64, 16, 1 << 17
+    need = b.ss_scan_fwd_workspace_bytes(batch, dim, N, L, b.SS_BF16)
+    assert need > 32 * MB
+    p = ctypes.c_void_p(ALIGNED)
+    st = b.lib.ss_scan_fwd_noalloc(batch, dim, N, L, b.SS_BF16, 0, p, p, None, p, p, p, None, None, None,
+                                   ctypes.c_void_p(ALIGNED + 1024 * MB), None, None, None, None)
+    assert st == b.SS_ERR_WORKSPACE
+    msg = b.last_error()
+    assert str(need) in msg and str(32 * MB) in msg
