@@ -125,7 +125,7 @@ Plan auto_plan(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype 
   Plan p;
   p.groups = dstate >= 4 ? 4 : dstate;
   p.lanes = dstate >= 8 ? 2 : 1;
-  p.tile = ssscan::tile_len(p.groups, io_code(io));
+  p.tile = ssscan::tile_len(p.groups, p.lanes, io_code(io));
   const int64_t cpb = 64 / p.lanes;
   const int64_t wgs = ((dim + cpb - 1) / cpb) * batch;
   const int64_t waves = wgs * p.groups;
@@ -146,7 +146,7 @@ Plan auto_plan(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_dtype 
   // VALU work per channel (130M-shaped layer: 384 -> 768 workgroups).
   if (chunks == 1 && dstate >= 16 && wgs < 2 * (simds / 4)) {
     p.lanes = 4;
-    p.tile = ssscan::tile_len(p.groups, io_code(io));
+    p.tile = ssscan::tile_len(p.groups, p.lanes, io_code(io));
   }
   int64_t cl = (seqlen + chunks - 1) / chunks;
   cl = ((cl + p.tile - 1) / p.tile) * p.tile;
@@ -173,7 +173,7 @@ ss_status make_plan(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_d
                 "plan.lanes_per_channel %d must be 1, 2 or 4 (4 with 4 state groups), with state_groups * "
                 "lanes_per_channel <= dstate (%d)",
                 in->lanes_per_channel, dstate);
-  p.tile = ssscan::tile_len(p.groups, io_code(io));
+  p.tile = ssscan::tile_len(p.groups, p.lanes, io_code(io));
   int64_t cl = in->chunk_len;
   if (cl <= 0) return fail(SS_ERR_INVALID_ARG, "plan.chunk_len must be positive (got %lld)", (long long)cl);
   if (cl >= seqlen) {

@@ -110,10 +110,14 @@ constexpr int bwd_chunk_tokens(int dstate) {
 int bwd_lanes_per_channel(int dstate);
 int bwd_chunk_len(int dstate);
 
-// Tokens per tile: each wave loads 16 bytes of every input row per tile.
-inline int tile_len(int groups, int io) { return groups * (io == kIoBf16 ? 8 : 4); }
+// Tokens of every input row a wave loads and owns per tile: 16 bytes, except
+// 32 bytes (8 fp32 tokens) for the four-lanes-per-channel plan, whose lanes
+// would otherwise own a single token each.
+constexpr int wave_tokens(int lanes, int io) { return io == kIoBf16 ? 8 : (lanes == 4 ? 8 : 4); }
+// Tokens per tile.
+inline int tile_len(int groups, int lanes, int io) { return groups * wave_tokens(lanes, io); }
 // Tokens of a row each lane loads per tile (its span).
-inline int span_len(int lanes, int io) { return (io == kIoBf16 ? 8 : 4) / lanes; }
+inline int span_len(int lanes, int io) { return wave_tokens(lanes, io) / lanes; }
 
 hipError_t launch_prep_bc(const ScanDims& dm, const void* B, const void* C, float* bc, hipStream_t s);
 hipError_t launch_scan(const ScanDims& dm, const ScanPtrs& p, bool aggregate, bool zoh, hipStream_t s);

@@ -52,7 +52,8 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
   constexpr int CPB = 64 / K;            // channels per workgroup (K adjacent lanes per channel)
   constexpr int SG = G * K;              // state groups (one per lane of a channel per wave)
   constexpr int NS = N / SG;             // state components per lane
-  constexpr int TPW = IO::kPerSpan;      // tokens owned per wave per tile (16 bytes of a row)
+  // tokens owned per wave per tile (16 bytes of a row; 32 for fp32 with four lanes per channel)
+  constexpr int TPW = wave_tokens(K, IO::kPerSpan == 8 ? kIoBf16 : kIoF32);
   constexpr int SPAN = TPW / K;          // of which each lane of a channel owns SPAN
   constexpr int T = TPW * G;             // tile length
   constexpr int THREADS = 64 * G;
@@ -137,7 +138,8 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
     for (int k = 0; k < BC_PER_THREAD; ++k) {
       const int piece = tid + k * THREADS;
       const int64_t tok = ts + piece / TOK_PIECES;
-      if (piece < BC_PIECES && (whole || tok < t1)) cbc[k] = bc_row[ts * TOK_PIECES + piece];
+      if (BC_PIECES % THREADS == 0 && whole) cbc[k] = bc_row[ts * TOK_PIECES + piece];   // every thread, no mask
+      else if (piece < BC_PIECES && (whole || tok < t1)) cbc[k] = bc_row[ts * TOK_PIECES + piece];
       else cbc[k] = Piece{};
     }
   };
@@ -180,7 +182,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
     }
 #pragma unroll
     for (int k = 0; k < BC_PER_THREAD; ++k)
-      if (tid + k * THREADS < BC_PIECES) s_bc[tid + k * THREADS] = cbc[k];
+      if (BC_PIECES % THREADS == 0 || tid + k * THREADS < BC_PIECES) s_bc[tid + k * THREADS] = cbc[k];
     // prefetch the next tile: plain vector loads when it is whole and aligned
     // (every tile but the last), masked loads otherwise
     if (vec && ts + 2 * T <= t1) {
@@ -209,7 +211,9 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
     __builtin_amdgcn_s_setprio(2);
 
     // phase B: this lane's state components through every token of the tile.
-    // The LDS operands of token j + 1 are read before token j is computed.
+    // The LDS operands of token j + PD are read before token j is computed (PD
+    // tokens ahead: with one component per lane a token's work is too short to
+    // cover an LDS read's latency).
     float yp[SHARE_DD ? 1 : T];
     struct Ops {
       float d, dx, bcv[2 * NS];
@@ -255,23 +259,35 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
       } else {
         // both lanes of a channel end with the channel's sum over this wave's components
         // the K lanes of a channel (adjacent in a quad) end with the channel's sum
-        if constexpr (K >= 2) acc += __builtin_amdgcn_update_dpp(0.0f, acc, 0xB1, 0xf, 0xf, false);   // [1,0,3,2]
-        if constexpr (K == 4) acc += __builtin_amdgcn_update_dpp(0.0f, acc, 0x4E, 0xf, 0xf, false);   // [2,3,0,1]
-        if constexpr (SHARE_DD) s_part[j][w][c] = acc;
-        else yp[j] = acc;
+        // (the empty asm stops the compiler from refolding the readout product into
+        // the first DPP add, which costs a move and a second multiply)
+        if constexpr (K >= 2) asm volatile("" : "+v"(acc));
+        if constexpr (K >= 2) acc += __builtin_amdgcn_update_dpp(0.0f, acc, 0xB1, 0xf, 0xf, true);   // [1,0,3,2]
+        if constexpr (K == 4) acc += __builtin_amdgcn_update_dpp(0.0f, acc, 0x4E, 0xf, 0xf, true);   // [2,3,0,1]
+        // one lane of the channel stores the sum (the others hold the same value);
+        // the empty asm keeps the DPP add (fused into one instruction) ahead of
+        // the masked store instead of sunk into it
+        if constexpr (SHARE_DD) {
+          if constexpr (K >= 2) asm volatile("" : "+v"(acc));
+          if (K == 1 || hk == 0) s_part[j][w][c] = acc;
+        } else {
+          yp[j] = acc;
+        }
       }
     };
     const int nj = FULL ? T : (int)(t1 - ts);
     constexpr int NMID = (T > CKL) ? T / CKL - 1 : 1;   // checkpoint positions inside the tile
     float hmid[NMID][NS];
-    Ops cur, nxt;
-    fetch(0, cur);
+    constexpr int PD = NS == 1 ? 3 : 2;   // tokens of LDS operands in flight ahead
+    Ops ring[PD + 1];
+#pragma unroll
+    for (int q = 0; q < PD; ++q)
+      if (q < T && (FULL || q < nj)) fetch(q, ring[q]);
 #pragma unroll
     for (int j = 0; j < T; ++j) {
       if (FULL || j < nj) {
-        if (j + 1 < T && (FULL || j + 1 < nj)) fetch(j + 1, nxt);
-        compute(j, cur);
-        cur = nxt;
+        if (j + PD < T && (FULL || j + PD < nj)) fetch(j + PD, ring[(j + PD) % (PD + 1)]);
+        compute(j, ring[j % (PD + 1)]);
         if constexpr (CKPT && T > CKL) {
           // the state after token ts + j enters checkpoint chunk (ts + j + 1) / CKL;
           // tiles start at multiples of T, so inside a tile the positions are
