@@ -367,6 +367,9 @@ ss_status scan_fwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, 
   dm.lanes = p.lanes;
   dm.io = io_code(io);
   dm.vec = (seqlen % ssscan::span_len(p.lanes, dm.io)) == 0 ? 1 : 0;
+  // buffer resources address a workgroup's rows with 32-bit offsets
+  dm.buf = (dm.vec && (64 / p.lanes) * seqlen * elem_bytes(io) < (int64_t(1) << 31) &&
+            seqlen * 2 * dstate * 4 < (int64_t(1) << 31)) ? 1 : 0;
   dm.dt_row = dt_row ? 1 : 0;
   dm.ck_count = ck_count;
 
@@ -511,6 +514,9 @@ ss_status shard_state_impl(int64_t batch, int64_t dim, int dstate, int64_t seqle
   dm.lanes = p.lanes;
   dm.io = io_code(io);
   dm.vec = (seqlen % ssscan::span_len(p.lanes, dm.io)) == 0 ? 1 : 0;
+  // buffer resources address a workgroup's rows with 32-bit offsets
+  dm.buf = (dm.vec && (64 / p.lanes) * seqlen * elem_bytes(io) < (int64_t(1) << 31) &&
+            seqlen * 2 * dstate * 4 < (int64_t(1) << 31)) ? 1 : 0;
   char* ws = static_cast<char*>(workspace);
   float* bcw = reinterpret_cast<float*>(ws + wl.bc);
   e = ssscan::launch_prep_bc(dm, B, B, bcw, s);   // C is not read by the aggregate pass

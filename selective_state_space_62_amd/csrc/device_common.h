@@ -120,6 +120,57 @@ __device__ __forceinline__ void store_span(typename IO::T* __restrict__ base, in
   }
 }
 
+// Buffer-resource forms of the span load and store, for whole aligned spans:
+// the workgroup's rows are one buffer (base and size in scalar registers), the
+// lane's row and token offset a 32-bit register offset fixed for the whole
+// sequence, and the tile's token offset a scalar offset, so advancing a tile
+// costs no vector instructions.  Raw buffer resource word 3 for gfx9-class parts.
+constexpr int kBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufferWord3);
+}
+
+template <typename IO, int SPAN>
+__device__ __forceinline__ void buf_load_span(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                              uint32_t (&w)[SpanT<IO, SPAN>::kWords]) {
+  constexpr int B = SpanT<IO, SPAN>::kBytes;
+  if constexpr (B == 16) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+  } else if constexpr (B == 8) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    w[0] = v[0]; w[1] = v[1];
+  } else {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+  }
+}
+
+template <typename IO, int SPAN>
+__device__ __forceinline__ void buf_store_span(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                               const float (&v)[SPAN]) {
+  constexpr int B = SpanT<IO, SPAN>::kBytes;
+  uint32_t o[SpanT<IO, SPAN>::kWords];
+  if constexpr (IO::kPerSpan == 4) {
+#pragma unroll
+    for (int i = 0; i < SPAN; ++i) o[i] = __float_as_uint(v[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < SPAN; i += 2) o[i >> 1] = pack_bf16x2(v[i], v[i + 1]);
+  }
+  if constexpr (B == 16) {
+    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+    const u4 d = {o[0], o[1], o[2], o[3]};
+    __builtin_amdgcn_raw_buffer_store_b128(d, r, voff, soff, 0);
+  } else if constexpr (B == 8) {
+    typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+    const u2 d = {o[0], o[1]};
+    __builtin_amdgcn_raw_buffer_store_b64(d, r, voff, soff, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b32(o[0], r, voff, soff, 0);
+  }
+}
+
 template <typename IO>
 __device__ __forceinline__ float load_one(const typename IO::T* __restrict__ base, int64_t idx) {
   if constexpr (IO::kPerSpan == 4) return base[idx];

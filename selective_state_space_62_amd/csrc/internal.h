@@ -30,6 +30,7 @@ struct ScanDims {
   int32_t lanes;        // lanes per channel (1, 2 or 4); each lane owns dstate/(groups*lanes) states
   int32_t dt_row;       // 1: dt is (batch, seqlen), one value per token shared by a row's channels
   int64_t ck_count;     // with ScanPtrs::ckpt: checkpoints per channel, ceil(seqlen / bwd_chunk_tokens(dstate))
+  int32_t buf;          // 1: whole aligned tiles go through buffer resources (every offset fits 31 bits)
 };
 
 struct ScanPtrs {

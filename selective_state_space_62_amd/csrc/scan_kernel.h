@@ -21,6 +21,14 @@ __device__ __forceinline__ int64_t xcd_logical_block(int64_t wg, int64_t nwg) {
   return (wg & 7) * (nwg >> 3) + (wg >> 3);
 }
 
+// A wave-uniform 64-bit value moved to scalar registers, so that the values
+// derived from it (loop bounds, offsets) are computed by the scalar unit.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // B/C tile pieces: 16 bytes (two state components) for N >= 2, 8 bytes for N = 1.
 template <int N>
 struct BcPiece {
@@ -42,7 +50,11 @@ struct BcPiece<1> {
 // CKPT_K (full pass only): also store the state entering every backward-pass
 // chunk, for a training step's backward.  It is a separate instantiation so
 // that the plain scan keeps its registers.
-template <int N, int G, int K, typename IO, bool AGG, bool ZOH, bool CKPT_K>
+// ZFAST (zero-order hold only): this launch takes the workgroups whose every
+// |A| is at least 1/16 (the (E - 1) x B / A form); the other launch takes the
+// rest (the phi form).  Each instantiation carries one form, so neither pays
+// the other's registers.
+template <int N, int G, int K, typename IO, bool AGG, bool ZOH, bool CKPT_K, bool ZFAST = false>
 __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 && N / (G * K) <= 2 ? 5 : 1, 10))) void scan_kernel(
     const ScanDims dm, const typename IO::T* __restrict__ x, const typename IO::T* __restrict__ dt,
     const typename IO::T* __restrict__ z, const float* __restrict__ bc, const float* __restrict__ A,
@@ -67,8 +79,11 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
   static_assert(K == 1 || K == 2 || K == 4, "one, two or four lanes per channel");
   constexpr bool SHARE_DD = (G * K) > 1;   // Delta is computed once and shared through LDS
 
-  __shared__ float2 s_dd[SHARE_DD ? T : 1][CPB];              // (Delta, Delta*x) per token and channel
-  __shared__ float s_part[(SHARE_DD && !AGG) ? T : 1][G][CPB];   // partial readouts per token, wave, channel
+  // (Delta, Delta*x) per token and channel, and partial readouts per token, wave
+  // and channel.  The rows are padded by one channel: the K lanes of a channel
+  // own tokens SPAN apart, which without the pad fall in the same LDS bank.
+  __shared__ float2 s_dd[SHARE_DD ? T : 1][CPB + 1];
+  __shared__ float s_part[(SHARE_DD && !AGG) ? T : 1][G][CPB + 1];
   __shared__ Piece s_bc[BC_PIECES];                           // the tile's B_n, C_n (token-major, n, B/C)
 
   const int tid = threadIdx.x;
@@ -82,10 +97,10 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
   const int64_t cblocks = (dm.dim + CPB - 1) / CPB;
   const int64_t nwg = cblocks * dm.batch * dm.num_chunks;
   int64_t lb = xcd_logical_block(blockIdx.x, nwg);
-  const int64_t cb = lb % cblocks;
+  const int64_t cb = uniform64(lb % cblocks);
   lb /= cblocks;
-  const int64_t b = lb % dm.batch;
-  const int64_t chunk = lb / dm.batch;
+  const int64_t b = uniform64(lb % dm.batch);
+  const int64_t chunk = uniform64(lb / dm.batch);
 
   const int64_t d = cb * CPB + c;
   const bool act = d < dm.dim;
@@ -102,6 +117,25 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
   float A2[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) A2[s] = A[dc * N + sg * NS + s] * kLog2e;
+  // Zero-order hold: the input term (e^(Delta A) - 1)/A B x.  For |A| >= 1/16 in
+  // every component of the wave it is evaluated as (E - 1) t with t = x B / A,
+  // E = e^(Delta A) already at hand: one fma, one multiply more than the first
+  // order form.  E - 1 carries the rounding of E, about 1e-7 absolute, so t's
+  // share of error stays near one rounding of a state of size x B / A.  Waves
+  // with a smaller |A| (A = 0 included) use phi(Delta A) Delta B x instead.
+  float inv_a[ZOH ? NS : 1];
+  if constexpr (ZOH) {
+    bool ok = true;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const float a = A[dc * N + sg * NS + s];
+      inv_a[s] = 1.0f / a;
+      ok = ok && (fabsf(a) >= 0.0625f) && (fabsf(a) <= 3.0e38f);
+    }
+    // the whole workgroup takes one form (its waves share the readout partials)
+    const bool wg_fast = __syncthreads_and(ok) != 0;
+    if (wg_fast != ZFAST) return;
+  }
   const float bias2 = dt_bias ? dt_bias[dc] * kLog2e : 0.0f;
   const float skip = Dskip ? Dskip[dc] : 0.0f;
 
@@ -131,18 +165,40 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
 
   // B/C of this batch row, re-laid out (token, n, {B, C}); pieces never straddle tokens
   const Piece* __restrict__ bc_row = reinterpret_cast<const Piece*>(bc + b * L * (2 * N));
-  Piece cbc[BC_PER_THREAD];
+  // A tile's raw inputs held in registers: this lane's spans of x, dt and z and
+  // this thread's pieces of the B/C tile.  The next tile's are loaded while the
+  // current one computes; whole tiles alternate between two of these.
+  struct Spans {
+    uint32_t x[SW], dt[SW], z[SW];
+    Piece bc[BC_PER_THREAD];
+  };
   // `whole`: every token of the tile lies inside the chunk (no per-piece check)
-  auto load_bc_tile = [&](int64_t ts, bool whole) {
+  auto load_bc_tile = [&](int64_t ts, bool whole, Spans& S) {
 #pragma unroll
     for (int k = 0; k < BC_PER_THREAD; ++k) {
       const int piece = tid + k * THREADS;
       const int64_t tok = ts + piece / TOK_PIECES;
-      if (BC_PIECES % THREADS == 0 && whole) cbc[k] = bc_row[ts * TOK_PIECES + piece];   // every thread, no mask
-      else if (piece < BC_PIECES && (whole || tok < t1)) cbc[k] = bc_row[ts * TOK_PIECES + piece];
-      else cbc[k] = Piece{};
+      if (BC_PIECES % THREADS == 0 && whole) S.bc[k] = bc_row[ts * TOK_PIECES + piece];   // every thread, no mask
+      else if (piece < BC_PIECES && (whole || tok < t1)) S.bc[k] = bc_row[ts * TOK_PIECES + piece];
+      else S.bc[k] = Piece{};
     }
   };
+  // Buffer resources of whole aligned tiles (dm.buf): the workgroup's rows of x,
+  // z and y, the dt rows (the workgroup's, or the batch row's shared one), and
+  // the batch row's B/C re-layout; per-lane offsets are fixed, the tile's token
+  // offset goes in a scalar register.  Without z the z loads read x (unused).
+  const bool use_buf = dm.buf != 0;
+  constexpr int EB = (int)sizeof(typename IO::T);
+  const int64_t row0 = b * dm.dim + cb * CPB;                  // the workgroup's first row
+  const int64_t nrows = (dm.dim - cb * CPB < CPB) ? dm.dim - cb * CPB : CPB;
+  const __amdgpu_buffer_rsrc_t rs_x = make_rsrc(x + row0 * L, nrows * L * EB);
+  const __amdgpu_buffer_rsrc_t rs_z = has_z ? make_rsrc(z + row0 * L, nrows * L * EB) : rs_x;
+  const __amdgpu_buffer_rsrc_t rs_dt =
+      dm.dt_row ? make_rsrc(dt + b * L, L * EB) : make_rsrc(dt + row0 * L, nrows * L * EB);
+  const __amdgpu_buffer_rsrc_t rs_bc = make_rsrc(bc + b * L * (2 * N), L * (2 * N) * 4);
+  const uint32_t vo_row = (uint32_t)(((dc - cb * CPB) * L + w * TPW + hk * SPAN) * EB);
+  const uint32_t vo_dt = dm.dt_row ? (uint32_t)((w * TPW + hk * SPAN) * EB) : vo_row;
+
   // first token of the span this lane owns in the tile starting at ts
   auto own_first = [&](int64_t ts) { return ts + w * TPW + hk * SPAN; };
   auto own_valid = [&](int64_t first) {
@@ -150,24 +206,53 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
     return (int)(v < 0 ? 0 : (v < SPAN ? v : SPAN));
   };
 
-  // raw spans of x, dt, z for this lane's tokens of the current tile (prefetched a tile ahead)
-  uint32_t cx[SW], cdt[SW], cz[SW] = {};
+  // the next whole tile (starting at ts) through the buffer resources
+  auto load_buf_tile = [&](int64_t ts, Spans& S) {
+    const uint32_t so = (uint32_t)(ts * EB);
+    buf_load_span<IO, SPAN>(rs_x, vo_row, so, S.x);
+    buf_load_span<IO, SPAN>(rs_dt, vo_dt, so, S.dt);
+    buf_load_span<IO, SPAN>(rs_z, vo_row, so, S.z);
+    const uint32_t sob = (uint32_t)(ts * TOK_PIECES * (int)sizeof(Piece));
+#pragma unroll
+    for (int k = 0; k < BC_PER_THREAD; ++k) {
+      if (BC_PIECES % THREADS == 0 || tid + k * THREADS < BC_PIECES) {
+        const uint32_t vo = (uint32_t)((tid + k * THREADS) * (int)sizeof(Piece));
+        if constexpr (sizeof(Piece) == 16) {
+          const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs_bc, vo, sob, 0);
+          S.bc[k] = Piece{__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3])};
+        } else {
+          const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs_bc, vo, sob, 0);
+          S.bc[k] = Piece{__uint_as_float(v[0]), __uint_as_float(v[1])};
+        }
+      }
+    }
+  };
+
+  Spans S0, S1;
+#pragma unroll
+  for (int k = 0; k < SW; ++k) S0.z[k] = S1.z[k] = 0u;   // z is read only with a gate
   {
     const int64_t tf = own_first(t0);
     const int valid = own_valid(tf);
-    load_span<IO, SPAN>(x, row + tf, valid, vec, cx);
-    load_span<IO, SPAN>(dt, dt_row + tf, valid, vec, cdt);
-    if (has_z) load_span<IO, SPAN>(z, row + tf, valid, vec, cz);
-    load_bc_tile(t0, t0 + T <= t1);
+    load_span<IO, SPAN>(x, row + tf, valid, vec, S0.x);
+    load_span<IO, SPAN>(dt, dt_row + tf, valid, vec, S0.dt);
+    if (has_z) load_span<IO, SPAN>(z, row + tf, valid, vec, S0.z);
+    load_bc_tile(t0, t0 + T <= t1, S0);
   }
 
-  // One tile.  FULL (a compile-time tag) means all T tokens lie inside the chunk:
-  // no per-token masks, no guards in the inner loop.
-  auto tile = [&](auto full_tag, auto ck_tag, int64_t ts) {
+  // One tile from the spans `cur`, loading the next tile's into `nxt`.  FULL (a
+  // compile-time tag) means all T tokens lie inside the chunk: no per-token
+  // masks, no guards in the inner loop.  NEXT_BUF (compile-time): the next tile
+  // is whole and goes through the buffer resources.
+  auto tile = [&](auto full_tag, auto ck_tag, auto nbuf_tag, int64_t ts, const Spans& cur, Spans& nxt) {
     constexpr bool FULL = decltype(full_tag)::value;
     constexpr bool CKPT = decltype(ck_tag)::value && CKPT_K;
+    constexpr bool NEXT_BUF = decltype(nbuf_tag)::value;
     const int64_t tf = own_first(ts);
     const int valid = FULL ? SPAN : own_valid(tf);
+    const uint32_t(&cx)[SW] = cur.x;
+    const uint32_t(&cdt)[SW] = cur.dt;
+    const uint32_t(&cz)[SW] = cur.z;
 
     // phase A: Delta and Delta*x for the owned tokens; stage the B/C tile
     float xv[SPAN], zv[SPAN], dl[SPAN], dx[SPAN];
@@ -178,26 +263,30 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
       const float delta = softplus_dt(span_elem<IO>(cdt, i), bias2);
       if constexpr (FULL) dl[i] = delta;
       else dl[i] = (i < valid) ? delta : 0.0f;            // padding tokens leave the state alone
-      dx[i] = dl[i] * xv[i];
+      dx[i] = ZOH ? xv[i] : dl[i] * xv[i];   // zero-order hold shares x itself
     }
 #pragma unroll
     for (int k = 0; k < BC_PER_THREAD; ++k)
-      if (BC_PIECES % THREADS == 0 || tid + k * THREADS < BC_PIECES) s_bc[tid + k * THREADS] = cbc[k];
+      if (BC_PIECES % THREADS == 0 || tid + k * THREADS < BC_PIECES) s_bc[tid + k * THREADS] = cur.bc[k];
     // prefetch the next tile: plain vector loads when it is whole and aligned
     // (every tile but the last), masked loads otherwise
-    if (vec && ts + 2 * T <= t1) {
+    if constexpr (NEXT_BUF) {
+      load_buf_tile(ts + T, nxt);
+    } else if (use_buf && ts + 2 * T <= t1) {
+      load_buf_tile(ts + T, nxt);
+    } else if (vec && ts + 2 * T <= t1) {
       const int64_t tn = tf + T;
-      load_span<IO, SPAN>(x, row + tn, SPAN, true, cx);
-      load_span<IO, SPAN>(dt, dt_row + tn, SPAN, true, cdt);
-      if (has_z) load_span<IO, SPAN>(z, row + tn, SPAN, true, cz);
-      load_bc_tile(ts + T, true);
+      load_span<IO, SPAN>(x, row + tn, SPAN, true, nxt.x);
+      load_span<IO, SPAN>(dt, dt_row + tn, SPAN, true, nxt.dt);
+      if (has_z) load_span<IO, SPAN>(z, row + tn, SPAN, true, nxt.z);
+      load_bc_tile(ts + T, true, nxt);
     } else if (ts + T < t1) {
       const int64_t tn = tf + T;
       const int validn = own_valid(tn);
-      load_span<IO, SPAN>(x, row + tn, validn, vec, cx);
-      load_span<IO, SPAN>(dt, dt_row + tn, validn, vec, cdt);
-      if (has_z) load_span<IO, SPAN>(z, row + tn, validn, vec, cz);
-      load_bc_tile(ts + T, ts + 2 * T <= t1);
+      load_span<IO, SPAN>(x, row + tn, validn, vec, nxt.x);
+      load_span<IO, SPAN>(dt, dt_row + tn, validn, vec, nxt.dt);
+      if (has_z) load_span<IO, SPAN>(z, row + tn, validn, vec, nxt.z);
+      load_bc_tile(ts + T, ts + 2 * T <= t1, nxt);
     }
     if constexpr (SHARE_DD) {
 #pragma unroll
@@ -243,14 +332,24 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
         }
       }
     };
-    auto compute = [&](int j, const Ops& o) {
+    // o.dx is Delta x (first order) or x (zero-order hold)
+    auto compute = [&](auto fz_tag, int j, const Ops& o) {
+      constexpr bool FASTZ = decltype(fz_tag)::value;
       float acc = 0.0f;
+      const float dxz = ZOH && !FASTZ ? o.d * o.dx : 0.0f;   // Delta x for the phi form
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const float u2 = o.d * A2[s];
         const float E = __builtin_amdgcn_exp2f(u2);
-        float in = o.dx * o.bcv[2 * s];                 // first order: Bbar x = Delta B x
-        if constexpr (ZOH) in *= zoh_phi(u2, E);        // zero-order hold: (e^u - 1)/u Delta B x
+        float in;
+        if constexpr (!ZOH) {
+          in = o.dx * o.bcv[2 * s];                       // first order: Bbar x = Delta B x
+        } else if constexpr (FASTZ) {
+          const float t = o.dx * (o.bcv[2 * s] * inv_a[s]);
+          in = fmaf(E, t, -t);                            // (e^u - 1) x B / A
+        } else {
+          in = (dxz * o.bcv[2 * s]) * zoh_phi(u2, E);     // (e^u - 1)/u Delta B x
+        }
         h[s] = fmaf(E, h[s], in);
         if constexpr (!AGG) acc = (s == 0) ? o.bcv[1] * h[0] : fmaf(o.bcv[2 * s + 1], h[s], acc);
       }
@@ -278,27 +377,30 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
     const int nj = FULL ? T : (int)(t1 - ts);
     constexpr int NMID = (T > CKL) ? T / CKL - 1 : 1;   // checkpoint positions inside the tile
     float hmid[NMID][NS];
-    constexpr int PD = NS == 1 ? 3 : 2;   // tokens of LDS operands in flight ahead
-    Ops ring[PD + 1];
+    constexpr int PD = NS == 1 ? 3 : (ZOH ? 1 : 2);   // tokens of LDS operands in flight ahead
+    auto sweep = [&](auto fz_tag) {
+      Ops ring[PD + 1];
 #pragma unroll
-    for (int q = 0; q < PD; ++q)
-      if (q < T && (FULL || q < nj)) fetch(q, ring[q]);
+      for (int q = 0; q < PD; ++q)
+        if (q < T && (FULL || q < nj)) fetch(q, ring[q]);
 #pragma unroll
-    for (int j = 0; j < T; ++j) {
-      if (FULL || j < nj) {
-        if (j + PD < T && (FULL || j + PD < nj)) fetch(j + PD, ring[(j + PD) % (PD + 1)]);
-        compute(j, ring[j % (PD + 1)]);
-        if constexpr (CKPT && T > CKL) {
-          // the state after token ts + j enters checkpoint chunk (ts + j + 1) / CKL;
-          // tiles start at multiples of T, so inside a tile the positions are
-          // fixed: keep a copy (no branch here), stored after the tile
-          if ((j + 1) % CKL == 0 && j + 1 < T) {
+      for (int j = 0; j < T; ++j) {
+        if (FULL || j < nj) {
+          if (j + PD < T && (FULL || j + PD < nj)) fetch(j + PD, ring[(j + PD) % (PD + 1)]);
+          compute(fz_tag, j, ring[j % (PD + 1)]);
+          if constexpr (CKPT && T > CKL) {
+            // the state after token ts + j enters checkpoint chunk (ts + j + 1) / CKL;
+            // tiles start at multiples of T, so inside a tile the positions are
+            // fixed: keep a copy (no branch here), stored after the tile
+            if ((j + 1) % CKL == 0 && j + 1 < T) {
 #pragma unroll
-            for (int s = 0; s < NS; ++s) hmid[(j + 1) / CKL - 1][s] = h[s];
+              for (int s = 0; s < NS; ++s) hmid[(j + 1) / CKL - 1][s] = h[s];
+            }
           }
         }
       }
-    }
+    };
+    sweep(std::integral_constant<bool, ZOH && ZFAST>{});
 
     if constexpr (CKPT) {
       if (ck_row) {
@@ -346,13 +448,28 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
 #pragma unroll
         for (int i = 0; i < SPAN; ++i) yv[i] *= silu(zv[i]);
       }
-      if (act && (FULL || valid > 0)) store_span<IO, SPAN>(y, row + tf, valid, vec, yv);
+      if (FULL && use_buf) {
+        if (act) buf_store_span<IO, SPAN>(make_rsrc(y + row0 * L, nrows * L * EB), vo_row, (uint32_t)(ts * EB), yv);
+      } else if (act && (FULL || valid > 0)) {
+        store_span<IO, SPAN>(y, row + tf, valid, vec, yv);
+      }
     }
   };
 
-  for (int64_t ts = t0; ts < t1; ts += T) {
-    if (ts + T <= t1) tile(std::true_type{}, std::integral_constant<bool, CKPT_K>{}, ts);
-    else tile(std::false_type{}, std::integral_constant<bool, CKPT_K>{}, ts);
+  using CkTag = std::integral_constant<bool, CKPT_K>;
+  int64_t ts = t0;
+  if (use_buf) {
+    // pairs of whole tiles whose next tiles are whole: the two span sets
+    // alternate, so nothing is copied between tiles
+    for (; ts + 3 * T <= t1; ts += 2 * T) {
+      tile(std::true_type{}, CkTag{}, std::true_type{}, ts, S0, S1);
+      tile(std::true_type{}, CkTag{}, std::true_type{}, ts + T, S1, S0);
+    }
+  }
+  for (; ts < t1; ts += T) {
+    if (ts + T <= t1) tile(std::true_type{}, CkTag{}, std::false_type{}, ts, S0, S1);
+    else tile(std::false_type{}, CkTag{}, std::false_type{}, ts, S0, S1);
+    S0 = S1;
   }
 
   if (act) {
@@ -368,23 +485,36 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
   }
 }
 
+template <int N, int G, int K, typename IO, bool AGG, bool ZOH, bool CKPT, bool ZFAST>
+hipError_t launch_scan_one(const ScanDims& dm, const ScanPtrs& p, hipStream_t s, int64_t nwg) {
+  using E = typename IO::T;
+  hipLaunchKernelGGL((scan_kernel<N, G, K, IO, AGG, ZOH, CKPT, ZFAST>), dim3((unsigned)nwg), dim3(64 * G), 0, s,
+                     dm, (const E*)p.x, (const E*)p.dt, (const E*)p.z, p.bc, p.A, p.Dskip, p.dt_bias, p.h0, p.h_in,
+                     (E*)p.y, p.h_final, p.agg_h, p.agg_s, CKPT ? p.ckpt : nullptr);
+  return hipGetLastError();
+}
+
+// Zero-order hold launches the kernel twice, once per form of the input term;
+// each workgroup runs in exactly one of the two.
+template <int N, int G, int K, typename IO, bool AGG, bool ZOH, bool CKPT>
+hipError_t launch_scan_z(const ScanDims& dm, const ScanPtrs& p, hipStream_t s, int64_t nwg) {
+  if constexpr (ZOH) {
+    const hipError_t e = launch_scan_one<N, G, K, IO, AGG, true, CKPT, true>(dm, p, s, nwg);
+    if (e != hipSuccess) return e;
+    return launch_scan_one<N, G, K, IO, AGG, true, CKPT, false>(dm, p, s, nwg);
+  } else {
+    return launch_scan_one<N, G, K, IO, AGG, false, CKPT, false>(dm, p, s, nwg);
+  }
+}
+
 template <int N, int G, int K, typename IO, bool AGG, bool ZOH>
 hipError_t launch_scan_t(const ScanDims& dm, const ScanPtrs& p, hipStream_t s) {
-  using E = typename IO::T;
   const int64_t cblocks = (dm.dim + 64 / K - 1) / (64 / K);
   const int64_t nwg = cblocks * dm.batch * dm.num_chunks;
   if constexpr (!AGG) {
-    if (p.ckpt) {
-      hipLaunchKernelGGL((scan_kernel<N, G, K, IO, false, ZOH, true>), dim3((unsigned)nwg), dim3(64 * G), 0, s,
-                         dm, (const E*)p.x, (const E*)p.dt, (const E*)p.z, p.bc, p.A, p.Dskip, p.dt_bias, p.h0,
-                         p.h_in, (E*)p.y, p.h_final, p.agg_h, p.agg_s, p.ckpt);
-      return hipGetLastError();
-    }
+    if (p.ckpt) return launch_scan_z<N, G, K, IO, false, ZOH, true>(dm, p, s, nwg);
   }
-  hipLaunchKernelGGL((scan_kernel<N, G, K, IO, AGG, ZOH, false>), dim3((unsigned)nwg), dim3(64 * G), 0, s, dm,
-                     (const E*)p.x, (const E*)p.dt, (const E*)p.z, p.bc, p.A, p.Dskip, p.dt_bias, p.h0, p.h_in,
-                     (E*)p.y, p.h_final, p.agg_h, p.agg_s, nullptr);
-  return hipGetLastError();
+  return launch_scan_z<N, G, K, IO, AGG, ZOH, false>(dm, p, s, nwg);
 }
 
 template <int N, int G, typename IO, bool AGG, bool ZOH>

@@ -123,8 +123,11 @@ def test_bwd_zoh_bf16(ss, o, dev):
 
 
 def test_bwd_zoh_checkpoints_and_determinism(ss, o, dev):
-    """A ZOH forward that stores checkpoints feeds the ZOH backward to identical
-    gradients; two runs give identical bits."""
+    """A ZOH forward that stores checkpoints feeds the ZOH backward; two runs give
+    identical bits.  The forward forms the input term as (E - 1) x B / A (every
+    |A| here is at least 0.3), the backward's own sweep as phi(u) Delta B x, so the
+    stored states differ from the sweep's by rounding: the gradients from the
+    checkpoints are held to the oracle, as for chunked plans."""
     import torch
     batch, D, N, L = 2, 96, 16, 130
     rng = np.random.default_rng(zlib.crc32(b"zoh-ckpt"))
@@ -142,8 +145,9 @@ def test_bwd_zoh_checkpoints_and_determinism(ss, o, dev):
     for k, v in g1.items():
         if v is not None:
             assert torch.equal(v, g2[k]), k
-            assert torch.equal(v, g3[k]), k
-    _compare(g1, _oracle(o, f64, par), "f32", "bwd zoh ckpt")
+    r = _oracle(o, f64, par)
+    _compare(g1, r, "f32", "bwd zoh own sweep")
+    _compare(g3, r, "f32", "bwd zoh from forward checkpoints")
 
 
 def test_bwd_zoh_dt_per_row(ss, o, dev):
