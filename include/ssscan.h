@@ -318,12 +318,12 @@ ss_status ss_scan_bwd_seg(int64_t batch, int64_t dim, int dstate, int64_t seqlen
 /* ss_scan_fwd_noalloc — for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
  * operation, arguments, layouts and errors are those of ss_scan_fwd_ex without
- * the workspace; nothing is allocated.  The scratch space (the B/C re-layout, and
- * on chunked plans the chunk aggregates and entering states) is a static device
- * array of SS_NOALLOC_SCRATCH_BYTES that every GPU the library runs on holds until
- * the process ends; its device address is looked up on the first call on each
- * device.  A call whose ss_scan_fwd_workspace_bytes() exceeds that size (at
- * dstate 16, more than 262,144 batch x sequence tokens unchunked) returns
+ * the workspace; nothing is allocated.  The scratch space (on chunked plans, the
+ * chunk aggregates and entering states; one-chunk plans need none) is a static
+ * device array of SS_NOALLOC_SCRATCH_BYTES that every GPU the library runs on
+ * holds until the process ends; its device address is looked up on the first
+ * call on each device.  A call whose ss_scan_fwd_workspace_bytes() exceeds that
+ * size (e.g. the million-token plan's 69 MB of chunk aggregates) returns
  * SS_ERR_WORKSPACE before any device work.  Every call on one GPU shares that
  * GPU's array: calls that overlap in time on one GPU (other streams, other host
  * threads) race, and the caller must order them.  The array keeps the last

@@ -192,16 +192,17 @@ ss_status make_plan(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss_d
 }
 
 struct WsLayout {
-  size_t bc, agg_h, agg_s, h_in, total;
+  size_t agg_h, agg_s, h_in, total;
 };
 
 size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// The forward's scratch: on chunked plans only, each chunk's end state from a
+// zero start and sum of Delta, and each chunk's entering state.
 WsLayout ws_layout(int64_t batch, int64_t dim, int dstate, int64_t seqlen, const Plan& p) {
+  (void)seqlen;
   WsLayout w{};
   size_t off = 0;
-  w.bc = off;
-  off += round256((size_t)batch * seqlen * dstate * 2 * sizeof(float));
   if (p.num_chunks > 1) {
     const size_t st = (size_t)batch * dim * p.num_chunks * dstate * sizeof(float);
     w.agg_h = off;
@@ -368,8 +369,8 @@ ss_status scan_fwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, 
   dm.io = io_code(io);
   dm.vec = (seqlen % ssscan::span_len(p.lanes, dm.io)) == 0 ? 1 : 0;
   // buffer resources address a workgroup's rows with 32-bit offsets
-  dm.buf = (dm.vec && (64 / p.lanes) * seqlen * elem_bytes(io) < (int64_t(1) << 31) &&
-            seqlen * 2 * dstate * 4 < (int64_t(1) << 31)) ? 1 : 0;
+  dm.buf = (dm.vec && seqlen % 4 == 0 && (64 / p.lanes) * seqlen * elem_bytes(io) < (int64_t(1) << 31) &&
+            dstate * seqlen * elem_bytes(io) < (int64_t(1) << 31)) ? 1 : 0;
   dm.dt_row = dt_row ? 1 : 0;
   dm.ck_count = ck_count;
 
@@ -382,7 +383,8 @@ ss_status scan_fwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, 
   sp.x = x;
   sp.dt = dt;
   sp.z = z;
-  sp.bc = reinterpret_cast<const float*>(ws + wl.bc);
+  sp.B = B;
+  sp.C = C;
   sp.A = A;
   sp.Dskip = Dskip;
   sp.dt_bias = dt_bias;
@@ -390,11 +392,7 @@ ss_status scan_fwd_impl(int64_t batch, int64_t dim, int dstate, int64_t seqlen, 
   sp.y = y;
   sp.h_final = h_final;
   sp.ckpt = ckpt;
-  float* bcw = reinterpret_cast<float*>(ws + wl.bc);
-
-  hipError_t e = ssscan::launch_prep_bc(dm, B, C, bcw, s);
-  if (e != hipSuccess) return hip_fail(e, "prep_bc launch");
-
+  hipError_t e;
   const bool timed = timing_on();
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   if (timed) {
@@ -515,16 +513,14 @@ ss_status shard_state_impl(int64_t batch, int64_t dim, int dstate, int64_t seqle
   dm.io = io_code(io);
   dm.vec = (seqlen % ssscan::span_len(p.lanes, dm.io)) == 0 ? 1 : 0;
   // buffer resources address a workgroup's rows with 32-bit offsets
-  dm.buf = (dm.vec && (64 / p.lanes) * seqlen * elem_bytes(io) < (int64_t(1) << 31) &&
-            seqlen * 2 * dstate * 4 < (int64_t(1) << 31)) ? 1 : 0;
+  dm.buf = (dm.vec && seqlen % 4 == 0 && (64 / p.lanes) * seqlen * elem_bytes(io) < (int64_t(1) << 31) &&
+            dstate * seqlen * elem_bytes(io) < (int64_t(1) << 31)) ? 1 : 0;
   char* ws = static_cast<char*>(workspace);
-  float* bcw = reinterpret_cast<float*>(ws + wl.bc);
-  e = ssscan::launch_prep_bc(dm, B, B, bcw, s);   // C is not read by the aggregate pass
-  if (e != hipSuccess) return hip_fail(e, "prep_bc launch");
   ssscan::ScanPtrs sp{};
   sp.x = x;
   sp.dt = dt;
-  sp.bc = bcw;
+  sp.B = B;
+  sp.C = B;   // the aggregate pass reads no C
   sp.A = A;
   sp.dt_bias = dt_bias;
   if (p.num_chunks == 1) {

@@ -37,7 +37,8 @@ struct ScanPtrs {
   const void* x;
   const void* dt;
   const void* z;        // nullable
-  const float* bc;      // workspace: (batch, seqlen, dstate, 2) fp32, B and C interleaved
+  const void* B;        // (batch, dstate, seqlen), io dtype
+  const void* C;        // (batch, dstate, seqlen), io dtype (not read by the aggregate pass)
   const float* A;
   const float* Dskip;   // nullable
   const float* dt_bias; // nullable

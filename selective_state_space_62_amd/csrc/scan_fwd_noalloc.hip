@@ -1,8 +1,8 @@
 // ss_scan_fwd_noalloc: the forward scan (ss_scan_fwd_ex) for callers that cannot
 // allocate device memory — code under HIP graph capture, tight serving loops,
-// harnesses that forbid hipMalloc.  Its scratch space (the B/C re-layout and, on
-// chunked plans, the chunk aggregates and entering states) is a static device
-// array of this file instead of a caller-owned workspace.
+// harnesses that forbid hipMalloc.  Its scratch space (on chunked plans, the
+// chunk aggregates and entering states) is a static device array of this file
+// instead of a caller-owned workspace.
 //
 // The array's name is a host-side stand-in in host code; its device address is
 // looked up once per device with hipGetSymbolAddress (each GPU holds its own

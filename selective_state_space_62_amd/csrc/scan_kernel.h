@@ -29,18 +29,6 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-// B/C tile pieces: 16 bytes (two state components) for N >= 2, 8 bytes for N = 1.
-template <int N>
-struct BcPiece {
-  using V = float4;
-  static constexpr int kFloats = 4;
-};
-template <>
-struct BcPiece<1> {
-  using V = float2;
-  static constexpr int kFloats = 2;
-};
-
 // At most 96 VGPRs (5 waves per SIMD) for the plans with two or four lanes per
 // channel and up to 2 state components per lane: with 4 waves per workgroup and
 // 28 KB of LDS, five workgroups fit on a CU at once, which the two-lanes-per-
@@ -57,7 +45,8 @@ struct BcPiece<1> {
 template <int N, int G, int K, typename IO, bool AGG, bool ZOH, bool CKPT_K, bool ZFAST = false>
 __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 && N / (G * K) <= 2 ? 5 : 1, 10))) void scan_kernel(
     const ScanDims dm, const typename IO::T* __restrict__ x, const typename IO::T* __restrict__ dt,
-    const typename IO::T* __restrict__ z, const float* __restrict__ bc, const float* __restrict__ A,
+    const typename IO::T* __restrict__ z, const typename IO::T* __restrict__ Bm,
+    const typename IO::T* __restrict__ Cm, const float* __restrict__ A,
     const float* __restrict__ Dskip, const float* __restrict__ dt_bias, const float* __restrict__ h0,
     const float* __restrict__ h_in, typename IO::T* __restrict__ y, float* __restrict__ h_final,
     float* __restrict__ agg_h, float* __restrict__ agg_s, float* __restrict__ ckpt) {
@@ -70,11 +59,13 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
   constexpr int T = TPW * G;             // tile length
   constexpr int THREADS = 64 * G;
   constexpr int SW = SpanT<IO, SPAN>::kWords;
-  using Piece = typename BcPiece<N>::V;
-  constexpr int PF = BcPiece<N>::kFloats;
-  constexpr int BC_PIECES = T * 2 * N / PF;                      // pieces of B/C per tile
-  constexpr int BC_PER_THREAD = (BC_PIECES + THREADS - 1) / THREADS;
-  constexpr int TOK_PIECES = 2 * N / PF;                         // pieces per token
+  // The tile's B/C: 2N rows (B_n, then C_n) of T tokens each, read straight
+  // from the (batch, N, L) inputs in runs of 4 tokens, one run per thread:
+  // thread q takes row q % 2N and tokens 4 (q / 2N) .. + 3, so that the lanes
+  // of a wave write different LDS banks.
+  constexpr int BC_RUNS = 2 * N * T / 4;
+  static_assert(BC_RUNS <= THREADS && T % 4 == 0, "one 4-token run of a B/C row per thread");
+  constexpr int BW = SpanT<IO, 4>::kWords;
   static_assert(NS >= 1 && N % SG == 0, "G * K must divide N");
   static_assert(K == 1 || K == 2 || K == 4, "one, two or four lanes per channel");
   constexpr bool SHARE_DD = (G * K) > 1;   // Delta is computed once and shared through LDS
@@ -84,7 +75,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
   // own tokens SPAN apart, which without the pad fall in the same LDS bank.
   __shared__ float2 s_dd[SHARE_DD ? T : 1][CPB + 1];
   __shared__ float s_part[(SHARE_DD && !AGG) ? T : 1][G][CPB + 1];
-  __shared__ Piece s_bc[BC_PIECES];                           // the tile's B_n, C_n (token-major, n, B/C)
+  __shared__ __attribute__((aligned(16))) float s_bc[T * 2 * N];   // the tile's B_n, C_n (token, n, {B, C})
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -163,25 +154,25 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
     }
   }
 
-  // B/C of this batch row, re-laid out (token, n, {B, C}); pieces never straddle tokens
-  const Piece* __restrict__ bc_row = reinterpret_cast<const Piece*>(bc + b * L * (2 * N));
+  // this thread's B/C run: row bc_r (B_n for bc_r < N, else C_(bc_r - N)), tokens
+  // 4 bc_g .. 4 bc_g + 3 of the tile; the aggregate pass reads no C
+  const bool bc_act = tid < BC_RUNS && (!AGG || tid % (2 * N) < N);
+  const int bc_r = tid % (2 * N);
+  const int bc_g = tid / (2 * N);
+  const int bc_n = bc_r < N ? bc_r : bc_r - N;
+  const typename IO::T* __restrict__ bc_src = (bc_r < N ? Bm : Cm) + (b * N + bc_n) * L;
+  const bool vec4 = (L % 4) == 0;
   // A tile's raw inputs held in registers: this lane's spans of x, dt and z and
-  // this thread's pieces of the B/C tile.  The next tile's are loaded while the
-  // current one computes; whole tiles alternate between two of these.
+  // this thread's run of B/C.  The next tile's are loaded while the current one
+  // computes; whole tiles alternate between two of these.
   struct Spans {
-    uint32_t x[SW], dt[SW], z[SW];
-    Piece bc[BC_PER_THREAD];
+    uint32_t x[SW], dt[SW], z[SW], bc[BW];
   };
-  // `whole`: every token of the tile lies inside the chunk (no per-piece check)
-  auto load_bc_tile = [&](int64_t ts, bool whole, Spans& S) {
-#pragma unroll
-    for (int k = 0; k < BC_PER_THREAD; ++k) {
-      const int piece = tid + k * THREADS;
-      const int64_t tok = ts + piece / TOK_PIECES;
-      if (BC_PIECES % THREADS == 0 && whole) S.bc[k] = bc_row[ts * TOK_PIECES + piece];   // every thread, no mask
-      else if (piece < BC_PIECES && (whole || tok < t1)) S.bc[k] = bc_row[ts * TOK_PIECES + piece];
-      else S.bc[k] = Piece{};
-    }
+  auto load_bc_tile = [&](int64_t ts, Spans& S) {
+    const int64_t first = ts + 4 * bc_g;
+    const int64_t v = t1 - first;
+    const int valid = bc_act ? (int)(v < 0 ? 0 : (v < 4 ? v : 4)) : 0;
+    load_span<IO, 4>(bc_src, first, valid, vec4, S.bc);
   };
   // Buffer resources of whole aligned tiles (dm.buf): the workgroup's rows of x,
   // z and y, the dt rows (the workgroup's, or the batch row's shared one), and
@@ -195,7 +186,6 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
   const __amdgpu_buffer_rsrc_t rs_z = has_z ? make_rsrc(z + row0 * L, nrows * L * EB) : rs_x;
   const __amdgpu_buffer_rsrc_t rs_dt =
       dm.dt_row ? make_rsrc(dt + b * L, L * EB) : make_rsrc(dt + row0 * L, nrows * L * EB);
-  const __amdgpu_buffer_rsrc_t rs_bc = make_rsrc(bc + b * L * (2 * N), L * (2 * N) * 4);
   const uint32_t vo_row = (uint32_t)(((dc - cb * CPB) * L + w * TPW + hk * SPAN) * EB);
   const uint32_t vo_dt = dm.dt_row ? (uint32_t)((w * TPW + hk * SPAN) * EB) : vo_row;
 
@@ -212,32 +202,22 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
     buf_load_span<IO, SPAN>(rs_x, vo_row, so, S.x);
     buf_load_span<IO, SPAN>(rs_dt, vo_dt, so, S.dt);
     buf_load_span<IO, SPAN>(rs_z, vo_row, so, S.z);
-    const uint32_t sob = (uint32_t)(ts * TOK_PIECES * (int)sizeof(Piece));
-#pragma unroll
-    for (int k = 0; k < BC_PER_THREAD; ++k) {
-      if (BC_PIECES % THREADS == 0 || tid + k * THREADS < BC_PIECES) {
-        const uint32_t vo = (uint32_t)((tid + k * THREADS) * (int)sizeof(Piece));
-        if constexpr (sizeof(Piece) == 16) {
-          const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs_bc, vo, sob, 0);
-          S.bc[k] = Piece{__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3])};
-        } else {
-          const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs_bc, vo, sob, 0);
-          S.bc[k] = Piece{__uint_as_float(v[0]), __uint_as_float(v[1])};
-        }
-      }
-    }
+    // (B or C differs between lanes, so the run comes through a plain vector load)
+    if (bc_act) load_span<IO, 4>(bc_src, ts + 4 * bc_g, 4, true, S.bc);
   };
 
   Spans S0, S1;
 #pragma unroll
   for (int k = 0; k < SW; ++k) S0.z[k] = S1.z[k] = 0u;   // z is read only with a gate
+#pragma unroll
+  for (int k = 0; k < BW; ++k) S0.bc[k] = S1.bc[k] = 0u;
   {
     const int64_t tf = own_first(t0);
     const int valid = own_valid(tf);
     load_span<IO, SPAN>(x, row + tf, valid, vec, S0.x);
     load_span<IO, SPAN>(dt, dt_row + tf, valid, vec, S0.dt);
     if (has_z) load_span<IO, SPAN>(z, row + tf, valid, vec, S0.z);
-    load_bc_tile(t0, t0 + T <= t1, S0);
+    load_bc_tile(t0, S0);
   }
 
   // One tile from the spans `cur`, loading the next tile's into `nxt`.  FULL (a
@@ -265,9 +245,10 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
       else dl[i] = (i < valid) ? delta : 0.0f;            // padding tokens leave the state alone
       dx[i] = ZOH ? xv[i] : dl[i] * xv[i];   // zero-order hold shares x itself
     }
+    if (bc_act) {
 #pragma unroll
-    for (int k = 0; k < BC_PER_THREAD; ++k)
-      if (BC_PIECES % THREADS == 0 || tid + k * THREADS < BC_PIECES) s_bc[tid + k * THREADS] = cur.bc[k];
+      for (int i = 0; i < 4; ++i) s_bc[(4 * bc_g + i) * (2 * N) + 2 * bc_n + (bc_r < N ? 0 : 1)] = span_elem<IO>(cur.bc, i);
+    }
     // prefetch the next tile: plain vector loads when it is whole and aligned
     // (every tile but the last), masked loads otherwise
     if constexpr (NEXT_BUF) {
@@ -279,14 +260,14 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
       load_span<IO, SPAN>(x, row + tn, SPAN, true, nxt.x);
       load_span<IO, SPAN>(dt, dt_row + tn, SPAN, true, nxt.dt);
       if (has_z) load_span<IO, SPAN>(z, row + tn, SPAN, true, nxt.z);
-      load_bc_tile(ts + T, true, nxt);
+      load_bc_tile(ts + T, nxt);
     } else if (ts + T < t1) {
       const int64_t tn = tf + T;
       const int validn = own_valid(tn);
       load_span<IO, SPAN>(x, row + tn, validn, vec, nxt.x);
       load_span<IO, SPAN>(dt, dt_row + tn, validn, vec, nxt.dt);
       if (has_z) load_span<IO, SPAN>(z, row + tn, validn, vec, nxt.z);
-      load_bc_tile(ts + T, ts + 2 * T <= t1, nxt);
+      load_bc_tile(ts + T, nxt);
     }
     if constexpr (SHARE_DD) {
 #pragma unroll
@@ -316,7 +297,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
         o.d = dl[j];
         o.dx = dx[j];
       }
-      const float* src = reinterpret_cast<const float*>(s_bc) + j * (2 * N) + 2 * sg * NS;
+      const float* src = s_bc + j * (2 * N) + 2 * sg * NS;
       if constexpr (NS == 1) {
         const float2 v = *reinterpret_cast<const float2*>(src);
         o.bcv[0] = v.x;
@@ -489,7 +470,8 @@ template <int N, int G, int K, typename IO, bool AGG, bool ZOH, bool CKPT, bool 
 hipError_t launch_scan_one(const ScanDims& dm, const ScanPtrs& p, hipStream_t s, int64_t nwg) {
   using E = typename IO::T;
   hipLaunchKernelGGL((scan_kernel<N, G, K, IO, AGG, ZOH, CKPT, ZFAST>), dim3((unsigned)nwg), dim3(64 * G), 0, s,
-                     dm, (const E*)p.x, (const E*)p.dt, (const E*)p.z, p.bc, p.A, p.Dskip, p.dt_bias, p.h0, p.h_in,
+                     dm, (const E*)p.x, (const E*)p.dt, (const E*)p.z, (const E*)p.B, (const E*)p.C, p.A, p.Dskip,
+                     p.dt_bias, p.h0, p.h_in,
                      (E*)p.y, p.h_final, p.agg_h, p.agg_s, CKPT ? p.ckpt : nullptr);
   return hipGetLastError();
 }

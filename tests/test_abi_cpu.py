@@ -81,7 +81,7 @@ def _scan_status(**kw):
     (dict(h_final=ALIGNED + 8 + (1 << 36)), b.SS_ERR_INVALID_ARG),
     (dict(Dskip=ALIGNED + 2), b.SS_ERR_INVALID_ARG),
     (dict(workspace=None), b.SS_ERR_WORKSPACE),
-    (dict(workspace_bytes=100), b.SS_ERR_WORKSPACE),
+    (dict(workspace_bytes=100, plan=(1, 64)), b.SS_ERR_WORKSPACE),   # chunked: chunk aggregates
     (dict(workspace=ALIGNED + (1 << 36) + 64), b.SS_ERR_WORKSPACE),
     (dict(y=ALIGNED + 4096), b.SS_ERR_INVALID_ARG),              # overlaps x
     (dict(plan=(3, 256)), b.SS_ERR_UNSUPPORTED),
@@ -101,7 +101,7 @@ def test_scan_validation(case, status):
 
 
 def test_output_overlapping_workspace_is_rejected():
-    (batch, dim, N, L, io), p, plan = _scan_args()
+    (batch, dim, N, L, io), p, plan = _scan_args(plan=(1, 64))   # chunked: the workspace holds chunk aggregates
     p["h_final"] = p["workspace"] + 256
     st = b.lib.ss_scan_fwd(batch, dim, N, L, io, p["x"], p["dt"], p["z"], p["B"], p["C"], p["A"], p["Dskip"],
                            p["dt_bias"], p["h0"], p["y"], p["h_final"], p["workspace"], p["workspace_bytes"],
@@ -110,14 +110,13 @@ def test_output_overlapping_workspace_is_rejected():
 
 
 def test_workspace_bytes():
-    # B and C re-laid out as (batch, L, N, 2) fp32, rounded to 256 bytes
-    assert b.ss_scan_fwd_workspace_bytes(8, 5120, 16, 2048, b.SS_BF16, (4, 2048)) == 8 * 2048 * 32 * 4
-    assert b.ss_scan_fwd_workspace_bytes(1, 16, 4, 64, b.SS_F32, (4, 64)) == 2048
-    # chunked: + chunk end states, Delta sums and chunk initial states
+    # one chunk: the scan reads B and C itself and needs no scratch (the minimum 256 bytes)
+    assert b.ss_scan_fwd_workspace_bytes(8, 5120, 16, 2048, b.SS_BF16, (4, 2048)) == 256
+    assert b.ss_scan_fwd_workspace_bytes(1, 16, 4, 64, b.SS_F32, (4, 64)) == 256
+    # chunked: chunk end states, Delta sums and chunk initial states, each rounded to 256 bytes
     n = b.ss_scan_fwd_workspace_bytes(1, 2048, 16, 1 << 20, b.SS_BF16, (4, 1 << 15))
-    bc = (1 << 20) * 32 * 4
     st = 2048 * 32 * 16 * 4
-    assert n == bc + st + 2048 * 32 * 4 + st
+    assert n == st + 2048 * 32 * 4 + st
     assert b.ss_scan_fwd_workspace_bytes(1, 16, 3, 64, b.SS_F32, None) == 0
     assert b.ss_scan_fwd_workspace_bytes(1, 16, 4, 64, b.SS_F32, (4, 8)) == 0
 
@@ -226,7 +225,7 @@ def test_bwd_workspace_bytes():
     (dict(h_end=ALIGNED + (1 << 33) + 8), b.SS_ERR_INVALID_ARG),
     (dict(dsum=ALIGNED + (1 << 30)), b.SS_ERR_INVALID_ARG),        # dsum overlaps dt
     (dict(workspace=None), b.SS_ERR_WORKSPACE),
-    (dict(workspace_bytes=64), b.SS_ERR_WORKSPACE),
+    (dict(seqlen=16384, workspace_bytes=64), b.SS_ERR_WORKSPACE),   # chunked inside the shard
 ])
 def test_shard_state_validation(case, status):
     a = dict(batch=2, dim=64, dstate=16, seqlen=512, io=b.SS_BF16, x=ALIGNED, dt=ALIGNED + (1 << 30),
@@ -352,7 +351,7 @@ def test_noalloc_scan_refuses_shapes_beyond_its_static_scratch():
     before any device work: a shape that needs more is refused with
     SS_ERR_WORKSPACE and a message naming both sizes."""
     assert b.ss_scan_fwd_noalloc_max_bytes() == 32 * MB
-    batch, dim, N, L = 4, 64, 16, 1 << 17
+    batch, dim, N, L = 1, 2048, 16, 1 << 20   # the million-token plan: 256 chunks, 69 MB of aggregates
     need = b.ss_scan_fwd_workspace_bytes(batch, dim, N, L, b.SS_BF16)
     assert need > 32 * MB
     p = ctypes.c_void_p(ALIGNED)

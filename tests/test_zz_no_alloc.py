@@ -98,7 +98,7 @@ def test_noalloc_rejects_oversized_calls(b, dev):
     import torch
     limit = b.ss_scan_fwd_noalloc_max_bytes()
     assert limit == 32 << 20
-    batch, D, N, L = 2, 64, 16, 1 << 17   # B/C re-layout alone: 2 x 2^17 x 32 x 4 B = 32 MiB + chunk buffers
+    batch, D, N, L = 1, 2048, 16, 1 << 20   # the million-token plan: 256 chunks, 69 MB of chunk aggregates
     need = b.ss_scan_fwd_workspace_bytes(batch, D, N, L, b.SS_BF16, None)
     assert need > limit
     x = torch.zeros((1, 16), dtype=torch.bfloat16, device=dev)   # never read: the size check comes first
