@@ -83,24 +83,64 @@ __global__ __launch_bounds__(256) void prep_bc_kernel(const typename IO::T* __re
   }
 }
 
-// Exclusive scan of the chunk aggregates, one lane per (b, d, n):
-// h_in[c] = state entering chunk c; h <- exp(A * sum Delta_c) h + h_end_c.
-__global__ __launch_bounds__(256) void combine_kernel(int64_t nstate, int64_t dim, int dstate, int num_chunks,
+// Exclusive scan of the chunk aggregates: h_in[c] = the state entering chunk
+// c.  A chunk's pair (P, H) = (exp(A * sum Delta_c), its end state from a zero
+// start) acts on a state as h -> P h + H; composing an earlier pair with a later
+// one gives (P1 P2, P2 H1 + H2), an associative operation, so the scan runs in
+// parallel.  One wave takes one (b, d): lane l owns state component n = l % N
+// and the l / N-th of R = 64 / N contiguous groups of chunks.  Each lane folds
+// its group into one pair (the decay from the group's summed Delta), the waves'
+// R groups are scanned across lanes N apart with cross-lane shifts
+// (ds_bpermute), and each lane then walks its group from the state entering
+// it, writing h_in.  The loads and stores of one chunk are N adjacent floats.
+template <int N>
+__global__ __launch_bounds__(256) void combine_kernel(int64_t nch, int64_t dim, int num_chunks,
                                                       const float* __restrict__ A, const float* __restrict__ agg_h,
                                                       const float* __restrict__ agg_s, const float* __restrict__ h0,
                                                       float* __restrict__ h_in) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= nstate) return;
-  const int64_t ch = i / dstate;
-  const int n = (int)(i - ch * dstate);
+  constexpr int R = 64 / N;   // groups of chunks per (b, d)
+  const int64_t ch = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / 64;   // (b, d) of this wave
+  if (ch >= nch) return;
+  const int lane = threadIdx.x & 63;
+  const int n = lane % N;
+  const int g = lane / N;
   const int64_t d = ch % dim;
-  const float a2 = A[d * dstate + n] * dev::kLog2e;
-  float h = h0 ? h0[i] : 0.0f;
-  for (int c = 0; c < num_chunks; ++c) {
-    const int64_t k = (ch * num_chunks + c) * dstate + n;
-    h_in[k] = h;
-    const float decay = __builtin_amdgcn_exp2f(a2 * agg_s[ch * num_chunks + c]);
-    h = fmaf(decay, h, agg_h[k]);
+  const float a2 = A[d * N + n] * dev::kLog2e;
+  const int per = (num_chunks + R - 1) / R;
+  const int c0 = g * per < num_chunks ? g * per : num_chunks;
+  const int c1 = c0 + per < num_chunks ? c0 + per : num_chunks;
+  const float* __restrict__ hs = agg_h + ch * (int64_t)num_chunks * N + n;
+  const float* __restrict__ ss = agg_s + ch * (int64_t)num_chunks;
+
+  // this lane's group as one pair: H from a zero start, S = the group's sum of Delta
+  float H = 0.0f, S = 0.0f;
+  for (int c = c0; c < c1; ++c) {
+    const float sc = ss[c];
+    H = fmaf(__builtin_amdgcn_exp2f(a2 * sc), H, hs[(int64_t)c * N]);
+    S += sc;
+  }
+  float P = __builtin_amdgcn_exp2f(a2 * S);
+  // inclusive scan over the R groups (lanes N apart): Hillis-Steele doubling
+#pragma unroll
+  for (int off = N; off < 64; off *= 2) {
+    const float Pp = __shfl_up(P, off, 64);
+    const float Hp = __shfl_up(H, off, 64);
+    if (lane >= off) {
+      H = fmaf(P, Hp, H);   // (Pp, Hp) then (P, H)
+      P = Pp * P;
+    }
+  }
+  // exclusive: the groups before this one
+  float Pe = __shfl_up(P, N, 64), He = __shfl_up(H, N, 64);
+  if (g == 0) {
+    Pe = 1.0f;
+    He = 0.0f;
+  }
+  float h = fmaf(Pe, h0 ? h0[ch * N + n] : 0.0f, He);
+  float* __restrict__ out = h_in + ch * (int64_t)num_chunks * N + n;
+  for (int c = c0; c < c1; ++c) {
+    out[(int64_t)c * N] = h;
+    h = fmaf(__builtin_amdgcn_exp2f(a2 * ss[c]), h, hs[(int64_t)c * N]);
   }
 }
 
@@ -188,9 +228,16 @@ hipError_t launch_scan(const ScanDims& dm, const ScanPtrs& p, bool aggregate, bo
 
 hipError_t launch_combine(const ScanDims& dm, const float* A, const float* agg_h, const float* agg_s,
                           const float* h0, float* h_in, hipStream_t s) {
-  const int64_t nstate = dm.batch * dm.dim * dm.dstate;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((nstate + 255) / 256)), dim3(256), 0, s, nstate, dm.dim,
-                     dm.dstate, dm.num_chunks, A, agg_h, agg_s, h0, h_in);
+  const int64_t nch = dm.batch * dm.dim;
+  const dim3 grid((unsigned)((nch + 3) / 4));   // four waves per workgroup, one (b, d) per wave
+  switch (dm.dstate) {
+    case 1: hipLaunchKernelGGL(combine_kernel<1>, grid, dim3(256), 0, s, nch, dm.dim, dm.num_chunks, A, agg_h, agg_s, h0, h_in); break;
+    case 2: hipLaunchKernelGGL(combine_kernel<2>, grid, dim3(256), 0, s, nch, dm.dim, dm.num_chunks, A, agg_h, agg_s, h0, h_in); break;
+    case 4: hipLaunchKernelGGL(combine_kernel<4>, grid, dim3(256), 0, s, nch, dm.dim, dm.num_chunks, A, agg_h, agg_s, h0, h_in); break;
+    case 8: hipLaunchKernelGGL(combine_kernel<8>, grid, dim3(256), 0, s, nch, dm.dim, dm.num_chunks, A, agg_h, agg_s, h0, h_in); break;
+    case 16: hipLaunchKernelGGL(combine_kernel<16>, grid, dim3(256), 0, s, nch, dm.dim, dm.num_chunks, A, agg_h, agg_s, h0, h_in); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
