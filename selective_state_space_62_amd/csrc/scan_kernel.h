@@ -382,6 +382,15 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
       }
     };
     sweep(std::integral_constant<bool, ZOH && ZFAST>{});
+    if constexpr (AGG) {
+      // The aggregate pass stores nothing per token: left free, the compiler
+      // sinks its sweep below the barrier that ends the tile, keeping every LDS
+      // operand of the tile live across it (up to 256 VGPRs, one or two waves
+      // per SIMD instead of five).  Consuming the results here pins the sweep.
+#pragma unroll
+      for (int s = 0; s < NS; ++s) asm volatile("" : "+v"(h[s]));
+      asm volatile("" : "+v"(dsum));
+    }
 
     if constexpr (CKPT) {
       if (ck_row) {
