@@ -149,6 +149,18 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
   __shared__ float s_bc[CK][2 * N];    // B_n, C_n of the chunk's tokens
   __shared__ float2 s_pp[CK][G][CPB];  // per-wave partial sums (readout; dDelta and sum lam B)
   __shared__ float s_dr[CK][CPB];      // dr per token and channel
+  // dx, ddt and dz are gathered in LDS over the 128 bytes of a row that one
+  // cache line holds (64 bf16 or 32 fp32 tokens, several chunks) and written as
+  // whole lines once the group's lowest chunk is done (chunks run last to
+  // first): a lane's own 4 or 8 bytes per row and chunk, stored directly, reach
+  // HBM as partial lines.  Rows are padded to 34 words so that the owners'
+  // writes fall in distinct banks.  The zero-order-hold form keeps direct
+  // stores: it runs four workgroups per CU, which the extra 13 KB would not fit.
+  constexpr bool STAGE = !ZOH;
+  constexpr int GT = 128 / (int)sizeof(T);   // tokens per staged group
+  constexpr int ROWW = 128 / 4 + 2;          // words per staged row
+  static_assert(GT % CK == 0 && kSpan == 2, "a group holds whole chunks; a lane owns two tokens");
+  __shared__ __attribute__((aligned(16))) uint32_t s_out[STAGE ? 3 : 1][STAGE ? CPB : 1][ROWW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -312,6 +324,53 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
 #pragma unroll
   for (int s = 0; s < NS; ++s) ckn[s] = act ? ck_row[(ke - 1) * ck_stride + s] : 0.0f;
 
+  // the owned tokens' values of output o (0 dx, 1 ddt, 2 dz) into the staged
+  // group of chunk k
+  auto stage_out = [&](int o, int64_t k, const float (&v)[kSpan]) {
+    const int tg = (int)(k * CK % GT) + j_own;   // even: a lane owns a token pair
+    if constexpr (sizeof(T) == 2) {
+      s_out[o][c][tg >> 1] = pack_bf16x2(v[0], v[1]);
+    } else {
+      *reinterpret_cast<uint2*>(&s_out[o][c][tg]) = make_uint2(__float_as_uint(v[0]), __float_as_uint(v[1]));
+    }
+  };
+  // The staged group starting at token g0 (a multiple of GT) to HBM, one
+  // 16-byte piece of a row per thread and step; rows past dim and tokens past
+  // the sequence are not written.  Whole pieces of 16-byte aligned rows go out
+  // as one vector store.
+  auto flush_out = [&](int64_t g0) {
+    constexpr int EPP = 16 / (int)sizeof(T);   // elements per piece
+    const int64_t gend = (g0 + GT < L) ? g0 + GT : L;
+#pragma unroll
+    for (int o = 0; o < 3; ++o) {
+      if ((o == 1 && dm.dt_row) || (o == 2 && !has_z)) continue;
+      T* __restrict__ dst = static_cast<T*>(o == 0 ? p.dx : (o == 1 ? p.ddt : p.dz));
+      const bool al16 = (L * (int64_t)sizeof(T)) % 16 == 0 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0;
+#pragma unroll
+      for (int pc = tid; pc < CPB * 8; pc += THREADS) {
+        const int r = pc >> 3, q = pc & 7;
+        const int64_t dr_ = cb * CPB + r;
+        const int64_t t = g0 + q * EPP;
+        if (dr_ >= dm.dim || t >= gend) continue;
+        const uint2 lo = *reinterpret_cast<const uint2*>(&s_out[o][r][q * 4]);
+        const uint2 hi = *reinterpret_cast<const uint2*>(&s_out[o][r][q * 4 + 2]);
+        T* const out = dst + (b * dm.dim + dr_) * L + t;
+        if (al16 && t + EPP <= gend) {
+          *reinterpret_cast<uint4*>(out) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        } else {
+          const uint32_t wd[4] = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+          for (int e = 0; e < EPP; ++e) {
+            if (t + e < gend) {
+              if constexpr (sizeof(T) == 2) out[e] = (T)(wd[e >> 1] >> (16 * (e & 1)));
+              else out[e] = __uint_as_float(wd[e]);
+            }
+          }
+        }
+      }
+    }
+  };
+
   auto chunk = [&](auto full_tag, int64_t k) {
     constexpr bool FULL = decltype(full_tag)::value;
     const int64_t t0 = k * CK;
@@ -389,7 +448,11 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
         dD_acc = fmaf(drv, xv[i], dD_acc);
         s_dr[j][c] = drv;
       }
-      if (has_z && act && (FULL || valid > 0)) store_span<IO, kSpan>(static_cast<T*>(p.dz), row + tf, valid, vec, dzv);
+      if constexpr (STAGE) {
+        if (has_z) stage_out(2, k, dzv);
+      } else {
+        if (has_z && act && (FULL || valid > 0)) store_span<IO, kSpan>(static_cast<T*>(p.dz), row + tf, valid, vec, dzv);
+      }
     }
     __syncthreads();
 
@@ -479,7 +542,10 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
         ddtv[i] = dv;   // zero for padding tokens and inactive channels
         if (FULL || i < valid) dbias_acc += dv;
       }
-      if (act && (FULL || valid > 0)) {
+      if constexpr (STAGE) {
+        stage_out(0, k, dxv);
+        if (!dm.dt_row) stage_out(1, k, ddtv);
+      } else if (act && (FULL || valid > 0)) {
         store_span<IO, kSpan>(static_cast<T*>(p.dx), row + tf, valid, vec, dxv);
         if (!dm.dt_row) store_span<IO, kSpan>(static_cast<T*>(p.ddt), row + tf, valid, vec, ddtv);
       }
@@ -496,6 +562,9 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
       }
     }
     __syncthreads();
+    if constexpr (STAGE) {
+      if (t0 % GT == 0) flush_out(t0);
+    }
   };
   {
     int64_t k = ke - 1;
