@@ -155,8 +155,12 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
   }
 
   // this thread's B/C run: row bc_r (B_n for bc_r < N, else C_(bc_r - N)), tokens
-  // 4 bc_g .. 4 bc_g + 3 of the tile; the aggregate pass reads no C
-  const bool bc_act = tid < BC_RUNS && (!AGG || tid % (2 * N) < N);
+  // 4 bc_g .. 4 bc_g + 3 of the tile (the aggregate pass loads C too and never
+  // reads it).  With a run for every thread (N = 16) the loads are
+  // unconditional: a load under an exec mask leaves the compiler unsure how many
+  // memory operations are in flight, and it then waits for all of them,
+  // including the previous tile's y store, before using the next run.
+  const bool bc_act = BC_RUNS >= THREADS || tid < BC_RUNS;
   const int bc_r = tid % (2 * N);
   const int bc_g = tid / (2 * N);
   const int bc_n = bc_r < N ? bc_r : bc_r - N;
@@ -439,7 +443,10 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
         for (int i = 0; i < SPAN; ++i) yv[i] *= silu(zv[i]);
       }
       if (FULL && use_buf) {
-        if (act) buf_store_span<IO, SPAN>(make_rsrc(y + row0 * L, nrows * L * EB), vo_row, (uint32_t)(ts * EB), yv);
+        // unconditional for the same reason as the B/C loads: lanes of channels
+        // past dim store beyond the buffer's range, which the hardware drops
+        const uint32_t vo_y = act ? vo_row : 0x80000000u;
+        buf_store_span<IO, SPAN>(make_rsrc(y + row0 * L, nrows * L * EB), vo_y, (uint32_t)(ts * EB), yv);
       } else if (act && (FULL || valid > 0)) {
         store_span<IO, SPAN>(y, row + tf, valid, vec, yv);
       }
