@@ -126,7 +126,12 @@ __device__ __forceinline__ float zoh_psi(float u2, float E) {
 
 // Three waves per SIMD at N = 16 (about 160 VGPRs); at most 32 KB of LDS.
 // ZOH: the zero-order-hold input term, c = Delta phi(Delta A) in place of Delta.
-template <int N, int G, int K, typename IO, bool ZOH>
+// VEC: every row's lane spans are aligned for one vector access (an even
+// length).  It is a template parameter so that the chunk loop has no runtime
+// choice between a vector load and element loads: with one, the compiler cannot
+// count the memory operations in flight and waits for all of them (the previous
+// chunk's stores included) before using the next chunk's operands.
+template <int N, int G, int K, typename IO, bool ZOH, bool VEC>
 __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10))) void scan_bwd_kernel(
     const BwdDims dm, const BwdPtrs p) {
   using T = typename IO::T;
@@ -182,7 +187,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
   const int64_t ch = b * dm.dim + dc;
   const int64_t row = ch * L;
   const int64_t dt_row = dm.dt_row ? b * L : row;   // dt per (row, token) is shared by the row's channels
-  const bool vec = dm.vec != 0;
+  constexpr bool vec = VEC;
   const bool has_z = p.z != nullptr;
   const int64_t nck = (L + CK - 1) / CK;   // chunks of the whole sequence
   // this workgroup's chunks [kb, ke): its segment of the sequence
@@ -226,11 +231,12 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
     load_span<IO, kSpan>(x, row + t0 + j_own, valid, vec, f.x);
     load_span<IO, kSpan>(dt, dt_row + t0 + j_own, valid, vec, f.dt);
     if (grads) {
-      if (has_z) load_span<IO, kSpan>(z, row + t0 + j_own, valid, vec, f.z);
+      // without z, x stands in (its values are never used): no branch around the load
+      load_span<IO, kSpan>(has_z ? z : x, row + t0 + j_own, valid, vec, f.z);
       load_span<IO, kSpan>(dy, row + t0 + j_own, valid, vec, f.dy);
     }
     f.bc = make_float2(0.0f, 0.0f);
-    if (tid < CK * N && (WHOLE || t0 + tid / N < chunk_end(k)))
+    if ((CK * N >= THREADS || tid < CK * N) && (WHOLE || t0 + tid / N < chunk_end(k)))
       f.bc = reinterpret_cast<const float2*>(bc_row + t0 * (2 * N))[tid];
   };
   // Delta and Delta x of the owned tokens into LDS (zero Delta for padding
@@ -244,7 +250,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
       if constexpr (ZOH) s_dd[j_own + i][c] = make_float4(dl[i], dl[i] * xv[i], xv[i], dl[i] * dl[i] * xv[i]);
       else s_dd[j_own + i][c] = make_float2(dl[i], dl[i] * xv[i]);
     }
-    if (tid < CK * N) reinterpret_cast<float2*>(&s_bc[0][0])[tid] = f.bc;
+    if (CK * N >= THREADS || tid < CK * N) reinterpret_cast<float2*>(&s_bc[0][0])[tid] = f.bc;
   };
 
   // ---- 1. forward sweep: the state at every chunk start (unless the forward
@@ -315,7 +321,8 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
   const bool pw = (lane & 15) < K && (NS == 2 || (prow & 1) == 0);
   const int pwhich = NS == 2 ? (prow & 1) : (prow >> 1);   // 0: dB, 1: dC
   const int ps = NS == 2 ? (prow >> 1) : 0;
-  float* __restrict__ pdst = part_blk + (int64_t)(pwhich * N + sg * NS + ps) * CK;
+  // this lane's first partial within a chunk's block (bytes)
+  const uint32_t pofs = (uint32_t)((pwhich * N + sg * NS + ps) * CK * 4);
 
   Fetch f;
   if (ke == kfull) fetch(std::true_type{}, ke - 1, true, f);
@@ -374,6 +381,8 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
   auto chunk = [&](auto full_tag, int64_t k) {
     constexpr bool FULL = decltype(full_tag)::value;
     const int64_t t0 = k * CK;
+    // the chunk's block of dB/dC partials (NPART outputs x CK tokens, fp32)
+    const __amdgpu_buffer_rsrc_t rs_part = make_rsrc(part_blk + k * (NPART * CK), NPART * CK * 4);
     const int64_t t1 = chunk_end(k);
     const int nj = FULL ? CK : (int)(t1 - t0);
     const int64_t tf = t0 + j_own;
@@ -396,7 +405,9 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
     if (k > kb) {
       fetch(std::true_type{}, k - 1, true, f);   // every chunk before the last is whole
 #pragma unroll
-      for (int s = 0; s < NS; ++s) ckn[s] = act ? ck_row[(k - 1) * ck_stride + s] : 0.0f;
+      // inactive lanes read their clamped (valid) row: an unmasked load, whose
+      // values give them finite states and, with their zero dy, zero gradients
+      for (int s = 0; s < NS; ++s) ckn[s] = ck_row[(k - 1) * ck_stride + s];
     }
     __syncthreads();
 
@@ -512,11 +523,16 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
       // the dB/dC partials of a group of consecutive tokens, stored once the
       // group is done (padding tokens of the ragged last chunk write zeros,
       // which nothing reads)
+      // Every lane issues the store: lanes that hold no sum store past the end of
+      // the chunk's block, which the hardware drops.  A masked store could be
+      // skipped as a whole, and the compiler would then wait for every memory
+      // operation in flight before using the next chunk's operands.
       constexpr int SV = (CK % 4 == 0) ? 4 : 2;
-      if (j % SV == 0 && pw) {
-        float* const q = pdst + k * (NPART * CK) + j;
-        if constexpr (SV == 4) *reinterpret_cast<float4*>(q) = make_float4(uo[j], uo[j + 1], uo[j + 2], uo[j + 3]);
-        else *reinterpret_cast<float2*>(q) = make_float2(uo[j], uo[j + 1]);
+      if (j % SV == 0) {
+        float pv[SV];
+#pragma unroll
+        for (int e = 0; e < SV; ++e) pv[e] = uo[j + e];
+        buf_store_span<F32, SV>(rs_part, pw ? pofs + (uint32_t)(j * 4) : 0x80000000u, 0u, pv);
       }
     }
     __syncthreads();
@@ -789,7 +805,10 @@ hipError_t launch_segment_agg_n(const BwdDims& dm, const BwdPtrs& p, hipStream_t
 template <int N, int G, int K, typename IO, bool ZOH>
 hipError_t launch_bwd_t(const BwdDims& dm, const BwdPtrs& p, hipStream_t s) {
   const int64_t nwg = dm.cblocks * dm.batch * dm.nseg;
-  hipLaunchKernelGGL((scan_bwd_kernel<N, G, K, IO, ZOH>), dim3((unsigned)nwg), dim3(64 * G), 0, s, dm, p);
+  if (dm.vec)
+    hipLaunchKernelGGL((scan_bwd_kernel<N, G, K, IO, ZOH, true>), dim3((unsigned)nwg), dim3(64 * G), 0, s, dm, p);
+  else
+    hipLaunchKernelGGL((scan_bwd_kernel<N, G, K, IO, ZOH, false>), dim3((unsigned)nwg), dim3(64 * G), 0, s, dm, p);
   return hipGetLastError();
 }
 
