@@ -76,6 +76,19 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
   __shared__ float2 s_dd[SHARE_DD ? T : 1][CPB + 1];
   __shared__ float s_part[(SHARE_DD && !AGG) ? T : 1][G][CPB + 1];
   __shared__ __attribute__((aligned(16))) float s_bc[T * 2 * N];   // the tile's B_n, C_n (token, n, {B, C})
+  // A whole tile's y goes through LDS: the owners write their spans in phase C,
+  // and after the next tile's first barrier every thread stores 8 bytes, the
+  // lanes of a row covering its whole segment of the tile in one instruction.
+  // Stored straight from the owners, each wave put 16 bytes on each of the
+  // block's rows per tile: four times the write requests.  Used when the block's
+  // tile of y is exactly 8 bytes per thread and a row's segment of the tile is
+  // at most half a cache line (64 bytes: the bf16 plans).  The fp32 four-lane
+  // plan's waves already fill a 128-byte line per row and tile, and staging
+  // only cost it time (0.148 -> 0.151 ms at the 130M shape).
+  constexpr int EBY = (int)sizeof(typename IO::T);
+  constexpr bool STAGE_Y = !AGG && SHARE_DD && CPB * T * EBY == 8 * THREADS && T * EBY <= 64;
+  constexpr int YROW = (T * EBY + 8) / 4;   // words per staged row (padded against bank conflicts)
+  __shared__ __attribute__((aligned(16))) uint32_t s_y[STAGE_Y ? CPB : 1][STAGE_Y ? YROW : 2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -228,6 +241,25 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
   // compile-time tag) means all T tokens lie inside the chunk: no per-token
   // masks, no guards in the inner loop.  NEXT_BUF (compile-time): the next tile
   // is whole and goes through the buffer resources.
+  // The staged tile of y (token y_pend_ts onward; -1: none) to HBM: thread q
+  // stores bytes 8 (q % PPR) .. + 7 of row q / PPR of the tile.  With nothing
+  // staged, or for rows past dim, the offset lies beyond the buffer and the
+  // hardware drops the store, so every tile issues the same stores.
+  int64_t y_pend_ts = -1;
+  auto flush_y = [&]() {
+    if constexpr (STAGE_Y) {
+      constexpr int PPR = T * EBY / 8;   // 8-byte pieces per row
+      const int r = tid / PPR, q = tid % PPR;
+      const uint2 v = *reinterpret_cast<const uint2*>(&s_y[r][2 * q]);
+      const bool ok = y_pend_ts >= 0 && r < nrows;
+      const uint32_t vo = ok ? (uint32_t)(r * L * EB + q * 8) : 0x80000000u;
+      const uint32_t so = (uint32_t)((y_pend_ts < 0 ? 0 : y_pend_ts) * EB);
+      typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+      const u2 d = {v.x, v.y};
+      __builtin_amdgcn_raw_buffer_store_b64(d, make_rsrc(y + row0 * L, nrows * L * EB), vo, so, 0);
+      y_pend_ts = -1;
+    }
+  };
   auto tile = [&](auto full_tag, auto ck_tag, auto nbuf_tag, int64_t ts, const Spans& cur, Spans& nxt) {
     constexpr bool FULL = decltype(full_tag)::value;
     constexpr bool CKPT = decltype(ck_tag)::value && CKPT_K;
@@ -278,6 +310,9 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
       for (int i = 0; i < SPAN; ++i) s_dd[w * TPW + hk * SPAN + i][c] = make_float2(dl[i], dx[i]);
     }
     __syncthreads();
+    if constexpr (STAGE_Y) {
+      if (use_buf) flush_y();
+    }
     // Phase B runs at a raised wave priority and phases C and A at the
     // default, so a SIMD's issue favours the waves sweeping the state over
     // those of other workgroups in their short owner phases (5-6% faster at
@@ -442,7 +477,21 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
 #pragma unroll
         for (int i = 0; i < SPAN; ++i) yv[i] *= silu(zv[i]);
       }
-      if (FULL && use_buf) {
+      if (STAGE_Y && FULL && use_buf) {
+        // into the staged tile, stored after the next tile's first barrier
+        uint32_t o[SpanT<IO, SPAN>::kWords];
+        if constexpr (IO::kPerSpan == 4) {
+#pragma unroll
+          for (int i = 0; i < SPAN; ++i) o[i] = __float_as_uint(yv[i]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < SPAN; i += 2) o[i >> 1] = pack_bf16x2(yv[i], yv[i + 1]);
+        }
+        const int w0 = (w * TPW + hk * SPAN) * EBY / 4;   // first word of this lane's span
+#pragma unroll
+        for (int q = 0; q < SpanT<IO, SPAN>::kWords; ++q) s_y[STAGE_Y ? c : 0][w0 + q] = o[q];
+        y_pend_ts = ts;
+      } else if (FULL && use_buf) {
         // unconditional for the same reason as the B/C loads: lanes of channels
         // past dim store beyond the buffer's range, which the hardware drops
         const uint32_t vo_y = act ? vo_row : 0x80000000u;
@@ -467,6 +516,12 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
     if (ts + T <= t1) tile(std::true_type{}, CkTag{}, std::false_type{}, ts, S0, S1);
     else tile(std::false_type{}, CkTag{}, std::false_type{}, ts, S0, S1);
     S0 = S1;
+  }
+  if constexpr (STAGE_Y) {
+    if (use_buf && y_pend_ts >= 0) {   // the chunk's last staged tile
+      __syncthreads();
+      flush_y();
+    }
   }
 
   if (act) {
