@@ -633,7 +633,8 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
 // * K per stage, which divides every segment length): the owner of each token
 // stages Delta, dr (and Delta x), and every lane runs its components back
 // through the stage.
-template <int N, int G, int K, typename IO, bool ZOH, bool FWD>
+// VEC: as for scan_bwd_kernel (no runtime choice between vector and element loads).
+template <int N, int G, int K, typename IO, bool ZOH, bool FWD, bool VEC>
 __global__ __launch_bounds__(64 * G) void bwd_segment_agg_kernel(const BwdDims dm, const BwdPtrs p) {
   using T = typename IO::T;
   constexpr int CPB = 64 / K;
@@ -673,7 +674,7 @@ __global__ __launch_bounds__(64 * G) void bwd_segment_agg_kernel(const BwdDims d
   const int64_t ch = b * dm.dim + dc;
   const int64_t row = ch * L;
   const int64_t dt_row = dm.dt_row ? b * L : row;
-  const bool vec = (L % AS) == 0;   // every lane's span is 16-byte aligned
+  constexpr bool vec = VEC;   // every lane's span is 16-byte aligned
   const bool has_z = p.z != nullptr;
   const int64_t t_begin = seg * dm.seg_len;
   const int64_t t_end = t_begin + dm.seg_len < L ? t_begin + dm.seg_len : L;
@@ -695,18 +696,23 @@ __global__ __launch_bounds__(64 * G) void bwd_segment_agg_kernel(const BwdDims d
     uint32_t x[FWD ? SW : 1], dt[SW], z[SW], dy[SW];
     BCV bc[CPT];
   };
-  auto fetch = [&](int64_t k, Fetch& f) {
+  // WHOLE (a compile-time tag): every token of stage k lies inside the segment,
+  // so no load of the stage is masked or branched (which would make the
+  // compiler wait for every memory operation in flight before the next use)
+  auto fetch = [&](auto whole_tag, int64_t k, Fetch& f) {
+    constexpr bool WHOLE = decltype(whole_tag)::value;
     const int64_t t0 = k * ST;
     const int64_t v = t_end - (t0 + j_own);
-    const int valid = (int)(v < 0 ? 0 : (v < AS ? v : AS));
+    const int valid = WHOLE ? AS : (int)(v < 0 ? 0 : (v < AS ? v : AS));
     if constexpr (FWD) load_span<IO, AS>(x, row + t0 + j_own, valid, vec, f.x);
     load_span<IO, AS>(dt, dt_row + t0 + j_own, valid, vec, f.dt);
-    if (has_z) load_span<IO, AS>(z, row + t0 + j_own, valid, vec, f.z);
+    // without z, x stands in (its values are never used)
+    load_span<IO, AS>(has_z ? z : x, row + t0 + j_own, valid, vec, f.z);
     load_span<IO, AS>(dy, row + t0 + j_own, valid, vec, f.dy);
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
       const int idx = tid + q * THREADS;
-      const bool in = idx < ST * N && t0 + idx / N < t_end;
+      const bool in = (ST * N % THREADS == 0 || idx < ST * N) && (WHOLE || t0 + idx / N < t_end);
       if constexpr (FWD) f.bc[q] = in ? reinterpret_cast<const float2*>(bc_row)[t0 * N + idx] : make_float2(0.0f, 0.0f);
       else f.bc[q] = in ? bc_row[(t0 * N + idx) * 2 + 1] : 0.0f;
     }
@@ -721,7 +727,11 @@ __global__ __launch_bounds__(64 * G) void bwd_segment_agg_kernel(const BwdDims d
   }
   float dsum = 0.0f;
   Fetch f;
-  fetch(se - 1, f);
+  // the segment's stages, last to first; only the last (at the sequence's end)
+  // can be partly outside it
+  const int64_t swhole = t_end / ST;   // stages below swhole are whole
+  if (se - 1 < swhole) fetch(std::true_type{}, se - 1, f);
+  else fetch(std::false_type{}, se - 1, f);
   for (int64_t k = se - 1; k >= sb; --k) {
     const int64_t nj = t_end - k * ST;   // tokens of the stage inside the segment (ST or fewer)
 #pragma unroll
@@ -739,9 +749,9 @@ __global__ __launch_bounds__(64 * G) void bwd_segment_agg_kernel(const BwdDims d
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
       const int idx = tid + q * THREADS;
-      if (idx < ST * N) s_bc[idx / N][idx % N] = f.bc[q];
+      if (ST * N % THREADS == 0 || idx < ST * N) s_bc[idx / N][idx % N] = f.bc[q];
     }
-    if (k > sb) fetch(k - 1, f);
+    if (k > sb) fetch(std::true_type{}, k - 1, f);   // every stage before the last is whole
     __syncthreads();
 #pragma unroll
     for (int j = ST - 1; j >= 0; --j) {
@@ -785,7 +795,10 @@ __global__ __launch_bounds__(64 * G) void bwd_segment_agg_kernel(const BwdDims d
 template <int N, int G, int K, typename IO, bool ZOH, bool FWD>
 hipError_t launch_segment_agg_t(const BwdDims& dm, const BwdPtrs& p, hipStream_t s) {
   const int64_t nwg = dm.cblocks * dm.batch * (dm.nseg - (FWD ? 0 : 1));
-  hipLaunchKernelGGL((bwd_segment_agg_kernel<N, G, K, IO, ZOH, FWD>), dim3((unsigned)nwg), dim3(64 * G), 0, s, dm, p);
+  if (dm.seqlen % IO::kPerSpan == 0)
+    hipLaunchKernelGGL((bwd_segment_agg_kernel<N, G, K, IO, ZOH, FWD, true>), dim3((unsigned)nwg), dim3(64 * G), 0, s, dm, p);
+  else
+    hipLaunchKernelGGL((bwd_segment_agg_kernel<N, G, K, IO, ZOH, FWD, false>), dim3((unsigned)nwg), dim3(64 * G), 0, s, dm, p);
   return hipGetLastError();
 }
 
