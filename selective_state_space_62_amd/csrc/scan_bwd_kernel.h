@@ -131,7 +131,9 @@ __device__ __forceinline__ float zoh_psi(float u2, float E) {
 // choice between a vector load and element loads: with one, the compiler cannot
 // count the memory operations in flight and waits for all of them (the previous
 // chunk's stores included) before using the next chunk's operands.
-template <int N, int G, int K, typename IO, bool ZOH, bool VEC>
+// SIN: the reverse pass's operands go through LDS in whole row pieces (bf16,
+// first order, rows a multiple of 8 tokens; see s_in below).
+template <int N, int G, int K, typename IO, bool ZOH, bool VEC, bool SIN>
 __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10))) void scan_bwd_kernel(
     const BwdDims dm, const BwdPtrs p) {
   using T = typename IO::T;
@@ -166,6 +168,21 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
   constexpr int ROWW = 128 / 4 + 2;          // words per staged row
   static_assert(GT % CK == 0 && kSpan == 2, "a group holds whole chunks; a lane owns two tokens");
   __shared__ __attribute__((aligned(16))) uint32_t s_out[STAGE ? 3 : 1][STAGE ? CPB : 1][ROWW];
+  // With SIN the reverse pass's operand rows (x, dt, z, dy) go through LDS as
+  // well, in 16-byte row spans: each wave loads the chunk's 32 bytes of 8 rows
+  // of all four operands (two lanes per row and operand), so a row's piece is
+  // requested once per chunk instead of a quarter by each wave.  When a
+  // workgroup's rows share their offset within the memory pages (rows of
+  // 2^20 bf16 tokens lie 2 MB apart), the vector L1 loses the line between
+  // the waves' requests and every quarter went to L2.  Chunk k's pieces sit in
+  // buffer k & 1, written at the end of chunk k + 1.  Rows are padded to 10
+  // words so that the owners' 4-byte reads fall in distinct banks.
+  constexpr bool STAGE_IN = SIN;
+  static_assert(!SIN || (STAGE && sizeof(T) == 2 && VEC && G == 4 && K == 2 && CK == 16),
+                "whole-piece loads: bf16 first order, 4 waves of 32 channels, 16-token chunks");
+  constexpr int IN_ROWW = CK * (int)sizeof(T) / 4 + 2;
+  __shared__ __attribute__((aligned(16))) uint32_t s_in[STAGE_IN ? 2 : 1][STAGE_IN ? 4 : 1][STAGE_IN ? CPB : 1]
+                                                       [STAGE_IN ? IN_ROWW : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -239,6 +256,46 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
     if ((CK * N >= THREADS || tid < CK * N) && (WHOLE || t0 + tid / N < chunk_end(k)))
       f.bc = reinterpret_cast<const float2*>(bc_row + t0 * (2 * N))[tid];
   };
+  // The reverse pass's loader lanes: operand in_a (x, dt, z, dy), row in_r of
+  // the block, 16-byte half in_h of the row's chunk piece
+  struct FetchIn {
+    uint32_t v[4];
+    float2 bc;
+  };
+  const int in_a = lane >> 4;
+  const int in_r = w * 8 + ((lane >> 1) & 7);
+  const int in_h = lane & 1;
+  const int64_t in_d = cb * CPB + in_r;
+  const int64_t in_row = (b * dm.dim + (in_d < dm.dim ? in_d : dm.dim - 1)) * L;   // clamped like dc
+  const T* __restrict__ in_src = in_a == 0 ? x : (in_a == 1 ? dt : (in_a == 2 ? (has_z ? z : x) : dy));
+  const int64_t in_base = (in_a == 1 && dm.dt_row ? b * L : in_row) + in_h * 8;
+  auto fetch_in = [&](auto whole_tag, int64_t k, FetchIn& f) {
+    constexpr bool WHOLE = decltype(whole_tag)::value;
+    const int64_t t0 = k * CK;
+    int valid = 8;
+    if constexpr (!WHOLE) {
+      const int64_t v = chunk_end(k) - (t0 + in_h * 8);
+      valid = v < 0 ? 0 : (v < 8 ? (int)v : 8);
+    }
+    if constexpr (STAGE_IN) load_span<IO, 8>(in_src, in_base + t0, valid, true, f.v);
+    f.bc = make_float2(0.0f, 0.0f);
+    if ((CK * N >= THREADS || tid < CK * N) && (WHOLE || t0 + tid / N < chunk_end(k)))
+      f.bc = reinterpret_cast<const float2*>(bc_row + t0 * (2 * N))[tid];
+  };
+  // a fetched chunk into LDS buffer bi, with its B and C
+  auto put_in = [&](int bi, const FetchIn& f) {
+    uint32_t* dst = &s_in[STAGE_IN ? bi : 0][STAGE_IN ? in_a : 0][STAGE_IN ? in_r : 0][STAGE_IN ? in_h * 4 : 0];
+    if constexpr (STAGE_IN) {
+      *reinterpret_cast<uint2*>(dst) = make_uint2(f.v[0], f.v[1]);
+      *reinterpret_cast<uint2*>(dst + 2) = make_uint2(f.v[2], f.v[3]);
+    }
+    if (CK * N >= THREADS || tid < CK * N) reinterpret_cast<float2*>(&s_bc[0][0])[tid] = f.bc;
+  };
+  // operand o (0 x, 1 dt, 2 z, 3 dy) of this lane's two owned tokens from buffer bi
+  auto in_word = [&](int bi, int o) -> uint32_t {
+    return s_in[STAGE_IN ? bi : 0][STAGE_IN ? o : 0][STAGE_IN ? c : 0][STAGE_IN ? j_own >> 1 : 0];
+  };
+
   // Delta and Delta x of the owned tokens into LDS (zero Delta for padding
   // tokens), and the chunk's B and C
   auto stage = [&](int valid, const Fetch& f, float (&xv)[kSpan], float (&dl)[kSpan], float (&v2)[kSpan]) {
@@ -325,8 +382,16 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
   const uint32_t pofs = (uint32_t)((pwhich * N + sg * NS + ps) * CK * 4);
 
   Fetch f;
-  if (ke == kfull) fetch(std::true_type{}, ke - 1, true, f);
-  else fetch(std::false_type{}, ke - 1, true, f);
+  FetchIn fi;
+  if constexpr (STAGE_IN) {
+    if (ke == kfull) fetch_in(std::true_type{}, ke - 1, fi);
+    else fetch_in(std::false_type{}, ke - 1, fi);
+    put_in((int)((ke - 1) & 1), fi);
+    __syncthreads();
+  } else {
+    if (ke == kfull) fetch(std::true_type{}, ke - 1, true, f);
+    else fetch(std::false_type{}, ke - 1, true, f);
+  }
   float ckn[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) ckn[s] = act ? ck_row[(ke - 1) * ck_stride + s] : 0.0f;
@@ -388,13 +453,26 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
     const int64_t tf = t0 + j_own;
     const int valid = FULL ? kSpan : own_valid(k);
     float xv[kSpan], dl[kSpan], v2[kSpan];
-    stage(valid, f, xv, dl, v2);
     // z and dy of the owned tokens stay raw until the owners use them
     uint32_t cz[SW], cdy[SW];
+    const int bi = (int)(k & 1);
+    if constexpr (STAGE_IN) {
+      const uint32_t xw[1] = {in_word(bi, 0)}, dw[1] = {in_word(bi, 1)};
 #pragma unroll
-    for (int q = 0; q < SW; ++q) {
-      cz[q] = f.z[q];
-      cdy[q] = f.dy[q];
+      for (int i = 0; i < kSpan; ++i) {
+        xv[i] = span_elem<IO>(xw, i);
+        const float dtv = span_elem<IO>(dw, i);
+        v2[i] = fmaf(dtv, kLog2e, bias2);
+        dl[i] = (i < valid) ? softplus_dt(dtv, bias2) : 0.0f;
+        s_dd[j_own + i][c] = make_float2(dl[i], dl[i] * xv[i]);
+      }
+    } else {
+      stage(valid, f, xv, dl, v2);
+#pragma unroll
+      for (int q = 0; q < SW; ++q) {
+        cz[q] = f.z[q];
+        cdy[q] = f.dy[q];
+      }
     }
     float hs[CK + 1][NS];   // hs[j] = the state before chunk token j
     // Es[j] = Abar of chunk token j, kept for the adjoint step (first order; the
@@ -403,7 +481,9 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
 #pragma unroll
     for (int s = 0; s < NS; ++s) hs[0][s] = ckn[s];
     if (k > kb) {
-      fetch(std::true_type{}, k - 1, true, f);   // every chunk before the last is whole
+      // every chunk before the last is whole
+      if constexpr (STAGE_IN) fetch_in(std::true_type{}, k - 1, fi);
+      else fetch(std::true_type{}, k - 1, true, f);
 #pragma unroll
       // inactive lanes read their clamped (valid) row: an unmasked load, whose
       // values give them finite states and, with their zero dy, zero gradients
@@ -446,6 +526,10 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
           for (int g = 0; g < G; ++g) r += s_pp[j][g][c].x;
         }
         r = fmaf(skip, xv[i], r);
+        if constexpr (STAGE_IN) {
+          cdy[0] = in_word(bi, 3);
+          cz[0] = in_word(bi, 2);
+        }
         const float dyv = act ? span_elem<IO>(cdy, i) : 0.0f;   // padding tokens load as zero
         float gate = 1.0f;
         dzv[i] = 0.0f;
@@ -575,6 +659,9 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
         const float u = bc_channel_sum<1, K>(d0, d1);
         if ((lane & 15) < K && (prow & 1) == 0 && (FULL || t0 + j_own + (prow >> 1) < t1))
           part_blk[(k * NPART + NOUT) * CK + j_own + (prow >> 1)] = u;
+      }
+      if constexpr (STAGE_IN) {
+        if (k > kb) put_in((int)((k - 1) & 1), fi);   // LDS free: chunk k + 1 is done with it
       }
     }
     __syncthreads();
@@ -818,10 +905,23 @@ hipError_t launch_segment_agg_n(const BwdDims& dm, const BwdPtrs& p, hipStream_t
 template <int N, int G, int K, typename IO, bool ZOH>
 hipError_t launch_bwd_t(const BwdDims& dm, const BwdPtrs& p, hipStream_t s) {
   const int64_t nwg = dm.cblocks * dm.batch * dm.nseg;
+  // Whole-piece operand loads for rows at least 1 MB long (bf16, first order):
+  // there the workgroup's rows share their offset in the memory pages (the
+  // million-token backward 58.0 -> 48.0 ms); at shorter rows they cost about
+  // 0.5% (2.8B-shaped layer) and buy nothing.
+  if constexpr (!ZOH && sizeof(typename IO::T) == 2 && G == 4 && K == 2) {
+    if (dm.vec && dm.seqlen % 8 == 0 && dm.seqlen * 2 >= (int64_t(1) << 20)) {
+      hipLaunchKernelGGL((scan_bwd_kernel<N, G, K, IO, ZOH, true, true>), dim3((unsigned)nwg), dim3(64 * G), 0, s,
+                         dm, p);
+      return hipGetLastError();
+    }
+  }
   if (dm.vec)
-    hipLaunchKernelGGL((scan_bwd_kernel<N, G, K, IO, ZOH, true>), dim3((unsigned)nwg), dim3(64 * G), 0, s, dm, p);
+    hipLaunchKernelGGL((scan_bwd_kernel<N, G, K, IO, ZOH, true, false>), dim3((unsigned)nwg), dim3(64 * G), 0, s, dm,
+                       p);
   else
-    hipLaunchKernelGGL((scan_bwd_kernel<N, G, K, IO, ZOH, false>), dim3((unsigned)nwg), dim3(64 * G), 0, s, dm, p);
+    hipLaunchKernelGGL((scan_bwd_kernel<N, G, K, IO, ZOH, false, false>), dim3((unsigned)nwg), dim3(64 * G), 0, s,
+                       dm, p);
   return hipGetLastError();
 }
 

@@ -11,7 +11,9 @@ are multiples of 64 tokens; the cases cut sequences into 2 to 10 segments, most
 with a ragged last one, and cover every state size, both I/O types, the
 zero-order hold, one dt per (row, token) and forward-saved checkpoints.  The
 million-token workload runs in the automatic split, the oracle checking 64
-channels over every token.
+channels over every token.  Rows of 2^19 tokens and more (bf16) run the reverse
+pass with its operands loaded through LDS in whole row pieces; two such cases
+are checked on every channel.
 """
 import zlib
 
@@ -157,6 +159,42 @@ def test_bwd_seg_dt_per_row(ss, o, dev):
     log("  shared dt gradient rel-L2 %.3e" % e)
     assert e <= 5e-5
     _compare(g, r, "f32", "bwd seg dt per row", skip=("ddt",))
+
+
+# Rows of at least 2^19 bf16 tokens (1 MB) take the reverse pass's whole-piece
+# operand loads through LDS.  (batch, D, N, L, optional inputs, one dt per row):
+# ragged last chunks, a second channel block with inactive channels, batch rows
+# past the first, N = 8 and 16, and the shared dt's row.
+LONG_ROWS = [
+    (2, 40, 16, (1 << 19) + 40, True, False),
+    (2, 33, 8, (1 << 19) + 8, False, True),
+]
+
+
+@pytest.mark.parametrize("case", LONG_ROWS, ids=["x".join(map(str, c[:4])) + ("-dtrow" if c[5] else "")
+                                                 for c in LONG_ROWS])
+def test_bwd_long_rows_bf16(ss, o, dev, case):
+    import torch
+    batch, D, N, L, optional, dt_row = case
+    log("bwd long rows bf16 %s" % (case,))
+    rng = np.random.default_rng(zlib.crc32(repr(("long-rows", case)).encode()))
+    raw, par, f64 = _problem(rng, batch, D, N, L, "bf16", optional)
+    if dt_row:
+        row = inputs.f32_to_bf16_bits((0.5 * rng.standard_normal((batch, L))).astype(np.float32))
+        full = np.ascontiguousarray(np.broadcast_to(row[:, None, :], (batch, D, L)))
+        raw["dt"], f64["dt"] = full, inputs.raw_to_f64(full, "bf16")
+    t, p = _upload(raw, par, "bf16", dev)
+    if dt_row:
+        t["dt"] = to_dev(row, "bf16", dev)
+    g = _bwd(ss, t, p)
+    del t
+    torch.cuda.empty_cache()
+    r = _oracle(o, f64, par)
+    if dt_row:
+        e = rel_l2(to_f64(g["ddt"]), r["ddt"].sum(axis=1))
+        log("  shared dt gradient rel-L2 %.3e" % e)
+        assert e <= 2e-2
+    _compare(g, r, "bf16", "bwd long rows %s" % (case,), skip=("ddt",) if dt_row else ())
 
 
 def test_bwd_seg_from_checkpoints(ss, o, dev):
