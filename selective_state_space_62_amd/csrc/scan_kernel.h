@@ -42,7 +42,8 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
 // |A| is at least 1/16 (the (E - 1) x B / A form); the other launch takes the
 // rest (the phi form).  Each instantiation carries one form, so neither pays
 // the other's registers.
-template <int N, int G, int K, typename IO, bool AGG, bool ZOH, bool CKPT_K, bool ZFAST = false>
+// ROWS: rows of at least 1 MB (see ROWOWN below).
+template <int N, int G, int K, typename IO, bool AGG, bool ZOH, bool CKPT_K, bool ZFAST = false, bool ROWS = false>
 __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 && N / (G * K) <= 2 ? 5 : 1, 10))) void scan_kernel(
     const ScanDims dm, const typename IO::T* __restrict__ x, const typename IO::T* __restrict__ dt,
     const typename IO::T* __restrict__ z, const typename IO::T* __restrict__ Bm,
@@ -86,7 +87,22 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
   // plan's waves already fill a 128-byte line per row and tile, and staging
   // only cost it time (0.148 -> 0.151 ms at the 130M shape).
   constexpr int EBY = (int)sizeof(typename IO::T);
-  constexpr bool STAGE_Y = !AGG && SHARE_DD && CPB * T * EBY == 8 * THREADS && T * EBY <= 64;
+  // Owners of the per-token work (phases A and C).  With ROWOWN (rows of at
+  // least 1 MB; bf16, four waves of 32 channels, 32-token tiles) lane l of wave
+  // w owns tokens SPAN (l % 8) .. + SPAN - 1 of row 8 w + l / 8: the 8 lanes of
+  // a row take its 64-byte segment of the tile, so each wave's load or store
+  // covers that segment of 8 rows in one instruction, and y needs no staging.
+  // Owning a span of its own channel, each wave reads 16 bytes of all 32 rows:
+  // when the rows share their offset within the memory pages (2^20-token rows
+  // lie 2 MB apart) the vector L1 loses the line between the waves' requests,
+  // and every piece goes to L2 (million-token forward 17.0 -> 14.1 ms).  At
+  // shorter rows that costs nothing, while the owners' reads of the readout
+  // partials meet two-way bank conflicts (2.8B-shaped layer 5% slower), so
+  // there a lane owns SPAN tokens of its own channel.
+  constexpr bool ROWOWN = ROWS;
+  static_assert(!ROWS || (SHARE_DD && K == 2 && G == 4 && CPB == 8 * G && T * EBY == 64 && SPAN * 8 == T),
+                "row segments: bf16, four waves of 32 channels, 32-token tiles");
+  constexpr bool STAGE_Y = !ROWOWN && !AGG && SHARE_DD && CPB * T * EBY == 8 * THREADS && T * EBY <= 64;
   constexpr int YROW = (T * EBY + 8) / 4;   // words per staged row (padded against bank conflicts)
   __shared__ __attribute__((aligned(16))) uint32_t s_y[STAGE_Y ? CPB : 1][STAGE_Y ? YROW : 2];
 
@@ -96,6 +112,8 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
   const int hk = lane % K;                // lane of the channel
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int sg = w * K + hk;              // state group of this lane
+  const int oc = ROWOWN ? w * 8 + (lane >> 3) : c;                  // owner: channel within the block
+  const int otok = ROWOWN ? (lane & 7) * SPAN : w * TPW + hk * SPAN;   // owner: first token in a tile
 
   // logical block -> (chunk, batch row, channel block), channel block fastest
   const int64_t cblocks = (dm.dim + CPB - 1) / CPB;
@@ -115,6 +133,12 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
   const int64_t ch = b * dm.dim + dc;
   const int64_t row = ch * L;
   const int64_t dt_row = dm.dt_row ? b * L : row;   // dt per (row, token) is shared by the row's channels
+  // the owner's channel (the same as the lane's own unless ROWOWN)
+  const int64_t od = cb * CPB + oc;
+  const bool oact = od < dm.dim;
+  const int64_t odc = oact ? od : dm.dim - 1;
+  const int64_t orow = (b * dm.dim + odc) * L;
+  const int64_t odt_row = dm.dt_row ? b * L : orow;
   const bool vec = dm.vec != 0;
   const bool has_z = z != nullptr;
 
@@ -140,8 +164,9 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
     const bool wg_fast = __syncthreads_and(ok) != 0;
     if (wg_fast != ZFAST) return;
   }
-  const float bias2 = dt_bias ? dt_bias[dc] * kLog2e : 0.0f;
-  const float skip = Dskip ? Dskip[dc] : 0.0f;
+  // the owner's (phases A and C)
+  const float bias2 = dt_bias ? dt_bias[odc] * kLog2e : 0.0f;
+  const float skip = Dskip ? Dskip[odc] : 0.0f;
 
   float h[NS];
   {
@@ -203,11 +228,11 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
   const __amdgpu_buffer_rsrc_t rs_z = has_z ? make_rsrc(z + row0 * L, nrows * L * EB) : rs_x;
   const __amdgpu_buffer_rsrc_t rs_dt =
       dm.dt_row ? make_rsrc(dt + b * L, L * EB) : make_rsrc(dt + row0 * L, nrows * L * EB);
-  const uint32_t vo_row = (uint32_t)(((dc - cb * CPB) * L + w * TPW + hk * SPAN) * EB);
-  const uint32_t vo_dt = dm.dt_row ? (uint32_t)((w * TPW + hk * SPAN) * EB) : vo_row;
+  const uint32_t vo_row = (uint32_t)(((odc - cb * CPB) * L + otok) * EB);
+  const uint32_t vo_dt = dm.dt_row ? (uint32_t)(otok * EB) : vo_row;
 
   // first token of the span this lane owns in the tile starting at ts
-  auto own_first = [&](int64_t ts) { return ts + w * TPW + hk * SPAN; };
+  auto own_first = [&](int64_t ts) { return ts + otok; };
   auto own_valid = [&](int64_t first) {
     const int64_t v = t1 - first;
     return (int)(v < 0 ? 0 : (v < SPAN ? v : SPAN));
@@ -218,7 +243,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
     const uint32_t so = (uint32_t)(ts * EB);
     buf_load_span<IO, SPAN>(rs_x, vo_row, so, S.x);
     buf_load_span<IO, SPAN>(rs_dt, vo_dt, so, S.dt);
-    buf_load_span<IO, SPAN>(rs_z, vo_row, so, S.z);
+    if constexpr (!AGG) buf_load_span<IO, SPAN>(rs_z, vo_row, so, S.z);   // the aggregate pass has no gate
     // (B or C differs between lanes, so the run comes through a plain vector load)
     if (bc_act) load_span<IO, 4>(bc_src, ts + 4 * bc_g, 4, true, S.bc);
   };
@@ -231,9 +256,9 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
   {
     const int64_t tf = own_first(t0);
     const int valid = own_valid(tf);
-    load_span<IO, SPAN>(x, row + tf, valid, vec, S0.x);
-    load_span<IO, SPAN>(dt, dt_row + tf, valid, vec, S0.dt);
-    if (has_z) load_span<IO, SPAN>(z, row + tf, valid, vec, S0.z);
+    load_span<IO, SPAN>(x, orow + tf, valid, vec, S0.x);
+    load_span<IO, SPAN>(dt, odt_row + tf, valid, vec, S0.dt);
+    if (!AGG && has_z) load_span<IO, SPAN>(z, orow + tf, valid, vec, S0.z);
     load_bc_tile(t0, S0);
   }
 
@@ -293,21 +318,21 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
       load_buf_tile(ts + T, nxt);
     } else if (vec && ts + 2 * T <= t1) {
       const int64_t tn = tf + T;
-      load_span<IO, SPAN>(x, row + tn, SPAN, true, nxt.x);
-      load_span<IO, SPAN>(dt, dt_row + tn, SPAN, true, nxt.dt);
-      if (has_z) load_span<IO, SPAN>(z, row + tn, SPAN, true, nxt.z);
+      load_span<IO, SPAN>(x, orow + tn, SPAN, true, nxt.x);
+      load_span<IO, SPAN>(dt, odt_row + tn, SPAN, true, nxt.dt);
+      if (!AGG && has_z) load_span<IO, SPAN>(z, orow + tn, SPAN, true, nxt.z);
       load_bc_tile(ts + T, nxt);
     } else if (ts + T < t1) {
       const int64_t tn = tf + T;
       const int validn = own_valid(tn);
-      load_span<IO, SPAN>(x, row + tn, validn, vec, nxt.x);
-      load_span<IO, SPAN>(dt, dt_row + tn, validn, vec, nxt.dt);
-      if (has_z) load_span<IO, SPAN>(z, row + tn, validn, vec, nxt.z);
+      load_span<IO, SPAN>(x, orow + tn, validn, vec, nxt.x);
+      load_span<IO, SPAN>(dt, odt_row + tn, validn, vec, nxt.dt);
+      if (!AGG && has_z) load_span<IO, SPAN>(z, orow + tn, validn, vec, nxt.z);
       load_bc_tile(ts + T, nxt);
     }
     if constexpr (SHARE_DD) {
 #pragma unroll
-      for (int i = 0; i < SPAN; ++i) s_dd[w * TPW + hk * SPAN + i][c] = make_float2(dl[i], dx[i]);
+      for (int i = 0; i < SPAN; ++i) s_dd[otok + i][oc] = make_float2(dl[i], dx[i]);
     }
     __syncthreads();
     if constexpr (STAGE_Y) {
@@ -464,10 +489,10 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
       for (int i = 0; i < SPAN; ++i) {
         float acc;
         if constexpr (SHARE_DD) {
-          const int j = w * TPW + hk * SPAN + i;
-          acc = s_part[j][0][c];
+          const int j = otok + i;
+          acc = s_part[j][0][oc];
 #pragma unroll
-          for (int g = 1; g < G; ++g) acc += s_part[j][g][c];
+          for (int g = 1; g < G; ++g) acc += s_part[j][g][oc];
         } else {
           acc = yp[i];
         }
@@ -487,17 +512,17 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
 #pragma unroll
           for (int i = 0; i < SPAN; i += 2) o[i >> 1] = pack_bf16x2(yv[i], yv[i + 1]);
         }
-        const int w0 = (w * TPW + hk * SPAN) * EBY / 4;   // first word of this lane's span
+        const int w0 = otok * EBY / 4;   // first word of this lane's span
 #pragma unroll
-        for (int q = 0; q < SpanT<IO, SPAN>::kWords; ++q) s_y[STAGE_Y ? c : 0][w0 + q] = o[q];
+        for (int q = 0; q < SpanT<IO, SPAN>::kWords; ++q) s_y[STAGE_Y ? oc : 0][w0 + q] = o[q];
         y_pend_ts = ts;
       } else if (FULL && use_buf) {
         // unconditional for the same reason as the B/C loads: lanes of channels
         // past dim store beyond the buffer's range, which the hardware drops
-        const uint32_t vo_y = act ? vo_row : 0x80000000u;
+        const uint32_t vo_y = oact ? vo_row : 0x80000000u;
         buf_store_span<IO, SPAN>(make_rsrc(y + row0 * L, nrows * L * EB), vo_y, (uint32_t)(ts * EB), yv);
-      } else if (act && (FULL || valid > 0)) {
-        store_span<IO, SPAN>(y, row + tf, valid, vec, yv);
+      } else if (oact && (FULL || valid > 0)) {
+        store_span<IO, SPAN>(y, orow + tf, valid, vec, yv);
       }
     }
   };
@@ -537,10 +562,10 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
   }
 }
 
-template <int N, int G, int K, typename IO, bool AGG, bool ZOH, bool CKPT, bool ZFAST>
+template <int N, int G, int K, typename IO, bool AGG, bool ZOH, bool CKPT, bool ZFAST, bool ROWS>
 hipError_t launch_scan_one(const ScanDims& dm, const ScanPtrs& p, hipStream_t s, int64_t nwg) {
   using E = typename IO::T;
-  hipLaunchKernelGGL((scan_kernel<N, G, K, IO, AGG, ZOH, CKPT, ZFAST>), dim3((unsigned)nwg), dim3(64 * G), 0, s,
+  hipLaunchKernelGGL((scan_kernel<N, G, K, IO, AGG, ZOH, CKPT, ZFAST, ROWS>), dim3((unsigned)nwg), dim3(64 * G), 0, s,
                      dm, (const E*)p.x, (const E*)p.dt, (const E*)p.z, (const E*)p.B, (const E*)p.C, p.A, p.Dskip,
                      p.dt_bias, p.h0, p.h_in,
                      (E*)p.y, p.h_final, p.agg_h, p.agg_s, CKPT ? p.ckpt : nullptr);
@@ -549,15 +574,25 @@ hipError_t launch_scan_one(const ScanDims& dm, const ScanPtrs& p, hipStream_t s,
 
 // Zero-order hold launches the kernel twice, once per form of the input term;
 // each workgroup runs in exactly one of the two.
-template <int N, int G, int K, typename IO, bool AGG, bool ZOH, bool CKPT>
+template <int N, int G, int K, typename IO, bool AGG, bool ZOH, bool CKPT, bool ROWS>
 hipError_t launch_scan_z(const ScanDims& dm, const ScanPtrs& p, hipStream_t s, int64_t nwg) {
   if constexpr (ZOH) {
-    const hipError_t e = launch_scan_one<N, G, K, IO, AGG, true, CKPT, true>(dm, p, s, nwg);
+    const hipError_t e = launch_scan_one<N, G, K, IO, AGG, true, CKPT, true, ROWS>(dm, p, s, nwg);
     if (e != hipSuccess) return e;
-    return launch_scan_one<N, G, K, IO, AGG, true, CKPT, false>(dm, p, s, nwg);
+    return launch_scan_one<N, G, K, IO, AGG, true, CKPT, false, ROWS>(dm, p, s, nwg);
   } else {
-    return launch_scan_one<N, G, K, IO, AGG, false, CKPT, false>(dm, p, s, nwg);
+    return launch_scan_one<N, G, K, IO, AGG, false, CKPT, false, ROWS>(dm, p, s, nwg);
   }
+}
+
+// rows of at least 1 MB take the row-segment owners (bf16, two lanes per
+// channel, four waves)
+template <int N, int G, int K, typename IO, bool AGG, bool ZOH, bool CKPT>
+hipError_t launch_scan_r(const ScanDims& dm, const ScanPtrs& p, hipStream_t s, int64_t nwg) {
+  if constexpr (K == 2 && G == 4 && sizeof(typename IO::T) == 2) {
+    if (dm.seqlen * 2 >= (int64_t(1) << 20)) return launch_scan_z<N, G, K, IO, AGG, ZOH, CKPT, true>(dm, p, s, nwg);
+  }
+  return launch_scan_z<N, G, K, IO, AGG, ZOH, CKPT, false>(dm, p, s, nwg);
 }
 
 template <int N, int G, int K, typename IO, bool AGG, bool ZOH>
@@ -565,9 +600,9 @@ hipError_t launch_scan_t(const ScanDims& dm, const ScanPtrs& p, hipStream_t s) {
   const int64_t cblocks = (dm.dim + 64 / K - 1) / (64 / K);
   const int64_t nwg = cblocks * dm.batch * dm.num_chunks;
   if constexpr (!AGG) {
-    if (p.ckpt) return launch_scan_z<N, G, K, IO, false, ZOH, true>(dm, p, s, nwg);
+    if (p.ckpt) return launch_scan_r<N, G, K, IO, false, ZOH, true>(dm, p, s, nwg);
   }
-  return launch_scan_z<N, G, K, IO, AGG, ZOH, false>(dm, p, s, nwg);
+  return launch_scan_r<N, G, K, IO, AGG, ZOH, false>(dm, p, s, nwg);
 }
 
 template <int N, int G, typename IO, bool AGG, bool ZOH>
