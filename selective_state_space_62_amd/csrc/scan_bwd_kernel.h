@@ -721,7 +721,12 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
 // stages Delta, dr (and Delta x), and every lane runs its components back
 // through the stage.
 // VEC: as for scan_bwd_kernel (no runtime choice between vector and element loads).
-template <int N, int G, int K, typename IO, bool ZOH, bool FWD, bool VEC>
+// ROWS (rows of at least 1 MB): the owners of a stage's tokens are the 8 lanes
+// of a row, lane l of wave w owning tokens 8 (l % 8) .. + 7 of row 8 w + l / 8,
+// so each wave's load covers a whole 128-byte line of 8 rows (as the scan's
+// row-segment owners; with a lane's own channel each line was read a quarter
+// by each wave, and with rows 2 MB apart every quarter went to L2).
+template <int N, int G, int K, typename IO, bool ZOH, bool FWD, bool VEC, bool ROWS>
 __global__ __launch_bounds__(64 * G) void bwd_segment_agg_kernel(const BwdDims dm, const BwdPtrs p) {
   using T = typename IO::T;
   constexpr int CPB = 64 / K;
@@ -734,9 +739,11 @@ __global__ __launch_bounds__(64 * G) void bwd_segment_agg_kernel(const BwdDims d
   constexpr int CPT = (ST * N + THREADS - 1) / THREADS;   // (B, C) pairs (C alone without FWD) each thread stages
   static_assert(64 % ST == 0, "a stage divides every segment length");
   static_assert(FWD || !ZOH, "the discretisation only enters the state's aggregate");
+  static_assert(!ROWS || (K == 2 && G == 4 && CPB == 8 * G && ST == 8 * AS), "row owners: 8 lanes per row");
   using BCV = std::conditional_t<FWD, float2, float>;
-  __shared__ float2 s_dr[ST][CPB];               // (Delta, dr) per token and channel
-  __shared__ float s_dx[FWD ? ST : 1][CPB];      // Delta x per token and channel
+  // (the row owners' writes need the rows padded by one channel to spread banks)
+  __shared__ float2 s_dr[ST][CPB + (ROWS ? 1 : 0)];               // (Delta, dr) per token and channel
+  __shared__ float s_dx[FWD ? ST : 1][CPB + (ROWS ? 1 : 0)];      // Delta x per token and channel
   __shared__ BCV s_bc[ST][N];                    // (B_n, C_n), or C_n, of the stage's tokens
 
   const int tid = threadIdx.x;
@@ -759,8 +766,6 @@ __global__ __launch_bounds__(64 * G) void bwd_segment_agg_kernel(const BwdDims d
   const int64_t dc = act ? d : dm.dim - 1;
   const int64_t L = dm.seqlen;
   const int64_t ch = b * dm.dim + dc;
-  const int64_t row = ch * L;
-  const int64_t dt_row = dm.dt_row ? b * L : row;
   constexpr bool vec = VEC;   // every lane's span is 16-byte aligned
   const bool has_z = p.z != nullptr;
   const int64_t t_begin = seg * dm.seg_len;
@@ -768,6 +773,13 @@ __global__ __launch_bounds__(64 * G) void bwd_segment_agg_kernel(const BwdDims d
   const int64_t sb = t_begin / ST;
   const int64_t se = (t_end + ST - 1) / ST;
   const int j_own = sg * AS;
+  // the owner of the stage tokens this lane loads and stages (its own channel unless ROWS)
+  const int oc = ROWS ? w * 8 + (lane >> 3) : c;
+  const int otok = ROWS ? (lane & 7) * AS : j_own;
+  const int64_t od = cb * CPB + oc;
+  const bool oact = od < dm.dim;
+  const int64_t orow = (b * dm.dim + (oact ? od : dm.dim - 1)) * L;
+  const int64_t odt_row = dm.dt_row ? b * L : orow;
 
   const T* __restrict__ x = static_cast<const T*>(p.x);
   const T* __restrict__ dt = static_cast<const T*>(p.dt);
@@ -776,7 +788,7 @@ __global__ __launch_bounds__(64 * G) void bwd_segment_agg_kernel(const BwdDims d
   float A2[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) A2[s] = p.A[dc * N + sg * NS + s] * kLog2e;
-  const float bias2 = p.dt_bias ? p.dt_bias[dc] * kLog2e : 0.0f;
+  const float bias2 = p.dt_bias ? p.dt_bias[oact ? od : dm.dim - 1] * kLog2e : 0.0f;   // the owner's
   const float* __restrict__ bc_row = p.bc + b * L * (2 * N);   // (token, n, {B, C})
 
   struct Fetch {
@@ -789,13 +801,13 @@ __global__ __launch_bounds__(64 * G) void bwd_segment_agg_kernel(const BwdDims d
   auto fetch = [&](auto whole_tag, int64_t k, Fetch& f) {
     constexpr bool WHOLE = decltype(whole_tag)::value;
     const int64_t t0 = k * ST;
-    const int64_t v = t_end - (t0 + j_own);
+    const int64_t v = t_end - (t0 + otok);
     const int valid = WHOLE ? AS : (int)(v < 0 ? 0 : (v < AS ? v : AS));
-    if constexpr (FWD) load_span<IO, AS>(x, row + t0 + j_own, valid, vec, f.x);
-    load_span<IO, AS>(dt, dt_row + t0 + j_own, valid, vec, f.dt);
+    if constexpr (FWD) load_span<IO, AS>(x, orow + t0 + otok, valid, vec, f.x);
+    load_span<IO, AS>(dt, odt_row + t0 + otok, valid, vec, f.dt);
     // without z, x stands in (its values are never used)
-    load_span<IO, AS>(has_z ? z : x, row + t0 + j_own, valid, vec, f.z);
-    load_span<IO, AS>(dy, row + t0 + j_own, valid, vec, f.dy);
+    load_span<IO, AS>(has_z ? z : x, orow + t0 + otok, valid, vec, f.z);
+    load_span<IO, AS>(dy, orow + t0 + otok, valid, vec, f.dy);
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
       const int idx = tid + q * THREADS;
@@ -823,15 +835,15 @@ __global__ __launch_bounds__(64 * G) void bwd_segment_agg_kernel(const BwdDims d
     const int64_t nj = t_end - k * ST;   // tokens of the stage inside the segment (ST or fewer)
 #pragma unroll
     for (int i = 0; i < AS; ++i) {
-      const float dl = (j_own + i < nj) ? softplus_dt(span_elem<IO>(f.dt, i), bias2) : 0.0f;
-      const float dyv = act ? span_elem<IO>(f.dy, i) : 0.0f;   // padding tokens load as zero
+      const float dl = (otok + i < nj) ? softplus_dt(span_elem<IO>(f.dt, i), bias2) : 0.0f;
+      const float dyv = oact ? span_elem<IO>(f.dy, i) : 0.0f;   // padding tokens load as zero
       float gate = 1.0f;
       if (has_z) {
         const float zv = span_elem<IO>(f.z, i);
         gate = zv * sigmoid2(zv * kLog2e);
       }
-      s_dr[j_own + i][c] = make_float2(dl, dyv * gate);
-      if constexpr (FWD) s_dx[j_own + i][c] = dl * span_elem<IO>(f.x, i);
+      s_dr[otok + i][oc] = make_float2(dl, dyv * gate);
+      if constexpr (FWD) s_dx[otok + i][oc] = dl * span_elem<IO>(f.x, i);
     }
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
@@ -882,10 +894,21 @@ __global__ __launch_bounds__(64 * G) void bwd_segment_agg_kernel(const BwdDims d
 template <int N, int G, int K, typename IO, bool ZOH, bool FWD>
 hipError_t launch_segment_agg_t(const BwdDims& dm, const BwdPtrs& p, hipStream_t s) {
   const int64_t nwg = dm.cblocks * dm.batch * (dm.nseg - (FWD ? 0 : 1));
-  if (dm.seqlen % IO::kPerSpan == 0)
-    hipLaunchKernelGGL((bwd_segment_agg_kernel<N, G, K, IO, ZOH, FWD, true>), dim3((unsigned)nwg), dim3(64 * G), 0, s, dm, p);
+  const bool vec = dm.seqlen % IO::kPerSpan == 0;
+  // rows of at least 1 MB (bf16, two lanes per channel): the row owners
+  if constexpr (sizeof(typename IO::T) == 2 && G == 4 && K == 2) {
+    if (vec && dm.seqlen * 2 >= (int64_t(1) << 20)) {
+      hipLaunchKernelGGL((bwd_segment_agg_kernel<N, G, K, IO, ZOH, FWD, true, true>), dim3((unsigned)nwg),
+                         dim3(64 * G), 0, s, dm, p);
+      return hipGetLastError();
+    }
+  }
+  if (vec)
+    hipLaunchKernelGGL((bwd_segment_agg_kernel<N, G, K, IO, ZOH, FWD, true, false>), dim3((unsigned)nwg),
+                       dim3(64 * G), 0, s, dm, p);
   else
-    hipLaunchKernelGGL((bwd_segment_agg_kernel<N, G, K, IO, ZOH, FWD, false>), dim3((unsigned)nwg), dim3(64 * G), 0, s, dm, p);
+    hipLaunchKernelGGL((bwd_segment_agg_kernel<N, G, K, IO, ZOH, FWD, false, false>), dim3((unsigned)nwg),
+                       dim3(64 * G), 0, s, dm, p);
   return hipGetLastError();
 }
 
