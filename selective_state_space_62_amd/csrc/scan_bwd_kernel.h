@@ -133,7 +133,14 @@ __device__ __forceinline__ float zoh_psi(float u2, float E) {
 // chunk's stores included) before using the next chunk's operands.
 // SIN: the reverse pass's operands go through LDS in whole row pieces (bf16,
 // first order, rows a multiple of 8 tokens; see s_in below).
-template <int N, int G, int K, typename IO, bool ZOH, bool VEC, bool SIN>
+// ZFAST (zero-order hold only): this launch takes the workgroups whose every
+// |A| is at least 1/16, where the input coefficient c = Delta phi(Delta A) is
+// evaluated as (E - 1) / A from the E = e^(Delta A) at hand, as the forward's
+// fast form does; the other launch takes the rest and evaluates phi.  E - 1 is
+// exact for E in [1/2, 2], so c carries E's rounding, about 1e-7 absolute;
+// dc/dA = Delta^2 psi(Delta A) keeps its series and closed form in both (its
+// closed form in terms of c cancels digits for small Delta A).
+template <int N, int G, int K, typename IO, bool ZOH, bool VEC, bool SIN, bool ZFAST = false>
 __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10))) void scan_bwd_kernel(
     const BwdDims dm, const BwdPtrs p) {
   using T = typename IO::T;
@@ -220,6 +227,30 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
   float A2[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) A2[s] = p.A[dc * N + sg * NS + s] * kLog2e;
+  float inv_a[ZOH && ZFAST ? NS : 1];
+  if constexpr (ZOH) {
+    bool ok = true;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const float a = p.A[dc * N + sg * NS + s];
+      if constexpr (ZFAST) inv_a[s] = 1.0f / a;
+      ok = ok && (fabsf(a) >= 0.0625f) && (fabsf(a) <= 3.0e38f);
+    }
+    // the whole workgroup takes one form (its waves share the LDS partials);
+    // nothing has been written yet
+    const bool wg_fast = __syncthreads_and(ok) != 0;
+    if (wg_fast != ZFAST) return;
+  }
+  // the zero-order-hold input term c B x: (E - 1) x B / A (fast form) or
+  // phi(u) Delta x B; o is the token's (Delta, Delta x, x, x Delta^2)
+  auto zoh_in = [&](int s, float u2, float E, float Bv, const auto& o) {
+    if constexpr (ZFAST) {
+      const float t = o.z * (Bv * inv_a[ZFAST ? s : 0]);
+      return fmaf(E, t, -t);
+    } else {
+      return (o.y * Bv) * zoh_phi(u2, E);
+    }
+  };
   const float bias2 = p.dt_bias ? p.dt_bias[dc] * kLog2e : 0.0f;
   const float skip = p.Dskip ? p.Dskip[dc] : 0.0f;
   const float* __restrict__ bc_row = p.bc + b * L * (2 * N);
@@ -343,8 +374,9 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
             float u2 = o.x * A2[s];
             if constexpr (ZOH) __asm__ volatile("" : "+v"(u2) : "v"(h[s]));   // token by token (registers)
             const float E = __builtin_amdgcn_exp2f(u2);
-            float in = o.y * s_bc[j][2 * (sg * NS + s)];
-            if constexpr (ZOH) in *= zoh_phi(u2, E);
+            float in;
+            if constexpr (ZOH) in = zoh_in(s, u2, E, s_bc[j][2 * (sg * NS + s)], o);
+            else in = o.y * s_bc[j][2 * (sg * NS + s)];
             h[s] = fmaf(E, h[s], in);
           }
         }
@@ -503,8 +535,9 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
           if constexpr (ZOH) __asm__ volatile("" : "+v"(u2) : "v"(hs[j][s]));   // token by token (registers)
           const float E = __builtin_amdgcn_exp2f(u2);
           if constexpr (!ZOH) Es[j][s] = E;
-          float in = o.y * s_bc[j][2 * (sg * NS + s)];
-          if constexpr (ZOH) in *= zoh_phi(u2, E);
+          float in;
+          if constexpr (ZOH) in = zoh_in(s, u2, E, s_bc[j][2 * (sg * NS + s)], o);
+          else in = o.y * s_bc[j][2 * (sg * NS + s)];
           hs[j + 1][s] = fmaf(E, hs[j][s], in);
           acc = fmaf(s_bc[j][2 * (sg * NS + s) + 1], hs[j + 1][s], acc);
         }
@@ -580,11 +613,13 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
           ddp = fmaf(ga, A2[s], ddp);
           dAacc[s] = fmaf(ga, o.x, dAacc[s]);
           if constexpr (ZOH) {
-            // c = Delta phi: dx and dB carry phi; dc/dDelta = e^u; dc/dA = Delta^2 psi
-            const float lp = lam[s] * zoh_phi(u2, E);
+            // c = Delta phi: dx and dB carry phi; dc/dDelta = e^u; dc/dA = Delta^2 psi.
+            // Fast form: lp = lam c, so sB already holds Delta sum lam phi B and
+            // dB = lam c x
+            const float lp = ZFAST ? lam[s] * ((E - 1.0f) * inv_a[ZFAST ? s : 0]) : lam[s] * zoh_phi(u2, E);
             const float lB = lam[s] * Bv;
             sB = fmaf(lp, Bv, sB);
-            dBv[s] = lp * o.y;
+            dBv[s] = lp * (ZFAST ? o.z : o.y);
             sE = fmaf(lB, E, sE);
             dAacc[s] = fmaf(lB, o.w * zoh_psi(u2, E), dAacc[s]);
             // keep the update here: sunk to the end of the chunk, it would hold
@@ -636,7 +671,8 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
             sB += pv.y;
           }
         }
-        dxv[i] = fmaf(sB, s_dd[j][c].x, s_dr[j][c] * skip);   // Delta and dr of the owned token from LDS
+        // Delta and dr of the owned token from LDS (the fast form's sB carries Delta)
+        dxv[i] = ZFAST ? sB + s_dr[j][c] * skip : fmaf(sB, s_dd[j][c].x, s_dr[j][c] * skip);
         // Euler: dDelta = (decay part) ln 2 + x sum lam B; ZOH: the lanes already added x sum lam e^u B
         const float dv = (ZOH ? ddp : fmaf(ddp, kLn2, sB * xv[i])) * sigmoid2(v2[i]);
         ddtv[i] = dv;   // zero for padding tokens and inactive channels
@@ -938,6 +974,26 @@ hipError_t launch_bwd_t(const BwdDims& dm, const BwdPtrs& p, hipStream_t s) {
                          dm, p);
       return hipGetLastError();
     }
+  }
+  // zero-order hold: two launches, one per form of the input coefficient; each
+  // workgroup runs in exactly one of them
+  if constexpr (ZOH) {
+    if (dm.vec) {
+      hipLaunchKernelGGL((scan_bwd_kernel<N, G, K, IO, ZOH, true, false, true>), dim3((unsigned)nwg), dim3(64 * G), 0,
+                         s, dm, p);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((scan_bwd_kernel<N, G, K, IO, ZOH, true, false, false>), dim3((unsigned)nwg), dim3(64 * G), 0,
+                         s, dm, p);
+    } else {
+      hipLaunchKernelGGL((scan_bwd_kernel<N, G, K, IO, ZOH, false, false, true>), dim3((unsigned)nwg), dim3(64 * G), 0,
+                         s, dm, p);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((scan_bwd_kernel<N, G, K, IO, ZOH, false, false, false>), dim3((unsigned)nwg), dim3(64 * G),
+                         0, s, dm, p);
+    }
+    return hipGetLastError();
   }
   if (dm.vec)
     hipLaunchKernelGGL((scan_bwd_kernel<N, G, K, IO, ZOH, true, false>), dim3((unsigned)nwg), dim3(64 * G), 0, s, dm,

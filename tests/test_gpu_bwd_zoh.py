@@ -124,10 +124,10 @@ def test_bwd_zoh_bf16(ss, o, dev):
 
 def test_bwd_zoh_checkpoints_and_determinism(ss, o, dev):
     """A ZOH forward that stores checkpoints feeds the ZOH backward; two runs give
-    identical bits.  The forward forms the input term as (E - 1) x B / A (every
-    |A| here is at least 0.3), the backward's own sweep as phi(u) Delta B x, so the
-    stored states differ from the sweep's by rounding: the gradients from the
-    checkpoints are held to the oracle, as for chunked plans."""
+    identical bits.  Every |A| here is at least 0.3, so the forward and the
+    backward's own sweep both form the input term as (E - 1) x B / A with the
+    same operations: the gradients from the stored checkpoints equal those from
+    the sweep bit for bit, and both are held to the oracle."""
     import torch
     batch, D, N, L = 2, 96, 16, 130
     rng = np.random.default_rng(zlib.crc32(b"zoh-ckpt"))
@@ -145,6 +145,9 @@ def test_bwd_zoh_checkpoints_and_determinism(ss, o, dev):
     for k, v in g1.items():
         if v is not None:
             assert torch.equal(v, g2[k]), k
+    for k, v in g1.items():
+        if v is not None:
+            assert torch.equal(v, g3[k]), k
     r = _oracle(o, f64, par)
     _compare(g1, r, "f32", "bwd zoh own sweep")
     _compare(g3, r, "f32", "bwd zoh from forward checkpoints")
