@@ -134,12 +134,12 @@ __device__ __forceinline__ float zoh_psi(float u2, float E) {
 // SIN: the reverse pass's operands go through LDS in whole row pieces (bf16,
 // first order, rows a multiple of 8 tokens; see s_in below).
 // ZFAST (zero-order hold only): this launch takes the workgroups whose every
-// |A| is at least 1/16, where the input coefficient c = Delta phi(Delta A) is
-// evaluated as (E - 1) / A from the E = e^(Delta A) at hand, as the forward's
-// fast form does; the other launch takes the rest and evaluates phi.  E - 1 is
-// exact for E in [1/2, 2], so c carries E's rounding, about 1e-7 absolute;
-// dc/dA = Delta^2 psi(Delta A) keeps its series and closed form in both (its
-// closed form in terms of c cancels digits for small Delta A).
+// |A| is at least 1/16, where the input coefficient c = Delta phi(Delta A)
+// comes from zoh_coef, as in the forward ((E - 1)/A from the E = e^(Delta A) at
+// hand where |Delta A| >= 1/10, a Taylor polynomial below; no reciprocal); the
+// other launch takes the rest and evaluates phi.  dc/dA = Delta^2 psi(Delta A)
+// keeps its series and closed form in both (its closed form in terms of c
+// cancels digits for small Delta A).
 template <int N, int G, int K, typename IO, bool ZOH, bool VEC, bool SIN, bool ZFAST = false>
 __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10))) void scan_bwd_kernel(
     const BwdDims dm, const BwdPtrs p) {
@@ -241,12 +241,12 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
     const bool wg_fast = __syncthreads_and(ok) != 0;
     if (wg_fast != ZFAST) return;
   }
-  // the zero-order-hold input term c B x: (E - 1) x B / A (fast form) or
-  // phi(u) Delta x B; o is the token's (Delta, Delta x, x, x Delta^2)
+  // the zero-order-hold input term c B x: zoh_coef's c times x B, with the
+  // forward's operations (fast form), or phi(u) Delta x B; o is the token's
+  // (Delta, Delta x, x, x Delta^2)
   auto zoh_in = [&](int s, float u2, float E, float Bv, const auto& o) {
     if constexpr (ZFAST) {
-      const float t = o.z * (Bv * inv_a[ZFAST ? s : 0]);
-      return fmaf(E, t, -t);
+      return zoh_coef(u2, E, o.x, inv_a[ZFAST ? s : 0]) * (o.z * Bv);
     } else {
       return (o.y * Bv) * zoh_phi(u2, E);
     }
@@ -616,7 +616,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
             // c = Delta phi: dx and dB carry phi; dc/dDelta = e^u; dc/dA = Delta^2 psi.
             // Fast form: lp = lam c, so sB already holds Delta sum lam phi B and
             // dB = lam c x
-            const float lp = ZFAST ? lam[s] * ((E - 1.0f) * inv_a[ZFAST ? s : 0]) : lam[s] * zoh_phi(u2, E);
+            const float lp = ZFAST ? lam[s] * zoh_coef(u2, E, o.x, inv_a[ZFAST ? s : 0]) : lam[s] * zoh_phi(u2, E);
             const float lB = lam[s] * Bv;
             sB = fmaf(lp, Bv, sB);
             dBv[s] = lp * (ZFAST ? o.z : o.y);

@@ -145,12 +145,11 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
   float A2[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) A2[s] = A[dc * N + sg * NS + s] * kLog2e;
-  // Zero-order hold: the input term (e^(Delta A) - 1)/A B x.  For |A| >= 1/16 in
-  // every component of the wave it is evaluated as (E - 1) t with t = x B / A,
-  // E = e^(Delta A) already at hand: one fma, one multiply more than the first
-  // order form.  E - 1 carries the rounding of E, about 1e-7 absolute, so t's
-  // share of error stays near one rounding of a state of size x B / A.  Waves
-  // with a smaller |A| (A = 0 included) use phi(Delta A) Delta B x instead.
+  // Zero-order hold: the input term c B x with c = (e^(Delta A) - 1)/A.  Where
+  // every |A| of the workgroup is at least 1/16, c comes from zoh_coef: (E - 1)/A
+  // from the E = e^(Delta A) already at hand where |Delta A| >= 1/10, a Taylor
+  // polynomial below (no reciprocal per element).  Workgroups with a smaller |A|
+  // (A = 0 included) use phi(Delta A) Delta B x instead.
   float inv_a[ZOH ? NS : 1];
   if constexpr (ZOH) {
     bool ok = true;
@@ -390,8 +389,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
         if constexpr (!ZOH) {
           in = o.dx * o.bcv[2 * s];                       // first order: Bbar x = Delta B x
         } else if constexpr (FASTZ) {
-          const float t = o.dx * (o.bcv[2 * s] * inv_a[s]);
-          in = fmaf(E, t, -t);                            // (e^u - 1) x B / A
+          in = zoh_coef(u2, E, o.d, inv_a[s]) * (o.dx * o.bcv[2 * s]);   // c x B (o.dx is x)
         } else {
           in = (dxz * o.bcv[2 * s]) * zoh_phi(u2, E);     // (e^u - 1)/u Delta B x
         }

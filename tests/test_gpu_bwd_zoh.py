@@ -186,3 +186,40 @@ def test_bwd_zoh_a_zero(ss, o, dev):
     par["A"] = A
     g, _, _ = _run(ss, raw, par, "f32", dev)
     _compare(g, _oracle(o, f64, par), "f32", "bwd zoh with A = 0 entries")
+
+
+@pytest.mark.parametrize("what,lo,hi", [
+    ("every |A| >= 1/16: the (E - 1)/A form in every workgroup", 0.07, 0.5),
+    ("|A| from 1e-3: both forms", 1e-3, 0.5),
+], ids=["fast-form", "both-forms"])
+def test_bwd_zoh_a_of_both_signs(ss, o, dev, what, lo, hi):
+    """Entries of A of either sign (e^(Delta A) above 1 where A > 0), short
+    sequences so that the growing components stay finite."""
+    rng = np.random.default_rng(zlib.crc32(repr(("zoh-sign", lo)).encode()))
+    raw, par, f64 = _problem(rng, 2, 96, 16, 40, "f32", True)
+    mag = rng.uniform(lo, hi, par["A"].shape)
+    par["A"] = (np.where(rng.random(mag.shape) < 0.5, -1.0, 1.0) * mag).astype(np.float32)
+    g, _, _ = _run(ss, raw, par, "f32", dev)
+    _compare(g, _oracle(o, f64, par), "f32", "bwd zoh, A of both signs (%s)" % what)
+
+
+@pytest.mark.parametrize("what,lo,hi,both_signs", [
+    ("every Delta A small, A < 0", 0.07, 0.5, False),
+    ("every Delta A small, A of either sign", 0.07, 0.5, True),
+    ("Delta about 1e-3, A in [-16, -1]", 1.0, 16.0, False),
+], ids=["small-u", "small-u-signs", "small-delta"])
+def test_bwd_zoh_small_delta_a(ss, o, dev, what, lo, hi, both_signs):
+    """Every |A| at least 1/16 (the coefficient without phi's reciprocal in every
+    workgroup) and every u = Delta A small (Delta about 1e-3), where e^u, rounded,
+    cannot hold u's low bits: the gradients must still reach fp32 parity."""
+    rng = np.random.default_rng(zlib.crc32(repr(("zoh-bwd-small-u", what)).encode()))
+    batch, D, N, L = 2, 128, 16, 256
+    raw, par, f64 = _problem(rng, batch, D, N, L, "f32", True)
+    raw["dt"] = (0.1 * rng.standard_normal((batch, D, L))).astype(np.float32)
+    f64["dt"] = raw["dt"].astype(np.float64)
+    par["dt_bias"] = np.full(D, np.log(np.expm1(1e-3)), np.float32)
+    mag = rng.uniform(lo, hi, (D, N))
+    sign = np.where(rng.random((D, N)) < 0.5, 1.0, -1.0) if both_signs else -1.0
+    par["A"] = (sign * mag).astype(np.float32)
+    g, _, _ = _run(ss, raw, par, "f32", dev)
+    _compare(g, _oracle(o, f64, par), "f32", "bwd zoh, %s" % what)

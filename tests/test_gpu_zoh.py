@@ -137,3 +137,35 @@ def test_zoh_decode_equals_zoh_scan_and_oracle(ss, dev, io):
                                    Dskip=par["Dskip"], dt_bias=par["dt_bias"], h0=par["h0"], zoh=True)
     tol = 1e-5 if io == "f32" else 2e-2
     assert rel_l2(to_f64(yd), yr) <= tol and rel_l2(to_f64(st), hr) <= tol
+
+
+SMALL_U = [
+    ("every Delta A small, A < 0", 0.07, 0.5, False),
+    ("every Delta A small, A of either sign", 0.07, 0.5, True),
+    ("Delta about 1e-3, A in [-16, -1]", 1.0, 16.0, False),
+]
+
+
+@pytest.mark.parametrize("what,lo,hi,both_signs", SMALL_U, ids=["small-u", "small-u-signs", "small-delta"])
+def test_zoh_scan_small_delta_a(ss, dev, what, lo, hi, both_signs):
+    """Every |A| at least 1/16, so every workgroup takes the coefficient
+    c = (e^u - 1)/A without phi's reciprocal, and every u = Delta A small
+    (Delta about 1e-3): there e^u, rounded, cannot hold u's low bits, and c must
+    still reach fp32 parity.  No skip term or gate, which would hide the state's
+    error in y."""
+    import torch
+    rng = np.random.default_rng(zlib.crc32(repr(("zoh-small-u", what)).encode()))
+    batch, D, N, L = 2, 128, 16, 256
+    raw, par, f64 = random_problem(rng, batch, D, N, L, "f32", with_z=False, with_skip=False, with_h0=False)
+    raw["dt"] = (0.1 * rng.standard_normal((batch, D, L))).astype(np.float32)
+    f64["dt"] = raw["dt"].astype(np.float64)
+    par["dt_bias"] = np.full(D, np.log(np.expm1(1e-3)), np.float32)
+    mag = rng.uniform(lo, hi, (D, N))
+    sign = np.where(rng.random((D, N)) < 0.5, 1.0, -1.0) if both_signs else -1.0
+    par["A"] = (sign * mag).astype(np.float32)
+    y, hf = _gpu(ss, raw, par, "f32", dev)
+    yr, hr = oracle.default().scan(f64["x"], f64["dt"], f64["B"], f64["C"], par["A"], dt_bias=par["dt_bias"],
+                                   zoh=True)
+    ey, eh = rel_l2(y, yr), rel_l2(hf, hr)
+    log("zoh scan, %s: rel-L2 y %.3e h %.3e" % (what, ey, eh))
+    assert ey <= 1e-5 and eh <= 1e-5
