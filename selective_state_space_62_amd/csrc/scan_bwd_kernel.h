@@ -133,14 +133,7 @@ __device__ __forceinline__ float zoh_psi(float u2, float E) {
 // chunk's stores included) before using the next chunk's operands.
 // SIN: the reverse pass's operands go through LDS in whole row pieces (bf16,
 // first order, rows a multiple of 8 tokens; see s_in below).
-// ZFAST (zero-order hold only): this launch takes the workgroups whose every
-// |A| is at least 1/16, where the input coefficient c = Delta phi(Delta A)
-// comes from zoh_coef, as in the forward ((E - 1)/A from the E = e^(Delta A) at
-// hand where |Delta A| >= 1/10, a Taylor polynomial below; no reciprocal); the
-// other launch takes the rest and evaluates phi.  dc/dA = Delta^2 psi(Delta A)
-// keeps its series and closed form in both (its closed form in terms of c
-// cancels digits for small Delta A).
-template <int N, int G, int K, typename IO, bool ZOH, bool VEC, bool SIN, bool ZFAST = false>
+template <int N, int G, int K, typename IO, bool ZOH, bool VEC, bool SIN>
 __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10))) void scan_bwd_kernel(
     const BwdDims dm, const BwdPtrs p) {
   using T = typename IO::T;
@@ -227,29 +220,21 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
   float A2[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) A2[s] = p.A[dc * N + sg * NS + s] * kLog2e;
-  float inv_a[ZOH && ZFAST ? NS : 1];
+  // Zero-order hold: the input coefficient c = Delta phi(Delta A) from zoh_coef,
+  // as in the forward: (E - 1)/A from the E = e^(Delta A) at hand where
+  // |Delta A| >= 1/10, a Taylor polynomial below (A = 0 included), with no
+  // reciprocal per element; dc/dA = Delta^2 psi(Delta A) keeps its series and
+  // closed form (its closed form in terms of c cancels digits for small
+  // Delta A).
+  float inv_a[ZOH ? NS : 1];
   if constexpr (ZOH) {
-    bool ok = true;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const float a = p.A[dc * N + sg * NS + s];
-      if constexpr (ZFAST) inv_a[s] = 1.0f / a;
-      ok = ok && (fabsf(a) >= 0.0625f) && (fabsf(a) <= 3.0e38f);
-    }
-    // the whole workgroup takes one form (its waves share the LDS partials);
-    // nothing has been written yet
-    const bool wg_fast = __syncthreads_and(ok) != 0;
-    if (wg_fast != ZFAST) return;
+    for (int s = 0; s < NS; ++s) inv_a[s] = 1.0f / p.A[dc * N + sg * NS + s];
   }
-  // the zero-order-hold input term c B x: zoh_coef's c times x B, with the
-  // forward's operations (fast form), or phi(u) Delta x B; o is the token's
-  // (Delta, Delta x, x, x Delta^2)
+  // the zero-order-hold input term c x B, with the forward's operations; o is
+  // the token's (Delta, Delta x, x, x Delta^2)
   auto zoh_in = [&](int s, float u2, float E, float Bv, const auto& o) {
-    if constexpr (ZFAST) {
-      return zoh_coef(u2, E, o.x, inv_a[ZFAST ? s : 0]) * (o.z * Bv);
-    } else {
-      return (o.y * Bv) * zoh_phi(u2, E);
-    }
+    return zoh_coef(u2, E, o.x, inv_a[ZOH ? s : 0]) * (o.z * Bv);
   };
   const float bias2 = p.dt_bias ? p.dt_bias[dc] * kLog2e : 0.0f;
   const float skip = p.Dskip ? p.Dskip[dc] : 0.0f;
@@ -613,13 +598,13 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
           ddp = fmaf(ga, A2[s], ddp);
           dAacc[s] = fmaf(ga, o.x, dAacc[s]);
           if constexpr (ZOH) {
-            // c = Delta phi: dx and dB carry phi; dc/dDelta = e^u; dc/dA = Delta^2 psi.
-            // Fast form: lp = lam c, so sB already holds Delta sum lam phi B and
+            // c = Delta phi: dx and dB carry c; dc/dDelta = e^u; dc/dA = Delta^2 psi.
+            // lp = lam c: sB holds sum lam c B (dx needs no further Delta), and
             // dB = lam c x
-            const float lp = ZFAST ? lam[s] * zoh_coef(u2, E, o.x, inv_a[ZFAST ? s : 0]) : lam[s] * zoh_phi(u2, E);
+            const float lp = lam[s] * zoh_coef(u2, E, o.x, inv_a[ZOH ? s : 0]);
             const float lB = lam[s] * Bv;
             sB = fmaf(lp, Bv, sB);
-            dBv[s] = lp * (ZFAST ? o.z : o.y);
+            dBv[s] = lp * o.z;
             sE = fmaf(lB, E, sE);
             dAacc[s] = fmaf(lB, o.w * zoh_psi(u2, E), dAacc[s]);
             // keep the update here: sunk to the end of the chunk, it would hold
@@ -672,7 +657,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
           }
         }
         // Delta and dr of the owned token from LDS (the fast form's sB carries Delta)
-        dxv[i] = ZFAST ? sB + s_dr[j][c] * skip : fmaf(sB, s_dd[j][c].x, s_dr[j][c] * skip);
+        dxv[i] = ZOH ? sB + s_dr[j][c] * skip : fmaf(sB, s_dd[j][c].x, s_dr[j][c] * skip);
         // Euler: dDelta = (decay part) ln 2 + x sum lam B; ZOH: the lanes already added x sum lam e^u B
         const float dv = (ZOH ? ddp : fmaf(ddp, kLn2, sB * xv[i])) * sigmoid2(v2[i]);
         ddtv[i] = dv;   // zero for padding tokens and inactive channels
@@ -974,26 +959,6 @@ hipError_t launch_bwd_t(const BwdDims& dm, const BwdPtrs& p, hipStream_t s) {
                          dm, p);
       return hipGetLastError();
     }
-  }
-  // zero-order hold: two launches, one per form of the input coefficient; each
-  // workgroup runs in exactly one of them
-  if constexpr (ZOH) {
-    if (dm.vec) {
-      hipLaunchKernelGGL((scan_bwd_kernel<N, G, K, IO, ZOH, true, false, true>), dim3((unsigned)nwg), dim3(64 * G), 0,
-                         s, dm, p);
-      const hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((scan_bwd_kernel<N, G, K, IO, ZOH, true, false, false>), dim3((unsigned)nwg), dim3(64 * G), 0,
-                         s, dm, p);
-    } else {
-      hipLaunchKernelGGL((scan_bwd_kernel<N, G, K, IO, ZOH, false, false, true>), dim3((unsigned)nwg), dim3(64 * G), 0,
-                         s, dm, p);
-      const hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((scan_bwd_kernel<N, G, K, IO, ZOH, false, false, false>), dim3((unsigned)nwg), dim3(64 * G),
-                         0, s, dm, p);
-    }
-    return hipGetLastError();
   }
   if (dm.vec)
     hipLaunchKernelGGL((scan_bwd_kernel<N, G, K, IO, ZOH, true, false>), dim3((unsigned)nwg), dim3(64 * G), 0, s, dm,

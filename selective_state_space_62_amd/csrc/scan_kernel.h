@@ -38,12 +38,8 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
 // CKPT_K (full pass only): also store the state entering every backward-pass
 // chunk, for a training step's backward.  It is a separate instantiation so
 // that the plain scan keeps its registers.
-// ZFAST (zero-order hold only): this launch takes the workgroups whose every
-// |A| is at least 1/16 (the (E - 1) x B / A form); the other launch takes the
-// rest (the phi form).  Each instantiation carries one form, so neither pays
-// the other's registers.
 // ROWS: rows of at least 1 MB (see ROWOWN below).
-template <int N, int G, int K, typename IO, bool AGG, bool ZOH, bool CKPT_K, bool ZFAST = false, bool ROWS = false>
+template <int N, int G, int K, typename IO, bool AGG, bool ZOH, bool CKPT_K, bool ROWS = false>
 __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 && N / (G * K) <= 2 ? 5 : 1, 10))) void scan_kernel(
     const ScanDims dm, const typename IO::T* __restrict__ x, const typename IO::T* __restrict__ dt,
     const typename IO::T* __restrict__ z, const typename IO::T* __restrict__ Bm,
@@ -145,23 +141,14 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
   float A2[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) A2[s] = A[dc * N + sg * NS + s] * kLog2e;
-  // Zero-order hold: the input term c B x with c = (e^(Delta A) - 1)/A.  Where
-  // every |A| of the workgroup is at least 1/16, c comes from zoh_coef: (E - 1)/A
-  // from the E = e^(Delta A) already at hand where |Delta A| >= 1/10, a Taylor
-  // polynomial below (no reciprocal per element).  Workgroups with a smaller |A|
-  // (A = 0 included) use phi(Delta A) Delta B x instead.
+  // Zero-order hold: the input term c B x with c = (e^(Delta A) - 1)/A from
+  // zoh_coef: (E - 1)/A from the E = e^(Delta A) already at hand where
+  // |Delta A| >= 1/10, a Taylor polynomial of Delta phi(Delta A) below (A = 0
+  // included), with no reciprocal per element.
   float inv_a[ZOH ? NS : 1];
   if constexpr (ZOH) {
-    bool ok = true;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const float a = A[dc * N + sg * NS + s];
-      inv_a[s] = 1.0f / a;
-      ok = ok && (fabsf(a) >= 0.0625f) && (fabsf(a) <= 3.0e38f);
-    }
-    // the whole workgroup takes one form (its waves share the readout partials)
-    const bool wg_fast = __syncthreads_and(ok) != 0;
-    if (wg_fast != ZFAST) return;
+    for (int s = 0; s < NS; ++s) inv_a[s] = 1.0f / A[dc * N + sg * NS + s];
   }
   // the owner's (phases A and C)
   const float bias2 = dt_bias ? dt_bias[odc] * kLog2e : 0.0f;
@@ -377,10 +364,8 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
       }
     };
     // o.dx is Delta x (first order) or x (zero-order hold)
-    auto compute = [&](auto fz_tag, int j, const Ops& o) {
-      constexpr bool FASTZ = decltype(fz_tag)::value;
+    auto compute = [&](int j, const Ops& o) {
       float acc = 0.0f;
-      const float dxz = ZOH && !FASTZ ? o.d * o.dx : 0.0f;   // Delta x for the phi form
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const float u2 = o.d * A2[s];
@@ -388,10 +373,8 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
         float in;
         if constexpr (!ZOH) {
           in = o.dx * o.bcv[2 * s];                       // first order: Bbar x = Delta B x
-        } else if constexpr (FASTZ) {
-          in = zoh_coef(u2, E, o.d, inv_a[s]) * (o.dx * o.bcv[2 * s]);   // c x B (o.dx is x)
         } else {
-          in = (dxz * o.bcv[2 * s]) * zoh_phi(u2, E);     // (e^u - 1)/u Delta B x
+          in = zoh_coef(u2, E, o.d, inv_a[s]) * (o.dx * o.bcv[2 * s]);   // c x B (o.dx is x)
         }
         h[s] = fmaf(E, h[s], in);
         if constexpr (!AGG) acc = (s == 0) ? o.bcv[1] * h[0] : fmaf(o.bcv[2 * s + 1], h[s], acc);
@@ -421,7 +404,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
     constexpr int NMID = (T > CKL) ? T / CKL - 1 : 1;   // checkpoint positions inside the tile
     float hmid[NMID][NS];
     constexpr int PD = NS == 1 ? 3 : (ZOH ? 1 : 2);   // tokens of LDS operands in flight ahead
-    auto sweep = [&](auto fz_tag) {
+    auto sweep = [&]() {
       Ops ring[PD + 1];
 #pragma unroll
       for (int q = 0; q < PD; ++q)
@@ -430,7 +413,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
       for (int j = 0; j < T; ++j) {
         if (FULL || j < nj) {
           if (j + PD < T && (FULL || j + PD < nj)) fetch(j + PD, ring[(j + PD) % (PD + 1)]);
-          compute(fz_tag, j, ring[j % (PD + 1)]);
+          compute(j, ring[j % (PD + 1)]);
           if constexpr (CKPT && T > CKL) {
             // the state after token ts + j enters checkpoint chunk (ts + j + 1) / CKL;
             // tiles start at multiples of T, so inside a tile the positions are
@@ -443,7 +426,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
         }
       }
     };
-    sweep(std::integral_constant<bool, ZOH && ZFAST>{});
+    sweep();
     if constexpr (AGG) {
       // The aggregate pass stores nothing per token: left free, the compiler
       // sinks its sweep below the barrier that ends the tile, keeping every LDS
@@ -560,27 +543,14 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
   }
 }
 
-template <int N, int G, int K, typename IO, bool AGG, bool ZOH, bool CKPT, bool ZFAST, bool ROWS>
+template <int N, int G, int K, typename IO, bool AGG, bool ZOH, bool CKPT, bool ROWS>
 hipError_t launch_scan_one(const ScanDims& dm, const ScanPtrs& p, hipStream_t s, int64_t nwg) {
   using E = typename IO::T;
-  hipLaunchKernelGGL((scan_kernel<N, G, K, IO, AGG, ZOH, CKPT, ZFAST, ROWS>), dim3((unsigned)nwg), dim3(64 * G), 0, s,
+  hipLaunchKernelGGL((scan_kernel<N, G, K, IO, AGG, ZOH, CKPT, ROWS>), dim3((unsigned)nwg), dim3(64 * G), 0, s,
                      dm, (const E*)p.x, (const E*)p.dt, (const E*)p.z, (const E*)p.B, (const E*)p.C, p.A, p.Dskip,
                      p.dt_bias, p.h0, p.h_in,
                      (E*)p.y, p.h_final, p.agg_h, p.agg_s, CKPT ? p.ckpt : nullptr);
   return hipGetLastError();
-}
-
-// Zero-order hold launches the kernel twice, once per form of the input term;
-// each workgroup runs in exactly one of the two.
-template <int N, int G, int K, typename IO, bool AGG, bool ZOH, bool CKPT, bool ROWS>
-hipError_t launch_scan_z(const ScanDims& dm, const ScanPtrs& p, hipStream_t s, int64_t nwg) {
-  if constexpr (ZOH) {
-    const hipError_t e = launch_scan_one<N, G, K, IO, AGG, true, CKPT, true, ROWS>(dm, p, s, nwg);
-    if (e != hipSuccess) return e;
-    return launch_scan_one<N, G, K, IO, AGG, true, CKPT, false, ROWS>(dm, p, s, nwg);
-  } else {
-    return launch_scan_one<N, G, K, IO, AGG, false, CKPT, false, ROWS>(dm, p, s, nwg);
-  }
 }
 
 // rows of at least 1 MB take the row-segment owners (bf16, two lanes per
@@ -588,9 +558,9 @@ hipError_t launch_scan_z(const ScanDims& dm, const ScanPtrs& p, hipStream_t s, i
 template <int N, int G, int K, typename IO, bool AGG, bool ZOH, bool CKPT>
 hipError_t launch_scan_r(const ScanDims& dm, const ScanPtrs& p, hipStream_t s, int64_t nwg) {
   if constexpr (K == 2 && G == 4 && sizeof(typename IO::T) == 2) {
-    if (dm.seqlen * 2 >= (int64_t(1) << 20)) return launch_scan_z<N, G, K, IO, AGG, ZOH, CKPT, true>(dm, p, s, nwg);
+    if (dm.seqlen * 2 >= (int64_t(1) << 20)) return launch_scan_one<N, G, K, IO, AGG, ZOH, CKPT, true>(dm, p, s, nwg);
   }
-  return launch_scan_z<N, G, K, IO, AGG, ZOH, CKPT, false>(dm, p, s, nwg);
+  return launch_scan_one<N, G, K, IO, AGG, ZOH, CKPT, false>(dm, p, s, nwg);
 }
 
 template <int N, int G, int K, typename IO, bool AGG, bool ZOH>
