@@ -215,20 +215,20 @@ __device__ __forceinline__ float zoh_phi(float u2, float E) {
 
 // The zero-order-hold input coefficient itself, c = (e^u - 1)/A = Delta phi(u)
 // with u = Delta A, for a caller that holds u2 = u log2(e), E = e^u, Delta and
-// inv_a = 1/A (A != 0).  For |u| >= 1/10 it is (E - 1) inv_a, with no
-// reciprocal per element: E - 1 carries E's own rounding, about 7e-8 absolute
-// below 1, so c is within 7e-7 relative there.  Below that the relative error
-// of E - 1 grows like 7e-8/|u| (E cannot hold the low bits of a small u: at
-// |u| = 1e-4 it is 7e-4), so there c = Delta (1 + u/2 + u^2/6 + u^3/24 +
-// u^4/120), the Taylor polynomial of phi in u2, whose first dropped term is
-// below 1.4e-8 relative.  Both are formed and one selected, without a branch.
+// inv_a = 1/A (A != 0).  For |u| >= 1/20 it is E inv_a - inv_a, one fma and no
+// reciprocal per element: E carries its own rounding, about 7e-8 absolute below
+// 1 (1.4e-7 above), so c is within 1.4e-6 relative there (2.9e-6 for A > 0).
+// Below that the relative error of E - 1 grows like 7e-8/|u| (E cannot hold
+// the low bits of a small u: at |u| = 1e-4 it is 7e-4), so there c = Delta (1 +
+// u/2 + u^2/6 + u^3/24), the Taylor polynomial of phi in u2, whose first
+// dropped term is below 5.3e-8 relative.  Both are formed and one selected,
+// without a branch; A = 0 (u = 0) gives c = Delta.
 __device__ __forceinline__ float zoh_coef(float u2, float E, float delta, float inv_a) {
-  float p = fmaf(u2, 0.00192362582f, 0.0138760274f);   // ln2^4/120, ln2^3/24
-  p = fmaf(p, u2, 0.0800755024f);                      // ln2^2/6
-  p = fmaf(p, u2, 0.346573591f);                       // ln2/2
+  float p = fmaf(u2, 0.0138760274f, 0.0800755024f);   // ln2^3/24, ln2^2/6
+  p = fmaf(p, u2, 0.346573591f);                      // ln2/2
   const float small = fmaf(delta * u2, p, delta);
-  const float large = (E - 1.0f) * inv_a;
-  return fabsf(u2) < 0.144269511f ? small : large;     // |u| < 1/10
+  const float large = fmaf(E, inv_a, -inv_a);
+  return fabsf(u2) < 0.0721347556f ? small : large;   // |u| < 1/20
 }
 
 // silu(z) = z / (1 + e^-z).  For z below about -88 the exponential overflows to

@@ -222,7 +222,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(3, 10)))
   for (int s = 0; s < NS; ++s) A2[s] = p.A[dc * N + sg * NS + s] * kLog2e;
   // Zero-order hold: the input coefficient c = Delta phi(Delta A) from zoh_coef,
   // as in the forward: (E - 1)/A from the E = e^(Delta A) at hand where
-  // |Delta A| >= 1/10, a Taylor polynomial below (A = 0 included), with no
+  // |Delta A| >= 1/20, a Taylor polynomial below (A = 0 included), with no
   // reciprocal per element; dc/dA = Delta^2 psi(Delta A) keeps its series and
   // closed form (its closed form in terms of c cancels digits for small
   // Delta A).

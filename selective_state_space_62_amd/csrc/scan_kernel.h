@@ -143,7 +143,7 @@ __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(K >= 2 &
   for (int s = 0; s < NS; ++s) A2[s] = A[dc * N + sg * NS + s] * kLog2e;
   // Zero-order hold: the input term c B x with c = (e^(Delta A) - 1)/A from
   // zoh_coef: (E - 1)/A from the E = e^(Delta A) already at hand where
-  // |Delta A| >= 1/10, a Taylor polynomial of Delta phi(Delta A) below (A = 0
+  // |Delta A| >= 1/20, a Taylor polynomial of Delta phi(Delta A) below (A = 0
   // included), with no reciprocal per element.
   float inv_a[ZOH ? NS : 1];
   if constexpr (ZOH) {
