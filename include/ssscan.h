@@ -254,9 +254,9 @@ ss_status ss_scan_bwd(int64_t batch, int64_t dim, int dstate, int64_t seqlen, ss
  *  SS_FLAG_ZOH         the zero-order-hold input term c = (e^(Delta A) - 1)/A
  *                      (Delta when A = 0) in place of Delta, whose derivatives
  *                      are dc/dDelta = e^(Delta A) and dc/dA = Delta^2 psi(Delta A),
- *                      psi(u) = (u e^u - e^u + 1)/u^2 (where every |A| of a
- *                      block of channels is at least 1/16, c is formed as
- *                      (e^(Delta A) - 1) * (1/A), as the forward does there);
+ *                      psi(u) = (u e^u - e^u + 1)/u^2 (c is formed as in the
+ *                      forward: (e^(Delta A) - 1)/A where |Delta A| >= 1/20, a
+ *                      Taylor polynomial of Delta phi(Delta A) below);
  *  SS_FLAG_DT_PER_ROW  dt is (batch, seqlen), and ddt, also (batch, seqlen) in the
  *                      I/O dtype, is the gradient of that shared dt, the sum over
  *                      channels of the per-channel gradient (in a fixed order).
