@@ -148,11 +148,10 @@ SMALL_U = [
 
 @pytest.mark.parametrize("what,lo,hi,both_signs", SMALL_U, ids=["small-u", "small-u-signs", "small-delta"])
 def test_zoh_scan_small_delta_a(ss, dev, what, lo, hi, both_signs):
-    """Every |A| at least 1/16, so every workgroup takes the coefficient
-    c = (e^u - 1)/A without phi's reciprocal, and every u = Delta A small
-    (Delta about 1e-3): there e^u, rounded, cannot hold u's low bits, and c must
-    still reach fp32 parity.  No skip term or gate, which would hide the state's
-    error in y."""
+    """Every u = Delta A small (Delta about 1e-3): there e^u, rounded, cannot
+    hold u's low bits, so c = (e^u - 1)/A formed as (E - 1)/A alone would miss
+    fp32 parity; the kernel's coefficient must still reach it.  No skip term or
+    gate, which would hide the state's error in y."""
     import torch
     rng = np.random.default_rng(zlib.crc32(repr(("zoh-small-u", what)).encode()))
     batch, D, N, L = 2, 128, 16, 256
