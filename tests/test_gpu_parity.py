@@ -181,6 +181,30 @@ def test_130m_layer_f32_full(ss, o, dev):
     check_state("130M-shaped h_final", hf, hr)
 
 
+def test_130m_layer_f32_zoh_full(ss, o, dev):
+    """The 130M-shaped workload with the zero-order hold (its four-lane plan),
+    checked against the oracle's expm1 form over every output.  Its Delta mostly
+    lies between 1e-3 and 1e-1, so many Delta A are small: the coefficient's
+    polynomial and its (E - 1)/A side are both exercised at full size."""
+    import torch
+    cfg = M130
+    log("130M-shaped layer, fp32, zero-order hold, full oracle check")
+    raw = inputs.scan_inputs_full(cfg)
+    A, dskip, bias = inputs.params(cfg)
+    t = {k: to_dev(v, cfg.io, dev) for k, v in raw.items()}
+    y, hf = ss.scan_fwd(t["x"], t["dt"], t["B"], t["C"], torch.from_numpy(A).to(dev), z=t["z"],
+                        Dskip=torch.from_numpy(dskip).to(dev), dt_bias=torch.from_numpy(bias).to(dev), zoh=True)
+    torch.cuda.synchronize()
+    y, hf = to_f64(y), to_f64(hf)
+    del t
+    f64 = {k: inputs.raw_to_f64(v, cfg.io) for k, v in raw.items()}
+    yr, hr = o.scan(f64["x"], f64["dt"], f64["B"], f64["C"], A, z=f64["z"], Dskip=dskip, dt_bias=bias, zoh=True)
+    chk = StrictCheck("130M-shaped y with ZOH, all %d channels" % (cfg.batch * cfg.dim), cfg.io)
+    chk.add(y.reshape(-1, cfg.seqlen), yr.reshape(-1, cfg.seqlen))
+    chk.assert_ok(tolerance(cfg), F32_CHANNEL_REL_L2)
+    check_state("130M-shaped h_final with ZOH", hf, hr)
+
+
 def _sampled_oracle(o, cfg, chans, par):
     """Oracle over sampled channels, drawn on the host; grouped by batch row."""
     A, dskip, bias = par
