@@ -222,3 +222,25 @@ def test_bwd_zoh_small_delta_a(ss, o, dev, what, lo, hi, both_signs):
     par["A"] = (sign * mag).astype(np.float32)
     g, _, _ = _run(ss, raw, par, "f32", dev)
     _compare(g, _oracle(o, f64, par), "f32", "bwd zoh, %s" % what)
+
+
+def test_bwd_zoh_130m_layer_full(ss, o, dev):
+    """The 130M-shaped layer (batch 8, D 1536, N 16, L 2048, fp32) with the
+    zero-order hold, every gradient in full against the oracle."""
+    import torch
+    from workloads import M130
+    from workloads import device as wdev
+    cfg = M130
+    t = wdev.scan_inputs(cfg, dev)
+    A, dskip, bias = wdev.params(cfg, dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(62103)
+    dy = torch.randn(t["x"].shape, generator=gen, device=dev, dtype=torch.float32)
+    dhf = torch.randn((cfg.batch, cfg.dim, cfg.dstate), generator=gen, device=dev, dtype=torch.float32)
+    g = ss.scan_bwd(t["x"], t["dt"], t["B"], t["C"], A, dy, z=t["z"], Dskip=dskip, dt_bias=bias, dh_final=dhf,
+                    zoh=True)
+    torch.cuda.synchronize()
+    f = {k: to_f64(v) for k, v in t.items()}
+    r = o.scan_bwd(f["x"], f["dt"], f["B"], f["C"], to_f64(A), to_f64(dy), z=f["z"], Dskip=to_f64(dskip),
+                   dt_bias=to_f64(bias), dh_final=to_f64(dhf), zoh=True)
+    _compare(g, r, "f32", "bwd zoh %s in full" % cfg.name)
